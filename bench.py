@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark one paged decode step on one MI355X and print one JSON line.
+
+A step is the whole hot path over one batch: ``reshape_and_cache`` writes every
+sequence's new token into its slot, then ``paged_attention_decode`` (partition kernel +
+partition-reduce kernel) attends over the paged K/V, all on one stream.  Inputs are
+seeded synthetic data built on the device before timing starts.
+
+Default workload: Llama-3-8B heads (32 query / 8 KV, head 128, bf16), 64 sequences of
+8,192 tokens, 16-token blocks scattered through a 40,960-block pool, partitions of 512.
+
+Reported next to the whole-step rate:
+* ``roofline``: algorithmic bytes of the partition kernel per launch divided by its
+  average duration, timed with HIP events recorded on the stream it runs on;
+* ``cpu_baseline``: the fp64 CPU oracle timed on a bounded sample of the same
+  workload (it checks the kernel's output on those sequences too).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0                 # MI355X HBM3E, 8 TB/s
+METRIC = "paged decode attention: seqs/s and achieved HBM GB/s (% of MI355X peak)"
+PARTITION_KERNEL = "pa_partition"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def algorithmic_bytes(lens, hq, hkv, d, elem, block_size=16):
+    """Bytes the method must move for one step (K+V of every context token, the table
+    entries and length read, Q in and O out), and the partition kernel's share."""
+    lens = np.asarray(lens, dtype=np.int64)
+    kv = int(np.sum(2 * lens * hkv * d * elem))
+    table = int(np.sum(4 * ((lens + block_size - 1) // block_size)))
+    nlen = 4 * len(lens)
+    q = len(lens) * hq * d * elem
+    o = len(lens) * hq * d * elem
+    return {"kv": kv, "table": table, "lens": nlen, "q": q, "o": o,
+            "partition_kernel": kv + table + nlen + q,
+            "write": len(lens) * (2 * hkv * d * elem * 2 + 8),
+            "step": kv + table + nlen + q + o + len(lens) * (2 * hkv * d * elem * 2 + 8)}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_68_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch of the partition kernel from committed rocprofv3 counter
+    runs (profiles/<kernel>_<workload>_traffic.json), if taken on the current source."""
+    path = os.path.join(PROFILE_DIR, f"{PARTITION_KERNEL}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(dc, budget_s: float):
+    """Time the fp64 oracle on the host on as many sequences as fit in ``budget_s``."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    cfg = dc.cfg
+    order = list(range(cfg.batch))
+    done, t_total, max_err = 0, 0.0, 0.0
+    from tests.device_case import to_host_bits   # plumbing: device bytes -> host bits
+    out_bits = to_host_bits(dc.out)
+    with threadpool_limits(limits=1):
+        for b in order:
+            kb, vb, table = dc.blocks_of(b)
+            t0 = time.perf_counter()
+            ref = oracle.paged_decode_seq(dc.case.query[b], kb, vb, table, int(dc.case.lengths[b]),
+                                          cfg.scale, cfg.block_size, cfg.dtype)
+            t_total += time.perf_counter() - t0
+            max_err = max(max_err, float(np.max(np.abs(oracle.to_f64(out_bits[b], cfg.dtype) - ref))))
+            done += 1
+            if t_total >= budget_s:
+                break
+    return {
+        "value": done / t_total,
+        "unit": "seqs/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {cfg.batch} sequences of one step (fp64 gather + softmax(qK^T)V, "
+                  f"BLAS limited to 1 thread), {t_total:.1f} s",
+        "max_abs_err_vs_gpu": max_err,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c3", help="workload: c1..c5 or a config name")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(each GPU would run its own share of sequences independently).", file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_68_amd as pk
+    from workloads import config_by_name, make_case
+    from tests.device_case import DeviceCase
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    cfg = config_by_name(args.config)
+    print(f"[bench] building {cfg.name} on the device", file=sys.stderr, flush=True)
+    case = make_case(cfg, where="device" if cfg.index in (3, 5) else "host", poison=False)
+    dc = DeviceCase(case)
+    elem = 2
+    nbytes = algorithmic_bytes(case.lengths, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, elem)
+    stream = torch.cuda.current_stream()
+
+    def step(ev_a=None, ev_b=None):
+        pk.reshape_and_cache(dc.pool, 0, dc.new_key, dc.new_value, dc.slots, stream)
+        if ev_a is not None:
+            ev_a.record(stream)
+        pk.paged_attention_partitions(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
+                                      cfg.partition_size, dc.workspace, stream)
+        if ev_b is not None:
+            ev_b.record(stream)
+        pk.paged_attention_reduce(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
+                                  cfg.partition_size, dc.workspace, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr, flush=True)
+
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev_a[i], ev_b[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    part_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
+    achieved = nbytes["partition_kernel"] / (part_ms * 1e-3) / 1e9
+    seqs_per_s = cfg.batch / (ms_step * 1e-3)
+    print(f"[bench] {ms_step * 1e3:.1f} us/step, partition kernel {part_ms * 1e3:.1f} us "
+          f"= {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+
+    traffic = load_traffic(cfg.name)
+    result = {
+        "metric": METRIC,
+        "value": seqs_per_s,
+        "unit": "seqs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "batch": cfg.batch,
+            "context_lens": "8192 each" if cfg.index == 3 else cfg.lengths,
+            "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
+            "block_size": cfg.block_size, "pool_blocks": cfg.num_blocks,
+            "partition_size": cfg.partition_size, "accumulate": "f32",
+            "step": "reshape_and_cache + paged_attention (partitions + reduce)",
+        },
+        "step_hbm_gbps": nbytes["step"] / (ms_step * 1e-3) / 1e9,
+        "step_frac_of_peak": nbytes["step"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": PARTITION_KERNEL,
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": nbytes["partition_kernel"],
+            "avg_launch_us": part_ms * 1e3,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(dc, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,205 @@
+/*
+ * pagedkv.h — C ABI of an MI355X (gfx950) paged KV-cache decode library.
+ *
+ * The library implements the hot path of PagedAttention decoding: for each sequence
+ * of a batch, one new query token attends over that sequence's keys and values,
+ * which live in fixed-size physical blocks scattered through a shared pool and are
+ * found through a per-sequence block table; a companion call writes each new
+ * token's key and value into its slot first.
+ *
+ * Sources (page title, section):
+ *  - "PagedAttention: Treating KV Memory Like Virtual Memory", "How the kernel reads
+ *    a block table": address = block_table[i / B] * block stride + (i mod B) * slot
+ *    stride; the kernel walks the history tile by tile with a running max and sum.
+ *  - "Why AI servers waste memory, and how paging fixes it", "The idea: a block
+ *    table" (position p lives in block table[p // B], slot p % B), "The real
+ *    implementation" (the append writes the token into slot `offset` of the last
+ *    block; a call that cannot succeed changes nothing), "Reading through the table"
+ *    (only the first `valid` slots of the last block are read).
+ *  - "PagedAttention and Virtual Memory Management", section 1 (M_KV closed form),
+ *    section 3 (block partitioning, physical block bytes), section 4 (Addr_K/Addr_V,
+ *    block-wise online-softmax decode, split across thread blocks with a
+ *    cross-block reduction).
+ *
+ * Conventions shared by every call
+ *  - All tensors are caller-owned device buffers (HBM of the current HIP device),
+ *    dense row-major, 16-byte aligned.  The library never allocates per call; the
+ *    only memory it may own is a pool it was asked to allocate in kv_pool_create.
+ *  - Compute calls only enqueue work on the caller's stream (0 = null stream).
+ *    There is no host synchronisation and no host read of device data.
+ *  - Every argument check runs on the host before anything is enqueued: a call that
+ *    returns an error has changed nothing.  A launch failure returns KV_ERR_HIP.
+ *  - Element type of Q, K, V and the attention output is the pool's dtype (fp16 or
+ *    bf16).  Arithmetic is fp32: 16-bit inputs are widened exactly, dot products,
+ *    softmax and the P.V accumulation are fp32, and the output is rounded to the
+ *    16-bit type with round-to-nearest-even.
+ *  - Results depend only on logical token positions: the output is bit-identical
+ *    under any relabelling of physical blocks, and run-to-run deterministic.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kv_dtype {
+    KV_DTYPE_F16 = 0,
+    KV_DTYPE_BF16 = 1
+} kv_dtype_t;
+
+typedef enum kv_status {
+    KV_OK = 0,
+    KV_ERR_INVALID_ARG = 1,    /* null pointer, negative size, layer out of range, misalignment */
+    KV_ERR_UNSUPPORTED = 2,    /* shape / dtype the kernels are not built for */
+    KV_ERR_WORKSPACE = 3,      /* workspace missing or smaller than required */
+    KV_ERR_OUT_OF_MEMORY = 4,  /* the pool allocation in kv_pool_create failed */
+    KV_ERR_HIP = 5             /* a HIP runtime call or kernel launch failed */
+} kv_status_t;
+
+/* Geometry of a KV pool.  Supported: block_size 16, head_dim 64 or 128,
+ * dtype KV_DTYPE_F16 / KV_DTYPE_BF16, num_blocks >= 1, num_kv_heads >= 1. */
+typedef struct kv_pool_desc {
+    int32_t num_layers;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;             /* kv_dtype_t */
+} kv_pool_desc_t;
+
+/* Opaque, immutable after creation: safe to use from several streams at once. */
+typedef struct kv_pool kv_pool_t;
+
+/* Human-readable name of a status code (static string). */
+const char* kv_status_string(kv_status_t status);
+
+/* Bytes of K+V per token over all layers, 2 * N_L * N_KV * d_h * b
+ * ("PagedAttention and Virtual Memory Management", section 1, M_KV(L) at L = 1).
+ * Returns 0 for an invalid or unsupported descriptor. */
+size_t kv_bytes_per_token(const kv_pool_desc_t* desc);
+
+/* Bytes of the whole pool: kv_bytes_per_token * num_blocks * block_size.
+ * Memory layout (per layer l, for K then V):
+ *   base + (2*l + 0) * S  : K cache [num_blocks][block_size][num_kv_heads][head_dim]
+ *   base + (2*l + 1) * S  : V cache, same shape
+ * with S = num_blocks * block_size * num_kv_heads * head_dim * 2 bytes.  Token row
+ * (block, offset) of one layer's K is contiguous (num_kv_heads * head_dim elements),
+ * so a whole block of one layer is one contiguous stretch.  Returns 0 if invalid. */
+size_t kv_pool_bytes(const kv_pool_desc_t* desc);
+
+/* Create a pool handle.
+ *  device_base == NULL : the library hipMallocs kv_pool_bytes(desc) bytes on the
+ *                        current device and frees them in kv_pool_destroy.
+ *  device_base != NULL : the caller's device memory is borrowed (never freed by the
+ *                        library); it must be 256-byte aligned and base_bytes must be
+ *                        >= kv_pool_bytes(desc).
+ * The pool contents are not initialised.  On error *out is left unchanged.
+ * Errors: KV_ERR_INVALID_ARG (null desc/out, bad sizes, misaligned or short base),
+ * KV_ERR_UNSUPPORTED (block_size, head_dim or dtype), KV_ERR_OUT_OF_MEMORY. */
+kv_status_t kv_pool_create(const kv_pool_desc_t* desc, void* device_base, size_t base_bytes,
+                           kv_pool_t** out);
+
+/* Destroy a handle; frees the pool memory only if the library allocated it.
+ * NULL is accepted and ignored.  The caller must ensure no enqueued work still uses it. */
+kv_status_t kv_pool_destroy(kv_pool_t* pool);
+
+/* Copy the pool's descriptor into *desc. */
+kv_status_t kv_pool_get_desc(const kv_pool_t* pool, kv_pool_desc_t* desc);
+
+/* Device addresses of layer `layer`'s K and V caches (either output may be NULL). */
+kv_status_t kv_pool_layer_ptrs(const kv_pool_t* pool, int32_t layer, void** k_cache,
+                               void** v_cache);
+
+/* Write new tokens' keys and values into their slots of layer `layer`.
+ *  key, value   : [num_tokens][num_kv_heads][head_dim], pool dtype.
+ *  slot_mapping : [num_tokens] int64, slot = physical_block * block_size + offset
+ *                 ("Why AI servers waste memory, and how paging fixes it", "The idea:
+ *                 a block table"; "2.1 PagedAttention", section 5: physical block
+ *                 number and offset).  A negative slot means "no write" (padding);
+ *                 slots >= num_blocks * block_size are also skipped.  Slots must be
+ *                 pairwise distinct; if two tokens name the same slot, which one
+ *                 lands is unspecified.
+ * The write is a bit copy.  It is ordered before later work on the same stream, so a
+ * paged_attention_decode enqueued after it on that stream reads the new tokens.
+ * num_tokens == 0 is a no-op. */
+kv_status_t reshape_and_cache(kv_pool_t* pool, int32_t layer, const void* key, const void* value,
+                              const int64_t* slot_mapping, int32_t num_tokens, hipStream_t stream);
+
+/* Workspace bytes paged_attention_decode needs for this batch shape: fp32 partial
+ * results (running max, running sum and unnormalised accumulator) of every
+ * (sequence, query head, partition).  0 when no sequence can have more than one
+ * partition (then workspace may be NULL).  partition_size 0 means 512.
+ * Returns SIZE_MAX for invalid arguments. */
+size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                       int32_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t partition_size);
+
+/* Decode attention for one layer.
+ *  out          : [batch][num_q_heads][head_dim], pool dtype (written).
+ *  query        : [batch][num_q_heads][head_dim], pool dtype.
+ *  block_tables : [batch][max_blocks_per_seq] int32; entry j of row b is the physical
+ *                 block holding tokens [16j, 16j+16) of sequence b.  Entries at or past
+ *                 ceil(context_lens[b] / 16) are never read (may hold -1).
+ *  context_lens : [batch] int32, number of tokens of each sequence, including a token
+ *                 just written by reshape_and_cache.  Values are clamped to
+ *                 [0, max_blocks_per_seq * 16]; a sequence of length 0 gets a zero
+ *                 output.  Slots at or past the length in the last block are never read.
+ *  num_q_heads  : multiple of the pool's num_kv_heads; query head h reads KV head
+ *                 h / (num_q_heads / num_kv_heads) (contiguous GQA groups); group
+ *                 sizes 1..8 are supported.
+ *  scale        : multiplies q.k before the softmax (normally 1/sqrt(head_dim)).
+ *  partition_size: tokens per split-context partition (multiple of 16; 0 = 512).  A
+ *                 sequence longer than one partition is split across work-groups
+ *                 whose partial results are combined by a second kernel
+ *                 ("PagedAttention and Virtual Memory Management", section 4,
+ *                 cross-block reduction).
+ *  workspace    : >= paged_attention_workspace_bytes(...) bytes of device memory,
+ *                 16-byte aligned; contents on entry do not matter.
+ * Table entries outside [0, num_blocks) for blocks a sequence uses are skipped (the
+ * output is then meaningless but no memory outside the pool is read).
+ * Errors: KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED (group size), KV_ERR_WORKSPACE,
+ * KV_ERR_HIP.  batch == 0 is a no-op. */
+kv_status_t paged_attention_decode(const kv_pool_t* pool, int32_t layer, void* out,
+                                   const void* query, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t batch, int32_t num_q_heads, float scale,
+                                   int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/* The two phases of paged_attention_decode, for callers that time or schedule them
+ * separately; same arguments.  paged_attention_partitions writes the partial results
+ * of every partition (and the final output of sequences that fit in one partition);
+ * paged_attention_reduce combines the partials of the other sequences into `out`.
+ * Enqueueing partitions then reduce on one stream is exactly paged_attention_decode. */
+kv_status_t paged_attention_partitions(const kv_pool_t* pool, int32_t layer, void* out,
+                                       const void* query, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                       int32_t batch, int32_t num_q_heads, float scale,
+                                       int32_t partition_size, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* out,
+                                   const void* query, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t batch, int32_t num_q_heads, float scale,
+                                   int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/* Test hook: copy each sequence's K and V, through its block table, into contiguous
+ * buffers ("Why AI servers waste memory, and how paging fixes it", "Reading through
+ * the table").  k_out, v_out: [batch][max_blocks_per_seq * 16][num_kv_heads][head_dim];
+ * row t of sequence b is the pool row (table[b][t / 16], t % 16) for t < context_lens[b]
+ * and zero otherwise.  Bit copy. */
+kv_status_t kv_pool_gather(const kv_pool_t* pool, int32_t layer, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t batch, void* k_out, void* v_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

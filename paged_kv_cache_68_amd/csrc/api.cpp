@@ -1,0 +1,326 @@
+// C ABI of the paged decode library: argument checks (host only, before anything is
+// enqueued), pool bookkeeping and kernel dispatch.  See include/pagedkv.h.
+
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include <hip/hip_runtime_api.h>
+
+#include "internal.h"
+
+using pkv::ceil_div;
+
+namespace {
+
+constexpr size_t kAlign = 16;
+
+bool aligned(const void* p, size_t a = kAlign) {
+    return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+kv_status_t check_desc(const kv_pool_desc_t* d) {
+    if (!d) return KV_ERR_INVALID_ARG;
+    if (d->num_layers < 1 || d->num_blocks < 1 || d->num_kv_heads < 1 || d->block_size < 1 ||
+        d->head_dim < 1)
+        return KV_ERR_INVALID_ARG;
+    if (d->block_size != pkv::kBlockSize) return KV_ERR_UNSUPPORTED;
+    if (d->head_dim != 64 && d->head_dim != 128) return KV_ERR_UNSUPPORTED;
+    if (d->dtype != KV_DTYPE_F16 && d->dtype != KV_DTYPE_BF16) return KV_ERR_UNSUPPORTED;
+    // a layer's cache must be addressable with 64-bit offsets and the slot count with int64
+    const unsigned __int128 bytes = static_cast<unsigned __int128>(d->num_blocks) * d->block_size *
+                                    d->num_kv_heads * d->head_dim * 2u * 2u * d->num_layers;
+    if (bytes >> 62) return KV_ERR_INVALID_ARG;
+    return KV_OK;
+}
+
+size_t cache_bytes(const kv_pool_desc_t* d) {
+    return static_cast<size_t>(d->num_blocks) * d->block_size * d->num_kv_heads * d->head_dim * 2u;
+}
+
+struct DecodeShape {
+    int32_t group = 0;
+    int32_t part_blocks = 0;
+    int32_t num_parts = 0;
+    size_t ws_needed = 0;
+};
+
+size_t workspace_for(int32_t batch, int32_t hq, int32_t d, int32_t num_parts) {
+    if (num_parts <= 1) return 0;
+    const size_t n = static_cast<size_t>(batch) * hq * num_parts;
+    const size_t acc = n * d * sizeof(float);
+    const size_t ml = n * 2 * sizeof(float);
+    return ((acc + 255) / 256) * 256 + ml;
+}
+
+kv_status_t check_decode(const kv_pool_t* pool, int32_t layer, void* out, const void* query,
+                         const int32_t* block_tables, int32_t max_blocks,
+                         const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                         float scale, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, DecodeShape* shape) {
+    if (!pool) return KV_ERR_INVALID_ARG;
+    const kv_pool_desc_t& d = pool->desc;
+    if (layer < 0 || layer >= d.num_layers) return KV_ERR_INVALID_ARG;
+    if (batch < 0) return KV_ERR_INVALID_ARG;
+    if (num_q_heads < 1) return KV_ERR_INVALID_ARG;
+    if (num_q_heads % d.num_kv_heads != 0) return KV_ERR_UNSUPPORTED;
+    const int32_t group = num_q_heads / d.num_kv_heads;
+    if (group > pkv::kMaxGroup) return KV_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return KV_ERR_INVALID_ARG;     // NaN scale
+    if (partition_size == 0) partition_size = pkv::kDefaultPartition;
+    if (partition_size < d.block_size || partition_size % d.block_size != 0)
+        return KV_ERR_INVALID_ARG;
+    if (batch == 0) {
+        shape->group = group;
+        return KV_OK;
+    }
+    if (max_blocks < 1) return KV_ERR_INVALID_ARG;
+    if (!out || !query || !block_tables || !context_lens) return KV_ERR_INVALID_ARG;
+    if (!aligned(out) || !aligned(query) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return KV_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(max_blocks) * d.block_size > INT32_MAX) return KV_ERR_INVALID_ARG;
+    const int32_t part_blocks = partition_size / d.block_size;
+    const int32_t num_parts = static_cast<int32_t>(ceil_div(max_blocks, part_blocks));
+    if (static_cast<int64_t>(batch) * d.num_kv_heads * num_parts > INT32_MAX)
+        return KV_ERR_INVALID_ARG;
+    const size_t need = workspace_for(batch, num_q_heads, d.head_dim, num_parts);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return KV_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return KV_ERR_INVALID_ARG;
+    }
+    shape->group = group;
+    shape->part_blocks = part_blocks;
+    shape->num_parts = num_parts;
+    shape->ws_needed = need;
+    return KV_OK;
+}
+
+pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const void* query,
+                          const int32_t* block_tables, int32_t max_blocks,
+                          const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                          float scale, void* workspace, const DecodeShape& s) {
+    const kv_pool_desc_t& d = pool->desc;
+    pkv::DecodeArgs a;
+    char* kc = pool->base + static_cast<size_t>(2 * layer) * pool->cache_bytes;
+    a.q = static_cast<const uint16_t*>(query);
+    a.k = reinterpret_cast<const uint16_t*>(kc);
+    a.v = reinterpret_cast<const uint16_t*>(kc + pool->cache_bytes);
+    a.tables = block_tables;
+    a.lens = context_lens;
+    a.out = static_cast<uint16_t*>(out);
+    const size_t n = static_cast<size_t>(batch) * num_q_heads * s.num_parts;
+    a.ws_acc = static_cast<float*>(workspace);
+    a.ws_ml = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                   ((n * d.head_dim * sizeof(float) + 255) / 256) * 256)
+                        : nullptr;
+    a.batch = batch;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = d.num_kv_heads;
+    a.max_blocks = max_blocks;
+    a.num_blocks = d.num_blocks;
+    a.part_blocks = s.part_blocks;
+    a.num_parts = s.num_parts;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return a;
+}
+
+enum Phase { kBoth = 3, kPartitions = 1, kReduce = 2 };
+
+kv_status_t decode_impl(int phases, const kv_pool_t* pool, int32_t layer, void* out,
+                        const void* query, const int32_t* block_tables, int32_t max_blocks,
+                        const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                        float scale, int32_t partition_size, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    DecodeShape s;
+    kv_status_t st = check_decode(pool, layer, out, query, block_tables, max_blocks, context_lens,
+                                  batch, num_q_heads, scale, partition_size, workspace,
+                                  workspace_bytes, &s);
+    if (st != KV_OK) return st;
+    if (batch == 0) return KV_OK;
+    const pkv::DecodeArgs a = make_args(pool, layer, out, query, block_tables, max_blocks,
+                                        context_lens, batch, num_q_heads, scale, workspace, s);
+    if (phases & kPartitions) {
+        if (pkv::launch_partitions(pool->desc.dtype, pool->desc.head_dim, s.group, a, stream) !=
+            hipSuccess)
+            return KV_ERR_HIP;
+    }
+    if ((phases & kReduce) && s.num_parts > 1) {
+        if (pkv::launch_reduce(pool->desc.dtype, pool->desc.head_dim, a, stream) != hipSuccess)
+            return KV_ERR_HIP;
+    }
+    return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kv_status_string(kv_status_t status) {
+    switch (status) {
+        case KV_OK: return "ok";
+        case KV_ERR_INVALID_ARG: return "invalid argument";
+        case KV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case KV_ERR_WORKSPACE: return "workspace missing or too small";
+        case KV_ERR_OUT_OF_MEMORY: return "out of device memory";
+        case KV_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t kv_bytes_per_token(const kv_pool_desc_t* desc) {
+    if (check_desc(desc) != KV_OK) return 0;
+    return 2u * static_cast<size_t>(desc->num_layers) * desc->num_kv_heads * desc->head_dim * 2u;
+}
+
+size_t kv_pool_bytes(const kv_pool_desc_t* desc) {
+    if (check_desc(desc) != KV_OK) return 0;
+    return kv_bytes_per_token(desc) * static_cast<size_t>(desc->num_blocks) * desc->block_size;
+}
+
+kv_status_t kv_pool_create(const kv_pool_desc_t* desc, void* device_base, size_t base_bytes,
+                           kv_pool_t** out) {
+    if (!out) return KV_ERR_INVALID_ARG;
+    const kv_status_t st = check_desc(desc);
+    if (st != KV_OK) return st;
+    const size_t need = kv_pool_bytes(desc);
+    if (device_base) {
+        if (!aligned(device_base, 256) || base_bytes < need) return KV_ERR_INVALID_ARG;
+    }
+    kv_pool_t* p = new (std::nothrow) kv_pool_t;
+    if (!p) return KV_ERR_OUT_OF_MEMORY;
+    p->desc = *desc;
+    p->cache_bytes = cache_bytes(desc);
+    p->owned = 0;
+    p->device = -1;
+    if (hipGetDevice(&p->device) != hipSuccess) {
+        (void)hipGetLastError();
+        p->device = -1;
+        if (!device_base) {      // allocation needs a device
+            delete p;
+            return KV_ERR_HIP;
+        }
+    }
+    if (device_base) {
+        p->base = static_cast<char*>(device_base);
+    } else {
+        void* mem = nullptr;
+        if (hipMalloc(&mem, need) != hipSuccess || !mem) {
+            (void)hipGetLastError();
+            delete p;
+            return KV_ERR_OUT_OF_MEMORY;
+        }
+        p->base = static_cast<char*>(mem);
+        p->owned = 1;
+    }
+    *out = p;
+    return KV_OK;
+}
+
+kv_status_t kv_pool_destroy(kv_pool_t* pool) {
+    if (!pool) return KV_OK;
+    kv_status_t st = KV_OK;
+    if (pool->owned && hipFree(pool->base) != hipSuccess) st = KV_ERR_HIP;
+    delete pool;
+    return st;
+}
+
+kv_status_t kv_pool_get_desc(const kv_pool_t* pool, kv_pool_desc_t* desc) {
+    if (!pool || !desc) return KV_ERR_INVALID_ARG;
+    *desc = pool->desc;
+    return KV_OK;
+}
+
+kv_status_t kv_pool_layer_ptrs(const kv_pool_t* pool, int32_t layer, void** k_cache,
+                               void** v_cache) {
+    if (!pool || layer < 0 || layer >= pool->desc.num_layers) return KV_ERR_INVALID_ARG;
+    char* kc = pool->base + static_cast<size_t>(2 * layer) * pool->cache_bytes;
+    if (k_cache) *k_cache = kc;
+    if (v_cache) *v_cache = kc + pool->cache_bytes;
+    return KV_OK;
+}
+
+kv_status_t reshape_and_cache(kv_pool_t* pool, int32_t layer, const void* key, const void* value,
+                              const int64_t* slot_mapping, int32_t num_tokens, hipStream_t stream) {
+    if (!pool || layer < 0 || layer >= pool->desc.num_layers || num_tokens < 0)
+        return KV_ERR_INVALID_ARG;
+    if (num_tokens == 0) return KV_OK;
+    if (!key || !value || !slot_mapping) return KV_ERR_INVALID_ARG;
+    if (!aligned(key) || !aligned(value) || !aligned(slot_mapping, 8)) return KV_ERR_INVALID_ARG;
+    const kv_pool_desc_t& d = pool->desc;
+    char* kc = pool->base + static_cast<size_t>(2 * layer) * pool->cache_bytes;
+    const int64_t num_slots = static_cast<int64_t>(d.num_blocks) * d.block_size;
+    const hipError_t e = pkv::launch_reshape_and_cache(
+        static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value), slot_mapping,
+        num_tokens, reinterpret_cast<uint16_t*>(kc),
+        reinterpret_cast<uint16_t*>(kc + pool->cache_bytes), num_slots,
+        d.num_kv_heads * d.head_dim, stream);
+    return e == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                       int32_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t partition_size) {
+    if (batch < 0 || num_q_heads < 1 || head_dim < 1 || max_blocks_per_seq < 1 ||
+        block_size != pkv::kBlockSize)
+        return SIZE_MAX;
+    if (partition_size == 0) partition_size = pkv::kDefaultPartition;
+    if (partition_size < block_size || partition_size % block_size != 0) return SIZE_MAX;
+    const int32_t parts = static_cast<int32_t>(ceil_div(max_blocks_per_seq, partition_size / block_size));
+    return workspace_for(batch, num_q_heads, head_dim, parts);
+}
+
+kv_status_t paged_attention_decode(const kv_pool_t* pool, int32_t layer, void* out,
+                                   const void* query, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t batch, int32_t num_q_heads, float scale,
+                                   int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    return decode_impl(kBoth, pool, layer, out, query, block_tables, max_blocks_per_seq,
+                       context_lens, batch, num_q_heads, scale, partition_size, workspace,
+                       workspace_bytes, stream);
+}
+
+kv_status_t paged_attention_partitions(const kv_pool_t* pool, int32_t layer, void* out,
+                                       const void* query, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                       int32_t batch, int32_t num_q_heads, float scale,
+                                       int32_t partition_size, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    return decode_impl(kPartitions, pool, layer, out, query, block_tables, max_blocks_per_seq,
+                       context_lens, batch, num_q_heads, scale, partition_size, workspace,
+                       workspace_bytes, stream);
+}
+
+kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* out,
+                                   const void* query, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t batch, int32_t num_q_heads, float scale,
+                                   int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    return decode_impl(kReduce, pool, layer, out, query, block_tables, max_blocks_per_seq,
+                       context_lens, batch, num_q_heads, scale, partition_size, workspace,
+                       workspace_bytes, stream);
+}
+
+kv_status_t kv_pool_gather(const kv_pool_t* pool, int32_t layer, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t batch, void* k_out, void* v_out, hipStream_t stream) {
+    if (!pool || layer < 0 || layer >= pool->desc.num_layers || batch < 0) return KV_ERR_INVALID_ARG;
+    if (batch == 0) return KV_OK;
+    if (max_blocks_per_seq < 1 || batch > 65535 || max_blocks_per_seq > 0x7fffffff / pkv::kBlockSize)
+        return KV_ERR_INVALID_ARG;
+    if (!block_tables || !context_lens || !k_out || !v_out) return KV_ERR_INVALID_ARG;
+    if (!aligned(k_out) || !aligned(v_out) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+        return KV_ERR_INVALID_ARG;
+    const kv_pool_desc_t& d = pool->desc;
+    const char* kc = pool->base + static_cast<size_t>(2 * layer) * pool->cache_bytes;
+    const hipError_t e = pkv::launch_gather(
+        reinterpret_cast<const uint16_t*>(kc), reinterpret_cast<const uint16_t*>(kc + pool->cache_bytes),
+        block_tables, max_blocks_per_seq, context_lens, batch, d.num_blocks,
+        d.num_kv_heads * d.head_dim, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out),
+        stream);
+    return e == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+}  // extern "C"

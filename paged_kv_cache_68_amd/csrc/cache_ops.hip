@@ -1,0 +1,91 @@
+// Cache write (reshape_and_cache) and the gather test hook, for gfx950.
+//
+// With the pool laid out [num_blocks][16][Hkv][D], slot = block * 16 + offset is
+// directly the index of a contiguous token row of Hkv*D elements, so the write of
+// "Why AI servers waste memory, and how paging fixes it" ("The real implementation":
+// the token lands in slot `offset` of block table[-1]) is a row copy to row `slot`.
+// Both kernels are pure bit copies with 16-byte (dwordx4) accesses.
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+
+namespace pkv {
+namespace {
+
+// One work-group per new token; lanes stride over the 16-byte chunks of the row.
+__global__ __launch_bounds__(256) void rc_scatter(const uint4* __restrict__ key,
+                                                  const uint4* __restrict__ value,
+                                                  const int64_t* __restrict__ slots,
+                                                  uint4* __restrict__ k_cache,
+                                                  uint4* __restrict__ v_cache, int64_t num_slots,
+                                                  int32_t row_chunks) {
+    const int64_t i = blockIdx.x;
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= num_slots) return;     // padding / out of range: no write
+    const uint4* ks = key + i * row_chunks;
+    const uint4* vs = value + i * row_chunks;
+    uint4* kd = k_cache + slot * row_chunks;
+    uint4* vd = v_cache + slot * row_chunks;
+    for (int32_t ch = threadIdx.x; ch < row_chunks; ch += blockDim.x) {
+        kd[ch] = ks[ch];
+        vd[ch] = vs[ch];
+    }
+}
+
+// One work-group per (table entry j, sequence b): the 16 rows of logical block j.
+__global__ __launch_bounds__(256) void kv_gather(const uint4* __restrict__ k_cache,
+                                                 const uint4* __restrict__ v_cache,
+                                                 const int32_t* __restrict__ tables,
+                                                 int32_t max_blocks,
+                                                 const int32_t* __restrict__ lens,
+                                                 int32_t num_blocks, int32_t row_chunks,
+                                                 uint4* __restrict__ k_out,
+                                                 uint4* __restrict__ v_out) {
+    const int j = blockIdx.x;
+    const int b = blockIdx.y;
+    int L = lens[b];
+    L = L < 0 ? 0 : (L > max_blocks * kBlockSize ? max_blocks * kBlockSize : L);
+    const int valid = min(kBlockSize, max(0, L - j * kBlockSize));
+    int blk = valid > 0 ? tables[static_cast<size_t>(b) * max_blocks + j] : -1;
+    const bool ok = static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks);
+    const size_t dst0 = (static_cast<size_t>(b) * max_blocks * kBlockSize + static_cast<size_t>(j) * kBlockSize) * row_chunks;
+    const size_t src0 = ok ? static_cast<size_t>(blk) * kBlockSize * row_chunks : 0;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    for (int idx = threadIdx.x; idx < kBlockSize * row_chunks; idx += blockDim.x) {
+        const int t = idx / row_chunks;
+        const bool take = ok && t < valid;
+        k_out[dst0 + idx] = take ? k_cache[src0 + idx] : zero;
+        v_out[dst0 + idx] = take ? v_cache[src0 + idx] : zero;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const uint16_t* key, const uint16_t* value,
+                                    const int64_t* slots, int32_t num_tokens, uint16_t* k_cache,
+                                    uint16_t* v_cache, int64_t num_slots, int32_t row_elems,
+                                    hipStream_t stream) {
+    if (num_tokens <= 0) return hipSuccess;
+    const int32_t chunks = row_elems / 8;
+    const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
+    hipLaunchKernelGGL(rc_scatter, dim3(num_tokens), dim3(threads), 0, stream,
+                       reinterpret_cast<const uint4*>(key), reinterpret_cast<const uint4*>(value),
+                       slots, reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache),
+                       num_slots, chunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* tables,
+                         int32_t max_blocks, const int32_t* lens, int32_t batch,
+                         int32_t num_blocks, int32_t row_elems, uint16_t* k_out, uint16_t* v_out,
+                         hipStream_t stream) {
+    if (batch <= 0 || max_blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kv_gather, dim3(max_blocks, batch), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4*>(k_cache), reinterpret_cast<const uint4*>(v_cache),
+                       tables, max_blocks, lens, num_blocks, row_elems / 8,
+                       reinterpret_cast<uint4*>(k_out), reinterpret_cast<uint4*>(v_out));
+    return hipGetLastError();
+}
+
+}  // namespace pkv

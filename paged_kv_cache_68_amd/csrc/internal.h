@@ -1,0 +1,60 @@
+// Internal declarations shared by the C ABI (api.cpp) and the HIP kernel files.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "pagedkv.h"
+
+struct kv_pool {
+    kv_pool_desc_t desc;
+    char* base;          // device address of layer 0's K cache
+    int owned;           // 1 if the library allocated `base`
+    int device;          // HIP device the pool lives on
+    size_t cache_bytes;  // bytes of one layer's K (or V) cache
+};
+
+namespace pkv {
+
+constexpr int kBlockSize = 16;          // tokens per physical block
+constexpr int kDefaultPartition = 512;  // tokens per split-context partition
+constexpr int kMaxGroup = 8;            // largest supported GQA group
+constexpr int kWavesPerGroup = 4;       // waves per work-group of the partition kernel
+
+// Everything the two decode kernels read; passed by value.
+struct DecodeArgs {
+    const uint16_t* q;       // [B][Hq][D]
+    const uint16_t* k;       // [nb][16][Hkv][D]
+    const uint16_t* v;
+    const int32_t* tables;   // [B][max_blocks]
+    const int32_t* lens;     // [B]
+    uint16_t* out;           // [B][Hq][D]
+    float* ws_acc;           // [B][Hq][P][D]   unnormalised accumulators
+    float* ws_ml;            // [B][Hq][P][2]   (running max in log2 units, running sum)
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t max_blocks;      // table row length
+    int32_t num_blocks;      // blocks in the pool
+    int32_t part_blocks;     // blocks per partition
+    int32_t num_parts;       // partitions of the longest possible sequence
+    float scale_log2;        // scale * log2(e): scores are kept in base-2 units
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+hipError_t launch_partitions(int dtype, int head_dim, int group, const DecodeArgs& a,
+                             hipStream_t stream);
+hipError_t launch_reduce(int dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_reshape_and_cache(const uint16_t* key, const uint16_t* value,
+                                    const int64_t* slots, int32_t num_tokens, uint16_t* k_cache,
+                                    uint16_t* v_cache, int64_t num_slots, int32_t row_elems,
+                                    hipStream_t stream);
+hipError_t launch_gather(const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* tables,
+                         int32_t max_blocks, const int32_t* lens, int32_t batch,
+                         int32_t num_blocks, int32_t row_elems, uint16_t* k_out, uint16_t* v_out,
+                         hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,347 @@
+// Paged decode attention for gfx950: the partition kernel (block-table gather, q.K^T,
+// online softmax, P.V in fp32) and the cross-partition reduce kernel.
+//
+// Method: "PagedAttention and Virtual Memory Management", section 4 (block-wise
+// decode with a running max / running sum, and the split across thread blocks whose
+// partial (m, l, O) are combined by a second kernel); "PagedAttention: Treating KV
+// Memory Like Virtual Memory", "How the kernel reads a block table" (one table lookup
+// per block, a tile never straddles two blocks); "Why AI servers waste memory, and
+// how paging fixes it", "Reading through the table" (only the first `valid` slots of
+// the last block are read).
+//
+// Work decomposition.  One work-group of 4 waves owns (sequence b, KV head, partition
+// p).  The partition's blocks are dealt to the waves round-robin.  Inside a wave a
+// 16-token block of one KV head is read with dwordx4 loads: each lane holds 8
+// consecutive elements of one token row, LPT = D/8 lanes cover a row and the wave
+// covers TPI = 64/LPT tokens per load, so a block takes NI = 16/TPI loads of K and NI
+// of V, each of them TPI whole rows.  q.k is v_dot2_f32_{f16,bf16} over the lane's 8
+// elements followed by a DPP sum over the LPT lanes of the row.  Each row of lanes
+// keeps its own running max / sum / accumulator over the tokens it sees (an online
+// softmax per row); rows, then waves, are merged with the cross-block rule at the end.
+// Every reduction order depends only on logical positions, so the result is
+// deterministic and independent of where blocks sit in the pool.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "device_common.h"
+
+namespace pkv {
+namespace {
+
+template <class S, int D, int G>
+__global__ __launch_bounds__(256) void pa_partition_valu(DecodeArgs a) {
+    constexpr int LPT = D / 8;       // lanes per token row
+    constexpr int TPI = 64 / LPT;    // token rows per wave load
+    constexpr int NI = 16 / TPI;     // loads per block per tensor
+    constexpr int W = kWavesPerGroup;
+
+    __shared__ float sm_ml[W][G][2];
+    __shared__ float sm_acc[W][G][D];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r = lane / LPT;        // token row inside a load
+    const int c = lane % LPT;        // 8-element chunk of the row
+
+    const int item = xcd_order(blockIdx.x, gridDim.x);
+    const int kvh = item % a.num_kv_heads;
+    const int rest = item / a.num_kv_heads;
+    const int b = rest % a.batch;
+    const int p = rest / a.batch;
+
+    int L = a.lens[b];
+    L = L < 0 ? 0 : (L > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : L);
+    const int nblk = (L + kBlockSize - 1) / kBlockSize;
+    const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
+    const int h0 = kvh * G;
+    const size_t out_row0 = (static_cast<size_t>(b) * a.num_q_heads + h0) * D;
+
+    if (L == 0) {
+        if (p == 0)
+            for (int i = threadIdx.x; i < G * D; i += blockDim.x) a.out[out_row0 + i] = 0;
+        return;
+    }
+    if (p >= nparts) return;
+    const int j0 = p * a.part_blocks;
+    const int j1 = min(nblk, j0 + a.part_blocks);
+
+    uint4 qv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        qv[g] = *reinterpret_cast<const uint4*>(a.q + out_row0 + static_cast<size_t>(g) * D + c * 8);
+
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+    }
+
+    const size_t row = static_cast<size_t>(a.num_kv_heads) * D;   // elements per token row
+    const size_t blk_elems = row * kBlockSize;
+    const uint16_t* kbase = a.k + static_cast<size_t>(kvh) * D + r * row + c * 8;
+    const uint16_t* vbase = a.v + static_cast<size_t>(kvh) * D + r * row + c * 8;
+    const int32_t* trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
+
+    uint4 kn[NI], vn[NI];
+    int j = j0 + wave;
+    int blk_next = 0;
+    bool ok_next = false;
+    if (j < j1) {
+        const int t = trow[j];
+        ok_next = static_cast<unsigned>(t) < static_cast<unsigned>(a.num_blocks);
+        blk_next = ok_next ? t : 0;
+        const uint16_t* kp = kbase + static_cast<size_t>(blk_next) * blk_elems;
+        const uint16_t* vp = vbase + static_cast<size_t>(blk_next) * blk_elems;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) kn[i] = *reinterpret_cast<const uint4*>(kp + i * TPI * row);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) vn[i] = *reinterpret_cast<const uint4*>(vp + i * TPI * row);
+    }
+
+    for (; j < j1; j += W) {
+        uint4 kc[NI], vc[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            kc[i] = kn[i];
+            vc[i] = vn[i];
+        }
+        const bool ok = ok_next;
+        // prefetch the wave's next block while this one is computed
+        const int jn = j + W;
+        if (jn < j1) {
+            const int t = trow[jn];
+            ok_next = static_cast<unsigned>(t) < static_cast<unsigned>(a.num_blocks);
+            blk_next = ok_next ? t : 0;
+            const uint16_t* kp = kbase + static_cast<size_t>(blk_next) * blk_elems;
+            const uint16_t* vp = vbase + static_cast<size_t>(blk_next) * blk_elems;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) kn[i] = *reinterpret_cast<const uint4*>(kp + i * TPI * row);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) vn[i] = *reinterpret_cast<const uint4*>(vp + i * TPI * row);
+        }
+        const int valid = ok ? min(kBlockSize, L - j * kBlockSize) : 0;
+
+        // scores of this row's NI tokens for the G heads (base-2 units)
+        float s[NI][G];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float t = S::dot2(qv[g].x, kc[i].x, 0.f);
+                t = S::dot2(qv[g].y, kc[i].y, t);
+                t = S::dot2(qv[g].z, kc[i].z, t);
+                t = S::dot2(qv[g].w, kc[i].w, t);
+                s[i][g] = group_sum<LPT>(t);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const bool tok_ok = (i * TPI + r) < valid;
+#pragma unroll
+            for (int g = 0; g < G; ++g) s[i][g] = tok_ok ? s[i][g] * a.scale_log2 : -INFINITY;
+        }
+
+        float pw[NI][G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float mb = s[0][g];
+#pragma unroll
+            for (int i = 1; i < NI; ++i) mb = fmaxf(mb, s[i][g]);
+            const float mn = fmaxf(m[g], mb);
+            const float mu = (mn == -INFINITY) ? 0.f : mn;
+            const float alpha = fast_exp2(m[g] - mu);
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                pw[i][g] = fast_exp2(s[i][g] - mu);
+                sum += pw[i][g];
+            }
+            l[g] = l[g] * alpha + sum;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
+            m[g] = mn;
+        }
+
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const bool tok_ok = (i * TPI + r) < valid;
+            const uint32_t w4[4] = {vc[i].x, vc[i].y, vc[i].z, vc[i].w};
+            float vf[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vf[2 * e] = tok_ok ? S::lo(w4[e]) : 0.f;
+                vf[2 * e + 1] = tok_ok ? S::hi(w4[e]) : 0.f;
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw[i][g], vf[e], acc[g][e]);
+        }
+    }
+
+    // merge the TPI rows of this wave (lanes with equal c)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float M = m[g];
+#pragma unroll
+        for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+        const float f = (M == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
+        float lt = l[g] * f;
+#pragma unroll
+        for (int off = LPT; off < 64; off <<= 1) lt += __shfl_xor(lt, off);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float t = acc[g][e] * f;
+#pragma unroll
+            for (int off = LPT; off < 64; off <<= 1) t += __shfl_xor(t, off);
+            acc[g][e] = t;
+        }
+        m[g] = M;
+        l[g] = lt;
+    }
+    if (r == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm_acc[wave][g][c * 8 + e] = acc[g][e];
+        if (c == 0)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                sm_ml[wave][g][0] = m[g];
+                sm_ml[wave][g][1] = l[g];
+            }
+    }
+    __syncthreads();
+
+    // merge the waves and write the partition's result
+    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+        const int g = idx / D;
+        const int dd = idx % D;
+        float M = sm_ml[0][g][0];
+#pragma unroll
+        for (int w = 1; w < W; ++w) M = fmaxf(M, sm_ml[w][g][0]);
+        float lsum = 0.f, A = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float f = (M == -INFINITY) ? 0.f : fast_exp2(sm_ml[w][g][0] - M);
+            lsum += f * sm_ml[w][g][1];
+            A += f * sm_acc[w][g][dd];
+        }
+        if (nparts == 1) {
+            a.out[out_row0 + idx] = S::narrow(lsum > 0.f ? A / lsum : 0.f);
+        } else {
+            const size_t ph = (static_cast<size_t>(b) * a.num_q_heads + h0 + g) * a.num_parts + p;
+            a.ws_acc[ph * D + dd] = A;
+            if (dd == 0) {
+                a.ws_ml[ph * 2 + 0] = M;
+                a.ws_ml[ph * 2 + 1] = lsum;
+            }
+        }
+    }
+}
+
+// One wave per (sequence, query head): combine the sequence's partitions in
+// ascending order, O = sum_k w_k acc_k / sum_k w_k l_k with w_k = 2^(m_k - max m).
+template <class S, int D>
+__global__ __launch_bounds__(256) void pa_reduce(DecodeArgs a) {
+    constexpr int PER = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (pair >= a.batch * a.num_q_heads) return;
+    const int b = pair / a.num_q_heads;
+    const int h = pair % a.num_q_heads;
+    int L = a.lens[b];
+    L = L < 0 ? 0 : (L > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : L);
+    const int nblk = (L + kBlockSize - 1) / kBlockSize;
+    const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
+    if (nparts <= 1) return;
+
+    const size_t ph0 = (static_cast<size_t>(b) * a.num_q_heads + h) * a.num_parts;
+    const float* ml = a.ws_ml + ph0 * 2;
+    const float* acc = a.ws_acc + ph0 * D;
+
+    float M = -INFINITY;
+    for (int k = lane; k < nparts; k += 64) M = fmaxf(M, ml[2 * k]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+    float A[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) A[e] = 0.f;
+    float lsum = 0.f;
+    for (int k = 0; k < nparts; ++k) {
+        const float w = (M == -INFINITY) ? 0.f : fast_exp2(ml[2 * k] - M);
+        lsum += w * ml[2 * k + 1];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) A[e] += w * acc[static_cast<size_t>(k) * D + lane + 64 * e];
+    }
+    uint16_t* o = a.out + (static_cast<size_t>(b) * a.num_q_heads + h) * D;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[lane + 64 * e] = S::narrow(lsum > 0.f ? A[e] / lsum : 0.f);
+}
+
+template <class S, int D, int G>
+hipError_t launch_part_t(const DecodeArgs& a, hipStream_t stream) {
+    const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.num_parts;
+    if (items <= 0) return hipSuccess;
+    if (items > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((pa_partition_valu<S, D, G>), dim3(static_cast<unsigned>(items)),
+                       dim3(64 * kWavesPerGroup), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class S, int D>
+hipError_t launch_part_g(int group, const DecodeArgs& a, hipStream_t stream) {
+    switch (group) {
+        case 1: return launch_part_t<S, D, 1>(a, stream);
+        case 2: return launch_part_t<S, D, 2>(a, stream);
+        case 3: return launch_part_t<S, D, 3>(a, stream);
+        case 4: return launch_part_t<S, D, 4>(a, stream);
+        case 5: return launch_part_t<S, D, 5>(a, stream);
+        case 6: return launch_part_t<S, D, 6>(a, stream);
+        case 7: return launch_part_t<S, D, 7>(a, stream);
+        case 8: return launch_part_t<S, D, 8>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <class S, int D>
+hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t stream) {
+    const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
+    if (pairs <= 0 || a.num_parts <= 1) return hipSuccess;
+    const int64_t groups = (pairs + 3) / 4;
+    if (groups > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((pa_reduce<S, D>), dim3(static_cast<unsigned>(groups)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_partitions(int dtype, int head_dim, int group, const DecodeArgs& a,
+                             hipStream_t stream) {
+    if (dtype == KV_DTYPE_F16) {
+        if (head_dim == 64) return launch_part_g<F16, 64>(group, a, stream);
+        if (head_dim == 128) return launch_part_g<F16, 128>(group, a, stream);
+    } else if (dtype == KV_DTYPE_BF16) {
+        if (head_dim == 64) return launch_part_g<BF16, 64>(group, a, stream);
+        if (head_dim == 128) return launch_part_g<BF16, 128>(group, a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_reduce(int dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
+    if (dtype == KV_DTYPE_F16) {
+        if (head_dim == 64) return launch_reduce_t<F16, 64>(a, stream);
+        if (head_dim == 128) return launch_reduce_t<F16, 128>(a, stream);
+    } else if (dtype == KV_DTYPE_BF16) {
+        if (head_dim == 64) return launch_reduce_t<BF16, 64>(a, stream);
+        if (head_dim == 128) return launch_reduce_t<BF16, 128>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

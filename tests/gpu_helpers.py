@@ -1,0 +1,42 @@
+"""Oracle-side helpers of the GPU tests: the oracle's answer for a case, for chosen
+sequences, and the error measure."""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from workloads import DecodeCase
+
+from .device_case import DeviceCase, TORCH_DT, to_dev, to_host_bits  # noqa: F401
+
+TOL = {"f16": 2e-3, "bf16": 8e-3}
+
+
+def oracle_after_write(case: DecodeCase):
+    """Host oracle for a host case: scatter the new tokens, then decode every sequence."""
+    cfg = case.cfg
+    kp = case.k_pool.copy()
+    vp = case.v_pool.copy()
+    oracle.scatter(kp, vp, case.new_key, case.new_value, case.slot_mapping, cfg.block_size)
+    ref = oracle.paged_decode(case.query, kp, vp, case.block_tables, case.lengths, cfg.scale,
+                              cfg.block_size, cfg.dtype)
+    return ref, kp, vp
+
+
+def oracle_for_seqs(dc: DeviceCase, seqs):
+    """Oracle outputs for the listed sequences, from the bytes the GPU holds (after the write)."""
+    cfg = dc.cfg
+    out = []
+    for b in seqs:
+        kb, vb, table = dc.blocks_of(b)
+        out.append(oracle.paged_decode_seq(dc.case.query[b], kb, vb, table,
+                                           int(dc.case.lengths[b]), cfg.scale, cfg.block_size,
+                                           cfg.dtype))
+    return np.stack(out)
+
+
+def max_abs_err(gpu_bits: np.ndarray, ref: np.ndarray, dtype: str) -> float:
+    got = oracle.to_f64(gpu_bits, dtype)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(np.max(np.abs(got - ref)))

@@ -281,8 +281,10 @@ def _device_pools(cfg, lens, tables, used, poison, device):
     gen.manual_seed(cfg.index)
     pools = []
     chunk = max(1, (1 << 27) // (bs * H * d))   # ~128M elements per draw
-    for _ in range(2):
-        pool = torch.empty((cfg.num_blocks, bs, H, d), dtype=tdt, device=dev)
+    # K and V share one allocation (K first) so a one-layer pool can adopt it as is
+    both = torch.empty((2, cfg.num_blocks, bs, H, d), dtype=tdt, device=dev)
+    for which in range(2):
+        pool = both[which]
         for s in range(0, cfg.num_blocks, chunk):
             e = min(cfg.num_blocks, s + chunk)
             pool[s:e] = torch.randn((e - s, bs, H, d), generator=gen, device=dev,
