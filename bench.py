@@ -115,6 +115,9 @@ def main(argv=None):
     ap.add_argument("--config", default="c3", help="workload: c1..c5 or a config name")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB elementwise copy (torch.neg on fp16), the "
+                         "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -130,6 +133,17 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        n = 1 << 29                                  # 2^29 fp16 = 1 GiB read + 1 GiB written
+        src = torch.ones(n, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read": 2 * n, "bytes_written": 2 * n,
+                                               "launches": 3, "kernel": "torch.neg fp16"}}))
+        return 0
+
     cfg = config_by_name(args.config)
     print(f"[bench] building {cfg.name} on the device", file=sys.stderr, flush=True)
     case = make_case(cfg, where="device" if cfg.index in (3, 5) else "host", poison=False)

@@ -20,11 +20,14 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libpagedkv.so"
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "cache_ops.hip", "paged_decode.hip"]
+SOURCES = ["api.cpp", "cache_ops.hip", "paged_decode.hip", "paged_decode_mfma.hip"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs: the online-softmax rescale touches them
+    # with VALU instructions every block, which AGPR accumulators would turn into copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

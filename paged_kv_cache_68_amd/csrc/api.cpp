@@ -71,6 +71,7 @@ kv_status_t check_decode(const kv_pool_t* pool, int32_t layer, void* out, const 
     if (partition_size == 0) partition_size = pkv::kDefaultPartition;
     if (partition_size < d.block_size || partition_size % d.block_size != 0)
         return KV_ERR_INVALID_ARG;
+    if (partition_size > pkv::kMaxPartition) return KV_ERR_UNSUPPORTED;
     if (batch == 0) {
         shape->group = group;
         return KV_OK;

@@ -11,6 +11,11 @@ namespace pkv {
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // fp16 storage: v_dot2_f32_f16 for q.k, exact widening, RNE narrowing.
 struct F16 {
@@ -27,6 +32,21 @@ struct F16 {
     }
     __device__ static __forceinline__ uint16_t narrow(float x) {
         return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+    }
+    // two fp32 -> packed 16-bit (RNE), `lo` in the low half
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+        const f16x2_t v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    // D += A(16x32) * B(32x16); each lane passes 8 k-elements of A and of B
+    __device__ static __forceinline__ f32x4_t mfma_k32(uint4 a, uint4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+    // D += A(16x16) * B(16x16); each lane passes 4 k-elements of A and of B
+    __device__ static __forceinline__ f32x4_t mfma_k16(uint2 a, uint2 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                     __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
     }
 };
 
@@ -45,13 +65,33 @@ struct BF16 {
         u += 0x7fffu + ((u >> 16) & 1u);   // round to nearest, ties to even
         return static_cast<uint16_t>(u >> 16);
     }
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+        const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    __device__ static __forceinline__ f32x4_t mfma_k32(uint4 a, uint4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ f32x4_t mfma_k16(uint2 a, uint2 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                         __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+    }
 };
+
+// 16-bit halves of two dwords: (x.lo, y.lo) and (x.hi, y.hi), x's half in the low half.
+__device__ __forceinline__ uint32_t lo_halves(uint32_t x, uint32_t y) {
+    return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_halves(uint32_t x, uint32_t y) {
+    return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
 
 // DPP lane move inside a row of 16 lanes (every control used here reads an in-row lane).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
-                                                              0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 CTRL, 0xf, 0xf, true));
 }
 
 constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
@@ -72,6 +112,29 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Lane exchanges across the four 16-lane rows of a wave.
+__device__ __forceinline__ float xor16(float x) {      // ds_swizzle, bit mode: lane ^ 16
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+__device__ __forceinline__ float xor32(float x, int addr_xor32) {   // addr = (lane ^ 32) * 4
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr_xor32, __builtin_bit_cast(int, x)));
+}
+
+// Buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes return zero and
+// touch no memory, which both masks the tail of a partly filled block and lets a wave
+// issue a fixed number of loads per iteration.
+constexpr int kBufferFlags = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
+}
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 load8(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Work-groups are handed to the 8 XCDs round-robin.  Renumber them so that each XCD
 // gets one contiguous range of logical work items (and so shares its L2 between

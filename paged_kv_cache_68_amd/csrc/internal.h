@@ -20,7 +20,9 @@ namespace pkv {
 
 constexpr int kBlockSize = 16;          // tokens per physical block
 constexpr int kDefaultPartition = 512;  // tokens per split-context partition
-constexpr int kMaxGroup = 8;            // largest supported GQA group
+constexpr int kMaxPartition = 4096;     // a wave holds its partition's table entries in one VGPR
+constexpr int kMaxGroup = 16;           // largest supported GQA group (MFMA path)
+constexpr int kMaxGroupValu = 8;        // largest group the VALU kernel is built for
 constexpr int kWavesPerGroup = 4;       // waves per work-group of the partition kernel
 
 // Everything the two decode kernels read; passed by value.
@@ -47,6 +49,8 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 hipError_t launch_partitions(int dtype, int head_dim, int group, const DecodeArgs& a,
                              hipStream_t stream);
+hipError_t launch_partitions_mfma(int dtype, int head_dim, int group, const DecodeArgs& a,
+                                  hipStream_t stream);
 hipError_t launch_reduce(int dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const uint16_t* key, const uint16_t* value,
                                     const int64_t* slots, int32_t num_tokens, uint16_t* k_cache,

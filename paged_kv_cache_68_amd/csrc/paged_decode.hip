@@ -23,6 +23,8 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "device_common.h"
 
@@ -244,11 +246,15 @@ __global__ __launch_bounds__(256) void pa_partition_valu(DecodeArgs a) {
     }
 }
 
-// One wave per (sequence, query head): combine the sequence's partitions in
-// ascending order, O = sum_k w_k acc_k / sum_k w_k l_k with w_k = 2^(m_k - max m).
+// One wave per (sequence, query head): combine the sequence's partitions,
+// O = sum_k w_k acc_k / sum_k w_k l_k with w_k = 2^(m_k - max m).  Lane k holds the
+// (m, l) of partition k (64 per pass); the accumulator rows are then streamed with the
+// weights broadcast from those lanes, eight independent loads in flight at a time.
+// The summation order is fixed (ascending k per dimension), so the result is
+// deterministic.
 template <class S, int D>
 __global__ __launch_bounds__(256) void pa_reduce(DecodeArgs a) {
-    constexpr int PER = D / 64;
+    constexpr int PER = D / 64;    // dimensions per lane
     const int lane = threadIdx.x & 63;
     const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (pair >= a.batch * a.num_q_heads) return;
@@ -261,11 +267,11 @@ __global__ __launch_bounds__(256) void pa_reduce(DecodeArgs a) {
     if (nparts <= 1) return;
 
     const size_t ph0 = (static_cast<size_t>(b) * a.num_q_heads + h) * a.num_parts;
-    const float* ml = a.ws_ml + ph0 * 2;
-    const float* acc = a.ws_acc + ph0 * D;
+    const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + ph0;
+    const float* acc = a.ws_acc + ph0 * D + PER * lane;
 
     float M = -INFINITY;
-    for (int k = lane; k < nparts; k += 64) M = fmaxf(M, ml[2 * k]);
+    for (int k = lane; k < nparts; k += 64) M = fmaxf(M, ml[k].x);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
 
@@ -273,15 +279,43 @@ __global__ __launch_bounds__(256) void pa_reduce(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) A[e] = 0.f;
     float lsum = 0.f;
-    for (int k = 0; k < nparts; ++k) {
-        const float w = (M == -INFINITY) ? 0.f : fast_exp2(ml[2 * k] - M);
-        lsum += w * ml[2 * k + 1];
+    for (int k0 = 0; k0 < nparts; k0 += 64) {
+        float w = 0.f;
+        if (k0 + lane < nparts) {
+            const float2 v = ml[k0 + lane];
+            w = (M == -INFINITY) ? 0.f : fast_exp2(v.x - M);
+            lsum += w * v.y;
+        }
+        const int cnt = min(64, nparts - k0);
+        const int wbits = __builtin_bit_cast(int, w);
+        int i = 0;
+        for (; i + 8 <= cnt; i += 8) {      // eight independent loads, then the FMAs in order
+            float x[8][PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) A[e] += w * acc[static_cast<size_t>(k) * D + lane + 64 * e];
+            for (int u = 0; u < 8; ++u) {
+                const float* src = acc + static_cast<size_t>(k0 + i + u) * D;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) x[u][e] = src[e];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wbits, i + u));
+#pragma unroll
+                for (int e = 0; e < PER; ++e) A[e] = fmaf(wi, x[u][e], A[e]);
+            }
+        }
+        for (; i < cnt; ++i) {
+            const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wbits, i));
+            const float* src = acc + static_cast<size_t>(k0 + i) * D;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) A[e] = fmaf(wi, src[e], A[e]);
+        }
     }
-    uint16_t* o = a.out + (static_cast<size_t>(b) * a.num_q_heads + h) * D;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) o[lane + 64 * e] = S::narrow(lsum > 0.f ? A[e] / lsum : 0.f);
+    for (int off = 1; off < 64; off <<= 1) lsum += __shfl_xor(lsum, off);
+    uint16_t* o = a.out + (static_cast<size_t>(b) * a.num_q_heads + h) * D + PER * lane;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = S::narrow(lsum > 0.f ? A[e] / lsum : 0.f);
 }
 
 template <class S, int D, int G>
@@ -321,8 +355,19 @@ hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Kernel choice: the matrix-core kernel for GQA groups of 2..16 (a real dense tile per
+// block), the VALU kernel for single-head groups (MHA).  PAGEDKV_KERNEL=valu forces the
+// VALU kernel for groups up to 8 (for comparisons); =mfma forces the matrix cores.
+static int kernel_choice(int group) {
+    const char* env = getenv("PAGEDKV_KERNEL");
+    if (env && strcmp(env, "valu") == 0 && group <= kMaxGroupValu) return 0;
+    if (env && strcmp(env, "mfma") == 0) return 1;
+    return group >= 2 ? 1 : 0;
+}
+
 hipError_t launch_partitions(int dtype, int head_dim, int group, const DecodeArgs& a,
                              hipStream_t stream) {
+    if (kernel_choice(group) == 1) return launch_partitions_mfma(dtype, head_dim, group, a, stream);
     if (dtype == KV_DTYPE_F16) {
         if (head_dim == 64) return launch_part_g<F16, 64>(group, a, stream);
         if (head_dim == 128) return launch_part_g<F16, 128>(group, a, stream);
