@@ -2,6 +2,7 @@
 // enqueued), pool bookkeeping and kernel dispatch.  See include/pagedkv.h.
 
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <new>
@@ -123,6 +124,10 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     a.part_blocks = s.part_blocks;
     a.num_parts = s.num_parts;
     a.scale_log2 = scale * 1.4426950408889634f;
+    // PAGEDKV_XCD_CHUNK overrides the chunk of the XCD renumbering (tuning knob)
+    const char* x = getenv("PAGEDKV_XCD_CHUNK");
+    a.xcd_chunk = x ? atoi(x) : 16;
+    if (a.xcd_chunk < 1) a.xcd_chunk = 1;
     return a;
 }
 
@@ -147,7 +152,13 @@ kv_status_t decode_impl(int phases, const kv_pool_t* pool, int32_t layer, void* 
             return KV_ERR_HIP;
     }
     if ((phases & kReduce) && s.num_parts > 1) {
-        if (pkv::launch_reduce(pool->desc.dtype, pool->desc.head_dim, a, stream) != hipSuccess)
+        // the partition kernel may already have merged chunks of partitions
+        const int chunk = pkv::partition_chunk(pool->desc.dtype, pool->desc.head_dim, s.group, a);
+        pkv::DecodeArgs r = a;
+        r.part_blocks = a.part_blocks * chunk;
+        r.num_parts = static_cast<int32_t>(ceil_div(a.num_parts, chunk));
+        if (r.num_parts > 1 &&
+            pkv::launch_reduce(pool->desc.dtype, pool->desc.head_dim, r, stream) != hipSuccess)
             return KV_ERR_HIP;
     }
     return KV_OK;

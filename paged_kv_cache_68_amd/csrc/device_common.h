@@ -59,11 +59,9 @@ struct BF16 {
     }
     __device__ static __forceinline__ float lo(uint32_t u) { return __uint_as_float(u << 16); }
     __device__ static __forceinline__ float hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+    // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32)
     __device__ static __forceinline__ uint16_t narrow(float x) {
-        uint32_t u = __float_as_uint(x);
-        if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-        u += 0x7fffu + ((u >> 16) & 1u);   // round to nearest, ties to even
-        return static_cast<uint16_t>(u >> 16);
+        return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
     }
     __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
         const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
@@ -136,14 +134,19 @@ __device__ __forceinline__ uint2 load8(__amdgpu_buffer_rsrc_t r, int off) {
 }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Work-groups are handed to the 8 XCDs round-robin.  Renumber them so that each XCD
-// gets one contiguous range of logical work items (and so shares its L2 between
-// neighbouring items).  Bijective on [0, n).
-__device__ __forceinline__ int xcd_order(int id, int n) {
+// Work-groups are handed to the 8 XCDs round-robin, in launch order.  Renumber them so
+// that each XCD walks through chunks of `chunk` consecutive work-groups: work-groups
+// that read the same blocks (neighbouring sequences of a shared prefix, the KV heads of
+// one block) meet in the same L2, while the chunks still rotate over the XCDs, so long
+// and short items stay evenly spread.  Bijective on [0, n); the tail that does not fill
+// a whole round of chunks keeps its own number.
+__device__ __forceinline__ int xcd_chunked(int id, int n, int chunk) {
     constexpr int kXcds = 8;
-    const int q = n / kXcds, r = n % kXcds;
-    const int x = id % kXcds, loc = id / kXcds;
-    return (x < r) ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
+    const int round = kXcds * chunk;
+    if (id >= (n / round) * round) return id;
+    const int x = id % kXcds;
+    const int slot = id / kXcds;
+    return (slot / chunk) * round + x * chunk + slot % chunk;
 }
 
 }  // namespace pkv

@@ -43,6 +43,7 @@ struct DecodeArgs {
     int32_t part_blocks;     // blocks per partition
     int32_t num_parts;       // partitions of the longest possible sequence
     float scale_log2;        // scale * log2(e): scores are kept in base-2 units
+    int32_t xcd_chunk;       // work-groups per XCD chunk in the launch renumbering
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -51,6 +52,10 @@ hipError_t launch_partitions(int dtype, int head_dim, int group, const DecodeArg
                              hipStream_t stream);
 hipError_t launch_partitions_mfma(int dtype, int head_dim, int group, const DecodeArgs& a,
                                   hipStream_t stream);
+// Partitions the partition kernel merges by itself before writing partial results
+// (the reduce kernel then combines chunks of that many partitions).
+int partition_chunk(int dtype, int head_dim, int group, const DecodeArgs& a);
+int partition_chunk_mfma(int group, int head_dim, const DecodeArgs& a);
 hipError_t launch_reduce(int dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const uint16_t* key, const uint16_t* value,
                                     const int64_t* slots, int32_t num_tokens, uint16_t* k_cache,

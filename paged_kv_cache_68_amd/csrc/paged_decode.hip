@@ -26,47 +26,41 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include "device_common.h"
+#include "partition_common.h"
 
 namespace pkv {
 namespace {
 
-template <class S, int D, int G>
-__global__ __launch_bounds__(256) void pa_partition_valu(DecodeArgs a) {
+template <class S, int D, int G, bool SPLIT>
+__global__ __launch_bounds__(256) void pa_partition_valu(DecodeArgs a, int n_items, int per_item) {
     constexpr int LPT = D / 8;       // lanes per token row
     constexpr int TPI = 64 / LPT;    // token rows per wave load
     constexpr int NI = 16 / TPI;     // loads per block per tensor
     constexpr int W = kWavesPerGroup;
-
-    __shared__ float sm_ml[W][G][2];
-    __shared__ float sm_acc[W][G][D];
+    struct Buf {
+        uint4 k[NI];
+        uint4 v[NI];
+    };
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = uniform(threadIdx.x >> 6);
     const int r = lane / LPT;        // token row inside a load
     const int c = lane % LPT;        // 8-element chunk of the row
 
-    const int item = xcd_order(blockIdx.x, gridDim.x);
-    const int kvh = item % a.num_kv_heads;
-    const int rest = item / a.num_kv_heads;
-    const int b = rest % a.batch;
-    const int p = rest / a.batch;
-
-    int L = a.lens[b];
-    L = L < 0 ? 0 : (L > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : L);
-    const int nblk = (L + kBlockSize - 1) / kBlockSize;
-    const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
-    const int h0 = kvh * G;
-    const size_t out_row0 = (static_cast<size_t>(b) * a.num_q_heads + h0) * D;
-
-    if (L == 0) {
-        if (p == 0)
-            for (int i = threadIdx.x; i < G * D; i += blockDim.x) a.out[out_row0 + i] = 0;
+    const int group_id = xcd_chunked(blockIdx.x, gridDim.x, a.xcd_chunk);
+    const int item = SPLIT ? group_id : group_id * W + wave;
+    if (!SPLIT && item >= n_items) return;
+    const Item it = decode_item(a, item, SPLIT ? 1 : per_item);
+    if (it.L == 0) {
+        store_empty<D>(a, it, G, SPLIT ? threadIdx.x : lane, SPLIT ? blockDim.x : 64);
         return;
     }
-    if (p >= nparts) return;
-    const int j0 = p * a.part_blocks;
-    const int j1 = min(nblk, j0 + a.part_blocks);
+    if (it.p >= it.nparts) return;
+    const int h0 = it.kvh * G;
+    const size_t out_row0 = (static_cast<size_t>(it.b) * a.num_q_heads + h0) * D;
+
+    BlockWalk walk;
+    walk.init(a, it, SPLIT ? wave : 0, SPLIT ? W : 1, lane);
 
     uint4 qv[G];
 #pragma unroll
@@ -82,61 +76,81 @@ __global__ __launch_bounds__(256) void pa_partition_valu(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
     }
 
-    const size_t row = static_cast<size_t>(a.num_kv_heads) * D;   // elements per token row
-    const size_t blk_elems = row * kBlockSize;
-    const uint16_t* kbase = a.k + static_cast<size_t>(kvh) * D + r * row + c * 8;
-    const uint16_t* vbase = a.v + static_cast<size_t>(kvh) * D + r * row + c * 8;
-    const int32_t* trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
+    const int row_bytes = a.num_kv_heads * D * 2;
+    const int off0 = (it.kvh * D + 8 * c) * 2 + r * row_bytes;   // + i * TPI * row_bytes
 
-    uint4 kn[NI], vn[NI];
-    int j = j0 + wave;
-    int blk_next = 0;
-    bool ok_next = false;
-    if (j < j1) {
-        const int t = trow[j];
-        ok_next = static_cast<unsigned>(t) < static_cast<unsigned>(a.num_blocks);
-        blk_next = ok_next ? t : 0;
-        const uint16_t* kp = kbase + static_cast<size_t>(blk_next) * blk_elems;
-        const uint16_t* vp = vbase + static_cast<size_t>(blk_next) * blk_elems;
+    auto load = [&](__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, Buf& buf) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) kn[i] = *reinterpret_cast<const uint4*>(kp + i * TPI * row);
+        for (int i = 0; i < NI; ++i) buf.k[i] = load16(rk, off0 + i * TPI * row_bytes);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) vn[i] = *reinterpret_cast<const uint4*>(vp + i * TPI * row);
-    }
+        for (int i = 0; i < NI; ++i) buf.v[i] = load16(rv, off0 + i * TPI * row_bytes);
+    };
 
-    for (; j < j1; j += W) {
-        uint4 kc[NI], vc[NI];
+    // merge the TPI rows of the wave (lanes with equal c) in place
+    auto merge_rows = [&]() {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            kc[i] = kn[i];
-            vc[i] = vn[i];
+        for (int g = 0; g < G; ++g) {
+            float M = m[g];
+#pragma unroll
+            for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+            const float f = (M == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
+            float lt = l[g] * f;
+#pragma unroll
+            for (int off = LPT; off < 64; off <<= 1) lt += __shfl_xor(lt, off);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float t = acc[g][e] * f;
+#pragma unroll
+                for (int off = LPT; off < 64; off <<= 1) t += __shfl_xor(t, off);
+                acc[g][e] = t;
+            }
+            m[g] = M;
+            l[g] = lt;
         }
-        const bool ok = ok_next;
-        // prefetch the wave's next block while this one is computed
-        const int jn = j + W;
-        if (jn < j1) {
-            const int t = trow[jn];
-            ok_next = static_cast<unsigned>(t) < static_cast<unsigned>(a.num_blocks);
-            blk_next = ok_next ? t : 0;
-            const uint16_t* kp = kbase + static_cast<size_t>(blk_next) * blk_elems;
-            const uint16_t* vp = vbase + static_cast<size_t>(blk_next) * blk_elems;
-#pragma unroll
-            for (int i = 0; i < NI; ++i) kn[i] = *reinterpret_cast<const uint4*>(kp + i * TPI * row);
-#pragma unroll
-            for (int i = 0; i < NI; ++i) vn[i] = *reinterpret_cast<const uint4*>(vp + i * TPI * row);
-        }
-        const int valid = ok ? min(kBlockSize, L - j * kBlockSize) : 0;
+    };
 
+    // (!SPLIT) result of partition p from this wave's state, then a fresh state.  After
+    // the row merge, lanes of row 0 hold elements [8c, 8c + 8) of every head; they go
+    // through this wave's LDS staging area so that every lane writes whole lines.
+    extern __shared__ float smem[];
+    float* stage = smem + wave * G * (D + 4);     // [G][D], then (m, l) per head, 16-B aligned
+    auto flush = [&](int p) {
+        merge_rows();
+        if (r == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                *reinterpret_cast<float4*>(stage + g * D + 8 * c) =
+                    make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+                *reinterpret_cast<float4*>(stage + g * D + 8 * c + 4) =
+                    make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
+            }
+            if (c == 0)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    *reinterpret_cast<float2*>(stage + G * D + 2 * g) = make_float2(m[g], l[g]);
+        }
+        // the LDS operations of one wave complete in order: the reads below see the writes
+        store_partition<S, D>(a, it, G, p, stage, stage + G * D, lane);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            m[g] = -INFINITY;
+            l[g] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+        }
+    };
+
+    auto process = [&](int k, int valid, const Buf& buf) {
         // scores of this row's NI tokens for the G heads (base-2 units)
         float s[NI][G];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                float t = S::dot2(qv[g].x, kc[i].x, 0.f);
-                t = S::dot2(qv[g].y, kc[i].y, t);
-                t = S::dot2(qv[g].z, kc[i].z, t);
-                t = S::dot2(qv[g].w, kc[i].w, t);
+                float t = S::dot2(qv[g].x, buf.k[i].x, 0.f);
+                t = S::dot2(qv[g].y, buf.k[i].y, t);
+                t = S::dot2(qv[g].z, buf.k[i].z, t);
+                t = S::dot2(qv[g].w, buf.k[i].w, t);
                 s[i][g] = group_sum<LPT>(t);
             }
         }
@@ -146,8 +160,9 @@ __global__ __launch_bounds__(256) void pa_partition_valu(DecodeArgs a) {
 #pragma unroll
             for (int g = 0; g < G; ++g) s[i][g] = tok_ok ? s[i][g] * a.scale_log2 : -INFINITY;
         }
-
         float pw[NI][G];
+        float alpha[G];
+        bool rescale = false;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float mb = s[0][g];
@@ -155,94 +170,64 @@ __global__ __launch_bounds__(256) void pa_partition_valu(DecodeArgs a) {
             for (int i = 1; i < NI; ++i) mb = fmaxf(mb, s[i][g]);
             const float mn = fmaxf(m[g], mb);
             const float mu = (mn == -INFINITY) ? 0.f : mn;
-            const float alpha = fast_exp2(m[g] - mu);
+            alpha[g] = fast_exp2(m[g] - mu);
             float sum = 0.f;
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 pw[i][g] = fast_exp2(s[i][g] - mu);
                 sum += pw[i][g];
             }
-            l[g] = l[g] * alpha + sum;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
+            l[g] = l[g] * alpha[g] + sum;
             m[g] = mn;
+            rescale |= alpha[g] != 1.f;
         }
-
+        if (__any(rescale)) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[g][e] *= alpha[g];
+        }
+        // P.V: rows past the valid tokens were loaded as zeros and have p = 0
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const bool tok_ok = (i * TPI + r) < valid;
-            const uint32_t w4[4] = {vc[i].x, vc[i].y, vc[i].z, vc[i].w};
+            const uint32_t w4[4] = {buf.v[i].x, buf.v[i].y, buf.v[i].z, buf.v[i].w};
             float vf[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                vf[2 * e] = tok_ok ? S::lo(w4[e]) : 0.f;
-                vf[2 * e + 1] = tok_ok ? S::hi(w4[e]) : 0.f;
+                vf[2 * e] = S::lo(w4[e]);
+                vf[2 * e + 1] = S::hi(w4[e]);
             }
 #pragma unroll
             for (int g = 0; g < G; ++g)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw[i][g], vf[e], acc[g][e]);
         }
-    }
+        if constexpr (!SPLIT) {     // last block of a partition: emit it
+            const int j = walk.jb + k;
+            if ((j + 1) % a.part_blocks == 0 || k + 1 == walk.nk) flush(j / a.part_blocks);
+        }
+    };
 
-    // merge the TPI rows of this wave (lanes with equal c)
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float M = m[g];
-#pragma unroll
-        for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-        const float f = (M == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
-        float lt = l[g] * f;
-#pragma unroll
-        for (int off = LPT; off < 64; off <<= 1) lt += __shfl_xor(lt, off);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float t = acc[g][e] * f;
-#pragma unroll
-            for (int off = LPT; off < 64; off <<= 1) t += __shfl_xor(t, off);
-            acc[g][e] = t;
-        }
-        m[g] = M;
-        l[g] = lt;
-    }
-    if (r == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sm_acc[wave][g][c * 8 + e] = acc[g][e];
-        if (c == 0)
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                sm_ml[wave][g][0] = m[g];
-                sm_ml[wave][g][1] = l[g];
-            }
-    }
-    __syncthreads();
+    walk_blocks<Buf>(a, it, walk, row_bytes, load, process);
 
-    // merge the waves and write the partition's result
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-        const int g = idx / D;
-        const int dd = idx % D;
-        float M = sm_ml[0][g][0];
+    if constexpr (SPLIT) {
+        merge_rows();
+        float* sm_ml = smem;                 // [W][G][2]
+        float* sm_acc = smem + W * G * 2;    // [W][G][D]
+        if (r == 0) {
 #pragma unroll
-        for (int w = 1; w < W; ++w) M = fmaxf(M, sm_ml[w][g][0]);
-        float lsum = 0.f, A = 0.f;
+            for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int w = 0; w < W; ++w) {
-            const float f = (M == -INFINITY) ? 0.f : fast_exp2(sm_ml[w][g][0] - M);
-            lsum += f * sm_ml[w][g][1];
-            A += f * sm_acc[w][g][dd];
+                for (int e = 0; e < 8; ++e) sm_acc[(wave * G + g) * D + c * 8 + e] = acc[g][e];
+            if (c == 0)
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    sm_ml[(wave * G + g) * 2 + 0] = m[g];
+                    sm_ml[(wave * G + g) * 2 + 1] = l[g];
+                }
         }
-        if (nparts == 1) {
-            a.out[out_row0 + idx] = S::narrow(lsum > 0.f ? A / lsum : 0.f);
-        } else {
-            const size_t ph = (static_cast<size_t>(b) * a.num_q_heads + h0 + g) * a.num_parts + p;
-            a.ws_acc[ph * D + dd] = A;
-            if (dd == 0) {
-                a.ws_ml[ph * 2 + 0] = M;
-                a.ws_ml[ph * 2 + 1] = lsum;
-            }
-        }
+        __syncthreads();
+        merge_waves_and_store<S, D>(a, it, G, sm_ml, sm_acc);
     }
 }
 
@@ -266,12 +251,14 @@ __global__ __launch_bounds__(256) void pa_reduce(DecodeArgs a) {
     const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
     if (nparts <= 1) return;
 
-    const size_t ph0 = (static_cast<size_t>(b) * a.num_q_heads + h) * a.num_parts;
-    const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + ph0;
-    const float* acc = a.ws_acc + ph0 * D + PER * lane;
+    // partition k of head h = kvh*G + g is row part_row(b, kvh, k) + g: rows G apart
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const size_t row0 = part_row(a, b, h / G, 0, G) + h % G;
+    const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + row0;
+    const float* acc = a.ws_acc + row0 * D + PER * lane;
 
     float M = -INFINITY;
-    for (int k = lane; k < nparts; k += 64) M = fmaxf(M, ml[k].x);
+    for (int k = lane; k < nparts; k += 64) M = fmaxf(M, ml[static_cast<size_t>(k) * G].x);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
 
@@ -282,7 +269,7 @@ __global__ __launch_bounds__(256) void pa_reduce(DecodeArgs a) {
     for (int k0 = 0; k0 < nparts; k0 += 64) {
         float w = 0.f;
         if (k0 + lane < nparts) {
-            const float2 v = ml[k0 + lane];
+            const float2 v = ml[static_cast<size_t>(k0 + lane) * G];
             w = (M == -INFINITY) ? 0.f : fast_exp2(v.x - M);
             lsum += w * v.y;
         }
@@ -293,7 +280,7 @@ __global__ __launch_bounds__(256) void pa_reduce(DecodeArgs a) {
             float x[8][PER];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const float* src = acc + static_cast<size_t>(k0 + i + u) * D;
+                const float* src = acc + static_cast<size_t>(k0 + i + u) * G * D;
 #pragma unroll
                 for (int e = 0; e < PER; ++e) x[u][e] = src[e];
             }
@@ -306,7 +293,7 @@ __global__ __launch_bounds__(256) void pa_reduce(DecodeArgs a) {
         }
         for (; i < cnt; ++i) {
             const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(wbits, i));
-            const float* src = acc + static_cast<size_t>(k0 + i) * D;
+            const float* src = acc + static_cast<size_t>(k0 + i) * G * D;
 #pragma unroll
             for (int e = 0; e < PER; ++e) A[e] = fmaf(wi, src[e], A[e]);
         }
@@ -323,8 +310,18 @@ hipError_t launch_part_t(const DecodeArgs& a, hipStream_t stream) {
     const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.num_parts;
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((pa_partition_valu<S, D, G>), dim3(static_cast<unsigned>(items)),
-                       dim3(64 * kWavesPerGroup), 0, stream, a);
+    const size_t lds = static_cast<size_t>(kWavesPerGroup) * G * (D + 4) * sizeof(float);
+    if (split_items(items)) {
+        hipLaunchKernelGGL((pa_partition_valu<S, D, G, true>), dim3(static_cast<unsigned>(items)),
+                           dim3(64 * kWavesPerGroup), lds, stream, a, static_cast<int>(items), 1);
+    } else {
+        static const int64_t slots = resident_waves(reinterpret_cast<const void*>(&pa_partition_valu<S, D, G, false>));
+        const int per = partitions_per_wave(items, slots, a.num_parts, a.part_blocks);
+        const int64_t waves = static_cast<int64_t>(a.batch) * a.num_kv_heads * ceil_div(a.num_parts, per);
+        const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+        hipLaunchKernelGGL((pa_partition_valu<S, D, G, false>), dim3(static_cast<unsigned>(groups)),
+                           dim3(64 * kWavesPerGroup), lds, stream, a, static_cast<int>(waves), per);
+    }
     return hipGetLastError();
 }
 
@@ -363,6 +360,11 @@ static int kernel_choice(int group) {
     if (env && strcmp(env, "valu") == 0 && group <= kMaxGroupValu) return 0;
     if (env && strcmp(env, "mfma") == 0) return 1;
     return group >= 2 ? 1 : 0;
+}
+
+int partition_chunk(int dtype, int head_dim, int group, const DecodeArgs& a) {
+    (void)dtype;
+    return kernel_choice(group) == 1 ? partition_chunk_mfma(group, head_dim, a) : 1;
 }
 
 hipError_t launch_partitions(int dtype, int head_dim, int group, const DecodeArgs& a,

@@ -29,68 +29,62 @@
 
 #include <type_traits>
 
-#include "device_common.h"
+#include "partition_common.h"
 
 namespace pkv {
 namespace {
 
-// SPLIT = true : the 4 waves of a work-group share one (sequence, KV head, partition)
-//                item, taking its blocks round-robin, and are merged through LDS.
-// SPLIT = false: each wave owns a whole item (the 4 waves of a work-group take 4
-//                consecutive items, i.e. 4 KV heads of the same blocks) and writes its
-//                result straight from registers.  Preferred when there are enough items
-//                to fill the GPU: no LDS, no barrier, and the start-up cost of a wave
-//                (table fetch, first loads) is spread over the whole partition.
-template <class S, int D, bool SPLIT>
-__global__ __launch_bounds__(256) void pa_partition_mfma(DecodeArgs a, int G, int n_items) {
+// Three ways to map (sequence, KV head, partition) items onto waves:
+//  kSplit : the 4 waves of a work-group share one item, taking its blocks
+//           round-robin, merged through LDS.  For small problems.
+//  kItem  : each wave owns whole items (one or more consecutive partitions, walked as
+//           one stream) and writes each partition's partial result to the workspace;
+//           a second kernel combines the partitions.
+//  kGroup : a work-group of NW waves owns a chunk of PC consecutive partitions of one
+//           (sequence, KV head); each wave walks PC/NW of them, leaves each partition's
+//           state in LDS, and the work-group combines the chunk with the cross-block
+//           rule.  A sequence that fits in one chunk gets its final output right away:
+//           no partial results go to HBM and no second kernel runs.
+enum Mode { kSplit = 0, kItem = 1, kGroup = 2 };
+
+template <class S, int D, int MODE>
+__global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, int n_items,
+                                                         int per_item, int ppw) {
+    constexpr bool SPLIT = MODE == kSplit;
     constexpr int W = kWavesPerGroup;
     constexpr int NQK = D / 32;    // score MFMAs per block
     constexpr int EPL = D / 16;    // value MFMAs per block = V elements per lane per token
     using VRow = typename std::conditional<EPL == 8, uint4, uint2>::type;
+    struct Buf {
+        uint4 k[NQK];
+        VRow v[4];
+    };
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int n = lane & 15;
     const int c = lane >> 4;
 
-    const int group_id = xcd_order(blockIdx.x, gridDim.x);
-    const int item = SPLIT ? group_id : group_id * W + wave;
-    if (!SPLIT && item >= n_items) return;
-    const int kvh = item % a.num_kv_heads;
-    const int rest = item / a.num_kv_heads;
-    const int b = rest % a.batch;
-    const int p = rest / a.batch;
-
-    int L = a.lens[b];
-    L = L < 0 ? 0 : (L > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : L);
-    const int nblk = (L + kBlockSize - 1) / kBlockSize;
-    const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
-    const int h0 = kvh * G;
-    const size_t out_row0 = (static_cast<size_t>(b) * a.num_q_heads + h0) * D;
-
-    if (L == 0) {
-        if (p == 0) {
-            const int t0 = SPLIT ? threadIdx.x : lane;
-            const int nt = SPLIT ? blockDim.x : 64;
-            for (int i = t0; i < G * D; i += nt) a.out[out_row0 + i] = 0;
-        }
+    const int group_id = xcd_chunked(blockIdx.x, gridDim.x, a.xcd_chunk);
+    const int item = MODE == kItem ? group_id * W + wave : group_id;
+    if (MODE == kItem && item >= n_items) return;
+    const Item it = decode_item(a, item, SPLIT ? 1 : per_item);
+    const bool wg_wide = MODE != kItem;          // the whole work-group works on `it`
+    if (it.L == 0) {
+        store_empty<D>(a, it, G, wg_wide ? threadIdx.x : lane, wg_wide ? blockDim.x : 64);
         return;
     }
-    if (p >= nparts) return;
-    const int j0 = p * a.part_blocks;
-    const int j1 = min(nblk, j0 + a.part_blocks);
-    // blocks of this wave: jb + js*k for k < nk  (nk <= 256: partitions <= 4096 tokens)
-    const int jb = SPLIT ? j0 + wave : j0;
-    const int js = SPLIT ? W : 1;
-    const int nk = j1 > jb ? (j1 - jb + js - 1) / js : 0;
+    if (it.p >= it.nparts) return;
+    const int h0 = it.kvh * G;
+    const size_t out_row0 = (static_cast<size_t>(it.b) * a.num_q_heads + h0) * D;
 
-    // this wave's table entries, 64 per VGPR
-    const int32_t* trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
-    int tab[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int k = 64 * t + lane;
-        tab[t] = (64 * t < nk && k < nk) ? trow[jb + js * k] : -1;
+    BlockWalk walk;
+    if constexpr (MODE == kGroup) {
+        // this wave's partitions: [p + wave*ppw, p + (wave+1)*ppw) within the chunk
+        const int jw = (it.p + wave * ppw) * a.part_blocks;
+        walk.init_range(a, it, min(jw, it.j1), min(jw + ppw * a.part_blocks, it.j1), lane);
+    } else {
+        walk.init(a, it, SPLIT ? wave : 0, SPLIT ? W : 1, lane);
     }
 
     // Q^T operand: head n (zero beyond the group), 8 elements per MFMA
@@ -103,6 +97,11 @@ __global__ __launch_bounds__(256) void pa_partition_mfma(DecodeArgs a, int G, in
                                                     8 * (4 * i + c));
     }
 
+    // The table entries and Q must be in registers before the first block can be
+    // addressed anyway; waiting for them here also tells the compiler that none of
+    // the loads below have to wait for them again.
+    __builtin_amdgcn_s_waitcnt(0);
+
     f32x4_t acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -110,46 +109,51 @@ __global__ __launch_bounds__(256) void pa_partition_mfma(DecodeArgs a, int G, in
     float l = 0.f;
 
     const int row_bytes = a.num_kv_heads * D * 2;
-    const size_t blk_elems = static_cast<size_t>(a.num_kv_heads) * D * kBlockSize;
-    const int koff = (kvh * D + 8 * c) * 2 + n * row_bytes;           // + 64 i
-    const int voff = (kvh * D + EPL * n) * 2 + 4 * c * row_bytes;     // + r * row_bytes
+    const int koff = (it.kvh * D + 8 * c) * 2 + n * row_bytes;           // + 64 i
+    const int voff = (it.kvh * D + EPL * n) * 2 + 4 * c * row_bytes;     // + r * row_bytes
     const int addr_x32 = (lane ^ 32) * 4;
 
-    // k-th block of the wave -> (valid tokens, K and V resources covering just them)
-    auto block_at = [&](int k, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv) -> int {
-        int valid = 0;
-        size_t off = 0;
-        if (k < nk) {
-            const int kk = k & 63;
-            const int t = k < 64 ? __builtin_amdgcn_readlane(tab[0], kk)
-                        : k < 128 ? __builtin_amdgcn_readlane(tab[1], kk)
-                        : k < 192 ? __builtin_amdgcn_readlane(tab[2], kk)
-                                  : __builtin_amdgcn_readlane(tab[3], kk);
-            const int j = jb + js * k;
-            if (static_cast<unsigned>(t) < static_cast<unsigned>(a.num_blocks)) {
-                valid = min(kBlockSize, L - j * kBlockSize);
-                off = static_cast<size_t>(t) * blk_elems;
-            }
-        }
-        rk = make_rsrc(a.k + off, valid * row_bytes);
-        rv = make_rsrc(a.v + off, valid * row_bytes);
-        return valid;
-    };
-    auto load_block = [&](__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint4 (&kk)[NQK],
-                          VRow (&vv)[4]) {
+    auto load = [&](__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, Buf& buf) {
 #pragma unroll
-        for (int i = 0; i < NQK; ++i) kk[i] = load16(rk, koff + 64 * i);
+        for (int i = 0; i < NQK; ++i) buf.k[i] = load16(rk, koff + 64 * i);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            if constexpr (EPL == 8) vv[r] = load16(rv, voff + r * row_bytes);
-            else vv[r] = load8(rv, voff + r * row_bytes);
+            if constexpr (EPL == 8) buf.v[r] = load16(rv, voff + r * row_bytes);
+            else buf.v[r] = load8(rv, voff + r * row_bytes);
         }
     };
 
-    auto process = [&](int valid, const uint4 (&kk)[NQK], const VRow (&vv)[4]) {
+    // (!SPLIT) result of partition p from this wave's state, then a fresh state.  The
+    // accumulators sit in 16 of the 64 lanes (n < G); they go through this wave's LDS
+    // staging area so that every lane writes whole lines.
+    extern __shared__ float smem[];
+    float* stage = smem + wave * G * (D + 4);     // [G][D], then (m, l) per head, 16-B aligned
+    auto flush = [&](int p) {
+        if constexpr (MODE == kGroup) stage = smem + (p - it.p) * G * (D + 4);
+        float lt = l + xor16(l);
+        lt += xor32(lt, addr_x32);
+        if (n < G) {
+            float* dst = stage + n * D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int e = 0; e < EPL; e += 4)
+                    *reinterpret_cast<float4*>(dst + EPL * (4 * c + r) + e) =
+                        make_float4(acc[e][r], acc[e + 1][r], acc[e + 2][r], acc[e + 3][r]);
+            if (c == 0) *reinterpret_cast<float2*>(stage + G * D + 2 * n) = make_float2(m, lt);
+        }
+        // the LDS operations of one wave complete in order: the reads below see the writes
+        if constexpr (MODE == kItem) store_partition<S, D>(a, it, G, p, stage, stage + G * D, lane);
+        m = -INFINITY;
+        l = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    };
+
+    auto process = [&](int k, int valid, const Buf& buf) {
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < NQK; ++i) s = S::mfma_k32(kk[i], qv[i], s);
+        for (int i = 0; i < NQK; ++i) s = S::mfma_k32(buf.k[i], qv[i], s);
         float sr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sr[r] = (4 * c + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
@@ -171,82 +175,34 @@ __global__ __launch_bounds__(256) void pa_partition_mfma(DecodeArgs a, int G, in
         const uint2 pt = make_uint2(S::pack2(pr[0], pr[1]), S::pack2(pr[2], pr[3]));
         // V^T operand of element e: (tok 4c, 4c+1 | 4c+2, 4c+3) at element EPL*n + e;
         // rows past the valid tokens were loaded as zeros
-        uint32_t w0[EPL / 2], w1[EPL / 2], w2[EPL / 2], w3[EPL / 2];
-        if constexpr (EPL == 8) {
-            w0[0] = vv[0].x; w0[1] = vv[0].y; w0[2] = vv[0].z; w0[3] = vv[0].w;
-            w1[0] = vv[1].x; w1[1] = vv[1].y; w1[2] = vv[1].z; w1[3] = vv[1].w;
-            w2[0] = vv[2].x; w2[1] = vv[2].y; w2[2] = vv[2].z; w2[3] = vv[2].w;
-            w3[0] = vv[3].x; w3[1] = vv[3].y; w3[2] = vv[3].z; w3[3] = vv[3].w;
-        } else {
-            w0[0] = vv[0].x; w0[1] = vv[0].y;
-            w1[0] = vv[1].x; w1[1] = vv[1].y;
-            w2[0] = vv[2].x; w2[1] = vv[2].y;
-            w3[0] = vv[3].x; w3[1] = vv[3].y;
-        }
 #pragma unroll
-        for (int k = 0; k < EPL / 2; ++k) {
-            const uint2 even = make_uint2(lo_halves(w0[k], w1[k]), lo_halves(w2[k], w3[k]));
-            const uint2 odd = make_uint2(hi_halves(w0[k], w1[k]), hi_halves(w2[k], w3[k]));
-            acc[2 * k] = S::mfma_k16(even, pt, acc[2 * k]);
-            acc[2 * k + 1] = S::mfma_k16(odd, pt, acc[2 * k + 1]);
+        for (int q = 0; q < EPL / 2; ++q) {
+            const uint32_t w0 = reinterpret_cast<const uint32_t*>(&buf.v[0])[q];
+            const uint32_t w1 = reinterpret_cast<const uint32_t*>(&buf.v[1])[q];
+            const uint32_t w2 = reinterpret_cast<const uint32_t*>(&buf.v[2])[q];
+            const uint32_t w3 = reinterpret_cast<const uint32_t*>(&buf.v[3])[q];
+            const uint2 even = make_uint2(lo_halves(w0, w1), lo_halves(w2, w3));
+            const uint2 odd = make_uint2(hi_halves(w0, w1), hi_halves(w2, w3));
+            acc[2 * q] = S::mfma_k16(even, pt, acc[2 * q]);
+            acc[2 * q + 1] = S::mfma_k16(odd, pt, acc[2 * q + 1]);
+        }
+        if constexpr (!SPLIT) {     // last block of a partition: emit it
+            const int j = walk.jb + k;
+            if ((j + 1) % a.part_blocks == 0 || k + 1 == walk.nk) flush(j / a.part_blocks);
         }
     };
 
-    // Two register sets, alternating.  Every iteration issues exactly one block's loads
-    // (an empty resource past the wave's last block), so the wait before computing a
-    // block always leaves the following block's loads in flight.
-    uint4 ka[NQK], kb[NQK];
-    VRow va[4], vb[4];
-    __amdgpu_buffer_rsrc_t rk, rv;
-    int valid_a = block_at(0, rk, rv);
-    load_block(rk, rv, ka, va);
-    for (int k = 0; k < nk; k += 2) {
-        const int valid_b = block_at(k + 1, rk, rv);
-        load_block(rk, rv, kb, vb);
-        process(valid_a, ka, va);
-        if (k + 1 >= nk) break;
-        valid_a = block_at(k + 2, rk, rv);
-        load_block(rk, rv, ka, va);
-        process(valid_b, kb, vb);
+    if constexpr (D == 128) walk_blocks3<Buf>(a, it, walk, row_bytes, load, process);
+    else walk_blocks<Buf>(a, it, walk, row_bytes, load, process);
+
+    if constexpr (MODE == kGroup) {
+        __syncthreads();
+        merge_chunk_and_store<S, D>(a, it, G, smem, per_item, (a.num_parts + per_item - 1) / per_item);
     }
-
-    // per-head totals: the four c-lanes of head n hold partial sums of l
-    l += xor16(l);
-    l += xor32(l, addr_x32);
-
-    if constexpr (!SPLIT) {
-        // lane (c, n) holds dims EPL*(4c + r) + e of head n: EPL contiguous values per r
-        if (n < G) {
-            const size_t h = static_cast<size_t>(h0 + n);
-            if (nparts == 1) {
-                uint16_t* o = a.out + (static_cast<size_t>(b) * a.num_q_heads + h) * D;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    uint32_t wv[EPL / 2];
-#pragma unroll
-                    for (int e = 0; e < EPL / 2; ++e)
-                        wv[e] = static_cast<uint32_t>(S::narrow(l > 0.f ? acc[2 * e][r] / l : 0.f)) |
-                                (static_cast<uint32_t>(S::narrow(l > 0.f ? acc[2 * e + 1][r] / l : 0.f)) << 16);
-                    uint16_t* dst = o + EPL * (4 * c + r);
-                    if constexpr (EPL == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-                    else *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0], wv[1]);
-                }
-            } else {
-                const size_t ph = (static_cast<size_t>(b) * a.num_q_heads + h) * a.num_parts + p;
-                float* wa = a.ws_acc + ph * D;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float* dst = wa + EPL * (4 * c + r);
-#pragma unroll
-                    for (int e = 0; e < EPL; e += 4)
-                        *reinterpret_cast<float4*>(dst + e) =
-                            make_float4(acc[e][r], acc[e + 1][r], acc[e + 2][r], acc[e + 3][r]);
-                }
-                if (c == 0) *reinterpret_cast<float2*>(a.ws_ml + ph * 2) = make_float2(m, l);
-            }
-        }
-    } else {
-        extern __shared__ float smem[];
+    if constexpr (SPLIT) {
+        // per-head totals: the four c-lanes of head n hold partial sums of l
+        l += xor16(l);
+        l += xor32(l, addr_x32);
         float* sm_ml = smem;                 // [W][G][2]
         float* sm_acc = smem + W * G * 2;    // [W][G][D]
         if (n < G) {
@@ -261,40 +217,8 @@ __global__ __launch_bounds__(256) void pa_partition_mfma(DecodeArgs a, int G, in
             }
         }
         __syncthreads();
-
-        for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-            const int g = idx / D;
-            const int dd = idx % D;
-            float M = sm_ml[g * 2];
-#pragma unroll
-            for (int w = 1; w < W; ++w) M = fmaxf(M, sm_ml[(w * G + g) * 2]);
-            float lsum = 0.f, A = 0.f;
-#pragma unroll
-            for (int w = 0; w < W; ++w) {
-                const float mw = sm_ml[(w * G + g) * 2];
-                const float f = (M == -INFINITY) ? 0.f : fast_exp2(mw - M);
-                lsum += f * sm_ml[(w * G + g) * 2 + 1];
-                A += f * sm_acc[(w * G + g) * D + dd];
-            }
-            if (nparts == 1) {
-                a.out[out_row0 + idx] = S::narrow(lsum > 0.f ? A / lsum : 0.f);
-            } else {
-                const size_t ph = (static_cast<size_t>(b) * a.num_q_heads + h0 + g) * a.num_parts + p;
-                a.ws_acc[ph * D + dd] = A;
-                if (dd == 0) {
-                    a.ws_ml[ph * 2 + 0] = M;
-                    a.ws_ml[ph * 2 + 1] = lsum;
-                }
-            }
-        }
+        merge_waves_and_store<S, D>(a, it, G, sm_ml, sm_acc);
     }
-}
-
-// One wave per item once there are enough items to fill the GPU several times over.
-static bool use_split(int64_t items) {
-    const char* env = getenv("PAGEDKV_SPLIT");
-    if (env) return env[0] == '1';
-    return items < 4096;
 }
 
 template <class S, int D>
@@ -302,19 +226,36 @@ hipError_t launch_t(int group, const DecodeArgs& a, hipStream_t stream) {
     const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.num_parts;
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidValue;
-    if (use_split(items)) {
-        const size_t lds = static_cast<size_t>(kWavesPerGroup) * group * (D + 2) * sizeof(float);
-        hipLaunchKernelGGL((pa_partition_mfma<S, D, true>), dim3(static_cast<unsigned>(items)),
-                           dim3(64 * kWavesPerGroup), lds, stream, a, group, static_cast<int>(items));
+    const size_t stage = static_cast<size_t>(group) * (D + 4) * sizeof(float);
+    const Plan pl = make_plan(a, static_cast<int>(stage), true);
+    if (pl.group_waves > 0) {
+        // partials (if any) are per chunk: the reduce kernel sees chunks as partitions
+        const int64_t wgs = static_cast<int64_t>(a.batch) * a.num_kv_heads * pl.chunks;
+        hipLaunchKernelGGL((pa_partition_mfma<S, D, kGroup>), dim3(static_cast<unsigned>(wgs)),
+                           dim3(64 * pl.group_waves), pl.chunk * stage, stream, a, group,
+                           static_cast<int>(wgs), pl.chunk, pl.ppw);
+    } else if (split_items(items)) {
+        hipLaunchKernelGGL((pa_partition_mfma<S, D, kSplit>), dim3(static_cast<unsigned>(items)),
+                           dim3(64 * kWavesPerGroup), kWavesPerGroup * stage, stream, a, group,
+                           static_cast<int>(items), 1, 1);
     } else {
-        const int64_t groups = (items + kWavesPerGroup - 1) / kWavesPerGroup;
-        hipLaunchKernelGGL((pa_partition_mfma<S, D, false>), dim3(static_cast<unsigned>(groups)),
-                           dim3(64 * kWavesPerGroup), 0, stream, a, group, static_cast<int>(items));
+        static const int64_t slots = resident_waves(reinterpret_cast<const void*>(&pa_partition_mfma<S, D, kItem>));
+        const int per = partitions_per_wave(items, slots, a.num_parts, a.part_blocks);
+        const int64_t waves = static_cast<int64_t>(a.batch) * a.num_kv_heads * ceil_div(a.num_parts, per);
+        const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+        hipLaunchKernelGGL((pa_partition_mfma<S, D, kItem>), dim3(static_cast<unsigned>(groups)),
+                           dim3(64 * kWavesPerGroup), kWavesPerGroup * stage, stream, a, group,
+                           static_cast<int>(waves), per, 1);
     }
     return hipGetLastError();
 }
 
 }  // namespace
+
+int partition_chunk_mfma(int group, int head_dim, const DecodeArgs& a) {
+    const int stage = group * (head_dim + 4) * static_cast<int>(sizeof(float));
+    return make_plan(a, stage, true).chunk;
+}
 
 hipError_t launch_partitions_mfma(int dtype, int head_dim, int group, const DecodeArgs& a,
                                   hipStream_t stream) {

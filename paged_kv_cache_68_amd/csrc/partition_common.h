@@ -1,0 +1,362 @@
+// Pieces shared by the two partition kernels (VALU for single-head groups, MFMA for
+// GQA groups): which (sequence, KV head, partition) a wave works on, how it finds its
+// blocks through the block table, and how it walks them with a fixed number of loads
+// in flight.
+//
+// Address translation follows "PagedAttention: Treating KV Memory Like Virtual Memory"
+// ("How the kernel reads a block table": the tile at position i lives at
+// block_table[i / B] * block stride + (i mod B) * slot stride) and section 4 of
+// "PagedAttention and Virtual Memory Management" (Addr_K / Addr_V).  B = 16 is a
+// power of two, so positions split into (block, slot) with a shift and a mask, and a
+// 16-token tile is exactly one block: the table is read once per block, not per token.
+#pragma once
+
+#include <stdlib.h>
+
+#include "device_common.h"
+
+namespace pkv {
+
+// One unit of work: partitions [p, p_end) of sequence b for KV head kvh, i.e. the
+// sequence's blocks [j0, j1).  A wave that owns several consecutive partitions walks
+// their blocks as one stream and emits one result per partition.
+struct Item {
+    int b, kvh;
+    int p, p_end;
+    int L;        // context length, clamped to the table width
+    int nparts;   // partitions this sequence actually has
+    int j0, j1;
+};
+
+// Items are numbered with the KV head fastest, then the sequence, then the partition
+// group: the 4 waves of a work-group take 4 KV heads of the same blocks.
+__device__ __forceinline__ Item decode_item(const DecodeArgs& a, int item, int per_item) {
+    Item it;
+    it.kvh = item % a.num_kv_heads;
+    const int rest = item / a.num_kv_heads;
+    it.b = rest % a.batch;
+    const int g = rest / a.batch;
+    int L = a.lens[it.b];
+    L = L < 0 ? 0 : (L > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : L);
+    it.L = L;
+    const int nblk = (L + kBlockSize - 1) / kBlockSize;
+    it.nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
+    it.p = g * per_item;
+    it.p_end = min(it.nparts, it.p + per_item);
+    it.j0 = it.p * a.part_blocks;
+    it.j1 = min(nblk, it.p_end * a.part_blocks);
+    return it;
+}
+
+// The blocks one wave visits: jb + js*k for k < nk.  Their table entries sit one per
+// lane in up to four VGPRs (partitions of at most 4096 tokens) and are fetched once.
+struct BlockWalk {
+    int jb, js, nk;
+    int tab[4];
+
+    __device__ __forceinline__ void init(const DecodeArgs& a, const Item& it, int first, int step,
+                                         int lane) {
+        jb = it.j0 + first;
+        js = step;
+        nk = it.j1 > jb ? (it.j1 - jb + js - 1) / js : 0;
+        const int32_t* trow = a.tables + static_cast<size_t>(it.b) * a.max_blocks;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k = 64 * t + lane;
+            tab[t] = (64 * t < nk && k < nk) ? trow[jb + js * k] : -1;
+        }
+    }
+
+    // Blocks [j_begin, j_end) of the item's sequence, one after another.
+    __device__ __forceinline__ void init_range(const DecodeArgs& a, const Item& it, int j_begin,
+                                               int j_end, int lane) {
+        jb = j_begin;
+        js = 1;
+        nk = j_end > jb ? j_end - jb : 0;
+        const int32_t* trow = a.tables + static_cast<size_t>(it.b) * a.max_blocks;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k = 64 * t + lane;
+            tab[t] = (64 * t < nk && k < nk) ? trow[jb + k] : -1;
+        }
+    }
+
+    // k-th block -> number of valid tokens and buffer resources over exactly those
+    // token rows of K and V (empty past the last block or for an out-of-range entry,
+    // so loads there return zeros and read nothing).
+    __device__ __forceinline__ int at(const DecodeArgs& a, const Item& it, int k, int row_bytes,
+                                      __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv) const {
+        int valid = 0;
+        size_t off = 0;
+        if (k < nk) {
+            const int kk = k & 63;
+            const int t = k < 64 ? __builtin_amdgcn_readlane(tab[0], kk)
+                        : k < 128 ? __builtin_amdgcn_readlane(tab[1], kk)
+                        : k < 192 ? __builtin_amdgcn_readlane(tab[2], kk)
+                                  : __builtin_amdgcn_readlane(tab[3], kk);
+            if (static_cast<unsigned>(t) < static_cast<unsigned>(a.num_blocks)) {
+                valid = min(kBlockSize, it.L - (jb + js * k) * kBlockSize);
+                off = static_cast<size_t>(t) * (static_cast<size_t>(row_bytes / 2) * kBlockSize);
+            }
+        }
+        // everything here is wave-uniform; say so, or the resource would be rebuilt
+        // lane by lane around every load
+        valid = uniform(valid);
+        const uint64_t uoff = (static_cast<uint64_t>(uniform(static_cast<int>(off >> 32))) << 32) |
+                              static_cast<uint32_t>(uniform(static_cast<int>(off & 0xffffffffu)));
+        rk = make_rsrc(a.k + uoff, valid * row_bytes);
+        rv = make_rsrc(a.v + uoff, valid * row_bytes);
+        return valid;
+    }
+};
+
+// Run `process(k, valid, buf)` over the wave's blocks with two register sets used in
+// turn.  Every iteration issues exactly one block's loads (an empty resource past the
+// last block), so the wait before a block is computed always leaves the next block's
+// loads in flight.
+template <class Buf, class Load, class Process>
+__device__ __forceinline__ void walk_blocks(const DecodeArgs& a, const Item& it, const BlockWalk& w,
+                                            int row_bytes, Load load, Process process) {
+    Buf ba, bb;
+    __amdgpu_buffer_rsrc_t rk, rv;
+    int valid_a = w.at(a, it, 0, row_bytes, rk, rv);
+    load(rk, rv, ba);
+    for (int k = 0; k < w.nk; k += 2) {
+        const int valid_b = w.at(a, it, k + 1, row_bytes, rk, rv);
+        load(rk, rv, bb);
+        // keep the scheduler from sinking these loads into the computation below:
+        // they must be issued before the wait for the current block's data
+        __builtin_amdgcn_sched_barrier(0);
+        process(k, valid_a, ba);
+        if (k + 1 >= w.nk) break;
+        valid_a = w.at(a, it, k + 2, row_bytes, rk, rv);
+        load(rk, rv, ba);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k + 1, valid_b, bb);
+    }
+}
+
+// Same walk with three register sets: two blocks' loads stay in flight while one is
+// computed.  For kernels whose register budget allows it at the same occupancy.
+template <class Buf, class Load, class Process>
+__device__ __forceinline__ void walk_blocks3(const DecodeArgs& a, const Item& it, const BlockWalk& w,
+                                             int row_bytes, Load load, Process process) {
+    Buf b0, b1, b2;
+    __amdgpu_buffer_rsrc_t rk, rv;
+    int v0 = w.at(a, it, 0, row_bytes, rk, rv);
+    load(rk, rv, b0);
+    int v1 = w.at(a, it, 1, row_bytes, rk, rv);
+    load(rk, rv, b1);
+    for (int k = 0; k < w.nk; k += 3) {
+        const int v2 = w.at(a, it, k + 2, row_bytes, rk, rv);
+        load(rk, rv, b2);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k, v0, b0);
+        if (k + 1 >= w.nk) break;
+        v0 = w.at(a, it, k + 3, row_bytes, rk, rv);
+        load(rk, rv, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k + 1, v1, b1);
+        if (k + 2 >= w.nk) break;
+        v1 = w.at(a, it, k + 4, row_bytes, rk, rv);
+        load(rk, rv, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k + 2, v2, b2);
+    }
+}
+
+// Partial results live in the workspace as [B][Hkv][P][G] rows (D floats of
+// accumulator, 2 floats of running max / sum): the G heads of one item are one
+// contiguous stretch, written with full, coalesced lines.
+__device__ __forceinline__ size_t part_row(const DecodeArgs& a, int b, int kvh, int p, int G) {
+    return ((static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.num_parts + p) * G;
+}
+
+// One wave writes the result of partition p of its item from a staging area in LDS
+// (st_acc[G][D] accumulators, st_ml[G][2] running max / sum): the final output if the
+// sequence has a single partition, else the fp32 partials.  All 64 lanes take part, each
+// with 16-byte accesses, so the global writes are whole contiguous lines.
+template <class S, int D>
+__device__ __forceinline__ void store_partition(const DecodeArgs& a, const Item& it, int G, int p,
+                                                const float* st_acc, const float* st_ml, int lane) {
+    const int n = G * D;
+    if (it.nparts == 1) {
+        uint16_t* o = a.out + (static_cast<size_t>(it.b) * a.num_q_heads + it.kvh * G) * D;
+        for (int i = lane * 8; i < n; i += 512) {
+            const float lg = st_ml[2 * (i / D) + 1];
+            const float4 x0 = *reinterpret_cast<const float4*>(st_acc + i);
+            const float4 x1 = *reinterpret_cast<const float4*>(st_acc + i + 4);
+            const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = static_cast<uint32_t>(S::narrow(lg > 0.f ? v[2 * e] / lg : 0.f)) |
+                       (static_cast<uint32_t>(S::narrow(lg > 0.f ? v[2 * e + 1] / lg : 0.f)) << 16);
+            *reinterpret_cast<uint4*>(o + i) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    } else {
+        const size_t row0 = part_row(a, it.b, it.kvh, p, G);
+        float* dst = a.ws_acc + row0 * D;
+        for (int i = lane * 4; i < n; i += 256)
+            *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(st_acc + i);
+        if (lane < 2 * G) a.ws_ml[row0 * 2 + lane] = st_ml[lane];
+    }
+}
+
+// Four waves that shared one item have left their (m, l) in sm_ml[W][G][2] and their
+// accumulators in sm_acc[W][G][D] (dimension order); merge them with the cross-block
+// rule and write the partition's result: the final output if the sequence has a single
+// partition, else the fp32 partials (m, l, acc) for the reduce kernel.
+template <class S, int D>
+__device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const Item& it, int G,
+                                                      const float* sm_ml, const float* sm_acc) {
+    constexpr int W = kWavesPerGroup;
+    const int h0 = it.kvh * G;
+    const size_t out_row0 = (static_cast<size_t>(it.b) * a.num_q_heads + h0) * D;
+    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+        const int g = idx / D;
+        const int dd = idx % D;
+        float M = sm_ml[g * 2];
+#pragma unroll
+        for (int w = 1; w < W; ++w) M = fmaxf(M, sm_ml[(w * G + g) * 2]);
+        float lsum = 0.f, A = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float f = (M == -INFINITY) ? 0.f : fast_exp2(sm_ml[(w * G + g) * 2] - M);
+            lsum += f * sm_ml[(w * G + g) * 2 + 1];
+            A += f * sm_acc[(w * G + g) * D + dd];
+        }
+        if (it.nparts == 1) {
+            a.out[out_row0 + idx] = S::narrow(lsum > 0.f ? A / lsum : 0.f);
+        } else {
+            const size_t row = part_row(a, it.b, it.kvh, it.p, G) + g;
+            a.ws_acc[row * D + dd] = A;
+            if (dd == 0) {
+                a.ws_ml[row * 2 + 0] = M;
+                a.ws_ml[row * 2 + 1] = lsum;
+            }
+        }
+    }
+}
+
+// A work-group has left the states of the np = p_end - p partitions of its chunk in LDS
+// (slot i: [G][D] accumulators, then (m, l) per head, G*(D+4) floats per slot); combine
+// them in ascending order with the cross-block rule.  If the chunk is the whole
+// sequence the result is final; otherwise it is written as the partial of chunk
+// p / chunk, with `nchunks` chunks per sequence, for the reduce kernel.
+template <class S, int D>
+__device__ __forceinline__ void merge_chunk_and_store(const DecodeArgs& a, const Item& it, int G,
+                                                      const float* smem, int chunk, int nchunks) {
+    const int np = it.p_end - it.p;
+    const int stride = G * (D + 4);
+    const bool whole = it.p == 0 && it.p_end == it.nparts;
+    const size_t out_row0 = (static_cast<size_t>(it.b) * a.num_q_heads + it.kvh * G) * D;
+    const size_t row0 = ((static_cast<size_t>(it.b) * a.num_kv_heads + it.kvh) * nchunks + it.p / chunk) * G;
+    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+        const int g = idx / D;
+        const int dd = idx % D;
+        float M = -INFINITY;
+        for (int i = 0; i < np; ++i) M = fmaxf(M, smem[i * stride + G * D + 2 * g]);
+        float lsum = 0.f, A = 0.f;
+        for (int i = 0; i < np; ++i) {
+            const float* st = smem + i * stride;
+            const float f = (M == -INFINITY) ? 0.f : fast_exp2(st[G * D + 2 * g] - M);
+            lsum += f * st[G * D + 2 * g + 1];
+            A += f * st[g * D + dd];
+        }
+        if (whole) {
+            a.out[out_row0 + idx] = S::narrow(lsum > 0.f ? A / lsum : 0.f);
+        } else {
+            a.ws_acc[(row0 + g) * D + dd] = A;
+            if (dd == 0) {
+                a.ws_ml[(row0 + g) * 2 + 0] = M;
+                a.ws_ml[(row0 + g) * 2 + 1] = lsum;
+            }
+        }
+    }
+}
+
+// Zero output for a sequence with no tokens (written once, by partition 0's item).
+template <int D>
+__device__ __forceinline__ void store_empty(const DecodeArgs& a, const Item& it, int G, int t0, int nt) {
+    if (it.p != 0) return;
+    const size_t out_row0 = (static_cast<size_t>(it.b) * a.num_q_heads + it.kvh * G) * D;
+    for (int i = t0; i < G * D; i += nt) a.out[out_row0 + i] = 0;
+}
+
+// Work-groups per XCD chunk in the launch renumbering (see xcd_chunked).
+constexpr int kXcdChunk = 16;
+
+// Choose between one wave per item and four waves sharing an item.  PAGEDKV_SPLIT=0/1
+// forces one of them (used by the tests to cover both on small inputs).
+inline bool split_items(int64_t items) {
+    const char* env = getenv("PAGEDKV_SPLIT");
+    if (env && (env[0] == '0' || env[0] == '1')) return env[0] == '1';
+    return items < 4096;
+}
+
+// Waves of `kernel` (256-thread work-groups) the GPU holds at once.
+inline int64_t resident_waves(const void* kernel) {
+    int dev = 0, cus = 0, blocks = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, 64 * kWavesPerGroup, 0) !=
+            hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return static_cast<int64_t>(cus) * blocks * kWavesPerGroup;
+}
+
+// Partitions per wave when waves own whole items: enough waves for about two rounds
+// of the GPU's resident waves (`slots`), at most 256 blocks of table per wave.
+inline int partitions_per_wave(int64_t items, int64_t slots, int num_parts, int part_blocks) {
+    const char* env = getenv("PAGEDKV_PARTS_PER_WAVE");     // override, for the tests
+    int64_t per = env ? atoi(env) : (slots > 0 ? items / (2 * slots) : 1);
+    const int64_t cap = 256 / part_blocks;
+    if (per > num_parts) per = num_parts;
+    if (per > cap) per = cap;
+    return per < 1 ? 1 : static_cast<int>(per);
+}
+
+// How the partition kernel covers the batch.  `chunk` partitions are combined inside
+// the kernel (1 unless a work-group merges a chunk), so the reduce kernel sees
+// `chunks` = ceil(P / chunk) partial results per sequence of `chunk * part_blocks`
+// blocks each.
+struct Plan {
+    int group_waves;   // > 0: work-groups of this many waves merge chunks in LDS
+    int ppw;           // partitions per wave in that mode
+    int chunk;
+    int chunks;
+};
+
+// Work-group chunks when there is enough work (the same threshold that sends waves to
+// whole items) and more than one partition; at most 8 waves and 16 partitions per
+// work-group, and the chunk's states must fit in 64 KiB of LDS.  PAGEDKV_GROUP=0
+// disables the mode; PAGEDKV_GROUP_WAVES / _PPW override its shape (tuning knobs).
+inline Plan make_plan(const DecodeArgs& a, int stage_bytes, bool group_capable) {
+    Plan pl{0, 1, 1, a.num_parts};
+    const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.num_parts;
+    const char* env = getenv("PAGEDKV_GROUP");
+    const bool allowed = group_capable && !(env && env[0] == '0') && !split_items(items);
+    if (!allowed || a.num_parts < 2) return pl;
+    int chunk = a.num_parts < 16 ? a.num_parts : 16;
+    const int lds_cap = (64 * 1024) / stage_bytes;
+    if (chunk > lds_cap) chunk = lds_cap;
+    if (chunk < 2) return pl;
+    int waves = chunk < 8 ? chunk : 8;
+    const char* ew = getenv("PAGEDKV_GROUP_WAVES");
+    if (ew && atoi(ew) > 0) waves = atoi(ew) < 8 ? atoi(ew) : 8;
+    int ppw = (chunk + waves - 1) / waves;
+    const char* ep = getenv("PAGEDKV_GROUP_PPW");
+    if (ep && atoi(ep) > 0) ppw = atoi(ep);
+    if (waves * ppw < chunk) chunk = waves * ppw;
+    waves = (chunk + ppw - 1) / ppw;      // no wave without a partition
+    pl.group_waves = waves;
+    pl.ppw = ppw;
+    pl.chunk = chunk;
+    pl.chunks = (a.num_parts + chunk - 1) / chunk;
+    return pl;
+}
+
+}  // namespace pkv

@@ -264,3 +264,25 @@ def test_scale_is_applied():
                                   torch.from_numpy(lens).cuda(), scale=scale)
         ref = oracle.paged_decode(q, kp, vp, tables, lens, scale, 16, "f16")
         assert max_abs_err(to_host_bits(out), ref, "f16") <= TOL["f16"]
+
+
+# ------------------------------------------------------------------ every launch shape
+
+@pytest.mark.parametrize("split,per", [("1", None), ("0", "1"), ("0", "2"), ("0", "3"), ("0", "8")])
+@pytest.mark.parametrize("kernel", ["auto", "valu"])
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(8, 2, 128, "bf16"), (4, 4, 128, "f16"), (14, 2, 64, "f16")])
+def test_launch_shapes_match_oracle(split, per, kernel, hq, hkv, d, dtype, monkeypatch):
+    """Four waves per partition, or one wave walking 1/2/3/8 partitions in one stream;
+    matrix-core and VALU kernels: all must match the oracle (and each other's bits
+    within a kernel, since the summation order depends only on logical positions)."""
+    monkeypatch.setenv("PAGEDKV_SPLIT", split)
+    if per is not None:
+        monkeypatch.setenv("PAGEDKV_PARTS_PER_WAVE", per)
+    if kernel != "auto":
+        monkeypatch.setenv("PAGEDKV_KERNEL", kernel)
+    lens = [1, 15, 16, 17, 511, 512, 513, 1024, 1025, 2000, 0, 3000]
+    cfg, lens, tables, kp, vp, q = _custom_case(lens, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=11)
+    out = _run_custom(cfg, lens, tables, kp, vp, q, 512)
+    ref = oracle.paged_decode(q, kp, vp, tables, lens, cfg.scale, 16, dtype)
+    assert max_abs_err(out, ref, dtype) <= TOL[dtype]
+    assert not out[10].any()                       # the empty sequence
