@@ -151,9 +151,10 @@ size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
  *                 output.  Slots at or past the length in the last block are never read.
  *  num_q_heads  : multiple of the pool's num_kv_heads; query head h reads KV head
  *                 h / (num_q_heads / num_kv_heads) (contiguous GQA groups); group
- *                 sizes 1..8 are supported.
+ *                 sizes 1..16 are supported.
  *  scale        : multiplies q.k before the softmax (normally 1/sqrt(head_dim)).
- *  partition_size: tokens per split-context partition (multiple of 16; 0 = 512).  A
+ *  partition_size: tokens per split-context partition (multiple of 16, at most 4096;
+ *                 0 = 512; larger values return KV_ERR_UNSUPPORTED).  A
  *                 sequence longer than one partition is split across work-groups
  *                 whose partial results are combined by a second kernel
  *                 ("PagedAttention and Virtual Memory Management", section 4,

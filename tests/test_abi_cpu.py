@@ -142,7 +142,7 @@ def test_decode_argument_checks():
     assert _decode(h, out=None) == E.KV_ERR_INVALID_ARG
     assert _decode(h, query=A + 2) == E.KV_ERR_INVALID_ARG     # misaligned
     assert _decode(h, hq=15) == E.KV_ERR_UNSUPPORTED           # not a multiple of Hkv
-    assert _decode(h, hq=18) == E.KV_ERR_UNSUPPORTED           # group 9 > 8
+    assert _decode(h, hq=34) == E.KV_ERR_UNSUPPORTED           # group 17 > 16
     assert _decode(h, hq=0) == E.KV_ERR_INVALID_ARG
     assert _decode(h, part=100) == E.KV_ERR_INVALID_ARG
     assert _decode(h, max_blocks=0) == E.KV_ERR_INVALID_ARG

@@ -139,7 +139,7 @@ def _small_cfg(hq, hkv, d, dtype, lens_name="fixed_1_16_17_40", nb=256, batch=4,
                         description="sweep")
 
 
-@pytest.mark.parametrize("g", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_group_and_head_dim_sweep(g, d, dtype):
