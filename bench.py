@@ -116,8 +116,9 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="run only a plain 1 GiB elementwise copy (torch.neg on fp16), the "
-                         "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
+                    help="run only a plain copy of known size (the cache-write kernel copying "
+                         "512 MiB to consecutive slots), the reference for scaling rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -134,14 +135,20 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     if args.copy_calibration:
-        n = 1 << 29                                  # 2^29 fp16 = 1 GiB read + 1 GiB written
-        src = torch.ones(n, dtype=torch.float16, device="cuda")
-        dst = torch.empty_like(src)
+        # reshape_and_cache as a plain row copy: 131,072 rows of 2 KiB, K and V, to
+        # consecutive slots -> 512 MiB read and 512 MiB written per launch
+        T = 131072
+        pool = pk.KVPool(1, T // 16, 8, 128, "bf16")
+        key = torch.ones((T, 8, 128), dtype=torch.bfloat16, device="cuda")
+        value = torch.ones_like(key)
+        slots = torch.arange(T, dtype=torch.int64, device="cuda")
         for _ in range(3):
-            torch.neg(src, out=dst)
+            pk.reshape_and_cache(pool, 0, key, value, slots)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration": {"bytes_read": 2 * n, "bytes_written": 2 * n,
-                                               "launches": 3, "kernel": "torch.neg fp16"}}))
+        nbytes = 2 * T * 8 * 128 * 2
+        print(json.dumps({"copy_calibration": {"kernel": "rc_scatter", "launches": 3,
+                                               "bytes_read_per_launch": nbytes,
+                                               "bytes_written_per_launch": nbytes}}))
         return 0
 
     cfg = config_by_name(args.config)
