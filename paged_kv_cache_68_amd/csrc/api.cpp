@@ -124,10 +124,11 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     a.part_blocks = s.part_blocks;
     a.num_parts = s.num_parts;
     a.scale_log2 = scale * 1.4426950408889634f;
-    // PAGEDKV_XCD_CHUNK overrides the chunk of the XCD renumbering (tuning knob)
+    // PAGEDKV_XCD_CHUNK overrides the chunk of the XCD renumbering (tuning knob; 0 keeps
+    // launch order)
     const char* x = getenv("PAGEDKV_XCD_CHUNK");
     a.xcd_chunk = x ? atoi(x) : 16;
-    if (a.xcd_chunk < 1) a.xcd_chunk = 1;
+    if (a.xcd_chunk < 0) a.xcd_chunk = 0;
     return a;
 }
 

@@ -139,9 +139,10 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 // that read the same blocks (neighbouring sequences of a shared prefix, the KV heads of
 // one block) meet in the same L2, while the chunks still rotate over the XCDs, so long
 // and short items stay evenly spread.  Bijective on [0, n); the tail that does not fill
-// a whole round of chunks keeps its own number.
+// a whole round of chunks keeps its own number.  chunk <= 0 keeps launch order.
 __device__ __forceinline__ int xcd_chunked(int id, int n, int chunk) {
     constexpr int kXcds = 8;
+    if (chunk <= 0) return id;
     const int round = kXcds * chunk;
     if (id >= (n / round) * round) return id;
     const int x = id % kXcds;

@@ -363,8 +363,7 @@ static int kernel_choice(int group) {
 }
 
 int partition_chunk(int dtype, int head_dim, int group, const DecodeArgs& a) {
-    (void)dtype;
-    return kernel_choice(group) == 1 ? partition_chunk_mfma(group, head_dim, a) : 1;
+    return kernel_choice(group) == 1 ? partition_chunk_mfma(dtype, group, head_dim, a) : 1;
 }
 
 hipError_t launch_partitions(int dtype, int head_dim, int group, const DecodeArgs& a,

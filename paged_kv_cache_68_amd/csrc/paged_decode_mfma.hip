@@ -40,16 +40,38 @@ namespace {
 //  kItem  : each wave owns whole items (one or more consecutive partitions, walked as
 //           one stream) and writes each partition's partial result to the workspace;
 //           a second kernel combines the partitions.
-//  kGroup : a work-group of NW waves owns a chunk of PC consecutive partitions of one
-//           (sequence, KV head); each wave walks PC/NW of them, leaves each partition's
-//           state in LDS, and the work-group combines the chunk with the cross-block
-//           rule.  A sequence that fits in one chunk gets its final output right away:
-//           no partial results go to HBM and no second kernel runs.
+//  kGroup : a work-group owns a chunk of `per_item` consecutive partitions of `heads`
+//           consecutive KV heads of one sequence, with blockDim / 64 / heads waves
+//           ("slots") per head; each wave walks `ppw` consecutive partitions of its head
+//           as one stream, leaves its state in LDS, and the work-group combines the
+//           slots of each head with the cross-block rule.  A sequence that fits in one
+//           chunk gets its final output right away: no partial results go to HBM and no
+//           second kernel runs.
 enum Mode { kSplit = 0, kItem = 1, kGroup = 2 };
+
+// kGroup: the blocks of chunk c (partitions [c * chunk, (c + 1) * chunk)) that slot
+// `slot` of KV head kvh of sequence b walks: partitions [p, p_end), possibly none.
+__device__ __forceinline__ Item group_item(const DecodeArgs& a, int b, int kvh, int c, int chunk,
+                                           int slot, int ppw) {
+    Item it;
+    it.b = b;
+    it.kvh = kvh;
+    int L = a.lens[b];
+    L = L < 0 ? 0 : (L > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : L);
+    it.L = L;
+    const int nblk = (L + kBlockSize - 1) / kBlockSize;
+    it.nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
+    const int chunk_end = min(it.nparts, (c + 1) * chunk);
+    it.p = c * chunk + slot * ppw;
+    it.p_end = max(it.p, min(chunk_end, it.p + ppw));
+    it.j0 = min(nblk, it.p * a.part_blocks);
+    it.j1 = min(nblk, it.p_end * a.part_blocks);
+    return it;
+}
 
 template <class S, int D, int MODE>
 __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, int n_items,
-                                                         int per_item, int ppw) {
+                                                         int per_item, int ppw, int heads) {
     constexpr bool SPLIT = MODE == kSplit;
     constexpr int W = kWavesPerGroup;
     constexpr int NQK = D / 32;    // score MFMAs per block
@@ -66,23 +88,37 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
     const int c = lane >> 4;
 
     const int group_id = xcd_chunked(blockIdx.x, gridDim.x, a.xcd_chunk);
-    const int item = MODE == kItem ? group_id * W + wave : group_id;
-    if (MODE == kItem && item >= n_items) return;
-    const Item it = decode_item(a, item, SPLIT ? 1 : per_item);
-    const bool wg_wide = MODE != kItem;          // the whole work-group works on `it`
-    if (it.L == 0) {
-        store_empty<D>(a, it, G, wg_wide ? threadIdx.x : lane, wg_wide ? blockDim.x : 64);
-        return;
+    Item it;
+    int chunk_id = 0;
+    if constexpr (MODE == kGroup) {
+        // work-group -> (KV heads [kvh0, kvh0 + heads), sequence, chunk); wave -> (head, slot)
+        const int ngrp = a.num_kv_heads / heads;
+        const int rest = group_id / ngrp;
+        chunk_id = rest / a.batch;
+        it = group_item(a, rest % a.batch, (group_id % ngrp) * heads + wave % heads, chunk_id,
+                        per_item, wave / heads, ppw);
+        // both exits below are the same for the whole work-group (same sequence, chunk)
+        if (it.L == 0) {
+            if (it.p == 0) store_empty<D>(a, it, G, lane, 64);
+            return;
+        }
+        if (chunk_id * per_item >= it.nparts) return;
+    } else {
+        const int item = MODE == kItem ? group_id * W + wave : group_id;
+        if (MODE == kItem && item >= n_items) return;
+        it = decode_item(a, item, SPLIT ? 1 : per_item);
+        if (it.L == 0) {
+            store_empty<D>(a, it, G, SPLIT ? threadIdx.x : lane, SPLIT ? blockDim.x : 64);
+            return;
+        }
+        if (it.p >= it.nparts) return;
     }
-    if (it.p >= it.nparts) return;
     const int h0 = it.kvh * G;
     const size_t out_row0 = (static_cast<size_t>(it.b) * a.num_q_heads + h0) * D;
 
     BlockWalk walk;
     if constexpr (MODE == kGroup) {
-        // this wave's partitions: [p + wave*ppw, p + (wave+1)*ppw) within the chunk
-        const int jw = (it.p + wave * ppw) * a.part_blocks;
-        walk.init_range(a, it, min(jw, it.j1), min(jw + ppw * a.part_blocks, it.j1), lane);
+        walk.init_range(a, it, it.j0, it.j1, lane);
     } else {
         walk.init(a, it, SPLIT ? wave : 0, SPLIT ? W : 1, lane);
     }
@@ -123,13 +159,13 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
         }
     };
 
-    // (!SPLIT) result of partition p from this wave's state, then a fresh state.  The
-    // accumulators sit in 16 of the 64 lanes (n < G); they go through this wave's LDS
-    // staging area so that every lane writes whole lines.
+    // (!SPLIT) this wave's state into its LDS stage, then a fresh state.  kItem: the
+    // result of partition p, written out from the stage so that every lane writes whole
+    // lines (the accumulators sit in 16 of the 64 lanes, n < G).  kGroup: the state the
+    // work-group merges.
     extern __shared__ float smem[];
     float* stage = smem + wave * G * (D + 4);     // [G][D], then (m, l) per head, 16-B aligned
     auto flush = [&](int p) {
-        if constexpr (MODE == kGroup) stage = smem + (p - it.p) * G * (D + 4);
         float lt = l + xor16(l);
         lt += xor32(lt, addr_x32);
         if (n < G) {
@@ -186,7 +222,7 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
             acc[2 * q] = S::mfma_k16(even, pt, acc[2 * q]);
             acc[2 * q + 1] = S::mfma_k16(odd, pt, acc[2 * q + 1]);
         }
-        if constexpr (!SPLIT) {     // last block of a partition: emit it
+        if constexpr (MODE == kItem) {     // last block of a partition: emit it
             const int j = walk.jb + k;
             if ((j + 1) % a.part_blocks == 0 || k + 1 == walk.nk) flush(j / a.part_blocks);
         }
@@ -196,8 +232,13 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
     else walk_blocks<Buf>(a, it, walk, row_bytes, load, process);
 
     if constexpr (MODE == kGroup) {
+        flush(it.p);
         __syncthreads();
-        merge_chunk_and_store<S, D>(a, it, G, smem, per_item, (a.num_parts + per_item - 1) / per_item);
+        const int nchunks = (a.num_parts + per_item - 1) / per_item;
+        const bool whole = chunk_id == 0 && it.nparts <= per_item;
+        merge_slots_and_store<S, D>(a, it.b, it.kvh - wave % heads, heads,
+                                    static_cast<int>(blockDim.x / 64) / heads, G, smem, chunk_id,
+                                    nchunks, whole);
     }
     if constexpr (SPLIT) {
         // per-head totals: the four c-lanes of head n hold partial sums of l
@@ -221,23 +262,34 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
     }
 }
 
+// Waves of the group-plan kernel the GPU holds at once.
+template <class S, int D>
+int64_t group_target_waves() {
+    static const int64_t waves = resident_waves(reinterpret_cast<const void*>(&pa_partition_mfma<S, D, kGroup>));
+    return waves;
+}
+
 template <class S, int D>
 hipError_t launch_t(int group, const DecodeArgs& a, hipStream_t stream) {
     const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.num_parts;
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidValue;
     const size_t stage = static_cast<size_t>(group) * (D + 4) * sizeof(float);
-    const Plan pl = make_plan(a, static_cast<int>(stage), true);
+    const Plan pl = make_plan(a, static_cast<int>(stage), true, group_target_waves<S, D>());
     if (pl.group_waves > 0) {
-        // partials (if any) are per chunk: the reduce kernel sees chunks as partitions
-        const int64_t wgs = static_cast<int64_t>(a.batch) * a.num_kv_heads * pl.chunks;
+        // partials (if any) are per chunk: the reduce kernel sees chunks as partitions.
+        // Work-groups keep launch order here: the XCDs then take neighbouring head
+        // pairs of the same blocks, which measured faster than chunked renumbering.
+        DecodeArgs g = a;
+        g.xcd_chunk = 0;
+        const int64_t wgs = static_cast<int64_t>(a.batch) * (a.num_kv_heads / pl.heads) * pl.chunks;
         hipLaunchKernelGGL((pa_partition_mfma<S, D, kGroup>), dim3(static_cast<unsigned>(wgs)),
-                           dim3(64 * pl.group_waves), pl.chunk * stage, stream, a, group,
-                           static_cast<int>(wgs), pl.chunk, pl.ppw);
+                           dim3(64 * pl.group_waves), pl.group_waves * stage, stream, g, group,
+                           static_cast<int>(wgs), pl.chunk, pl.ppw, pl.heads);
     } else if (split_items(items)) {
         hipLaunchKernelGGL((pa_partition_mfma<S, D, kSplit>), dim3(static_cast<unsigned>(items)),
                            dim3(64 * kWavesPerGroup), kWavesPerGroup * stage, stream, a, group,
-                           static_cast<int>(items), 1, 1);
+                           static_cast<int>(items), 1, 1, 1);
     } else {
         static const int64_t slots = resident_waves(reinterpret_cast<const void*>(&pa_partition_mfma<S, D, kItem>));
         const int per = partitions_per_wave(items, slots, a.num_parts, a.part_blocks);
@@ -245,16 +297,19 @@ hipError_t launch_t(int group, const DecodeArgs& a, hipStream_t stream) {
         const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
         hipLaunchKernelGGL((pa_partition_mfma<S, D, kItem>), dim3(static_cast<unsigned>(groups)),
                            dim3(64 * kWavesPerGroup), kWavesPerGroup * stage, stream, a, group,
-                           static_cast<int>(waves), per, 1);
+                           static_cast<int>(waves), per, 1, 1);
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
-int partition_chunk_mfma(int group, int head_dim, const DecodeArgs& a) {
+int partition_chunk_mfma(int dtype, int group, int head_dim, const DecodeArgs& a) {
     const int stage = group * (head_dim + 4) * static_cast<int>(sizeof(float));
-    return make_plan(a, stage, true).chunk;
+    int64_t target = 0;
+    if (dtype == KV_DTYPE_F16) target = head_dim == 64 ? group_target_waves<F16, 64>() : group_target_waves<F16, 128>();
+    else target = head_dim == 64 ? group_target_waves<BF16, 64>() : group_target_waves<BF16, 128>();
+    return make_plan(a, stage, true, target).chunk;
 }
 
 hipError_t launch_partitions_mfma(int dtype, int head_dim, int group, const DecodeArgs& a,

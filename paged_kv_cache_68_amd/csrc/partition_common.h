@@ -239,38 +239,44 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
     }
 }
 
-// A work-group has left the states of the np = p_end - p partitions of its chunk in LDS
-// (slot i: [G][D] accumulators, then (m, l) per head, G*(D+4) floats per slot); combine
-// them in ascending order with the cross-block rule.  If the chunk is the whole
-// sequence the result is final; otherwise it is written as the partial of chunk
-// p / chunk, with `nchunks` chunks per sequence, for the reduce kernel.
+// A work-group of `heads` KV heads x `slots` waves per head has left every wave's state
+// in LDS: wave w = hh + heads * s at smem + w * G * (D + 4), holding [G][D] accumulators
+// and then (m, l) per query head.  Combine the slots of each head, in ascending order,
+// with the cross-block rule.  If chunk c is the whole sequence the result is final;
+// otherwise it is chunk c's partial result (rows [B][Hkv][nchunks][G]) for the reduce
+// kernel.  The heads' output rows are contiguous, so the loop writes one stretch.
 template <class S, int D>
-__device__ __forceinline__ void merge_chunk_and_store(const DecodeArgs& a, const Item& it, int G,
-                                                      const float* smem, int chunk, int nchunks) {
-    const int np = it.p_end - it.p;
+__device__ __forceinline__ void merge_slots_and_store(const DecodeArgs& a, int b, int kvh0, int heads,
+                                                      int slots, int G, const float* smem, int c,
+                                                      int nchunks, bool whole) {
     const int stride = G * (D + 4);
-    const bool whole = it.p == 0 && it.p_end == it.nparts;
-    const size_t out_row0 = (static_cast<size_t>(it.b) * a.num_q_heads + it.kvh * G) * D;
-    const size_t row0 = ((static_cast<size_t>(it.b) * a.num_kv_heads + it.kvh) * nchunks + it.p / chunk) * G;
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-        const int g = idx / D;
-        const int dd = idx % D;
+    const int per_head = G * D;
+    const size_t out0 = (static_cast<size_t>(b) * a.num_q_heads + kvh0 * G) * D;
+    for (int idx = threadIdx.x; idx < heads * per_head; idx += blockDim.x) {
+        const int hh = idx / per_head;
+        const int rem = idx - hh * per_head;
+        const int g = rem / D;
+        const int dd = rem - g * D;
+        const float* st0 = smem + hh * stride;
+        const int step = heads * stride;
         float M = -INFINITY;
-        for (int i = 0; i < np; ++i) M = fmaxf(M, smem[i * stride + G * D + 2 * g]);
+        for (int s = 0; s < slots; ++s) M = fmaxf(M, st0[s * step + per_head + 2 * g]);
         float lsum = 0.f, A = 0.f;
-        for (int i = 0; i < np; ++i) {
-            const float* st = smem + i * stride;
-            const float f = (M == -INFINITY) ? 0.f : fast_exp2(st[G * D + 2 * g] - M);
-            lsum += f * st[G * D + 2 * g + 1];
-            A += f * st[g * D + dd];
+        for (int s = 0; s < slots; ++s) {
+            const float* st = st0 + s * step;
+            const float f = (M == -INFINITY) ? 0.f : fast_exp2(st[per_head + 2 * g] - M);
+            lsum += f * st[per_head + 2 * g + 1];
+            A += f * st[rem];
         }
         if (whole) {
-            a.out[out_row0 + idx] = S::narrow(lsum > 0.f ? A / lsum : 0.f);
+            a.out[out0 + idx] = S::narrow(lsum > 0.f ? A / lsum : 0.f);
         } else {
-            a.ws_acc[(row0 + g) * D + dd] = A;
+            const size_t row =
+                ((static_cast<size_t>(b) * a.num_kv_heads + kvh0 + hh) * nchunks + c) * G + g;
+            a.ws_acc[row * D + dd] = A;
             if (dd == 0) {
-                a.ws_ml[(row0 + g) * 2 + 0] = M;
-                a.ws_ml[(row0 + g) * 2 + 1] = lsum;
+                a.ws_ml[row * 2 + 0] = M;
+                a.ws_ml[row * 2 + 1] = lsum;
             }
         }
     }
@@ -319,43 +325,92 @@ inline int partitions_per_wave(int64_t items, int64_t slots, int num_parts, int 
     return per < 1 ? 1 : static_cast<int>(per);
 }
 
-// How the partition kernel covers the batch.  `chunk` partitions are combined inside
-// the kernel (1 unless a work-group merges a chunk), so the reduce kernel sees
-// `chunks` = ceil(P / chunk) partial results per sequence of `chunk * part_blocks`
-// blocks each.
+// Compute units of the current device (0 if the query fails).
+inline int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return cus;
+}
+
+inline int env_int(const char* name, int fallback) {
+    const char* e = getenv(name);
+    return (e && atoi(e) > 0) ? atoi(e) : fallback;
+}
+
+// How the partition kernel covers the batch.  In the group plan a work-group owns
+// `heads` consecutive KV heads of one sequence and `slots` waves per head; each wave
+// walks `ppw` consecutive partitions of its head as one stream (the cross-block rule
+// applied block by block), and the work-group merges its waves in LDS.  One work-group
+// covers `chunk` = slots * ppw partitions of a head; with chunks = ceil(P / chunk) > 1
+// the reduce kernel combines the chunks' partial results like partitions of
+// chunk * part_blocks blocks.  Outside the group plan chunk = 1.
 struct Plan {
-    int group_waves;   // > 0: work-groups of this many waves merge chunks in LDS
-    int ppw;           // partitions per wave in that mode
+    int group_waves;   // > 0: group plan with work-groups of this many waves
+    int heads;
+    int slots;
+    int ppw;
     int chunk;
     int chunks;
 };
 
-// Work-group chunks when there is enough work (the same threshold that sends waves to
-// whole items) and more than one partition; at most 8 waves and 16 partitions per
-// work-group, and the chunk's states must fit in 64 KiB of LDS.  PAGEDKV_GROUP=0
-// disables the mode; PAGEDKV_GROUP_WAVES / _PPW override its shape (tuning knobs).
-inline Plan make_plan(const DecodeArgs& a, int stage_bytes, bool group_capable) {
-    Plan pl{0, 1, 1, a.num_parts};
-    const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.num_parts;
+// Choice of the group plan (MFMA kernel, enough work, more than one partition):
+//  * heads = 2 when the KV head count is even and that still leaves a work-group per
+//    compute unit: the work-group then reads both heads' stretches of every token row
+//    of a block at once, which the memory system serves measurably faster than the same
+//    bytes fetched by unrelated work-groups;
+//  * enough chunks for one work-group per compute unit;
+//  * slots so that all waves together about fill the GPU once (`target_waves`), at most
+//    8 waves per work-group, each walking at most 256 blocks (its table entries sit in
+//    four registers), and every wave's LDS stage within 64 KiB.
+// PAGEDKV_GROUP=0 disables the plan; PAGEDKV_GROUP_HEADS / _SLOTS / _PPW override it.
+inline Plan make_plan(const DecodeArgs& a, int stage_bytes, bool group_capable,
+                      int64_t target_waves) {
+    Plan pl{0, 1, 1, 1, 1, a.num_parts};
+    const int P = a.num_parts;
+    const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads * P;
     const char* env = getenv("PAGEDKV_GROUP");
     const bool allowed = group_capable && !(env && env[0] == '0') && !split_items(items);
-    if (!allowed || a.num_parts < 2) return pl;
-    int chunk = a.num_parts < 16 ? a.num_parts : 16;
-    const int lds_cap = (64 * 1024) / stage_bytes;
-    if (chunk > lds_cap) chunk = lds_cap;
-    if (chunk < 2) return pl;
-    int waves = chunk < 8 ? chunk : 8;
-    const char* ew = getenv("PAGEDKV_GROUP_WAVES");
-    if (ew && atoi(ew) > 0) waves = atoi(ew) < 8 ? atoi(ew) : 8;
-    int ppw = (chunk + waves - 1) / waves;
-    const char* ep = getenv("PAGEDKV_GROUP_PPW");
-    if (ep && atoi(ep) > 0) ppw = atoi(ep);
-    if (waves * ppw < chunk) chunk = waves * ppw;
-    waves = (chunk + ppw - 1) / ppw;      // no wave without a partition
-    pl.group_waves = waves;
+    if (!allowed || P < 2) return pl;
+    const int64_t seqheads = static_cast<int64_t>(a.batch) * a.num_kv_heads;
+    const int64_t cus = device_cus() > 0 ? device_cus() : 256;
+    if (target_waves <= 0) target_waves = 8 * cus;
+
+    int heads = (a.num_kv_heads % 2 == 0 && seqheads / 2 >= cus) ? 2 : 1;
+    int64_t chunks = (cus + seqheads / heads - 1) / (seqheads / heads);
+    if (chunks > P) chunks = P;
+    int chunk = static_cast<int>((P + chunks - 1) / chunks);
+    int64_t slots = (target_waves + seqheads * chunks - 1) / (seqheads * chunks);
+    if (slots > 8 / heads) slots = 8 / heads;
+    if (slots > chunk) slots = chunk;
+    int ppw = (chunk + static_cast<int>(slots) - 1) / static_cast<int>(slots);
+
+    // overrides: the work-group shape is then taken as given (within the limits below)
+    const bool forced = getenv("PAGEDKV_GROUP_HEADS") || getenv("PAGEDKV_GROUP_SLOTS") ||
+                        getenv("PAGEDKV_GROUP_PPW");
+    if (forced) {
+        heads = env_int("PAGEDKV_GROUP_HEADS", heads);
+        slots = env_int("PAGEDKV_GROUP_SLOTS", static_cast<int>(slots));
+        ppw = env_int("PAGEDKV_GROUP_PPW", ppw);
+        chunk = P;
+    }
+    if (heads > 8 || a.num_kv_heads % heads != 0) heads = 1;
+    if (slots > 8 / heads) slots = 8 / heads;
+    while (slots > 1 && heads * slots * stage_bytes > 64 * 1024) --slots;
+    if (slots < 1) slots = 1;
+    const int max_ppw = 256 / a.part_blocks;
+    if (ppw > max_ppw) ppw = max_ppw;
+    if (slots * ppw < chunk) chunk = static_cast<int>(slots) * ppw;
+    slots = (chunk + ppw - 1) / ppw;        // no wave without a partition
+    pl.heads = heads;
+    pl.slots = static_cast<int>(slots);
     pl.ppw = ppw;
+    pl.group_waves = heads * pl.slots;
     pl.chunk = chunk;
-    pl.chunks = (a.num_parts + chunk - 1) / chunk;
+    pl.chunks = (P + chunk - 1) / chunk;
     return pl;
 }
 

@@ -286,3 +286,35 @@ def test_launch_shapes_match_oracle(split, per, kernel, hq, hkv, d, dtype, monke
     ref = oracle.paged_decode(q, kp, vp, tables, lens, cfg.scale, 16, dtype)
     assert max_abs_err(out, ref, dtype) <= TOL[dtype]
     assert not out[10].any()                       # the empty sequence
+
+
+@pytest.mark.parametrize("heads,slots,ppw", [(1, 1, 1), (1, 4, 2), (2, 4, 4), (2, 2, 1), (4, 2, 3),
+                                             (1, 8, 8), (2, 1, 8), (8, 1, 2)])
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(32, 8, 128, "bf16"), (16, 8, 64, "f16")])
+def test_group_plan_shapes_match_oracle(heads, slots, ppw, hq, hkv, d, dtype, monkeypatch):
+    """Work-groups of `heads` KV heads x `slots` waves, each wave walking `ppw`
+    partitions: one chunk per sequence or several (then the reduce kernel combines the
+    chunks' partials); short sequences leave waves without blocks."""
+    monkeypatch.setenv("PAGEDKV_SPLIT", "0")
+    monkeypatch.setenv("PAGEDKV_GROUP_HEADS", str(heads))
+    monkeypatch.setenv("PAGEDKV_GROUP_SLOTS", str(slots))
+    monkeypatch.setenv("PAGEDKV_GROUP_PPW", str(ppw))
+    lens = [1, 15, 16, 17, 511, 512, 513, 1024, 1025, 2000, 0, 4500]
+    cfg, lens, tables, kp, vp, q = _custom_case(lens, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=12)
+    out = _run_custom(cfg, lens, tables, kp, vp, q, 512)
+    ref = oracle.paged_decode(q, kp, vp, tables, lens, cfg.scale, 16, dtype)
+    assert max_abs_err(out, ref, dtype) <= TOL[dtype]
+    assert not out[10].any()
+    # the same plan gives the same bits every time
+    assert np.array_equal(_run_custom(cfg, lens, tables, kp, vp, q, 512), out)
+
+
+def test_group_plan_off_matches_oracle(monkeypatch):
+    """PAGEDKV_GROUP=0: one wave per item with partials for every partition."""
+    monkeypatch.setenv("PAGEDKV_SPLIT", "0")
+    monkeypatch.setenv("PAGEDKV_GROUP", "0")
+    lens = [1, 17, 513, 2000, 0, 4500]
+    cfg, lens, tables, kp, vp, q = _custom_case(lens, hq=32, hkv=8, d=128, dtype="bf16", seed=13)
+    out = _run_custom(cfg, lens, tables, kp, vp, q, 512)
+    ref = oracle.paged_decode(q, kp, vp, tables, lens, cfg.scale, 16, "bf16")
+    assert max_abs_err(out, ref, "bf16") <= TOL["bf16"]
