@@ -56,6 +56,8 @@ hipError_t launch_partitions_mfma(int dtype, int head_dim, int group, const Deco
 // (the reduce kernel then combines chunks of that many partitions).
 int partition_chunk(int dtype, int head_dim, int group, const DecodeArgs& a);
 int partition_chunk_mfma(int dtype, int group, int head_dim, const DecodeArgs& a);
+// Waves per work-group of the matrix-core kernel's group plan for this batch (0: not used).
+int group_waves_mfma(int dtype, int group, int head_dim, const DecodeArgs& a);
 hipError_t launch_reduce(int dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_reshape_and_cache(const uint16_t* key, const uint16_t* value,
                                     const int64_t* slots, int32_t num_tokens, uint16_t* k_cache,

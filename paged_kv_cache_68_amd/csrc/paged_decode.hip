@@ -353,22 +353,28 @@ hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 // Kernel choice: the matrix-core kernel for GQA groups of 2..16 (a real dense tile per
-// block), the VALU kernel for single-head groups (MHA).  PAGEDKV_KERNEL=valu forces the
-// VALU kernel for groups up to 8 (for comparisons); =mfma forces the matrix cores.
-static int kernel_choice(int group) {
+// block).  Single-head groups (MHA) go to it too when its group plan applies: whole
+// sequences per wave and no partial results beat the VALU kernel's one wave per
+// partition by several percent, and the unused matrix-core columns cost nothing in a
+// kernel bound by HBM.  Otherwise (small batches) they take the VALU kernel.
+// PAGEDKV_KERNEL=valu forces the VALU kernel for groups up to 8 (for comparisons);
+// =mfma forces the matrix cores.
+static int kernel_choice(int dtype, int head_dim, int group, const DecodeArgs& a) {
     const char* env = getenv("PAGEDKV_KERNEL");
     if (env && strcmp(env, "valu") == 0 && group <= kMaxGroupValu) return 0;
     if (env && strcmp(env, "mfma") == 0) return 1;
-    return group >= 2 ? 1 : 0;
+    if (group >= 2) return 1;
+    return group_waves_mfma(dtype, group, head_dim, a) > 0 ? 1 : 0;
 }
 
 int partition_chunk(int dtype, int head_dim, int group, const DecodeArgs& a) {
-    return kernel_choice(group) == 1 ? partition_chunk_mfma(dtype, group, head_dim, a) : 1;
+    return kernel_choice(dtype, head_dim, group, a) == 1 ? partition_chunk_mfma(dtype, group, head_dim, a) : 1;
 }
 
 hipError_t launch_partitions(int dtype, int head_dim, int group, const DecodeArgs& a,
                              hipStream_t stream) {
-    if (kernel_choice(group) == 1) return launch_partitions_mfma(dtype, head_dim, group, a, stream);
+    if (kernel_choice(dtype, head_dim, group, a) == 1)
+        return launch_partitions_mfma(dtype, head_dim, group, a, stream);
     if (dtype == KV_DTYPE_F16) {
         if (head_dim == 64) return launch_part_g<F16, 64>(group, a, stream);
         if (head_dim == 128) return launch_part_g<F16, 128>(group, a, stream);

@@ -1,4 +1,4 @@
-// Partition kernel on the matrix cores, for GQA groups of 2..16 query heads per KV head.
+// Partition kernel on the matrix cores, for GQA groups of 1..16 query heads per KV head.
 //
 // Same method and work decomposition as the VALU kernel (one work-group of 4 waves per
 // (sequence, KV head, 512-token partition); blocks dealt to waves round-robin; per-wave
@@ -304,12 +304,20 @@ hipError_t launch_t(int group, const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int partition_chunk_mfma(int dtype, int group, int head_dim, const DecodeArgs& a) {
+static Plan plan_mfma(int dtype, int group, int head_dim, const DecodeArgs& a) {
     const int stage = group * (head_dim + 4) * static_cast<int>(sizeof(float));
     int64_t target = 0;
     if (dtype == KV_DTYPE_F16) target = head_dim == 64 ? group_target_waves<F16, 64>() : group_target_waves<F16, 128>();
     else target = head_dim == 64 ? group_target_waves<BF16, 64>() : group_target_waves<BF16, 128>();
-    return make_plan(a, stage, true, target).chunk;
+    return make_plan(a, stage, true, target);
+}
+
+int partition_chunk_mfma(int dtype, int group, int head_dim, const DecodeArgs& a) {
+    return plan_mfma(dtype, group, head_dim, a).chunk;
+}
+
+int group_waves_mfma(int dtype, int group, int head_dim, const DecodeArgs& a) {
+    return plan_mfma(dtype, group, head_dim, a).group_waves;
 }
 
 hipError_t launch_partitions_mfma(int dtype, int head_dim, int group, const DecodeArgs& a,

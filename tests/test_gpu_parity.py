@@ -290,7 +290,8 @@ def test_launch_shapes_match_oracle(split, per, kernel, hq, hkv, d, dtype, monke
 
 @pytest.mark.parametrize("heads,slots,ppw", [(1, 1, 1), (1, 4, 2), (2, 4, 4), (2, 2, 1), (4, 2, 3),
                                              (1, 8, 8), (2, 1, 8), (8, 1, 2)])
-@pytest.mark.parametrize("hq,hkv,d,dtype", [(32, 8, 128, "bf16"), (16, 8, 64, "f16")])
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(32, 8, 128, "bf16"), (16, 8, 64, "f16"),
+                                           (8, 8, 128, "f16")])
 def test_group_plan_shapes_match_oracle(heads, slots, ppw, hq, hkv, d, dtype, monkeypatch):
     """Work-groups of `heads` KV heads x `slots` waves, each wave walking `ppw`
     partitions: one chunk per sequence or several (then the reduce kernel combines the
