@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 
 #include <hip/hip_runtime_api.h>
@@ -129,6 +130,14 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     const char* x = getenv("PAGEDKV_XCD_CHUNK");
     a.xcd_chunk = x ? atoi(x) : 16;
     if (a.xcd_chunk < 0) a.xcd_chunk = 0;
+    // bytes this call can touch: the sequences' table rows, and never more than the
+    // layer's K and V caches; PAGEDKV_STREAM=0/1 overrides the choice
+    const size_t block_bytes = static_cast<size_t>(pkv::kBlockSize) * d.num_kv_heads * d.head_dim * 2 * 2;
+    const size_t reach = block_bytes * std::min<size_t>(static_cast<size_t>(batch) * max_blocks,
+                                                       static_cast<size_t>(d.num_blocks));
+    a.stream_loads = reach > pkv::kStreamThresholdBytes ? 1 : 0;
+    const char* st = getenv("PAGEDKV_STREAM");
+    if (st && (st[0] == '0' || st[0] == '1')) a.stream_loads = st[0] - '0';
     return a;
 }
 

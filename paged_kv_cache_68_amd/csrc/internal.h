@@ -33,8 +33,8 @@ struct DecodeArgs {
     const int32_t* tables;   // [B][max_blocks]
     const int32_t* lens;     // [B]
     uint16_t* out;           // [B][Hq][D]
-    float* ws_acc;           // [B][Hq][P][D]   unnormalised accumulators
-    float* ws_ml;            // [B][Hq][P][2]   (running max in log2 units, running sum)
+    float* ws_acc;           // [B][Hkv][P][G][D]  unnormalised accumulators
+    float* ws_ml;            // [B][Hkv][P][G][2]  (running max in log2 units, running sum)
     int32_t batch;
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -44,7 +44,14 @@ struct DecodeArgs {
     int32_t num_parts;       // partitions of the longest possible sequence
     float scale_log2;        // scale * log2(e): scores are kept in base-2 units
     int32_t xcd_chunk;       // work-groups per XCD chunk in the launch renumbering
+    int32_t stream_loads;    // 1: K/V loads carry the non-temporal hint
 };
+
+// A call that can touch more K/V bytes than this streams them past the last-level cache
+// (256 MB Infinity Cache on MI355X): they could not stay cached until the next step
+// anyway.  Smaller working sets (a few sequences, a shared prefix, a small pool) keep
+// the default cache policy so that re-reads hit.
+constexpr size_t kStreamThresholdBytes = size_t(512) << 20;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

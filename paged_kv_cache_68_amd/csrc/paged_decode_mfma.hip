@@ -69,7 +69,7 @@ __device__ __forceinline__ Item group_item(const DecodeArgs& a, int b, int kvh, 
     return it;
 }
 
-template <class S, int D, int MODE>
+template <class S, int D, int MODE, bool NT>
 __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, int n_items,
                                                          int per_item, int ppw, int heads) {
     constexpr bool SPLIT = MODE == kSplit;
@@ -151,11 +151,11 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
 
     auto load = [&](__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, Buf& buf) {
 #pragma unroll
-        for (int i = 0; i < NQK; ++i) buf.k[i] = load16(rk, koff + 64 * i);
+        for (int i = 0; i < NQK; ++i) buf.k[i] = load16<NT>(rk, koff + 64 * i);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            if constexpr (EPL == 8) buf.v[r] = load16(rv, voff + r * row_bytes);
-            else buf.v[r] = load8(rv, voff + r * row_bytes);
+            if constexpr (EPL == 8) buf.v[r] = load16<NT>(rv, voff + r * row_bytes);
+            else buf.v[r] = load8<NT>(rv, voff + r * row_bytes);
         }
     };
 
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
 // Waves of the group-plan kernel the GPU holds at once.
 template <class S, int D>
 int64_t group_target_waves() {
-    static const int64_t waves = resident_waves(reinterpret_cast<const void*>(&pa_partition_mfma<S, D, kGroup>));
+    static const int64_t waves = resident_waves(reinterpret_cast<const void*>(&pa_partition_mfma<S, D, kGroup, false>));
     return waves;
 }
 
@@ -283,21 +283,25 @@ hipError_t launch_t(int group, const DecodeArgs& a, hipStream_t stream) {
         DecodeArgs g = a;
         g.xcd_chunk = 0;
         const int64_t wgs = static_cast<int64_t>(a.batch) * (a.num_kv_heads / pl.heads) * pl.chunks;
-        hipLaunchKernelGGL((pa_partition_mfma<S, D, kGroup>), dim3(static_cast<unsigned>(wgs)),
-                           dim3(64 * pl.group_waves), pl.group_waves * stage, stream, g, group,
-                           static_cast<int>(wgs), pl.chunk, pl.ppw, pl.heads);
+        auto kernel = a.stream_loads ? pa_partition_mfma<S, D, kGroup, true>
+                                     : pa_partition_mfma<S, D, kGroup, false>;
+        hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(64 * pl.group_waves),
+                           pl.group_waves * stage, stream, g, group, static_cast<int>(wgs),
+                           pl.chunk, pl.ppw, pl.heads);
     } else if (split_items(items)) {
-        hipLaunchKernelGGL((pa_partition_mfma<S, D, kSplit>), dim3(static_cast<unsigned>(items)),
+        hipLaunchKernelGGL((pa_partition_mfma<S, D, kSplit, false>), dim3(static_cast<unsigned>(items)),
                            dim3(64 * kWavesPerGroup), kWavesPerGroup * stage, stream, a, group,
                            static_cast<int>(items), 1, 1, 1);
     } else {
-        static const int64_t slots = resident_waves(reinterpret_cast<const void*>(&pa_partition_mfma<S, D, kItem>));
+        static const int64_t slots = resident_waves(reinterpret_cast<const void*>(&pa_partition_mfma<S, D, kItem, false>));
         const int per = partitions_per_wave(items, slots, a.num_parts, a.part_blocks);
         const int64_t waves = static_cast<int64_t>(a.batch) * a.num_kv_heads * ceil_div(a.num_parts, per);
         const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
-        hipLaunchKernelGGL((pa_partition_mfma<S, D, kItem>), dim3(static_cast<unsigned>(groups)),
-                           dim3(64 * kWavesPerGroup), kWavesPerGroup * stage, stream, a, group,
-                           static_cast<int>(waves), per, 1, 1);
+        auto kernel = a.stream_loads ? pa_partition_mfma<S, D, kItem, true>
+                                     : pa_partition_mfma<S, D, kItem, false>;
+        hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(groups)), dim3(64 * kWavesPerGroup),
+                           kWavesPerGroup * stage, stream, a, group, static_cast<int>(waves), per,
+                           1, 1);
     }
     return hipGetLastError();
 }

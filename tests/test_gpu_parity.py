@@ -319,3 +319,20 @@ def test_group_plan_off_matches_oracle(monkeypatch):
     out = _run_custom(cfg, lens, tables, kp, vp, q, 512)
     ref = oracle.paged_decode(q, kp, vp, tables, lens, cfg.scale, 16, "bf16")
     assert max_abs_err(out, ref, "bf16") <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("group", ["1", "0"])
+def test_streaming_loads_give_identical_bits(group, monkeypatch):
+    """The non-temporal load hint is a cache policy only: results are bit-identical with
+    and without it, in the group plan and in the one-wave-per-item plan."""
+    monkeypatch.setenv("PAGEDKV_SPLIT", "0")
+    monkeypatch.setenv("PAGEDKV_GROUP", group)
+    lens = [1, 17, 513, 2000, 0, 4500, 33]
+    cfg, lens, tables, kp, vp, q = _custom_case(lens, hq=32, hkv=8, d=128, dtype="bf16", seed=14)
+    outs = []
+    for stream in ("0", "1"):
+        monkeypatch.setenv("PAGEDKV_STREAM", stream)
+        outs.append(_run_custom(cfg, lens, tables, kp, vp, q, 512))
+    assert np.array_equal(outs[0], outs[1])
+    ref = oracle.paged_decode(q, kp, vp, tables, lens, cfg.scale, 16, "bf16")
+    assert max_abs_err(outs[1], ref, "bf16") <= TOL["bf16"]
