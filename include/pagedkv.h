@@ -154,11 +154,13 @@ size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
  *                 sizes 1..16 are supported.
  *  scale        : multiplies q.k before the softmax (normally 1/sqrt(head_dim)).
  *  partition_size: tokens per split-context partition (multiple of 16, at most 4096;
- *                 0 = 512; larger values return KV_ERR_UNSUPPORTED).  A
- *                 sequence longer than one partition is split across work-groups
- *                 whose partial results are combined by a second kernel
- *                 ("PagedAttention and Virtual Memory Management", section 4,
- *                 cross-block reduction).
+ *                 0 = 512; larger values return KV_ERR_UNSUPPORTED).  A sequence
+ *                 longer than one partition is split into partitions processed in
+ *                 parallel, whose partial results are combined with the cross-block
+ *                 rule ("PagedAttention and Virtual Memory Management", section 4,
+ *                 cross-block reduction): inside the partition kernel, through LDS,
+ *                 when one work-group holds all of a sequence's partitions, otherwise
+ *                 by a second kernel over partial results in the workspace.
  *  workspace    : >= paged_attention_workspace_bytes(...) bytes of device memory,
  *                 16-byte aligned; contents on entry do not matter.
  * Table entries outside [0, num_blocks) for blocks a sequence uses are skipped (the
@@ -173,10 +175,11 @@ kv_status_t paged_attention_decode(const kv_pool_t* pool, int32_t layer, void* o
                                    size_t workspace_bytes, hipStream_t stream);
 
 /* The two phases of paged_attention_decode, for callers that time or schedule them
- * separately; same arguments.  paged_attention_partitions writes the partial results
- * of every partition (and the final output of sequences that fit in one partition);
- * paged_attention_reduce combines the partials of the other sequences into `out`.
- * Enqueueing partitions then reduce on one stream is exactly paged_attention_decode. */
+ * separately; same arguments.  paged_attention_partitions writes the final output of
+ * every sequence whose partitions it could combine by itself and partial results for
+ * the others; paged_attention_reduce combines those partials into `out` (and enqueues
+ * nothing when there are none).  Enqueueing partitions then reduce on one stream is
+ * exactly paged_attention_decode. */
 kv_status_t paged_attention_partitions(const kv_pool_t* pool, int32_t layer, void* out,
                                        const void* query, const int32_t* block_tables,
                                        int32_t max_blocks_per_seq, const int32_t* context_lens,
