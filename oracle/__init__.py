@@ -7,3 +7,4 @@ product path.
 """
 
 from .oracle import *  # noqa: F401,F403
+from .block_manager import BlockManager, OutOfBlocks  # noqa: F401

@@ -17,7 +17,8 @@ Sources (page title, then the section / equation / figure used):
 [P3] "PagedAttention and Virtual Memory Management: Mathematical Foundations ..."
      — section 1 (M_KV closed form), section 3 (j = floor(t/B), o = t mod B, the
      t = 38 example, bytes per physical block), section 4 (Addr_K / Addr_V, the
-     block-wise online-softmax decode, and the cross-block reduction formula).
+     block-wise online-softmax decode, and the cross-block reduction formula),
+     section 5 (the copy-on-write copy of the rows a shared block already holds).
 
 Readings where the pages are silent or garbled (each is listed in the design doc):
 * GQA: query head h reads KV head h // G with G = Hq / Hkv (contiguous groups).
@@ -37,7 +38,7 @@ import numpy as np
 
 __all__ = [
     "to_f64", "kv_bytes_per_token", "kv_pool_bytes", "block_bytes", "locate",
-    "physical_address", "scatter", "gather", "attention_contiguous", "softmax_weights",
+    "physical_address", "scatter", "copy_blocks", "gather", "attention_contiguous", "softmax_weights",
     "paged_decode", "paged_decode_seq", "online_decode_seq", "partition_partials",
     "combine_partials", "partitioned_decode_seq", "brute_force_seq",
 ]
@@ -108,6 +109,17 @@ def scatter(k_pool: np.ndarray, v_pool: np.ndarray, key: np.ndarray, value: np.n
         blk, off = int(slot) // block_size, int(slot) % block_size
         k_pool[blk, off] = key[i]
         v_pool[blk, off] = value[i]
+
+
+def copy_blocks(pool: np.ndarray, copies) -> None:
+    """Copy-on-write copies, in place: for each (src, dst, rows), the first ``rows``
+    token rows of physical block src are copied into block dst; the other rows of dst
+    are left as they were   [P3 section 5, case 2: copy the o token vectors already in
+    p to p_new].  ``pool`` is one K or V cache, block index first.  A pure copy of the
+    stored bits; pairs are applied in order.
+    """
+    for src, dst, rows in copies:
+        pool[int(dst), :int(rows)] = pool[int(src), :int(rows)]
 
 
 def gather(pool: np.ndarray, table, length: int, block_size: int) -> np.ndarray:
