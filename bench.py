@@ -107,12 +107,102 @@ def cpu_baseline(dc, budget_s: float):
     }
 
 
+# Copy-on-write block copies (kv_copy_blocks), Llama-3-8B pool geometry over all 32
+# layers (8 KV heads x 128, bf16; 32 KiB per block per layer for K and for V).
+COW_WORKLOADS = {
+    # the first decode step after a 64-way fork of a 4,103-token prompt (the
+    # shared-prefix workload): 63 streams copy the 7 rows of the shared tail block
+    "llama3_8b_fork64_first_step": {"layers": 32, "blocks": 4096, "prompt": 4103, "forks": 64},
+    # a beam-search style reshuffle: 1,024 whole-block copies
+    "llama3_8b_cow_1024_blocks": {"layers": 32, "blocks": 4096, "copies": 1024, "rows": 16},
+}
+
+
+def bench_cow(args, name):
+    import torch
+    import paged_kv_cache_68_amd as pk
+
+    w = COW_WORKLOADS[name]
+    hkv, d, elem = 8, 128, 2
+    row_bytes = hkv * d * elem
+    pool = pk.KVPool(w["layers"], w["blocks"], hkv, d, "bf16")
+    pool.memory.view(torch.int16).random_(-30000, 30000)
+    if "prompt" in w:
+        mgr = pk.BlockManager(w["blocks"], 16)
+        mgr.add_request(0)
+        mgr.append_batch([0], [w["prompt"]])
+        for c in range(1, w["forks"]):
+            mgr.fork(0, c)
+        _, copies = mgr.append_batch(list(range(w["forks"])))
+        # host cost of the block manager for one decode step of these streams
+        t0 = time.perf_counter()
+        for _ in range(200):
+            mgr.append_batch(list(range(w["forks"])))
+        host_us = (time.perf_counter() - t0) / 200 * 1e6
+    else:
+        rng = np.random.default_rng(7)
+        perm = rng.permutation(w["blocks"])
+        n = w["copies"]
+        copies = np.stack([perm[:n], perm[n:2 * n], np.full(n, w["rows"])], axis=1).astype(np.int32)
+        host_us = None
+    copies_d = torch.from_numpy(np.ascontiguousarray(copies)).cuda()
+    nbytes = int(2 * np.sum(copies[:, 2]) * row_bytes * 2 * w["layers"])   # read + write, K and V
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pk.copy_blocks(pool, copies_d, stream)
+    torch.cuda.synchronize()
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev_a[i].record(stream)
+        pk.copy_blocks(pool, copies_d, stream)
+        ev_b[i].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
+    achieved = nbytes / (k_ms * 1e-3) / 1e9
+    result = {
+        "metric": "copy-on-write block copies (kv_copy_blocks): HBM GB/s, bytes read + written",
+        "value": achieved, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "copies": int(copies.shape[0]),
+                   "rows_per_copy": int(copies[0, 2]), **w},
+        "roofline": {"bound": "hbm", "kernel": "cow_copy", "achieved": achieved,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": k_ms * 1e3},
+        "host_block_manager_us_per_decode_step": host_us,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        # the oracle's copy on host arrays of two layers' K and V, scaled to all layers
+        host = np.zeros((w["blocks"], 16, hkv, d), dtype=np.uint16)
+        trip = [tuple(int(x) for x in c) for c in copies.tolist()]
+        sample_layers = 2
+        t0 = time.perf_counter()
+        for _ in range(2 * sample_layers):
+            oracle.copy_blocks(host, trip)
+        t_cpu = (time.perf_counter() - t0) * w["layers"] / sample_layers
+        result["cpu_baseline"] = {"value": nbytes / t_cpu / 1e9, "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"{sample_layers} of {w['layers']} layers (K and V), "
+                                            "scaled to all layers"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", help="workload: c1..c5 or a config name")
+    ap.add_argument("--cow", choices=sorted(COW_WORKLOADS),
+                    help="time the copy-on-write block copy on this workload instead")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -150,6 +240,9 @@ def main(argv=None):
                                                "bytes_read_per_launch": nbytes,
                                                "bytes_written_per_launch": nbytes}}))
         return 0
+
+    if args.cow:
+        return bench_cow(args, args.cow)
 
     cfg = config_by_name(args.config)
     print(f"[bench] building {cfg.name} on the device", file=sys.stderr, flush=True)

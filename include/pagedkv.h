@@ -58,7 +58,8 @@ typedef enum kv_status {
     KV_ERR_UNSUPPORTED = 2,    /* shape / dtype the kernels are not built for */
     KV_ERR_WORKSPACE = 3,      /* workspace missing or smaller than required */
     KV_ERR_OUT_OF_MEMORY = 4,  /* the pool allocation in kv_pool_create failed */
-    KV_ERR_HIP = 5             /* a HIP runtime call or kernel launch failed */
+    KV_ERR_HIP = 5,            /* a HIP runtime call or kernel launch failed */
+    KV_ERR_OUT_OF_BLOCKS = 6   /* the block manager has no free block for an append */
 } kv_status_t;
 
 /* Geometry of a KV pool.  Supported: block_size 16, head_dim 64 or 128,
@@ -192,6 +193,86 @@ kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* o
                                    int32_t batch, int32_t num_q_heads, float scale,
                                    int32_t partition_size, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
+
+/* Copy-on-write copies on the device, for every layer of the pool, K and V:
+ *  copies : [num_copies][3] int32 device array of (src, dst, rows); the first `rows`
+ *           token rows of physical block src are copied into block dst and the other
+ *           rows of dst are left as they are ("PagedAttention and Virtual Memory
+ *           Management", section 5, case 2: the o rows already in the shared block go
+ *           to the new block before the new token is written into slot o).
+ * kv_bm_append produces these triples.  Blocks named as dst must be distinct and not be
+ * the src of another triple of the same call (then the copies are independent; the
+ * manager's triples always are).  Enqueue it before the reshape_and_cache of the same
+ * step.  A triple with a block outside [0, num_blocks), rows outside [0, 16] or
+ * src == dst is skipped on the device.  num_copies == 0 is a no-op.
+ * Errors: KV_ERR_INVALID_ARG (null pool or copies, negative count, copies not 4-byte
+ * aligned), KV_ERR_HIP. */
+kv_status_t kv_copy_blocks(kv_pool_t* pool, const int32_t* copies, int32_t num_copies,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------ block manager
+ * Host-side bookkeeping that decides where tokens go: a free list of physical blocks,
+ * a reference count per block and a block table per request ("Why AI servers waste
+ * memory, and how paging fixes it": "The idea: a block table", "A hand-worked
+ * example", "The real implementation", "Sharing a prefix with copy-on-write";
+ * "PagedAttention and Virtual Memory Management", section 5).
+ *  - New blocks come from the front of the free list; freed blocks join its back.
+ *  - Request ids are the caller's 64-bit integers.
+ *  - Every call checks all it needs before changing anything: a call that returns an
+ *    error has changed nothing.
+ *  - Host memory only; all array arguments are host arrays.  Not thread-safe.
+ * One decode step with a pool: kv_bm_append (slots + copies) -> copy both to the device
+ * -> kv_copy_blocks -> reshape_and_cache -> kv_bm_export (tables, lengths) -> copy to
+ * the device -> paged_attention_decode. */
+typedef struct kv_block_manager kv_block_manager_t;
+
+/* A manager of num_blocks blocks of block_size token slots (any size >= 1; a pool used
+ * with it has block_size 16).  The free list starts as 0, 1, ..., num_blocks - 1. */
+kv_status_t kv_bm_create(int32_t num_blocks, int32_t block_size, kv_block_manager_t** out);
+kv_status_t kv_bm_destroy(kv_block_manager_t* bm);
+
+/* A new request with an empty table.  KV_ERR_INVALID_ARG if the id exists. */
+kv_status_t kv_bm_add_request(kv_block_manager_t* bm, int64_t rid);
+
+/* child starts as a copy of parent's table and length, and every block the table names
+ * gains one reference; nothing is allocated or copied.  Forking k - 1 children adds
+ * k - 1 to each block ("PagedAttention and Virtual Memory Management", section 5).
+ * KV_ERR_INVALID_ARG if parent is unknown or child exists. */
+kv_status_t kv_bm_fork(kv_block_manager_t* bm, int64_t parent, int64_t child);
+
+/* Drop the request: each block of its table loses one reference, front to back, and a
+ * block nobody names any more joins the back of the free list.  Its contents stay. */
+kv_status_t kv_bm_free_request(kv_block_manager_t* bm, int64_t rid);
+
+/* Reserve slots for counts[i] new tokens of request rids[i], request after request in
+ * the order given (counts == NULL: one token each, a decode step).
+ *  slots  : [sum counts] int64 out, slot = physical block * block_size + offset, in order.
+ *  copies : [n][3] int32 out (room for n triples), *num_copies set: (src, dst, rows) for
+ *           each append whose last block was shared and had room -- it got a new block
+ *           and the rows already written must be copied (kv_copy_blocks).
+ * A token at a block boundary takes a new block from the free list.
+ * All or nothing: KV_ERR_OUT_OF_BLOCKS if the free list cannot cover the whole batch,
+ * KV_ERR_INVALID_ARG for an unknown id, a negative count or buffers that are too small;
+ * in both cases nothing changed. */
+kv_status_t kv_bm_append(kv_block_manager_t* bm, const int64_t* rids, const int32_t* counts,
+                         int32_t n, int64_t* slots, int64_t slots_cap, int32_t* copies,
+                         int32_t copies_cap, int32_t* num_copies);
+
+/* Views. */
+kv_status_t kv_bm_get_length(const kv_block_manager_t* bm, int64_t rid, int32_t* length);
+kv_status_t kv_bm_get_table(const kv_block_manager_t* bm, int64_t rid, int32_t* table,
+                            int32_t cap, int32_t* num);
+/* Block tables and lengths of rids[0..n) in the layout paged_attention_decode reads:
+ * tables [n][max_blocks] int32, padded with -1; lengths [n] int32.  KV_ERR_INVALID_ARG
+ * if an id is unknown or a table is longer than max_blocks (then nothing is written). */
+kv_status_t kv_bm_export(const kv_block_manager_t* bm, const int64_t* rids, int32_t n,
+                         int32_t max_blocks, int32_t* tables, int32_t* lengths);
+/* Number of free blocks (-1 for a null manager). */
+int32_t kv_bm_num_free(const kv_block_manager_t* bm);
+kv_status_t kv_bm_ref_count(const kv_block_manager_t* bm, int32_t block, int32_t* count);
+/* The free list, front first. */
+kv_status_t kv_bm_free_list(const kv_block_manager_t* bm, int32_t* blocks, int32_t cap,
+                            int32_t* num);
 
 /* Test hook: copy each sequence's K and V, through its block table, into contiguous
  * buffers ("Why AI servers waste memory, and how paging fixes it", "Reading through

@@ -22,6 +22,7 @@ __all__ = [
     "KVPool", "kv_pool_bytes", "kv_bytes_per_token", "reshape_and_cache",
     "paged_attention_workspace_bytes", "paged_attention_decode", "paged_attention_partitions",
     "paged_attention_reduce", "kv_pool_gather", "make_desc", "PagedKVError",
+    "BlockManager", "OutOfBlocks", "copy_blocks",
 ]
 
 BLOCK_SIZE = 16
@@ -210,3 +211,6 @@ def kv_pool_gather(pool: KVPool, layer: int, block_tables, context_lens, k_out, 
                                int(block_tables.shape[1]), _ptr(context_lens), batch, _ptr(k_out),
                                _ptr(v_out), _stream(stream)),
           "kv_pool_gather")
+
+
+from .block_manager import BlockManager, OutOfBlocks, copy_blocks  # noqa: E402

@@ -22,11 +22,13 @@ KV_ERR_UNSUPPORTED = 2
 KV_ERR_WORKSPACE = 3
 KV_ERR_OUT_OF_MEMORY = 4
 KV_ERR_HIP = 5
+KV_ERR_OUT_OF_BLOCKS = 6
 
 STATUS_NAMES = {
     KV_OK: "KV_OK", KV_ERR_INVALID_ARG: "KV_ERR_INVALID_ARG",
     KV_ERR_UNSUPPORTED: "KV_ERR_UNSUPPORTED", KV_ERR_WORKSPACE: "KV_ERR_WORKSPACE",
     KV_ERR_OUT_OF_MEMORY: "KV_ERR_OUT_OF_MEMORY", KV_ERR_HIP: "KV_ERR_HIP",
+    KV_ERR_OUT_OF_BLOCKS: "KV_ERR_OUT_OF_BLOCKS",
 }
 
 
@@ -54,6 +56,9 @@ _i32 = ctypes.c_int32
 _sz = ctypes.c_size_t
 _f32 = ctypes.c_float
 _pool = ctypes.c_void_p      # kv_pool_t*
+_bm = ctypes.c_void_p        # kv_block_manager_t*
+_i64 = ctypes.c_int64
+_pi32 = ctypes.POINTER(ctypes.c_int32)
 
 _DECODE_ARGS = [_pool, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _sz, _vp]
 
@@ -71,6 +76,19 @@ SIGNATURES = {
     "paged_attention_partitions": (_i32, _DECODE_ARGS),
     "paged_attention_reduce": (_i32, _DECODE_ARGS),
     "kv_pool_gather": (_i32, [_pool, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "kv_copy_blocks": (_i32, [_pool, _vp, _i32, _vp]),
+    "kv_bm_create": (_i32, [_i32, _i32, ctypes.POINTER(_bm)]),
+    "kv_bm_destroy": (_i32, [_bm]),
+    "kv_bm_add_request": (_i32, [_bm, _i64]),
+    "kv_bm_fork": (_i32, [_bm, _i64, _i64]),
+    "kv_bm_free_request": (_i32, [_bm, _i64]),
+    "kv_bm_append": (_i32, [_bm, _vp, _vp, _i32, _vp, _i64, _vp, _i32, _pi32]),
+    "kv_bm_get_length": (_i32, [_bm, _i64, _pi32]),
+    "kv_bm_get_table": (_i32, [_bm, _i64, _vp, _i32, _pi32]),
+    "kv_bm_export": (_i32, [_bm, _vp, _i32, _i32, _vp, _vp]),
+    "kv_bm_num_free": (_i32, [_bm]),
+    "kv_bm_ref_count": (_i32, [_bm, _i32, _pi32]),
+    "kv_bm_free_list": (_i32, [_bm, _vp, _i32, _pi32]),
 }
 
 

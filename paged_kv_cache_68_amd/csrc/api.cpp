@@ -186,6 +186,7 @@ const char* kv_status_string(kv_status_t status) {
         case KV_ERR_WORKSPACE: return "workspace missing or too small";
         case KV_ERR_OUT_OF_MEMORY: return "out of device memory";
         case KV_ERR_HIP: return "HIP runtime error";
+        case KV_ERR_OUT_OF_BLOCKS: return "no free block";
     }
     return "unknown status";
 }
@@ -277,6 +278,18 @@ kv_status_t reshape_and_cache(kv_pool_t* pool, int32_t layer, const void* key, c
         num_tokens, reinterpret_cast<uint16_t*>(kc),
         reinterpret_cast<uint16_t*>(kc + pool->cache_bytes), num_slots,
         d.num_kv_heads * d.head_dim, stream);
+    return e == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+kv_status_t kv_copy_blocks(kv_pool_t* pool, const int32_t* copies, int32_t num_copies,
+                           hipStream_t stream) {
+    if (!pool || num_copies < 0) return KV_ERR_INVALID_ARG;
+    if (num_copies == 0) return KV_OK;
+    if (!copies || !aligned(copies, 4)) return KV_ERR_INVALID_ARG;
+    const kv_pool_desc_t& d = pool->desc;
+    const hipError_t e = pkv::launch_copy_blocks(
+        reinterpret_cast<uint16_t*>(pool->base), copies, num_copies, d.num_layers, d.num_blocks,
+        d.num_kv_heads * d.head_dim, pool->cache_bytes / 2, stream);
     return e == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 

@@ -1,4 +1,5 @@
-// Cache write (reshape_and_cache) and the gather test hook, for gfx950.
+// Cache write (reshape_and_cache), the copy-on-write block copy and the gather test
+// hook, for gfx950.
 //
 // With the pool laid out [num_blocks][16][Hkv][D], slot = block * 16 + offset is
 // directly the index of a contiguous token row of Hkv*D elements, so the write of
@@ -60,7 +61,43 @@ __global__ __launch_bounds__(256) void kv_gather(const uint4* __restrict__ k_cac
     }
 }
 
+// Copy-on-write copies ("PagedAttention and Virtual Memory Management", section 5,
+// case 2: the o token rows already in the shared block p go to the new block p_new).
+// copies[i] = (src, dst, rows).  One work-group per (copy, layer, K or V): the first
+// `rows` rows of a block are one contiguous stretch of rows * row_chunks 16-byte
+// chunks, copied with coalesced dwordx4 accesses.  A triple with a block outside the
+// pool, rows outside [0, 16] or src == dst is skipped.
+__global__ __launch_bounds__(256) void cow_copy(uint4* __restrict__ base,
+                                                const int32_t* __restrict__ copies,
+                                                int32_t num_blocks, int32_t row_chunks,
+                                                size_t cache_chunks) {
+    const int i = blockIdx.x;
+    const int tensor = blockIdx.y;                   // 2 * layer + (0 for K, 1 for V)
+    const int src = copies[3 * i + 0];
+    const int dst = copies[3 * i + 1];
+    const int rows = copies[3 * i + 2];
+    if (static_cast<unsigned>(src) >= static_cast<unsigned>(num_blocks) ||
+        static_cast<unsigned>(dst) >= static_cast<unsigned>(num_blocks) || src == dst ||
+        rows <= 0 || rows > kBlockSize)
+        return;
+    const size_t block_chunks = static_cast<size_t>(kBlockSize) * row_chunks;
+    const uint4* from = base + tensor * cache_chunks + static_cast<size_t>(src) * block_chunks;
+    uint4* to = base + tensor * cache_chunks + static_cast<size_t>(dst) * block_chunks;
+    const int n = rows * row_chunks;
+    for (int ch = threadIdx.x; ch < n; ch += blockDim.x) to[ch] = from[ch];
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(uint16_t* base, const int32_t* copies, int32_t num_copies,
+                              int32_t num_layers, int32_t num_blocks, int32_t row_elems,
+                              size_t cache_elems, hipStream_t stream) {
+    if (num_copies <= 0) return hipSuccess;
+    hipLaunchKernelGGL(cow_copy, dim3(num_copies, 2 * num_layers), dim3(256), 0, stream,
+                       reinterpret_cast<uint4*>(base), copies, num_blocks, row_elems / 8,
+                       cache_elems / 8);
+    return hipGetLastError();
+}
 
 hipError_t launch_reshape_and_cache(const uint16_t* key, const uint16_t* value,
                                     const int64_t* slots, int32_t num_tokens, uint16_t* k_cache,

@@ -70,6 +70,11 @@ hipError_t launch_reshape_and_cache(const uint16_t* key, const uint16_t* value,
                                     const int64_t* slots, int32_t num_tokens, uint16_t* k_cache,
                                     uint16_t* v_cache, int64_t num_slots, int32_t row_elems,
                                     hipStream_t stream);
+// base: layer 0's K cache; the 2 * num_layers caches follow each other, cache_elems
+// 16-bit elements apart.
+hipError_t launch_copy_blocks(uint16_t* base, const int32_t* copies, int32_t num_copies,
+                              int32_t num_layers, int32_t num_blocks, int32_t row_elems,
+                              size_t cache_elems, hipStream_t stream);
 hipError_t launch_gather(const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* tables,
                          int32_t max_blocks, const int32_t* lens, int32_t batch,
                          int32_t num_blocks, int32_t row_elems, uint16_t* k_out, uint16_t* v_out,

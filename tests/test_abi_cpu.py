@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for code in range(6):
+    for code in range(7):
         assert _lib.status_string(code) and _lib.status_string(code) != "unknown status"
 
 
