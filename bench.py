@@ -201,6 +201,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", help="workload: c1..c5 or a config name")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="rebuild the workload with this block size (8, 16, 32, 64); the pool "
+                         "keeps the same number of token slots")
     ap.add_argument("--cow", choices=sorted(COW_WORKLOADS),
                     help="time the copy-on-write block copy on this workload instead")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
@@ -245,6 +248,11 @@ def main(argv=None):
         return bench_cow(args, args.cow)
 
     cfg = config_by_name(args.config)
+    if args.block_size and args.block_size != cfg.block_size:
+        import dataclasses
+        B = args.block_size
+        cfg = dataclasses.replace(cfg, block_size=B, num_blocks=cfg.num_blocks * cfg.block_size // B,
+                                  name=f"{cfg.name}_b{B}")
     print(f"[bench] building {cfg.name} on the device", file=sys.stderr, flush=True)
     case = make_case(cfg, where="device" if cfg.index in (3, 5) else "host", poison=False)
     dc = DeviceCase(case)

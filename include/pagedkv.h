@@ -62,8 +62,10 @@ typedef enum kv_status {
     KV_ERR_OUT_OF_BLOCKS = 6   /* the block manager has no free block for an append */
 } kv_status_t;
 
-/* Geometry of a KV pool.  Supported: block_size 16, head_dim 64 or 128,
- * dtype KV_DTYPE_F16 / KV_DTYPE_BF16, num_blocks >= 1, num_kv_heads >= 1. */
+/* Geometry of a KV pool.  Supported: block_size 8, 16, 32 or 64 ("PagedAttention and
+ * Virtual Memory Management", section 3: B is typically 8, 16 or 32; 16 is the usual
+ * default), head_dim 64 or 128, dtype KV_DTYPE_F16 / KV_DTYPE_BF16, num_blocks >= 1,
+ * num_kv_heads >= 1. */
 typedef struct kv_pool_desc {
     int32_t num_layers;
     int32_t num_blocks;
@@ -144,18 +146,20 @@ size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
  *  out          : [batch][num_q_heads][head_dim], pool dtype (written).
  *  query        : [batch][num_q_heads][head_dim], pool dtype.
  *  block_tables : [batch][max_blocks_per_seq] int32; entry j of row b is the physical
- *                 block holding tokens [16j, 16j+16) of sequence b.  Entries at or past
- *                 ceil(context_lens[b] / 16) are never read (may hold -1).
+ *                 block holding tokens [Bj, Bj+B) of sequence b (B = the pool's
+ *                 block_size).  Entries at or past ceil(context_lens[b] / B) are never
+ *                 read (may hold -1).
  *  context_lens : [batch] int32, number of tokens of each sequence, including a token
  *                 just written by reshape_and_cache.  Values are clamped to
- *                 [0, max_blocks_per_seq * 16]; a sequence of length 0 gets a zero
+ *                 [0, max_blocks_per_seq * B]; a sequence of length 0 gets a zero
  *                 output.  Slots at or past the length in the last block are never read.
  *  num_q_heads  : multiple of the pool's num_kv_heads; query head h reads KV head
  *                 h / (num_q_heads / num_kv_heads) (contiguous GQA groups); group
  *                 sizes 1..16 are supported.
  *  scale        : multiplies q.k before the softmax (normally 1/sqrt(head_dim)).
- *  partition_size: tokens per split-context partition (multiple of 16, at most 4096;
- *                 0 = 512; larger values return KV_ERR_UNSUPPORTED).  A sequence
+ *  partition_size: tokens per split-context partition (a multiple of B, at most 4096
+ *                 and at most 2048 when B = 8; 0 = 512; larger values return
+ *                 KV_ERR_UNSUPPORTED).  A sequence
  *                 longer than one partition is split into partitions processed in
  *                 parallel, whose partial results are combined with the cross-block
  *                 rule ("PagedAttention and Virtual Memory Management", section 4,
@@ -203,7 +207,7 @@ kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* o
  * kv_bm_append produces these triples.  Blocks named as dst must be distinct and not be
  * the src of another triple of the same call (then the copies are independent; the
  * manager's triples always are).  Enqueue it before the reshape_and_cache of the same
- * step.  A triple with a block outside [0, num_blocks), rows outside [0, 16] or
+ * step.  A triple with a block outside [0, num_blocks), rows outside [0, block_size] or
  * src == dst is skipped on the device.  num_copies == 0 is a no-op.
  * Errors: KV_ERR_INVALID_ARG (null pool or copies, negative count, copies not 4-byte
  * aligned), KV_ERR_HIP. */
@@ -227,7 +231,7 @@ kv_status_t kv_copy_blocks(kv_pool_t* pool, const int32_t* copies, int32_t num_c
 typedef struct kv_block_manager kv_block_manager_t;
 
 /* A manager of num_blocks blocks of block_size token slots (any size >= 1; a pool used
- * with it has block_size 16).  The free list starts as 0, 1, ..., num_blocks - 1. */
+ * with it has the same block_size).  The free list starts as 0, 1, ..., num_blocks - 1. */
 kv_status_t kv_bm_create(int32_t num_blocks, int32_t block_size, kv_block_manager_t** out);
 kv_status_t kv_bm_destroy(kv_block_manager_t* bm);
 
@@ -276,8 +280,8 @@ kv_status_t kv_bm_free_list(const kv_block_manager_t* bm, int32_t* blocks, int32
 
 /* Test hook: copy each sequence's K and V, through its block table, into contiguous
  * buffers ("Why AI servers waste memory, and how paging fixes it", "Reading through
- * the table").  k_out, v_out: [batch][max_blocks_per_seq * 16][num_kv_heads][head_dim];
- * row t of sequence b is the pool row (table[b][t / 16], t % 16) for t < context_lens[b]
+ * the table").  k_out, v_out: [batch][max_blocks_per_seq * B][num_kv_heads][head_dim];
+ * row t of sequence b is the pool row (table[b][t / B], t % B) for t < context_lens[b]
  * and zero otherwise.  Bit copy. */
 kv_status_t kv_pool_gather(const kv_pool_t* pool, int32_t layer, const int32_t* block_tables,
                            int32_t max_blocks_per_seq, const int32_t* context_lens,

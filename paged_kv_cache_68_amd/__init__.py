@@ -161,7 +161,7 @@ def alloc_workspace(pool: KVPool, batch, num_q_heads, max_blocks_per_seq, partit
                     device=None):
     torch = _torch()
     n = paged_attention_workspace_bytes(batch, num_q_heads, pool.head_dim, max_blocks_per_seq,
-                                        BLOCK_SIZE, partition_size)
+                                        pool.desc.block_size, partition_size)
     if n == 0:
         return None
     return torch.empty(n, dtype=torch.uint8, device=device or pool.memory.device)

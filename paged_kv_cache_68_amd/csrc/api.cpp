@@ -27,7 +27,8 @@ kv_status_t check_desc(const kv_pool_desc_t* d) {
     if (d->num_layers < 1 || d->num_blocks < 1 || d->num_kv_heads < 1 || d->block_size < 1 ||
         d->head_dim < 1)
         return KV_ERR_INVALID_ARG;
-    if (d->block_size != pkv::kBlockSize) return KV_ERR_UNSUPPORTED;
+    if (d->block_size != 8 && d->block_size != 16 && d->block_size != 32 && d->block_size != 64)
+        return KV_ERR_UNSUPPORTED;
     if (d->head_dim != 64 && d->head_dim != 128) return KV_ERR_UNSUPPORTED;
     if (d->dtype != KV_DTYPE_F16 && d->dtype != KV_DTYPE_BF16) return KV_ERR_UNSUPPORTED;
     // a layer's cache must be addressable with 64-bit offsets and the slot count with int64
@@ -73,7 +74,9 @@ kv_status_t check_decode(const kv_pool_t* pool, int32_t layer, void* out, const 
     if (partition_size == 0) partition_size = pkv::kDefaultPartition;
     if (partition_size < d.block_size || partition_size % d.block_size != 0)
         return KV_ERR_INVALID_ARG;
-    if (partition_size > pkv::kMaxPartition) return KV_ERR_UNSUPPORTED;
+    const int32_t tile = d.block_size < pkv::kTile ? d.block_size : pkv::kTile;
+    if (partition_size > pkv::kMaxPartition || partition_size > pkv::kMaxTilesPerWave * tile)
+        return KV_ERR_UNSUPPORTED;
     if (batch == 0) {
         shape->group = group;
         return KV_OK;
@@ -83,8 +86,9 @@ kv_status_t check_decode(const kv_pool_t* pool, int32_t layer, void* out, const 
     if (!aligned(out) || !aligned(query) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
         return KV_ERR_INVALID_ARG;
     if (static_cast<int64_t>(max_blocks) * d.block_size > INT32_MAX) return KV_ERR_INVALID_ARG;
-    const int32_t part_blocks = partition_size / d.block_size;
-    const int32_t num_parts = static_cast<int32_t>(ceil_div(max_blocks, part_blocks));
+    const int32_t part_blocks = partition_size / tile;          // in tiles
+    const int32_t num_parts = static_cast<int32_t>(
+        ceil_div(static_cast<int64_t>(max_blocks) * d.block_size, partition_size));
     if (static_cast<int64_t>(batch) * d.num_kv_heads * num_parts > INT32_MAX)
         return KV_ERR_INVALID_ARG;
     const size_t need = workspace_for(batch, num_q_heads, d.head_dim, num_parts);
@@ -122,6 +126,10 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     a.num_kv_heads = d.num_kv_heads;
     a.max_blocks = max_blocks;
     a.num_blocks = d.num_blocks;
+    a.block_size = d.block_size;
+    a.tile_tokens = d.block_size < pkv::kTile ? d.block_size : pkv::kTile;
+    a.tiles_log2 = 0;
+    while ((a.tile_tokens << a.tiles_log2) < d.block_size) ++a.tiles_log2;
     a.part_blocks = s.part_blocks;
     a.num_parts = s.num_parts;
     a.scale_log2 = scale * 1.4426950408889634f;
@@ -132,7 +140,7 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     if (a.xcd_chunk < 0) a.xcd_chunk = 0;
     // bytes this call can touch: the sequences' table rows, and never more than the
     // layer's K and V caches; PAGEDKV_STREAM=0/1 overrides the choice
-    const size_t block_bytes = static_cast<size_t>(pkv::kBlockSize) * d.num_kv_heads * d.head_dim * 2 * 2;
+    const size_t block_bytes = static_cast<size_t>(d.block_size) * d.num_kv_heads * d.head_dim * 2 * 2;
     const size_t reach = block_bytes * std::min<size_t>(static_cast<size_t>(batch) * max_blocks,
                                                        static_cast<size_t>(d.num_blocks));
     a.stream_loads = reach > pkv::kStreamThresholdBytes ? 1 : 0;
@@ -289,7 +297,7 @@ kv_status_t kv_copy_blocks(kv_pool_t* pool, const int32_t* copies, int32_t num_c
     const kv_pool_desc_t& d = pool->desc;
     const hipError_t e = pkv::launch_copy_blocks(
         reinterpret_cast<uint16_t*>(pool->base), copies, num_copies, d.num_layers, d.num_blocks,
-        d.num_kv_heads * d.head_dim, pool->cache_bytes / 2, stream);
+        d.block_size, d.num_kv_heads * d.head_dim, pool->cache_bytes / 2, stream);
     return e == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
@@ -297,11 +305,12 @@ size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
                                        int32_t max_blocks_per_seq, int32_t block_size,
                                        int32_t partition_size) {
     if (batch < 0 || num_q_heads < 1 || head_dim < 1 || max_blocks_per_seq < 1 ||
-        block_size != pkv::kBlockSize)
+        (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64))
         return SIZE_MAX;
     if (partition_size == 0) partition_size = pkv::kDefaultPartition;
     if (partition_size < block_size || partition_size % block_size != 0) return SIZE_MAX;
-    const int32_t parts = static_cast<int32_t>(ceil_div(max_blocks_per_seq, partition_size / block_size));
+    const int32_t parts = static_cast<int32_t>(
+        ceil_div(static_cast<int64_t>(max_blocks_per_seq) * block_size, partition_size));
     return workspace_for(batch, num_q_heads, head_dim, parts);
 }
 
@@ -343,7 +352,8 @@ kv_status_t kv_pool_gather(const kv_pool_t* pool, int32_t layer, const int32_t* 
                            int32_t batch, void* k_out, void* v_out, hipStream_t stream) {
     if (!pool || layer < 0 || layer >= pool->desc.num_layers || batch < 0) return KV_ERR_INVALID_ARG;
     if (batch == 0) return KV_OK;
-    if (max_blocks_per_seq < 1 || batch > 65535 || max_blocks_per_seq > 0x7fffffff / pkv::kBlockSize)
+    if (max_blocks_per_seq < 1 || batch > 65535 ||
+        max_blocks_per_seq > 0x7fffffff / pool->desc.block_size)
         return KV_ERR_INVALID_ARG;
     if (!block_tables || !context_lens || !k_out || !v_out) return KV_ERR_INVALID_ARG;
     if (!aligned(k_out) || !aligned(v_out) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
@@ -352,7 +362,7 @@ kv_status_t kv_pool_gather(const kv_pool_t* pool, int32_t layer, const int32_t* 
     const char* kc = pool->base + static_cast<size_t>(2 * layer) * pool->cache_bytes;
     const hipError_t e = pkv::launch_gather(
         reinterpret_cast<const uint16_t*>(kc), reinterpret_cast<const uint16_t*>(kc + pool->cache_bytes),
-        block_tables, max_blocks_per_seq, context_lens, batch, d.num_blocks,
+        block_tables, max_blocks_per_seq, context_lens, batch, d.num_blocks, d.block_size,
         d.num_kv_heads * d.head_dim, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out),
         stream);
     return e == hipSuccess ? KV_OK : KV_ERR_HIP;

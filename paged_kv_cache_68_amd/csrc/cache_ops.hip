@@ -1,7 +1,7 @@
 // Cache write (reshape_and_cache), the copy-on-write block copy and the gather test
 // hook, for gfx950.
 //
-// With the pool laid out [num_blocks][16][Hkv][D], slot = block * 16 + offset is
+// With the pool laid out [num_blocks][B][Hkv][D], slot = block * B + offset is
 // directly the index of a contiguous token row of Hkv*D elements, so the write of
 // "Why AI servers waste memory, and how paging fixes it" ("The real implementation":
 // the token lands in slot `offset` of block table[-1]) is a row copy to row `slot`.
@@ -34,26 +34,26 @@ __global__ __launch_bounds__(256) void rc_scatter(const uint4* __restrict__ key,
     }
 }
 
-// One work-group per (table entry j, sequence b): the 16 rows of logical block j.
+// One work-group per (table entry j, sequence b): the B rows of logical block j.
 __global__ __launch_bounds__(256) void kv_gather(const uint4* __restrict__ k_cache,
                                                  const uint4* __restrict__ v_cache,
                                                  const int32_t* __restrict__ tables,
                                                  int32_t max_blocks,
                                                  const int32_t* __restrict__ lens,
-                                                 int32_t num_blocks, int32_t row_chunks,
-                                                 uint4* __restrict__ k_out,
+                                                 int32_t num_blocks, int32_t block_size,
+                                                 int32_t row_chunks, uint4* __restrict__ k_out,
                                                  uint4* __restrict__ v_out) {
     const int j = blockIdx.x;
     const int b = blockIdx.y;
     int L = lens[b];
-    L = L < 0 ? 0 : (L > max_blocks * kBlockSize ? max_blocks * kBlockSize : L);
-    const int valid = min(kBlockSize, max(0, L - j * kBlockSize));
+    L = L < 0 ? 0 : (L > max_blocks * block_size ? max_blocks * block_size : L);
+    const int valid = min(block_size, max(0, L - j * block_size));
     int blk = valid > 0 ? tables[static_cast<size_t>(b) * max_blocks + j] : -1;
     const bool ok = static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks);
-    const size_t dst0 = (static_cast<size_t>(b) * max_blocks * kBlockSize + static_cast<size_t>(j) * kBlockSize) * row_chunks;
-    const size_t src0 = ok ? static_cast<size_t>(blk) * kBlockSize * row_chunks : 0;
+    const size_t dst0 = (static_cast<size_t>(b) * max_blocks + j) * block_size * row_chunks;
+    const size_t src0 = ok ? static_cast<size_t>(blk) * block_size * row_chunks : 0;
     const uint4 zero = make_uint4(0, 0, 0, 0);
-    for (int idx = threadIdx.x; idx < kBlockSize * row_chunks; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < block_size * row_chunks; idx += blockDim.x) {
         const int t = idx / row_chunks;
         const bool take = ok && t < valid;
         k_out[dst0 + idx] = take ? k_cache[src0 + idx] : zero;
@@ -66,11 +66,11 @@ __global__ __launch_bounds__(256) void kv_gather(const uint4* __restrict__ k_cac
 // copies[i] = (src, dst, rows).  One work-group per (copy, layer, K or V): the first
 // `rows` rows of a block are one contiguous stretch of rows * row_chunks 16-byte
 // chunks, copied with coalesced dwordx4 accesses.  A triple with a block outside the
-// pool, rows outside [0, 16] or src == dst is skipped.
+// pool, rows outside [0, block_size] or src == dst is skipped.
 __global__ __launch_bounds__(256) void cow_copy(uint4* __restrict__ base,
                                                 const int32_t* __restrict__ copies,
-                                                int32_t num_blocks, int32_t row_chunks,
-                                                size_t cache_chunks) {
+                                                int32_t num_blocks, int32_t block_size,
+                                                int32_t row_chunks, size_t cache_chunks) {
     const int i = blockIdx.x;
     const int tensor = blockIdx.y;                   // 2 * layer + (0 for K, 1 for V)
     const int src = copies[3 * i + 0];
@@ -78,9 +78,9 @@ __global__ __launch_bounds__(256) void cow_copy(uint4* __restrict__ base,
     const int rows = copies[3 * i + 2];
     if (static_cast<unsigned>(src) >= static_cast<unsigned>(num_blocks) ||
         static_cast<unsigned>(dst) >= static_cast<unsigned>(num_blocks) || src == dst ||
-        rows <= 0 || rows > kBlockSize)
+        rows <= 0 || rows > block_size)
         return;
-    const size_t block_chunks = static_cast<size_t>(kBlockSize) * row_chunks;
+    const size_t block_chunks = static_cast<size_t>(block_size) * row_chunks;
     const uint4* from = base + tensor * cache_chunks + static_cast<size_t>(src) * block_chunks;
     uint4* to = base + tensor * cache_chunks + static_cast<size_t>(dst) * block_chunks;
     const int n = rows * row_chunks;
@@ -90,12 +90,12 @@ __global__ __launch_bounds__(256) void cow_copy(uint4* __restrict__ base,
 }  // namespace
 
 hipError_t launch_copy_blocks(uint16_t* base, const int32_t* copies, int32_t num_copies,
-                              int32_t num_layers, int32_t num_blocks, int32_t row_elems,
-                              size_t cache_elems, hipStream_t stream) {
+                              int32_t num_layers, int32_t num_blocks, int32_t block_size,
+                              int32_t row_elems, size_t cache_elems, hipStream_t stream) {
     if (num_copies <= 0) return hipSuccess;
     hipLaunchKernelGGL(cow_copy, dim3(num_copies, 2 * num_layers), dim3(256), 0, stream,
-                       reinterpret_cast<uint4*>(base), copies, num_blocks, row_elems / 8,
-                       cache_elems / 8);
+                       reinterpret_cast<uint4*>(base), copies, num_blocks, block_size,
+                       row_elems / 8, cache_elems / 8);
     return hipGetLastError();
 }
 
@@ -115,12 +115,12 @@ hipError_t launch_reshape_and_cache(const uint16_t* key, const uint16_t* value,
 
 hipError_t launch_gather(const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* tables,
                          int32_t max_blocks, const int32_t* lens, int32_t batch,
-                         int32_t num_blocks, int32_t row_elems, uint16_t* k_out, uint16_t* v_out,
-                         hipStream_t stream) {
+                         int32_t num_blocks, int32_t block_size, int32_t row_elems,
+                         uint16_t* k_out, uint16_t* v_out, hipStream_t stream) {
     if (batch <= 0 || max_blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL(kv_gather, dim3(max_blocks, batch), dim3(256), 0, stream,
                        reinterpret_cast<const uint4*>(k_cache), reinterpret_cast<const uint4*>(v_cache),
-                       tables, max_blocks, lens, num_blocks, row_elems / 8,
+                       tables, max_blocks, lens, num_blocks, block_size, row_elems / 8,
                        reinterpret_cast<uint4*>(k_out), reinterpret_cast<uint4*>(v_out));
     return hipGetLastError();
 }

@@ -18,9 +18,11 @@ struct kv_pool {
 
 namespace pkv {
 
-constexpr int kBlockSize = 16;          // tokens per physical block
+constexpr int kBlockSize = 16;          // default tokens per physical block (the VALU kernel's)
+constexpr int kTile = 16;               // tokens per matrix-core tile
+constexpr int kMaxTilesPerWave = 256;   // a wave holds one table entry per tile in 4 VGPRs
 constexpr int kDefaultPartition = 512;  // tokens per split-context partition
-constexpr int kMaxPartition = 4096;     // a wave holds its partition's table entries in one VGPR
+constexpr int kMaxPartition = 4096;     // at most 256 tiles of 16 tokens per wave
 constexpr int kMaxGroup = 16;           // largest supported GQA group (MFMA path)
 constexpr int kMaxGroupValu = 8;        // largest group the VALU kernel is built for
 constexpr int kWavesPerGroup = 4;       // waves per work-group of the partition kernel
@@ -28,7 +30,7 @@ constexpr int kWavesPerGroup = 4;       // waves per work-group of the partition
 // Everything the two decode kernels read; passed by value.
 struct DecodeArgs {
     const uint16_t* q;       // [B][Hq][D]
-    const uint16_t* k;       // [nb][16][Hkv][D]
+    const uint16_t* k;       // [nb][block_size][Hkv][D]
     const uint16_t* v;
     const int32_t* tables;   // [B][max_blocks]
     const int32_t* lens;     // [B]
@@ -40,7 +42,10 @@ struct DecodeArgs {
     int32_t num_kv_heads;
     int32_t max_blocks;      // table row length
     int32_t num_blocks;      // blocks in the pool
-    int32_t part_blocks;     // blocks per partition
+    int32_t block_size;      // tokens per block: 8, 16, 32 or 64
+    int32_t tile_tokens;     // tokens per tile the kernels walk: min(block_size, 16)
+    int32_t tiles_log2;      // log2(block_size / tile_tokens): tiles per block
+    int32_t part_blocks;     // tiles per partition (tiles are blocks when block_size <= 16)
     int32_t num_parts;       // partitions of the longest possible sequence
     float scale_log2;        // scale * log2(e): scores are kept in base-2 units
     int32_t xcd_chunk;       // work-groups per XCD chunk in the launch renumbering
@@ -73,11 +78,11 @@ hipError_t launch_reshape_and_cache(const uint16_t* key, const uint16_t* value,
 // base: layer 0's K cache; the 2 * num_layers caches follow each other, cache_elems
 // 16-bit elements apart.
 hipError_t launch_copy_blocks(uint16_t* base, const int32_t* copies, int32_t num_copies,
-                              int32_t num_layers, int32_t num_blocks, int32_t row_elems,
-                              size_t cache_elems, hipStream_t stream);
+                              int32_t num_layers, int32_t num_blocks, int32_t block_size,
+                              int32_t row_elems, size_t cache_elems, hipStream_t stream);
 hipError_t launch_gather(const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* tables,
                          int32_t max_blocks, const int32_t* lens, int32_t batch,
-                         int32_t num_blocks, int32_t row_elems, uint16_t* k_out, uint16_t* v_out,
-                         hipStream_t stream);
+                         int32_t num_blocks, int32_t block_size, int32_t row_elems,
+                         uint16_t* k_out, uint16_t* v_out, hipStream_t stream);
 
 }  // namespace pkv

@@ -245,10 +245,9 @@ __global__ __launch_bounds__(256) void pa_reduce(DecodeArgs a) {
     if (pair >= a.batch * a.num_q_heads) return;
     const int b = pair / a.num_q_heads;
     const int h = pair % a.num_q_heads;
-    int L = a.lens[b];
-    L = L < 0 ? 0 : (L > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : L);
-    const int nblk = (L + kBlockSize - 1) / kBlockSize;
-    const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
+    const int L = clamped_length(a, b);
+    const int ntiles = (L + a.tile_tokens - 1) / a.tile_tokens;
+    const int nparts = (ntiles + a.part_blocks - 1) / a.part_blocks;
     if (nparts <= 1) return;
 
     // partition k of head h = kvh*G + g is row part_row(b, kvh, k) + g: rows G apart

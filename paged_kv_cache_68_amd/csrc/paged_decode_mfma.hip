@@ -56,16 +56,14 @@ __device__ __forceinline__ Item group_item(const DecodeArgs& a, int b, int kvh, 
     Item it;
     it.b = b;
     it.kvh = kvh;
-    int L = a.lens[b];
-    L = L < 0 ? 0 : (L > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : L);
-    it.L = L;
-    const int nblk = (L + kBlockSize - 1) / kBlockSize;
-    it.nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
+    it.L = clamped_length(a, b);
+    const int ntiles = (it.L + a.tile_tokens - 1) / a.tile_tokens;
+    it.nparts = (ntiles + a.part_blocks - 1) / a.part_blocks;
     const int chunk_end = min(it.nparts, (c + 1) * chunk);
     it.p = c * chunk + slot * ppw;
     it.p_end = max(it.p, min(chunk_end, it.p + ppw));
-    it.j0 = min(nblk, it.p * a.part_blocks);
-    it.j1 = min(nblk, it.p_end * a.part_blocks);
+    it.j0 = min(ntiles, it.p * a.part_blocks);
+    it.j1 = min(ntiles, it.p_end * a.part_blocks);
     return it;
 }
 

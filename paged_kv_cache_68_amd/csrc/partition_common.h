@@ -6,9 +6,11 @@
 // Address translation follows "PagedAttention: Treating KV Memory Like Virtual Memory"
 // ("How the kernel reads a block table": the tile at position i lives at
 // block_table[i / B] * block stride + (i mod B) * slot stride) and section 4 of
-// "PagedAttention and Virtual Memory Management" (Addr_K / Addr_V).  B = 16 is a
-// power of two, so positions split into (block, slot) with a shift and a mask, and a
-// 16-token tile is exactly one block: the table is read once per block, not per token.
+// "PagedAttention and Virtual Memory Management" (Addr_K / Addr_V).  The block size B
+// (8, 16, 32 or 64) is a power of two, so positions split into (block, slot) with a
+// shift and a mask.  The kernels walk tiles of T = min(B, 16) tokens: a tile never
+// straddles two blocks, a block holds B / T tiles, and the table is read once per tile,
+// not per token.
 #pragma once
 
 #include <stdlib.h>
@@ -18,8 +20,8 @@
 namespace pkv {
 
 // One unit of work: partitions [p, p_end) of sequence b for KV head kvh, i.e. the
-// sequence's blocks [j0, j1).  A wave that owns several consecutive partitions walks
-// their blocks as one stream and emits one result per partition.
+// sequence's tiles [j0, j1).  A wave that owns several consecutive partitions walks
+// their tiles as one stream and emits one result per partition.
 struct Item {
     int b, kvh;
     int p, p_end;
@@ -27,6 +29,13 @@ struct Item {
     int nparts;   // partitions this sequence actually has
     int j0, j1;
 };
+
+// Length of sequence b, clamped to [0, table width * B].
+__device__ __forceinline__ int clamped_length(const DecodeArgs& a, int b) {
+    const int L = a.lens[b];
+    const int cap = a.max_blocks * a.block_size;
+    return L < 0 ? 0 : (L > cap ? cap : L);
+}
 
 // Items are numbered with the KV head fastest, then the sequence, then the partition
 // group: the 4 waves of a work-group take 4 KV heads of the same blocks.
@@ -36,20 +45,18 @@ __device__ __forceinline__ Item decode_item(const DecodeArgs& a, int item, int p
     const int rest = item / a.num_kv_heads;
     it.b = rest % a.batch;
     const int g = rest / a.batch;
-    int L = a.lens[it.b];
-    L = L < 0 ? 0 : (L > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : L);
-    it.L = L;
-    const int nblk = (L + kBlockSize - 1) / kBlockSize;
-    it.nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
+    it.L = clamped_length(a, it.b);
+    const int ntiles = (it.L + a.tile_tokens - 1) / a.tile_tokens;
+    it.nparts = (ntiles + a.part_blocks - 1) / a.part_blocks;
     it.p = g * per_item;
     it.p_end = min(it.nparts, it.p + per_item);
     it.j0 = it.p * a.part_blocks;
-    it.j1 = min(nblk, it.p_end * a.part_blocks);
+    it.j1 = min(ntiles, it.p_end * a.part_blocks);
     return it;
 }
 
-// The blocks one wave visits: jb + js*k for k < nk.  Their table entries sit one per
-// lane in up to four VGPRs (partitions of at most 4096 tokens) and are fetched once.
+// The tiles one wave visits: jb + js*k for k < nk.  The table entry of each tile's
+// block sits one per lane in up to four VGPRs (at most 256 tiles) and is fetched once.
 struct BlockWalk {
     int jb, js, nk;
     int tab[4];
@@ -63,11 +70,11 @@ struct BlockWalk {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int k = 64 * t + lane;
-            tab[t] = (64 * t < nk && k < nk) ? trow[jb + js * k] : -1;
+            tab[t] = (64 * t < nk && k < nk) ? trow[(jb + js * k) >> a.tiles_log2] : -1;
         }
     }
 
-    // Blocks [j_begin, j_end) of the item's sequence, one after another.
+    // Tiles [j_begin, j_end) of the item's sequence, one after another.
     __device__ __forceinline__ void init_range(const DecodeArgs& a, const Item& it, int j_begin,
                                                int j_end, int lane) {
         jb = j_begin;
@@ -77,13 +84,14 @@ struct BlockWalk {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int k = 64 * t + lane;
-            tab[t] = (64 * t < nk && k < nk) ? trow[jb + k] : -1;
+            tab[t] = (64 * t < nk && k < nk) ? trow[(jb + k) >> a.tiles_log2] : -1;
         }
     }
 
-    // k-th block -> number of valid tokens and buffer resources over exactly those
-    // token rows of K and V (empty past the last block or for an out-of-range entry,
-    // so loads there return zeros and read nothing).
+    // k-th tile -> number of valid tokens and buffer resources over exactly those
+    // token rows of K and V (empty past the last tile or for an out-of-range entry,
+    // so loads there return zeros and read nothing).  Tile j is rows
+    // [(j mod B/T) * T, ... + T) of block table[j / (B/T)].
     __device__ __forceinline__ int at(const DecodeArgs& a, const Item& it, int k, int row_bytes,
                                       __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv) const {
         int valid = 0;
@@ -95,8 +103,10 @@ struct BlockWalk {
                         : k < 192 ? __builtin_amdgcn_readlane(tab[2], kk)
                                   : __builtin_amdgcn_readlane(tab[3], kk);
             if (static_cast<unsigned>(t) < static_cast<unsigned>(a.num_blocks)) {
-                valid = min(kBlockSize, it.L - (jb + js * k) * kBlockSize);
-                off = static_cast<size_t>(t) * (static_cast<size_t>(row_bytes / 2) * kBlockSize);
+                const int j = jb + js * k;
+                valid = min(a.tile_tokens, it.L - j * a.tile_tokens);
+                const int row = (j & ((1 << a.tiles_log2) - 1)) * a.tile_tokens;
+                off = (static_cast<size_t>(t) * a.block_size + row) * static_cast<size_t>(row_bytes / 2);
             }
         }
         // everything here is wave-uniform; say so, or the resource would be rebuilt
@@ -316,10 +326,10 @@ inline int64_t resident_waves(const void* kernel) {
 
 // Partitions per wave when waves own whole items: enough waves for about two rounds
 // of the GPU's resident waves (`slots`), at most 256 blocks of table per wave.
-inline int partitions_per_wave(int64_t items, int64_t slots, int num_parts, int part_blocks) {
+inline int partitions_per_wave(int64_t items, int64_t slots, int num_parts, int part_tiles) {
     const char* env = getenv("PAGEDKV_PARTS_PER_WAVE");     // override, for the tests
     int64_t per = env ? atoi(env) : (slots > 0 ? items / (2 * slots) : 1);
-    const int64_t cap = 256 / part_blocks;
+    const int64_t cap = kMaxTilesPerWave / part_tiles;
     if (per > num_parts) per = num_parts;
     if (per > cap) per = cap;
     return per < 1 ? 1 : static_cast<int>(per);
@@ -401,7 +411,7 @@ inline Plan make_plan(const DecodeArgs& a, int stage_bytes, bool group_capable,
     if (slots > 8 / heads) slots = 8 / heads;
     while (slots > 1 && heads * slots * stage_bytes > 64 * 1024) --slots;
     if (slots < 1) slots = 1;
-    const int max_ppw = 256 / a.part_blocks;
+    const int max_ppw = kMaxTilesPerWave / a.part_blocks;
     if (ppw > max_ppw) ppw = max_ppw;
     if (slots * ppw < chunk) chunk = static_cast<int>(slots) * ppw;
     slots = (chunk + ppw - 1) / ppw;        // no wave without a partition

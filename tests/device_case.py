@@ -31,6 +31,7 @@ class DeviceCase:
         self.cfg = cfg
         if case.where == "host":
             self.pool = pk.KVPool(1, cfg.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.dtype,
+                                  block_size=cfg.block_size,
                                   device=device)
             self.pool.k_cache(0).copy_(to_dev(case.k_pool, cfg.dtype, device))
             self.pool.v_cache(0).copy_(to_dev(case.v_pool, cfg.dtype, device))
@@ -41,6 +42,7 @@ class DeviceCase:
             mem = torch.empty(0, dtype=torch.uint8, device=k.device).set_(k.untyped_storage())
             case.k_pool = case.v_pool = None
             self.pool = pk.KVPool(1, cfg.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.dtype,
+                                  block_size=cfg.block_size,
                                   base=mem)
         self.query = to_dev(case.query, cfg.dtype, device)
         self.new_key = to_dev(case.new_key, cfg.dtype, device)
@@ -72,7 +74,7 @@ class DeviceCase:
     def blocks_of(self, b: int):
         """Host bits of sequence b's blocks (K, V) and the matching relabelled table."""
         L = int(self.case.lengths[b])
-        nblk = max(1, -(-L // 16))
+        nblk = max(1, -(-L // self.cfg.block_size))
         ids = torch.from_numpy(self.case.block_tables[b, :nblk].astype(np.int64)).to(self.out.device)
         kb = to_host_bits(self.pool.k_cache(0).index_select(0, ids))
         vb = to_host_bits(self.pool.v_cache(0).index_select(0, ids))

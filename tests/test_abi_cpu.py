@@ -53,7 +53,8 @@ def test_pool_bytes_closed_form(layers, hkv, d, dtype, per_token):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("block_size", 8, _lib.KV_ERR_UNSUPPORTED),
+    ("block_size", 12, _lib.KV_ERR_UNSUPPORTED),
+    ("block_size", 128, _lib.KV_ERR_UNSUPPORTED),
     ("head_dim", 96, _lib.KV_ERR_UNSUPPORTED),
     ("dtype", 7, _lib.KV_ERR_UNSUPPORTED),
     ("num_blocks", 0, _lib.KV_ERR_INVALID_ARG),
@@ -116,7 +117,11 @@ def test_workspace_bytes():
     assert lib.paged_attention_workspace_bytes(64, 32, 128, 512, 16, 0) == expect
     SIZE_MAX = (1 << 64) - 1
     assert lib.paged_attention_workspace_bytes(4, 14, 64, 3, 16, 100) == SIZE_MAX
-    assert lib.paged_attention_workspace_bytes(4, 14, 64, 3, 8, 512) == SIZE_MAX
+    assert lib.paged_attention_workspace_bytes(4, 14, 64, 3, 12, 512) == SIZE_MAX
+    # other block sizes: partitions count tokens, not blocks
+    assert lib.paged_attention_workspace_bytes(4, 14, 64, 64, 8, 512) == 0          # 512 tokens
+    n = 4 * 14 * 2
+    assert lib.paged_attention_workspace_bytes(4, 14, 64, 32, 32, 512) == ((n * 64 * 4 + 255) // 256) * 256 + n * 8
 
 
 A = FAKE_BASE + (1 << 20)    # aligned fake device pointers

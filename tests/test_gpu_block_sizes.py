@@ -1,0 +1,158 @@
+"""Block sizes 8, 32 and 64 ("PagedAttention and Virtual Memory Management", section 3:
+B is typically 8, 16 or 32): cache write and gather bit-exact, decode within the usual
+tolerances, on every launch plan, against the oracle run at the same block size."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import paged_kv_cache_68_amd as pk  # noqa: E402
+from workloads import config_by_name, make_case, nan_bits, round_to_bits  # noqa: E402
+
+from .gpu_helpers import TOL, DeviceCase, max_abs_err, oracle_after_write, to_dev, to_host_bits  # noqa: E402
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _case(lens, B, hq, hkv, d, dtype, seed):
+    """Scattered pool of block size B holding the given lengths (stale slots NaN)."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int32)
+    need = int(sum(-(-int(L) // B) for L in lens))
+    nb = need + 8
+    perm = rng.permutation(nb)
+    W = max(1, max(-(-int(L) // B) for L in lens))
+    tables = np.full((len(lens), W), -1, dtype=np.int32)
+    pos = 0
+    for b, L in enumerate(lens):
+        n = -(-int(L) // B)
+        tables[b, :n] = perm[pos:pos + n]
+        pos += n
+    kp = np.full((nb, B, hkv, d), nan_bits(dtype), dtype=np.uint16)
+    vp = np.full((nb, B, hkv, d), nan_bits(dtype), dtype=np.uint16)
+    for b, L in enumerate(lens):
+        for t in range(int(L)):
+            blk = tables[b, t // B]
+            kp[blk, t % B] = round_to_bits(rng.standard_normal((hkv, d), dtype=np.float32), dtype)
+            vp[blk, t % B] = round_to_bits(rng.standard_normal((hkv, d), dtype=np.float32), dtype)
+    q = round_to_bits(rng.standard_normal((len(lens), hq, d), dtype=np.float32), dtype)
+    return lens, tables, kp, vp, q, nb
+
+
+def _run(B, lens, tables, kp, vp, q, nb, hkv, d, dtype, part=512):
+    pool = pk.KVPool(1, nb, hkv, d, dtype, block_size=B)
+    pool.k_cache(0).copy_(to_dev(kp, dtype))
+    pool.v_cache(0).copy_(to_dev(vp, dtype))
+    qd = to_dev(q, dtype)
+    out = torch.empty_like(qd)
+    pk.paged_attention_decode(pool, 0, out, qd, torch.from_numpy(tables).cuda(),
+                              torch.from_numpy(lens).cuda(), scale=1.0 / np.sqrt(d),
+                              partition_size=part)
+    torch.cuda.synchronize()
+    return to_host_bits(out)
+
+
+PLANS = [
+    {"PAGEDKV_SPLIT": "1"},
+    {"PAGEDKV_SPLIT": "0"},
+    {"PAGEDKV_SPLIT": "0", "PAGEDKV_GROUP": "0", "PAGEDKV_PARTS_PER_WAVE": "2"},
+    {"PAGEDKV_SPLIT": "0", "PAGEDKV_GROUP_HEADS": "2", "PAGEDKV_GROUP_SLOTS": "2", "PAGEDKV_GROUP_PPW": "1"},
+    {"PAGEDKV_SPLIT": "1", "PAGEDKV_KERNEL": "valu"},
+    {"PAGEDKV_SPLIT": "0", "PAGEDKV_GROUP": "0", "PAGEDKV_KERNEL": "valu"},
+]
+
+
+@pytest.mark.parametrize("plan", range(len(PLANS)))
+@pytest.mark.parametrize("B", [8, 32, 64])
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(32, 8, 128, "bf16"), (14, 2, 64, "f16"), (8, 8, 128, "f16")])
+def test_decode_matches_oracle(B, plan, hq, hkv, d, dtype, monkeypatch):
+    for k, v in PLANS[plan].items():
+        monkeypatch.setenv(k, v)
+    _say(f"block size {B} plan {PLANS[plan]} hq={hq} hkv={hkv} d={d} {dtype}")
+    lens = [1, B - 1, B, B + 1, 511, 512, 513, 2000, 0, 4500, 17]
+    lens, tables, kp, vp, q, nb = _case(lens, B, hq, hkv, d, dtype, seed=40 + B)
+    out = _run(B, lens, tables, kp, vp, q, nb, hkv, d, dtype)
+    ref = oracle.paged_decode(q, kp, vp, tables, lens, 1.0 / np.sqrt(d), B, dtype)
+    assert max_abs_err(out, ref, dtype) <= TOL[dtype]
+    assert not out[8].any()
+
+
+@pytest.mark.parametrize("B", [8, 32, 64])
+def test_partition_sizes(B):
+    lens = [1, B + 1, 700, 2000, 4100]
+    lens, tables, kp, vp, q, nb = _case(lens, B, 16, 4, 128, "bf16", seed=50 + B)
+    ref = oracle.paged_decode(q, kp, vp, tables, lens, 1.0 / np.sqrt(128), B, "bf16")
+    for part in sorted({B, 64, 512, 2048} | ({4096} if B >= 16 else set())):
+        if part % B:
+            continue
+        out = _run(B, lens, tables, kp, vp, q, nb, 4, 128, "bf16", part)
+        assert max_abs_err(out, ref, "bf16") <= TOL["bf16"], part
+
+
+def test_block_size_8_rejects_partitions_past_2048():
+    pool = pk.KVPool(1, 64, 2, 64, "f16", block_size=8)
+    q = torch.zeros((1, 4, 64), dtype=torch.float16, device="cuda")
+    out = torch.empty_like(q)
+    t = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    ln = torch.ones(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(pk.PagedKVError):
+        pk.paged_attention_decode(pool, 0, out, q, t, ln, scale=0.1, partition_size=4096)
+
+
+@pytest.mark.parametrize("B", [8, 32, 64])
+@pytest.mark.parametrize("cfg_idx", [1, 2])
+def test_cache_write_gather_and_decode_configs(B, cfg_idx):
+    """The C1 / C2 workloads rebuilt at block size B: write bit-exact, gather
+    bit-exact, decode within tolerance."""
+    base = config_by_name(cfg_idx)
+    cfg = dataclasses.replace(base, block_size=B, num_blocks=max(16, base.num_blocks * 16 // B),
+                              name=f"{base.name}_b{B}")
+    _say(f"{cfg.name}")
+    case = make_case(cfg)
+    dc = DeviceCase(case)
+    out = to_host_bits(dc.step())
+    torch.cuda.synchronize()
+    ref, kp, vp = oracle_after_write(case)
+    assert np.array_equal(to_host_bits(dc.pool.k_cache(0)), kp)
+    assert np.array_equal(to_host_bits(dc.pool.v_cache(0)), vp)
+    assert max_abs_err(out, ref, cfg.dtype) <= TOL[cfg.dtype]
+    W = dc.tables.shape[1]
+    kg = torch.empty((cfg.batch, W * B, cfg.num_kv_heads, cfg.head_dim), dtype=dc.query.dtype, device="cuda")
+    vg = torch.empty_like(kg)
+    pk.kv_pool_gather(dc.pool, 0, dc.tables, dc.lens, kg, vg)
+    torch.cuda.synchronize()
+    kgh, vgh = to_host_bits(kg), to_host_bits(vg)
+    for b in range(cfg.batch):
+        L = int(case.lengths[b])
+        assert np.array_equal(kgh[b, :L], oracle.gather(kp, case.block_tables[b], L, B))
+        assert np.array_equal(vgh[b, :L], oracle.gather(vp, case.block_tables[b], L, B))
+        assert not kgh[b, L:].any() and not vgh[b, L:].any()
+
+
+def test_copy_blocks_block_size_64():
+    B, nb, hkv, d = 64, 40, 2, 64
+    rng = np.random.default_rng(60)
+    pool = pk.KVPool(2, nb, hkv, d, "f16", block_size=B)
+    host = []
+    for layer in range(2):
+        for which in (pool.k_cache, pool.v_cache):
+            bits = round_to_bits(rng.standard_normal((nb, B, hkv, d), dtype=np.float32), "f16")
+            which(layer).copy_(to_dev(bits, "f16"))
+            host.append(bits)
+    perm = rng.permutation(nb)
+    copies = np.stack([perm[:10], perm[10:20], [0, 1, 63, 64, 17, 33, 5, 64, 48, 2]], axis=1).astype(np.int32)
+    pk.copy_blocks(pool, torch.from_numpy(copies).cuda())
+    torch.cuda.synchronize()
+    got = [to_host_bits(f(l)) for l in range(2) for f in (pool.k_cache, pool.v_cache)]
+    for g, h in zip(got, host):
+        want = h.copy()
+        oracle.copy_blocks(want, copies.tolist())
+        assert np.array_equal(g, want)
