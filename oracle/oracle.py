@@ -37,7 +37,8 @@ import math
 import numpy as np
 
 __all__ = [
-    "to_f64", "kv_bytes_per_token", "kv_pool_bytes", "block_bytes", "locate",
+    "to_f64", "fp8_to_f64", "encode_fp8", "quantize_fp8", "FP8_MAX", "kv_bytes_per_token",
+    "kv_pool_bytes", "block_bytes", "locate",
     "physical_address", "scatter", "copy_blocks", "gather", "attention_contiguous", "softmax_weights",
     "paged_decode", "paged_decode_seq", "online_decode_seq", "partition_partials",
     "combine_partials", "partitioned_decode_seq", "brute_force_seq",
@@ -47,13 +48,83 @@ __all__ = [
 # ---------------------------------------------------------------- storage types
 
 def to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """uint16 bit patterns of fp16 / bf16 -> exact float64 values."""
+    """Stored bit patterns -> exact float64 values: uint16 of fp16 / bf16, or uint8
+    codes of fp8 (E4M3, see ``fp8_to_f64``)."""
+    if dtype == "fp8":
+        return fp8_to_f64(bits)
     bits = np.asarray(bits, dtype=np.uint16)
     if dtype == "f16":
         return bits.view(np.float16).astype(np.float64)
     if dtype == "bf16":
         return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     raise ValueError(dtype)
+
+
+# FP8 keys and values (one byte per element: b = 1 in P3 section 1).  The pages fix only
+# the width; the format taken is the 8-bit E4M3 layout with 1 sign bit, 4 exponent bits
+# (bias 7) and 3 mantissa bits, no infinities, and S.1111.111 as NaN, so the largest
+# finite magnitude is 1.75 * 2**8 = 448.  No scale factor is applied.
+
+FP8_MAX = 448.0
+
+
+def fp8_to_f64(codes: np.ndarray) -> np.ndarray:
+    """uint8 E4M3 codes -> exact float64 values (exponent field 0: subnormal m * 2**-9)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def encode_fp8(x: np.ndarray) -> np.ndarray:
+    """float64 values -> uint8 E4M3 codes: round to nearest, ties to the even code;
+    magnitudes past 448 (and infinities) saturate to 448; NaN -> S.1111.111 with the
+    input's sign.  Each value is rounded on the grid of its binade (the subnormal grid
+    2**-9 below 2**-6)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    flat_x, flat_o = x.reshape(-1), out.reshape(-1)
+    for i, v in enumerate(flat_x.tolist()):
+        s = 0x80 if math.copysign(1.0, v) < 0 else 0
+        if math.isnan(v):
+            flat_o[i] = s | 0x7F
+            continue
+        a = abs(v)
+        if a >= FP8_MAX:
+            flat_o[i] = s | 0x7E
+            continue
+        if a < 2.0 ** -6:                          # subnormal grid, step 2**-9
+            q = _round_half_even(a / 2.0 ** -9)    # 0..8; 8 is the smallest normal
+            flat_o[i] = s | q
+            continue
+        e = math.floor(math.log2(a))
+        while 2.0 ** e > a:                        # guard the log against rounding
+            e -= 1
+        while 2.0 ** (e + 1) <= a:
+            e += 1
+        q = _round_half_even((a / 2.0 ** e - 1.0) * 8.0)   # 0..8
+        if q == 8:
+            e, q = e + 1, 0
+        code = ((e + 7) << 3) | q
+        flat_o[i] = s | min(code, 0x7E)            # 1.75 * 2**8 is the largest finite
+    return out
+
+
+def _round_half_even(t: float) -> int:
+    f = math.floor(t)
+    r = t - f
+    if r > 0.5 or (r == 0.5 and f % 2 == 1):
+        f += 1
+    return int(f)
+
+
+def quantize_fp8(bits: np.ndarray, src_dtype: str) -> np.ndarray:
+    """16-bit key / value rows (fp16 or bf16 bit patterns) -> E4M3 codes, element-wise
+    (the cache write of an FP8 pool)."""
+    return encode_fp8(to_f64(bits, src_dtype))
 
 
 # ---------------------------------------------------------------- footprint
@@ -169,20 +240,22 @@ def attention_contiguous(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: flo
     return out
 
 
-def paged_decode_seq(q_bits, k_pool_bits, v_pool_bits, table, length, scale, block_size, dtype):
-    """Decode one sequence: gather K/V through its table, then contiguous attention."""
+def paged_decode_seq(q_bits, k_pool_bits, v_pool_bits, table, length, scale, block_size, dtype,
+                     q_dtype=None):
+    """Decode one sequence: gather K/V through its table, then contiguous attention.
+    ``dtype`` is the pools' storage type, ``q_dtype`` the query's (default: the same)."""
     kc = to_f64(gather(k_pool_bits, table, length, block_size), dtype)
     vc = to_f64(gather(v_pool_bits, table, length, block_size), dtype)
-    return attention_contiguous(to_f64(q_bits, dtype), kc, vc, scale)
+    return attention_contiguous(to_f64(q_bits, q_dtype or dtype), kc, vc, scale)
 
 
 def paged_decode(query_bits, k_pool_bits, v_pool_bits, block_tables, lengths, scale,
-                 block_size, dtype, seqs=None) -> np.ndarray:
+                 block_size, dtype, seqs=None, q_dtype=None) -> np.ndarray:
     """Whole batch (or the sequences listed in ``seqs``): fp64 [n, Hq, d]."""
     idx = range(len(lengths)) if seqs is None else seqs
     return np.stack([
         paged_decode_seq(query_bits[b], k_pool_bits, v_pool_bits, block_tables[b],
-                         int(lengths[b]), scale, block_size, dtype)
+                         int(lengths[b]), scale, block_size, dtype, q_dtype)
         for b in idx])
 
 
