@@ -29,10 +29,17 @@
  *    There is no host synchronisation and no host read of device data.
  *  - Every argument check runs on the host before anything is enqueued: a call that
  *    returns an error has changed nothing.  A launch failure returns KV_ERR_HIP.
- *  - Element type of Q, K, V and the attention output is the pool's dtype (fp16 or
- *    bf16).  Arithmetic is fp32: 16-bit inputs are widened exactly, dot products,
- *    softmax and the P.V accumulation are fp32, and the output is rounded to the
- *    16-bit type with round-to-nearest-even.
+ *  - K and V are stored in the pool's dtype: fp16, bf16, or FP8 E4M3 (one byte per
+ *    element; "PagedAttention and Virtual Memory Management", section 1: b = 1 for
+ *    FP8).  Queries, attention outputs and the new keys / values given to
+ *    reshape_and_cache use the pool's io_dtype (fp16 or bf16; for 16-bit pools it is
+ *    the pool's dtype).  Arithmetic is fp32: stored values are widened exactly, dot
+ *    products, softmax and the P.V accumulation are fp32, and the output is rounded to
+ *    the io type with round-to-nearest-even.
+ *  - FP8 E4M3: 1 sign, 4 exponent (bias 7) and 3 mantissa bits, no infinities,
+ *    S.1111.111 is NaN, largest finite magnitude 448, no scale factor.  The cache write
+ *    rounds to the nearest code (ties to even), saturates larger magnitudes and
+ *    infinities to +-448 and writes NaN as S.1111.111.
  *  - Results depend only on logical token positions: the output is bit-identical
  *    under any relabelling of physical blocks, and run-to-run deterministic.
  */
@@ -49,7 +56,8 @@ extern "C" {
 
 typedef enum kv_dtype {
     KV_DTYPE_F16 = 0,
-    KV_DTYPE_BF16 = 1
+    KV_DTYPE_BF16 = 1,
+    KV_DTYPE_FP8_E4M3 = 2      /* pool storage only */
 } kv_dtype_t;
 
 typedef enum kv_status {
@@ -64,15 +72,17 @@ typedef enum kv_status {
 
 /* Geometry of a KV pool.  Supported: block_size 8, 16, 32 or 64 ("PagedAttention and
  * Virtual Memory Management", section 3: B is typically 8, 16 or 32; 16 is the usual
- * default), head_dim 64 or 128, dtype KV_DTYPE_F16 / KV_DTYPE_BF16, num_blocks >= 1,
- * num_kv_heads >= 1. */
+ * default), head_dim 64 or 128, dtype KV_DTYPE_F16 / KV_DTYPE_BF16 / KV_DTYPE_FP8_E4M3,
+ * num_blocks >= 1, num_kv_heads >= 1.  io_dtype: KV_DTYPE_F16 or KV_DTYPE_BF16 for an
+ * FP8 pool; ignored (taken as dtype) for a 16-bit pool. */
 typedef struct kv_pool_desc {
     int32_t num_layers;
     int32_t num_blocks;
     int32_t block_size;
     int32_t num_kv_heads;
     int32_t head_dim;
-    int32_t dtype;             /* kv_dtype_t */
+    int32_t dtype;             /* kv_dtype_t: storage of K and V */
+    int32_t io_dtype;          /* kv_dtype_t: queries, outputs, new keys / values */
 } kv_pool_desc_t;
 
 /* Opaque, immutable after creation: safe to use from several streams at once. */
@@ -81,8 +91,9 @@ typedef struct kv_pool kv_pool_t;
 /* Human-readable name of a status code (static string). */
 const char* kv_status_string(kv_status_t status);
 
-/* Bytes of K+V per token over all layers, 2 * N_L * N_KV * d_h * b
- * ("PagedAttention and Virtual Memory Management", section 1, M_KV(L) at L = 1).
+/* Bytes of K+V per token over all layers, 2 * N_L * N_KV * d_h * b, b = 2 for fp16 /
+ * bf16 and 1 for FP8 ("PagedAttention and Virtual Memory Management", section 1,
+ * M_KV(L) at L = 1).
  * Returns 0 for an invalid or unsupported descriptor. */
 size_t kv_bytes_per_token(const kv_pool_desc_t* desc);
 
@@ -90,7 +101,7 @@ size_t kv_bytes_per_token(const kv_pool_desc_t* desc);
  * Memory layout (per layer l, for K then V):
  *   base + (2*l + 0) * S  : K cache [num_blocks][block_size][num_kv_heads][head_dim]
  *   base + (2*l + 1) * S  : V cache, same shape
- * with S = num_blocks * block_size * num_kv_heads * head_dim * 2 bytes.  Token row
+ * with S = num_blocks * block_size * num_kv_heads * head_dim * b bytes.  Token row
  * (block, offset) of one layer's K is contiguous (num_kv_heads * head_dim elements),
  * so a whole block of one layer is one contiguous stretch.  Returns 0 if invalid. */
 size_t kv_pool_bytes(const kv_pool_desc_t* desc);
@@ -119,7 +130,9 @@ kv_status_t kv_pool_layer_ptrs(const kv_pool_t* pool, int32_t layer, void** k_ca
                                void** v_cache);
 
 /* Write new tokens' keys and values into their slots of layer `layer`.
- *  key, value   : [num_tokens][num_kv_heads][head_dim], pool dtype.
+ *  key, value   : [num_tokens][num_kv_heads][head_dim], io dtype.  For an FP8 pool each
+ *                 element is rounded to E4M3 as stated above; otherwise the write is a
+ *                 bit copy.
  *  slot_mapping : [num_tokens] int64, slot = physical_block * block_size + offset
  *                 ("Why AI servers waste memory, and how paging fixes it", "The idea:
  *                 a block table"; "2.1 PagedAttention", section 5: physical block
@@ -127,7 +140,7 @@ kv_status_t kv_pool_layer_ptrs(const kv_pool_t* pool, int32_t layer, void** k_ca
  *                 slots >= num_blocks * block_size are also skipped.  Slots must be
  *                 pairwise distinct; if two tokens name the same slot, which one
  *                 lands is unspecified.
- * The write is a bit copy.  It is ordered before later work on the same stream, so a
+ * The write is ordered before later work on the same stream, so a
  * paged_attention_decode enqueued after it on that stream reads the new tokens.
  * num_tokens == 0 is a no-op. */
 kv_status_t reshape_and_cache(kv_pool_t* pool, int32_t layer, const void* key, const void* value,
@@ -143,8 +156,8 @@ size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
                                        int32_t partition_size);
 
 /* Decode attention for one layer.
- *  out          : [batch][num_q_heads][head_dim], pool dtype (written).
- *  query        : [batch][num_q_heads][head_dim], pool dtype.
+ *  out          : [batch][num_q_heads][head_dim], io dtype (written).
+ *  query        : [batch][num_q_heads][head_dim], io dtype.
  *  block_tables : [batch][max_blocks_per_seq] int32; entry j of row b is the physical
  *                 block holding tokens [Bj, Bj+B) of sequence b (B = the pool's
  *                 block_size).  Entries at or past ceil(context_lens[b] / B) are never
@@ -280,9 +293,9 @@ kv_status_t kv_bm_free_list(const kv_block_manager_t* bm, int32_t* blocks, int32
 
 /* Test hook: copy each sequence's K and V, through its block table, into contiguous
  * buffers ("Why AI servers waste memory, and how paging fixes it", "Reading through
- * the table").  k_out, v_out: [batch][max_blocks_per_seq * B][num_kv_heads][head_dim];
- * row t of sequence b is the pool row (table[b][t / B], t % B) for t < context_lens[b]
- * and zero otherwise.  Bit copy. */
+ * the table").  k_out, v_out: [batch][max_blocks_per_seq * B][num_kv_heads][head_dim]
+ * in the pool's storage dtype; row t of sequence b is the pool row (table[b][t / B],
+ * t % B) for t < context_lens[b] and zero otherwise.  Bit copy. */
 kv_status_t kv_pool_gather(const kv_pool_t* pool, int32_t layer, const int32_t* block_tables,
                            int32_t max_blocks_per_seq, const int32_t* context_lens,
                            int32_t batch, void* k_out, void* v_out, hipStream_t stream);

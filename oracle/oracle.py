@@ -83,42 +83,24 @@ def encode_fp8(x: np.ndarray) -> np.ndarray:
     """float64 values -> uint8 E4M3 codes: round to nearest, ties to the even code;
     magnitudes past 448 (and infinities) saturate to 448; NaN -> S.1111.111 with the
     input's sign.  Each value is rounded on the grid of its binade (the subnormal grid
-    2**-9 below 2**-6)."""
+    2**-9 below 2**-6); every scaling below is by a power of two, so exact in fp64, and
+    ``np.rint`` rounds halves to even."""
     x = np.asarray(x, dtype=np.float64)
-    out = np.empty(x.shape, dtype=np.uint8)
-    flat_x, flat_o = x.reshape(-1), out.reshape(-1)
-    for i, v in enumerate(flat_x.tolist()):
-        s = 0x80 if math.copysign(1.0, v) < 0 else 0
-        if math.isnan(v):
-            flat_o[i] = s | 0x7F
-            continue
-        a = abs(v)
-        if a >= FP8_MAX:
-            flat_o[i] = s | 0x7E
-            continue
-        if a < 2.0 ** -6:                          # subnormal grid, step 2**-9
-            q = _round_half_even(a / 2.0 ** -9)    # 0..8; 8 is the smallest normal
-            flat_o[i] = s | q
-            continue
-        e = math.floor(math.log2(a))
-        while 2.0 ** e > a:                        # guard the log against rounding
-            e -= 1
-        while 2.0 ** (e + 1) <= a:
-            e += 1
-        q = _round_half_even((a / 2.0 ** e - 1.0) * 8.0)   # 0..8
-        if q == 8:
-            e, q = e + 1, 0
-        code = ((e + 7) << 3) | q
-        flat_o[i] = s | min(code, 0x7E)            # 1.75 * 2**8 is the largest finite
-    return out
-
-
-def _round_half_even(t: float) -> int:
-    f = math.floor(t)
-    r = t - f
-    if r > 0.5 or (r == 0.5 and f % 2 == 1):
-        f += 1
-    return int(f)
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.int64)
+    a = np.abs(np.where(np.isnan(x), 0.0, x))
+    # normal binades: a = m * 2**e with m in [1, 2); 3 mantissa bits
+    _, E = np.frexp(np.where((a > 0) & np.isfinite(a), a, 1.0))
+    e = E.astype(np.int64) - 1
+    q = np.rint((np.ldexp(np.where(np.isfinite(a), a, 1.0), -e) - 1.0) * 8.0).astype(np.int64)
+    e = np.where(q == 8, e + 1, e)
+    q = np.where(q == 8, 0, q)
+    normal = ((e + 7) << 3) | q
+    # subnormal grid below 2**-6: code m = a / 2**-9 rounded (8 is the smallest normal)
+    sub = np.rint(np.where(a < 2.0 ** -6, a, 0.0) / 2.0 ** -9).astype(np.int64)
+    code = np.where(a < 2.0 ** -6, sub, np.minimum(normal, 0x7E))
+    code = np.where(a >= FP8_MAX, 0x7E, code)                        # saturate, incl. inf
+    code = np.where(np.isnan(x), 0x7F, code)
+    return (code | sign).astype(np.uint8)
 
 
 def quantize_fp8(bits: np.ndarray, src_dtype: str) -> np.ndarray:

@@ -13,7 +13,7 @@ import math
 from typing import Optional
 
 from ._lib import (  # noqa: F401
-    KV_DTYPE_BF16, KV_DTYPE_F16, KV_ERR_HIP, KV_ERR_INVALID_ARG, KV_ERR_OUT_OF_MEMORY,
+    KV_DTYPE_BF16, KV_DTYPE_F16, KV_DTYPE_FP8_E4M3, KV_ERR_HIP, KV_ERR_INVALID_ARG, KV_ERR_OUT_OF_MEMORY,
     KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE, KV_OK, KVPoolDesc, PagedKVError, check, lib,
     status_string,
 )
@@ -35,22 +35,35 @@ def _torch():
 
 
 def _dtype_code(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
     torch = _torch()
     if dtype in ("f16", "float16", torch.float16):
         return KV_DTYPE_F16
     if dtype in ("bf16", "bfloat16", torch.bfloat16):
         return KV_DTYPE_BF16
+    if dtype in ("fp8", "fp8_e4m3", "float8_e4m3fn", torch.float8_e4m3fn):
+        return KV_DTYPE_FP8_E4M3
     raise ValueError(f"unsupported dtype {dtype}")
 
 
 def _torch_dtype(code: int):
+    """torch dtype of a pool's stored elements (E4M3 codes are viewed as uint8)."""
     torch = _torch()
-    return {KV_DTYPE_F16: torch.float16, KV_DTYPE_BF16: torch.bfloat16}[code]
+    return {KV_DTYPE_F16: torch.float16, KV_DTYPE_BF16: torch.bfloat16,
+            KV_DTYPE_FP8_E4M3: torch.uint8}[code]
 
 
-def make_desc(num_layers, num_blocks, num_kv_heads, head_dim, dtype, block_size=BLOCK_SIZE):
+def make_desc(num_layers, num_blocks, num_kv_heads, head_dim, dtype, block_size=BLOCK_SIZE,
+              io_dtype=None):
+    """Pool descriptor.  ``dtype`` is the storage of K and V (f16, bf16 or fp8);
+    ``io_dtype`` the 16-bit type of queries, outputs and new keys / values (default:
+    ``dtype`` for a 16-bit pool, bf16 for an FP8 pool)."""
+    code = _dtype_code(dtype)
+    io = _dtype_code(io_dtype) if io_dtype is not None else (
+        KV_DTYPE_BF16 if code == KV_DTYPE_FP8_E4M3 else code)
     return KVPoolDesc(int(num_layers), int(num_blocks), int(block_size), int(num_kv_heads),
-                      int(head_dim), _dtype_code(dtype) if not isinstance(dtype, int) else dtype)
+                      int(head_dim), code, io)
 
 
 def kv_pool_bytes(desc: KVPoolDesc) -> int:
@@ -80,9 +93,10 @@ class KVPool:
     """
 
     def __init__(self, num_layers, num_blocks, num_kv_heads, head_dim, dtype,
-                 block_size=BLOCK_SIZE, device=None, base=None):
+                 block_size=BLOCK_SIZE, device=None, base=None, io_dtype=None):
         torch = _torch()
-        self.desc = make_desc(num_layers, num_blocks, num_kv_heads, head_dim, dtype, block_size)
+        self.desc = make_desc(num_layers, num_blocks, num_kv_heads, head_dim, dtype, block_size,
+                              io_dtype)
         nbytes = kv_pool_bytes(self.desc)
         if nbytes == 0:
             # let the library name the problem
@@ -94,7 +108,8 @@ class KVPool:
             dev = torch.device(device if device is not None else "cuda")
             base = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.memory = base
-        self.dtype = _torch_dtype(self.desc.dtype)
+        self.dtype = _torch_dtype(self.desc.dtype)            # stored K / V elements
+        self.io_dtype = _torch_dtype(self.desc.io_dtype)      # queries, outputs, new K / V
         h = ctypes.c_void_p()
         check(lib().kv_pool_create(ctypes.byref(self.desc), base.data_ptr(),
                                    base.numel() * base.element_size(), ctypes.byref(h)),

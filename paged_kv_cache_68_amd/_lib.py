@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
 KV_DTYPE_F16 = 0
 KV_DTYPE_BF16 = 1
+KV_DTYPE_FP8_E4M3 = 2
 
 KV_OK = 0
 KV_ERR_INVALID_ARG = 1
@@ -40,6 +41,7 @@ class KVPoolDesc(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32),
     ]
 
 

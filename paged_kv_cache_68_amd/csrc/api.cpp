@@ -22,6 +22,10 @@ bool aligned(const void* p, size_t a = kAlign) {
     return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
 
+// Bytes per stored K / V element, and the 16-bit type of queries, outputs and new keys.
+size_t elem_bytes(const kv_pool_desc_t& d) { return d.dtype == KV_DTYPE_FP8_E4M3 ? 1 : 2; }
+int32_t io_dtype(const kv_pool_desc_t& d) { return d.dtype == KV_DTYPE_FP8_E4M3 ? d.io_dtype : d.dtype; }
+
 kv_status_t check_desc(const kv_pool_desc_t* d) {
     if (!d) return KV_ERR_INVALID_ARG;
     if (d->num_layers < 1 || d->num_blocks < 1 || d->num_kv_heads < 1 || d->block_size < 1 ||
@@ -30,16 +34,21 @@ kv_status_t check_desc(const kv_pool_desc_t* d) {
     if (d->block_size != 8 && d->block_size != 16 && d->block_size != 32 && d->block_size != 64)
         return KV_ERR_UNSUPPORTED;
     if (d->head_dim != 64 && d->head_dim != 128) return KV_ERR_UNSUPPORTED;
-    if (d->dtype != KV_DTYPE_F16 && d->dtype != KV_DTYPE_BF16) return KV_ERR_UNSUPPORTED;
+    if (d->dtype != KV_DTYPE_F16 && d->dtype != KV_DTYPE_BF16 && d->dtype != KV_DTYPE_FP8_E4M3)
+        return KV_ERR_UNSUPPORTED;
+    if (d->dtype == KV_DTYPE_FP8_E4M3 && d->io_dtype != KV_DTYPE_F16 && d->io_dtype != KV_DTYPE_BF16)
+        return KV_ERR_UNSUPPORTED;
     // a layer's cache must be addressable with 64-bit offsets and the slot count with int64
     const unsigned __int128 bytes = static_cast<unsigned __int128>(d->num_blocks) * d->block_size *
-                                    d->num_kv_heads * d->head_dim * 2u * 2u * d->num_layers;
+                                    d->num_kv_heads * d->head_dim * elem_bytes(*d) * 2u *
+                                    d->num_layers;
     if (bytes >> 62) return KV_ERR_INVALID_ARG;
     return KV_OK;
 }
 
 size_t cache_bytes(const kv_pool_desc_t* d) {
-    return static_cast<size_t>(d->num_blocks) * d->block_size * d->num_kv_heads * d->head_dim * 2u;
+    return static_cast<size_t>(d->num_blocks) * d->block_size * d->num_kv_heads * d->head_dim *
+           elem_bytes(*d);
 }
 
 struct DecodeShape {
@@ -111,8 +120,9 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     pkv::DecodeArgs a;
     char* kc = pool->base + static_cast<size_t>(2 * layer) * pool->cache_bytes;
     a.q = static_cast<const uint16_t*>(query);
-    a.k = reinterpret_cast<const uint16_t*>(kc);
-    a.v = reinterpret_cast<const uint16_t*>(kc + pool->cache_bytes);
+    a.k = reinterpret_cast<const uint8_t*>(kc);
+    a.v = reinterpret_cast<const uint8_t*>(kc + pool->cache_bytes);
+    a.row_bytes = d.num_kv_heads * d.head_dim * static_cast<int32_t>(elem_bytes(d));
     a.tables = block_tables;
     a.lens = context_lens;
     a.out = static_cast<uint16_t*>(out);
@@ -140,7 +150,7 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     if (a.xcd_chunk < 0) a.xcd_chunk = 0;
     // bytes this call can touch: the sequences' table rows, and never more than the
     // layer's K and V caches; PAGEDKV_STREAM=0/1 overrides the choice
-    const size_t block_bytes = static_cast<size_t>(d.block_size) * d.num_kv_heads * d.head_dim * 2 * 2;
+    const size_t block_bytes = static_cast<size_t>(d.block_size) * a.row_bytes * 2;
     const size_t reach = block_bytes * std::min<size_t>(static_cast<size_t>(batch) * max_blocks,
                                                        static_cast<size_t>(d.num_blocks));
     a.stream_loads = reach > pkv::kStreamThresholdBytes ? 1 : 0;
@@ -165,18 +175,20 @@ kv_status_t decode_impl(int phases, const kv_pool_t* pool, int32_t layer, void* 
     const pkv::DecodeArgs a = make_args(pool, layer, out, query, block_tables, max_blocks,
                                         context_lens, batch, num_q_heads, scale, workspace, s);
     if (phases & kPartitions) {
-        if (pkv::launch_partitions(pool->desc.dtype, pool->desc.head_dim, s.group, a, stream) !=
+        if (pkv::launch_partitions(pool->desc.dtype, io_dtype(pool->desc), pool->desc.head_dim,
+                                   s.group, a, stream) !=
             hipSuccess)
             return KV_ERR_HIP;
     }
     if ((phases & kReduce) && s.num_parts > 1) {
         // the partition kernel may already have merged chunks of partitions
-        const int chunk = pkv::partition_chunk(pool->desc.dtype, pool->desc.head_dim, s.group, a);
+        const int chunk = pkv::partition_chunk(pool->desc.dtype, io_dtype(pool->desc),
+                                               pool->desc.head_dim, s.group, a);
         pkv::DecodeArgs r = a;
         r.part_blocks = a.part_blocks * chunk;
         r.num_parts = static_cast<int32_t>(ceil_div(a.num_parts, chunk));
         if (r.num_parts > 1 &&
-            pkv::launch_reduce(pool->desc.dtype, pool->desc.head_dim, r, stream) != hipSuccess)
+            pkv::launch_reduce(io_dtype(pool->desc), pool->desc.head_dim, r, stream) != hipSuccess)
             return KV_ERR_HIP;
     }
     return KV_OK;
@@ -201,7 +213,8 @@ const char* kv_status_string(kv_status_t status) {
 
 size_t kv_bytes_per_token(const kv_pool_desc_t* desc) {
     if (check_desc(desc) != KV_OK) return 0;
-    return 2u * static_cast<size_t>(desc->num_layers) * desc->num_kv_heads * desc->head_dim * 2u;
+    return 2u * static_cast<size_t>(desc->num_layers) * desc->num_kv_heads * desc->head_dim *
+           elem_bytes(*desc);
 }
 
 size_t kv_pool_bytes(const kv_pool_desc_t* desc) {
@@ -282,10 +295,8 @@ kv_status_t reshape_and_cache(kv_pool_t* pool, int32_t layer, const void* key, c
     char* kc = pool->base + static_cast<size_t>(2 * layer) * pool->cache_bytes;
     const int64_t num_slots = static_cast<int64_t>(d.num_blocks) * d.block_size;
     const hipError_t e = pkv::launch_reshape_and_cache(
-        static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value), slot_mapping,
-        num_tokens, reinterpret_cast<uint16_t*>(kc),
-        reinterpret_cast<uint16_t*>(kc + pool->cache_bytes), num_slots,
-        d.num_kv_heads * d.head_dim, stream);
+        key, value, slot_mapping, num_tokens, kc, kc + pool->cache_bytes, num_slots,
+        d.num_kv_heads * d.head_dim, d.dtype, io_dtype(d), stream);
     return e == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
@@ -296,8 +307,9 @@ kv_status_t kv_copy_blocks(kv_pool_t* pool, const int32_t* copies, int32_t num_c
     if (!copies || !aligned(copies, 4)) return KV_ERR_INVALID_ARG;
     const kv_pool_desc_t& d = pool->desc;
     const hipError_t e = pkv::launch_copy_blocks(
-        reinterpret_cast<uint16_t*>(pool->base), copies, num_copies, d.num_layers, d.num_blocks,
-        d.block_size, d.num_kv_heads * d.head_dim, pool->cache_bytes / 2, stream);
+        pool->base, copies, num_copies, d.num_layers, d.num_blocks, d.block_size,
+        d.num_kv_heads * d.head_dim * static_cast<int32_t>(elem_bytes(d)), pool->cache_bytes,
+        stream);
     return e == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
@@ -361,10 +373,9 @@ kv_status_t kv_pool_gather(const kv_pool_t* pool, int32_t layer, const int32_t* 
     const kv_pool_desc_t& d = pool->desc;
     const char* kc = pool->base + static_cast<size_t>(2 * layer) * pool->cache_bytes;
     const hipError_t e = pkv::launch_gather(
-        reinterpret_cast<const uint16_t*>(kc), reinterpret_cast<const uint16_t*>(kc + pool->cache_bytes),
-        block_tables, max_blocks_per_seq, context_lens, batch, d.num_blocks, d.block_size,
-        d.num_kv_heads * d.head_dim, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out),
-        stream);
+        kc, kc + pool->cache_bytes, block_tables, max_blocks_per_seq, context_lens, batch,
+        d.num_blocks, d.block_size, d.num_kv_heads * d.head_dim * static_cast<int32_t>(elem_bytes(d)),
+        k_out, v_out, stream);
     return e == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 

@@ -4,8 +4,9 @@
 // With the pool laid out [num_blocks][B][Hkv][D], slot = block * B + offset is
 // directly the index of a contiguous token row of Hkv*D elements, so the write of
 // "Why AI servers waste memory, and how paging fixes it" ("The real implementation":
-// the token lands in slot `offset` of block table[-1]) is a row copy to row `slot`.
-// Both kernels are pure bit copies with 16-byte (dwordx4) accesses.
+// the token lands in slot `offset` of block table[-1]) is a row copy to row `slot`,
+// a bit copy with 16-byte (dwordx4) accesses; into an FP8 pool each value is rounded to
+// E4M3 on the way.  The block copy and the gather are bit copies.
 
 #include <hip/hip_runtime.h>
 
@@ -31,6 +32,37 @@ __global__ __launch_bounds__(256) void rc_scatter(const uint4* __restrict__ key,
     for (int32_t ch = threadIdx.x; ch < row_chunks; ch += blockDim.x) {
         kd[ch] = ks[ch];
         vd[ch] = vs[ch];
+    }
+}
+
+// The same write into an FP8 pool: each lane reads 8 values of the 16-bit row (16 bytes),
+// widens them exactly to fp32 and writes their 8 E4M3 codes (8 bytes).
+template <class S>
+__device__ __forceinline__ uint2 to_fp8x8(uint4 x) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[e] = fp8x2_from(S::lo(w[e]), S::hi(w[e]));
+    return make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+}
+
+template <class S>
+__global__ __launch_bounds__(256) void rc_quantize(const uint4* __restrict__ key,
+                                                   const uint4* __restrict__ value,
+                                                   const int64_t* __restrict__ slots,
+                                                   uint2* __restrict__ k_cache,
+                                                   uint2* __restrict__ v_cache, int64_t num_slots,
+                                                   int32_t row_chunks) {
+    const int64_t i = blockIdx.x;
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= num_slots) return;
+    const uint4* ks = key + i * row_chunks;
+    const uint4* vs = value + i * row_chunks;
+    uint2* kd = k_cache + slot * row_chunks;
+    uint2* vd = v_cache + slot * row_chunks;
+    for (int32_t ch = threadIdx.x; ch < row_chunks; ch += blockDim.x) {
+        kd[ch] = to_fp8x8<S>(ks[ch]);
+        vd[ch] = to_fp8x8<S>(vs[ch]);
     }
 }
 
@@ -89,39 +121,47 @@ __global__ __launch_bounds__(256) void cow_copy(uint4* __restrict__ base,
 
 }  // namespace
 
-hipError_t launch_copy_blocks(uint16_t* base, const int32_t* copies, int32_t num_copies,
+hipError_t launch_copy_blocks(char* base, const int32_t* copies, int32_t num_copies,
                               int32_t num_layers, int32_t num_blocks, int32_t block_size,
-                              int32_t row_elems, size_t cache_elems, hipStream_t stream) {
+                              int32_t row_bytes, size_t cache_bytes, hipStream_t stream) {
     if (num_copies <= 0) return hipSuccess;
     hipLaunchKernelGGL(cow_copy, dim3(num_copies, 2 * num_layers), dim3(256), 0, stream,
                        reinterpret_cast<uint4*>(base), copies, num_blocks, block_size,
-                       row_elems / 8, cache_elems / 8);
+                       row_bytes / 16, cache_bytes / 16);
     return hipGetLastError();
 }
 
-hipError_t launch_reshape_and_cache(const uint16_t* key, const uint16_t* value,
-                                    const int64_t* slots, int32_t num_tokens, uint16_t* k_cache,
-                                    uint16_t* v_cache, int64_t num_slots, int32_t row_elems,
-                                    hipStream_t stream) {
+hipError_t launch_reshape_and_cache(const void* key, const void* value, const int64_t* slots,
+                                    int32_t num_tokens, void* k_cache, void* v_cache,
+                                    int64_t num_slots, int32_t row_elems, int kv_dtype,
+                                    int io_dtype, hipStream_t stream) {
     if (num_tokens <= 0) return hipSuccess;
-    const int32_t chunks = row_elems / 8;
+    const int32_t chunks = row_elems / 8;          // 8 values: 16 input bytes
     const int threads = chunks >= 256 ? 256 : ((chunks + 63) / 64) * 64;
-    hipLaunchKernelGGL(rc_scatter, dim3(num_tokens), dim3(threads), 0, stream,
-                       reinterpret_cast<const uint4*>(key), reinterpret_cast<const uint4*>(value),
-                       slots, reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache),
-                       num_slots, chunks);
+    const uint4* k = static_cast<const uint4*>(key);
+    const uint4* v = static_cast<const uint4*>(value);
+    if (kv_dtype == KV_DTYPE_FP8_E4M3) {
+        auto kernel = io_dtype == KV_DTYPE_F16 ? rc_quantize<F16> : rc_quantize<BF16>;
+        hipLaunchKernelGGL(kernel, dim3(num_tokens), dim3(threads), 0, stream, k, v, slots,
+                           static_cast<uint2*>(k_cache), static_cast<uint2*>(v_cache), num_slots,
+                           chunks);
+    } else {
+        hipLaunchKernelGGL(rc_scatter, dim3(num_tokens), dim3(threads), 0, stream, k, v, slots,
+                           static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), num_slots,
+                           chunks);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_gather(const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* tables,
+hipError_t launch_gather(const void* k_cache, const void* v_cache, const int32_t* tables,
                          int32_t max_blocks, const int32_t* lens, int32_t batch,
-                         int32_t num_blocks, int32_t block_size, int32_t row_elems,
-                         uint16_t* k_out, uint16_t* v_out, hipStream_t stream) {
+                         int32_t num_blocks, int32_t block_size, int32_t row_bytes,
+                         void* k_out, void* v_out, hipStream_t stream) {
     if (batch <= 0 || max_blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL(kv_gather, dim3(max_blocks, batch), dim3(256), 0, stream,
-                       reinterpret_cast<const uint4*>(k_cache), reinterpret_cast<const uint4*>(v_cache),
-                       tables, max_blocks, lens, num_blocks, block_size, row_elems / 8,
-                       reinterpret_cast<uint4*>(k_out), reinterpret_cast<uint4*>(v_out));
+                       static_cast<const uint4*>(k_cache), static_cast<const uint4*>(v_cache),
+                       tables, max_blocks, lens, num_blocks, block_size, row_bytes / 16,
+                       static_cast<uint4*>(k_out), static_cast<uint4*>(v_out));
     return hipGetLastError();
 }
 

@@ -48,6 +48,12 @@ struct F16 {
         return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
                                                      __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
     }
+    // two E4M3 codes (bytes 0-1, or 2-3 with HI) -> packed fp16, exact: every E4M3 value
+    // is an fp16 value (v_cvt_scalef32_pk_f16_fp8 with scale 1)
+    template <bool HI>
+    __device__ static __forceinline__ uint32_t from_fp8x2(uint32_t w) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+    }
 };
 
 // bf16 storage: v_dot2_f32_bf16 for q.k; widening is a 16-bit shift.
@@ -75,7 +81,29 @@ struct BF16 {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
                                                          __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
     }
+    // two E4M3 codes -> packed bf16, exact (v_cvt_scalef32_pk_bf16_fp8 with scale 1)
+    template <bool HI>
+    __device__ static __forceinline__ uint32_t from_fp8x2(uint32_t w) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+    }
 };
+
+// Four E4M3 codes (one dword, code i in byte i) -> four 16-bit values of S, in order.
+template <class S>
+__device__ __forceinline__ uint2 fp8x4_to(uint32_t w) {
+    return make_uint2(S::template from_fp8x2<false>(w), S::template from_fp8x2<true>(w));
+}
+
+// Two fp32 values -> two E4M3 codes in the low 16 bits (value a in byte 0): round to
+// nearest even (v_cvt_pk_fp8_f32), magnitudes past 448 and infinities saturated to
+// +-448, NaN written as S.1111.111 with its sign.
+__device__ __forceinline__ uint32_t fp8x2_from(float a, float b) {
+    auto sat = [](float x) { return __builtin_isnan(x) ? x : fminf(fmaxf(x, -448.f), 448.f); };
+    uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false)) & 0xffffu;
+    if (__builtin_isnan(a)) w = (w & 0xff00u) | 0x7fu | ((__float_as_uint(a) >> 24) & 0x80u);
+    if (__builtin_isnan(b)) w = (w & 0x00ffu) | ((0x7fu | ((__float_as_uint(b) >> 24) & 0x80u)) << 8);
+    return w;
+}
 
 // 16-bit halves of two dwords: (x.lo, y.lo) and (x.hi, y.hi), x's half in the low half.
 __device__ __forceinline__ uint32_t lo_halves(uint32_t x, uint32_t y) {
@@ -136,6 +164,10 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int off) {
 template <bool NT = false>
 __device__ __forceinline__ uint2 load8(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, NT ? 2 : 0));
+}
+template <bool NT = false>
+__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, NT ? 2 : 0);
 }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

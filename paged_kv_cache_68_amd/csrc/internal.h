@@ -30,8 +30,9 @@ constexpr int kWavesPerGroup = 4;       // waves per work-group of the partition
 // Everything the two decode kernels read; passed by value.
 struct DecodeArgs {
     const uint16_t* q;       // [B][Hq][D]
-    const uint16_t* k;       // [nb][block_size][Hkv][D]
-    const uint16_t* v;
+    const uint8_t* k;        // [nb][block_size][Hkv][D], elements of the storage type
+    const uint8_t* v;
+    int32_t row_bytes;       // bytes of one token row of K (Hkv * D * element bytes)
     const int32_t* tables;   // [B][max_blocks]
     const int32_t* lens;     // [B]
     uint16_t* out;           // [B][Hq][D]
@@ -60,29 +61,32 @@ constexpr size_t kStreamThresholdBytes = size_t(512) << 20;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-hipError_t launch_partitions(int dtype, int head_dim, int group, const DecodeArgs& a,
-                             hipStream_t stream);
-hipError_t launch_partitions_mfma(int dtype, int head_dim, int group, const DecodeArgs& a,
-                                  hipStream_t stream);
+// kv_dtype: storage of K and V (KV_DTYPE_*); io_dtype: queries and outputs (16-bit).
+hipError_t launch_partitions(int kv_dtype, int io_dtype, int head_dim, int group,
+                             const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_partitions_mfma(int kv_dtype, int io_dtype, int head_dim, int group,
+                                  const DecodeArgs& a, hipStream_t stream);
 // Partitions the partition kernel merges by itself before writing partial results
 // (the reduce kernel then combines chunks of that many partitions).
-int partition_chunk(int dtype, int head_dim, int group, const DecodeArgs& a);
-int partition_chunk_mfma(int dtype, int group, int head_dim, const DecodeArgs& a);
+int partition_chunk(int kv_dtype, int io_dtype, int head_dim, int group, const DecodeArgs& a);
+int partition_chunk_mfma(int kv_dtype, int io_dtype, int group, int head_dim, const DecodeArgs& a);
 // Waves per work-group of the matrix-core kernel's group plan for this batch (0: not used).
-int group_waves_mfma(int dtype, int group, int head_dim, const DecodeArgs& a);
-hipError_t launch_reduce(int dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_reshape_and_cache(const uint16_t* key, const uint16_t* value,
-                                    const int64_t* slots, int32_t num_tokens, uint16_t* k_cache,
-                                    uint16_t* v_cache, int64_t num_slots, int32_t row_elems,
-                                    hipStream_t stream);
-// base: layer 0's K cache; the 2 * num_layers caches follow each other, cache_elems
-// 16-bit elements apart.
-hipError_t launch_copy_blocks(uint16_t* base, const int32_t* copies, int32_t num_copies,
+int group_waves_mfma(int kv_dtype, int io_dtype, int group, int head_dim, const DecodeArgs& a);
+hipError_t launch_reduce(int io_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
+// New tokens' rows ([T][row_elems] in io_dtype) into their slots: a bit copy for a
+// 16-bit pool, E4M3 rounding for an FP8 pool.
+hipError_t launch_reshape_and_cache(const void* key, const void* value, const int64_t* slots,
+                                    int32_t num_tokens, void* k_cache, void* v_cache,
+                                    int64_t num_slots, int32_t row_elems, int kv_dtype,
+                                    int io_dtype, hipStream_t stream);
+// base: layer 0's K cache; the 2 * num_layers caches follow each other, cache_bytes
+// apart; rows of row_bytes bytes.
+hipError_t launch_copy_blocks(char* base, const int32_t* copies, int32_t num_copies,
                               int32_t num_layers, int32_t num_blocks, int32_t block_size,
-                              int32_t row_elems, size_t cache_elems, hipStream_t stream);
-hipError_t launch_gather(const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* tables,
+                              int32_t row_bytes, size_t cache_bytes, hipStream_t stream);
+hipError_t launch_gather(const void* k_cache, const void* v_cache, const int32_t* tables,
                          int32_t max_blocks, const int32_t* lens, int32_t batch,
-                         int32_t num_blocks, int32_t block_size, int32_t row_elems,
-                         uint16_t* k_out, uint16_t* v_out, hipStream_t stream);
+                         int32_t num_blocks, int32_t block_size, int32_t row_bytes,
+                         void* k_out, void* v_out, hipStream_t stream);
 
 }  // namespace pkv

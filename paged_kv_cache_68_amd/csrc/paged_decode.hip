@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void pa_partition_valu(DecodeArgs a, int n_ite
         for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
     }
 
-    const int row_bytes = a.num_kv_heads * D * 2;
+    const int row_bytes = a.row_bytes;
     const int off0 = (it.kvh * D + 8 * c) * 2 + r * row_bytes;   // + i * TPI * row_bytes
 
     auto load = [&](__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, Buf& buf) {
@@ -358,37 +358,40 @@ hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t stream) {
 // kernel bound by HBM.  Otherwise (small batches) they take the VALU kernel.
 // PAGEDKV_KERNEL=valu forces the VALU kernel for groups up to 8 (for comparisons);
 // =mfma forces the matrix cores.
-static int kernel_choice(int dtype, int head_dim, int group, const DecodeArgs& a) {
+static int kernel_choice(int kv_dtype, int io_dtype, int head_dim, int group, const DecodeArgs& a) {
+    if (kv_dtype == KV_DTYPE_FP8_E4M3) return 1;          // FP8 keys: matrix cores only
     const char* env = getenv("PAGEDKV_KERNEL");
     if (env && strcmp(env, "valu") == 0 && group <= kMaxGroupValu) return 0;
     if (env && strcmp(env, "mfma") == 0) return 1;
     if (group >= 2) return 1;
-    return group_waves_mfma(dtype, group, head_dim, a) > 0 ? 1 : 0;
+    return group_waves_mfma(kv_dtype, io_dtype, group, head_dim, a) > 0 ? 1 : 0;
 }
 
-int partition_chunk(int dtype, int head_dim, int group, const DecodeArgs& a) {
-    return kernel_choice(dtype, head_dim, group, a) == 1 ? partition_chunk_mfma(dtype, group, head_dim, a) : 1;
+int partition_chunk(int kv_dtype, int io_dtype, int head_dim, int group, const DecodeArgs& a) {
+    return kernel_choice(kv_dtype, io_dtype, head_dim, group, a) == 1
+               ? partition_chunk_mfma(kv_dtype, io_dtype, group, head_dim, a)
+               : 1;
 }
 
-hipError_t launch_partitions(int dtype, int head_dim, int group, const DecodeArgs& a,
-                             hipStream_t stream) {
-    if (kernel_choice(dtype, head_dim, group, a) == 1)
-        return launch_partitions_mfma(dtype, head_dim, group, a, stream);
-    if (dtype == KV_DTYPE_F16) {
+hipError_t launch_partitions(int kv_dtype, int io_dtype, int head_dim, int group,
+                             const DecodeArgs& a, hipStream_t stream) {
+    if (kernel_choice(kv_dtype, io_dtype, head_dim, group, a) == 1)
+        return launch_partitions_mfma(kv_dtype, io_dtype, head_dim, group, a, stream);
+    if (kv_dtype == KV_DTYPE_F16) {
         if (head_dim == 64) return launch_part_g<F16, 64>(group, a, stream);
         if (head_dim == 128) return launch_part_g<F16, 128>(group, a, stream);
-    } else if (dtype == KV_DTYPE_BF16) {
+    } else if (kv_dtype == KV_DTYPE_BF16) {
         if (head_dim == 64) return launch_part_g<BF16, 64>(group, a, stream);
         if (head_dim == 128) return launch_part_g<BF16, 128>(group, a, stream);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_reduce(int dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
-    if (dtype == KV_DTYPE_F16) {
+hipError_t launch_reduce(int io_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream) {
+    if (io_dtype == KV_DTYPE_F16) {
         if (head_dim == 64) return launch_reduce_t<F16, 64>(a, stream);
         if (head_dim == 128) return launch_reduce_t<F16, 128>(a, stream);
-    } else if (dtype == KV_DTYPE_BF16) {
+    } else if (io_dtype == KV_DTYPE_BF16) {
         if (head_dim == 64) return launch_reduce_t<BF16, 64>(a, stream);
         if (head_dim == 128) return launch_reduce_t<BF16, 128>(a, stream);
     }

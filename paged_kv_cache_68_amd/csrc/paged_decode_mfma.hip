@@ -21,6 +21,13 @@
 //    and re-packs them with v_perm into four-token columns, one per MFMA.
 // Each lane keeps a partial running sum over its 4 tokens; the running max is shared
 // by the head's lanes, so the accumulator rescale is uniform per head.
+//
+// FP8 keys and values (KV8): a lane loads the E4M3 codes it needs as whole 16-byte (K)
+// and 8- or 4-byte (V) pieces and widens them exactly to the query's 16-bit type in
+// registers (two values per instruction), so the matrix-core products above run
+// unchanged.  For the score product the lane of column group c then supplies the
+// contiguous elements [c D/4, (c+1) D/4) of its token, 8 per MFMA; Q^T is loaded with
+// the same assignment (the contraction does not care which lane supplies which k).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -67,7 +74,17 @@ __device__ __forceinline__ Item group_item(const DecodeArgs& a, int b, int kvh, 
     return it;
 }
 
-template <class S, int D, int MODE, bool NT>
+template <bool KV8, int NQK, int EPL> struct KVBuf;
+template <int NQK, int EPL> struct KVBuf<false, NQK, EPL> {      // 16-bit K and V
+    uint4 k[NQK];
+    typename std::conditional<EPL == 8, uint4, uint2>::type v[4];
+};
+template <int NQK, int EPL> struct KVBuf<true, NQK, EPL> {       // E4M3 codes
+    uint4 k[NQK / 2];
+    typename std::conditional<EPL == 8, uint2, uint32_t>::type v[4];
+};
+
+template <class S, int D, int MODE, bool NT, bool KV8>
 __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, int n_items,
                                                          int per_item, int ppw, int heads) {
     constexpr bool SPLIT = MODE == kSplit;
@@ -75,10 +92,7 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
     constexpr int NQK = D / 32;    // score MFMAs per block
     constexpr int EPL = D / 16;    // value MFMAs per block = V elements per lane per token
     using VRow = typename std::conditional<EPL == 8, uint4, uint2>::type;
-    struct Buf {
-        uint4 k[NQK];
-        VRow v[4];
-    };
+    using Buf = KVBuf<KV8, NQK, EPL>;
 
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
@@ -121,14 +135,15 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
         walk.init(a, it, SPLIT ? wave : 0, SPLIT ? W : 1, lane);
     }
 
-    // Q^T operand: head n (zero beyond the group), 8 elements per MFMA
+    // Q^T operand: head n (zero beyond the group), 8 elements per MFMA: elements
+    // 8 (4i + c) for 16-bit keys, c D/4 + 8i for FP8 keys (matching the K operand)
     uint4 qv[NQK];
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
         qv[i] = make_uint4(0, 0, 0, 0);
+        const int e0 = KV8 ? c * (D / 4) + 8 * i : 8 * (4 * i + c);
         if (n < G)
-            qv[i] = *reinterpret_cast<const uint4*>(a.q + out_row0 + static_cast<size_t>(n) * D +
-                                                    8 * (4 * i + c));
+            qv[i] = *reinterpret_cast<const uint4*>(a.q + out_row0 + static_cast<size_t>(n) * D + e0);
     }
 
     // The table entries and Q must be in registers before the first block can be
@@ -142,18 +157,55 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
     float m = -INFINITY;
     float l = 0.f;
 
-    const int row_bytes = a.num_kv_heads * D * 2;
-    const int koff = (it.kvh * D + 8 * c) * 2 + n * row_bytes;           // + 64 i
-    const int voff = (it.kvh * D + EPL * n) * 2 + 4 * c * row_bytes;     // + r * row_bytes
+    const int row_bytes = a.row_bytes;
+    constexpr int EB = KV8 ? 1 : 2;                                       // bytes per element
+    const int koff = KV8 ? it.kvh * D + c * (D / 4) + n * row_bytes       // + 16 i
+                         : (it.kvh * D + 8 * c) * 2 + n * row_bytes;      // + 64 i
+    const int voff = (it.kvh * D + EPL * n) * EB + 4 * c * row_bytes;     // + r * row_bytes
     const int addr_x32 = (lane ^ 32) * 4;
 
     auto load = [&](__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, Buf& buf) {
+        if constexpr (KV8) {
 #pragma unroll
-        for (int i = 0; i < NQK; ++i) buf.k[i] = load16<NT>(rk, koff + 64 * i);
+            for (int i = 0; i < NQK / 2; ++i) buf.k[i] = load16<NT>(rk, koff + 16 * i);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if constexpr (EPL == 8) buf.v[r] = load16<NT>(rv, voff + r * row_bytes);
-            else buf.v[r] = load8<NT>(rv, voff + r * row_bytes);
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (EPL == 8) buf.v[r] = load8<NT>(rv, voff + r * row_bytes);
+                else buf.v[r] = load4<NT>(rv, voff + r * row_bytes);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NQK; ++i) buf.k[i] = load16<NT>(rk, koff + 64 * i);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (EPL == 8) buf.v[r] = load16<NT>(rv, voff + r * row_bytes);
+                else buf.v[r] = load8<NT>(rv, voff + r * row_bytes);
+            }
+        }
+    };
+
+    // the K operand of MFMA i and the V rows, as 16-bit values of S
+    auto k_operand = [&](const Buf& buf, int i) -> uint4 {
+        if constexpr (KV8) {
+            const uint32_t* w = reinterpret_cast<const uint32_t*>(buf.k) + 2 * i;
+            const uint2 lo = fp8x4_to<S>(w[0]);
+            const uint2 hi = fp8x4_to<S>(w[1]);
+            return make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+            return buf.k[i];
+        }
+    };
+    auto v_row = [&](const Buf& buf, int r) -> VRow {
+        if constexpr (KV8) {
+            if constexpr (EPL == 8) {
+                const uint2 lo = fp8x4_to<S>(buf.v[r].x);
+                const uint2 hi = fp8x4_to<S>(buf.v[r].y);
+                return make_uint4(lo.x, lo.y, hi.x, hi.y);
+            } else {
+                return fp8x4_to<S>(buf.v[r]);
+            }
+        } else {
+            return buf.v[r];
         }
     };
 
@@ -187,7 +239,7 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
     auto process = [&](int k, int valid, const Buf& buf) {
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < NQK; ++i) s = S::mfma_k32(buf.k[i], qv[i], s);
+        for (int i = 0; i < NQK; ++i) s = S::mfma_k32(k_operand(buf, i), qv[i], s);
         float sr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sr[r] = (4 * c + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
@@ -209,12 +261,15 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
         const uint2 pt = make_uint2(S::pack2(pr[0], pr[1]), S::pack2(pr[2], pr[3]));
         // V^T operand of element e: (tok 4c, 4c+1 | 4c+2, 4c+3) at element EPL*n + e;
         // rows past the valid tokens were loaded as zeros
+        VRow vr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vr[r] = v_row(buf, r);
 #pragma unroll
         for (int q = 0; q < EPL / 2; ++q) {
-            const uint32_t w0 = reinterpret_cast<const uint32_t*>(&buf.v[0])[q];
-            const uint32_t w1 = reinterpret_cast<const uint32_t*>(&buf.v[1])[q];
-            const uint32_t w2 = reinterpret_cast<const uint32_t*>(&buf.v[2])[q];
-            const uint32_t w3 = reinterpret_cast<const uint32_t*>(&buf.v[3])[q];
+            const uint32_t w0 = reinterpret_cast<const uint32_t*>(&vr[0])[q];
+            const uint32_t w1 = reinterpret_cast<const uint32_t*>(&vr[1])[q];
+            const uint32_t w2 = reinterpret_cast<const uint32_t*>(&vr[2])[q];
+            const uint32_t w3 = reinterpret_cast<const uint32_t*>(&vr[3])[q];
             const uint2 even = make_uint2(lo_halves(w0, w1), lo_halves(w2, w3));
             const uint2 odd = make_uint2(hi_halves(w0, w1), hi_halves(w2, w3));
             acc[2 * q] = S::mfma_k16(even, pt, acc[2 * q]);
@@ -261,19 +316,20 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
 }
 
 // Waves of the group-plan kernel the GPU holds at once.
-template <class S, int D>
+template <class S, int D, bool KV8>
 int64_t group_target_waves() {
-    static const int64_t waves = resident_waves(reinterpret_cast<const void*>(&pa_partition_mfma<S, D, kGroup, false>));
+    static const int64_t waves =
+        resident_waves(reinterpret_cast<const void*>(&pa_partition_mfma<S, D, kGroup, false, KV8>));
     return waves;
 }
 
-template <class S, int D>
+template <class S, int D, bool KV8>
 hipError_t launch_t(int group, const DecodeArgs& a, hipStream_t stream) {
     const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.num_parts;
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidValue;
     const size_t stage = static_cast<size_t>(group) * (D + 4) * sizeof(float);
-    const Plan pl = make_plan(a, static_cast<int>(stage), true, group_target_waves<S, D>());
+    const Plan pl = make_plan(a, static_cast<int>(stage), true, group_target_waves<S, D, KV8>());
     if (pl.group_waves > 0) {
         // partials (if any) are per chunk: the reduce kernel sees chunks as partitions.
         // Work-groups keep launch order here: the XCDs then take neighbouring head
@@ -281,22 +337,23 @@ hipError_t launch_t(int group, const DecodeArgs& a, hipStream_t stream) {
         DecodeArgs g = a;
         g.xcd_chunk = 0;
         const int64_t wgs = static_cast<int64_t>(a.batch) * (a.num_kv_heads / pl.heads) * pl.chunks;
-        auto kernel = a.stream_loads ? pa_partition_mfma<S, D, kGroup, true>
-                                     : pa_partition_mfma<S, D, kGroup, false>;
+        auto kernel = a.stream_loads ? pa_partition_mfma<S, D, kGroup, true, KV8>
+                                     : pa_partition_mfma<S, D, kGroup, false, KV8>;
         hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(64 * pl.group_waves),
                            pl.group_waves * stage, stream, g, group, static_cast<int>(wgs),
                            pl.chunk, pl.ppw, pl.heads);
     } else if (split_items(items)) {
-        hipLaunchKernelGGL((pa_partition_mfma<S, D, kSplit, false>), dim3(static_cast<unsigned>(items)),
+        hipLaunchKernelGGL((pa_partition_mfma<S, D, kSplit, false, KV8>), dim3(static_cast<unsigned>(items)),
                            dim3(64 * kWavesPerGroup), kWavesPerGroup * stage, stream, a, group,
                            static_cast<int>(items), 1, 1, 1);
     } else {
-        static const int64_t slots = resident_waves(reinterpret_cast<const void*>(&pa_partition_mfma<S, D, kItem, false>));
+        static const int64_t slots =
+            resident_waves(reinterpret_cast<const void*>(&pa_partition_mfma<S, D, kItem, false, KV8>));
         const int per = partitions_per_wave(items, slots, a.num_parts, a.part_blocks);
         const int64_t waves = static_cast<int64_t>(a.batch) * a.num_kv_heads * ceil_div(a.num_parts, per);
         const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
-        auto kernel = a.stream_loads ? pa_partition_mfma<S, D, kItem, true>
-                                     : pa_partition_mfma<S, D, kItem, false>;
+        auto kernel = a.stream_loads ? pa_partition_mfma<S, D, kItem, true, KV8>
+                                     : pa_partition_mfma<S, D, kItem, false, KV8>;
         hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(groups)), dim3(64 * kWavesPerGroup),
                            kWavesPerGroup * stage, stream, a, group, static_cast<int>(waves), per,
                            1, 1);
@@ -304,35 +361,50 @@ hipError_t launch_t(int group, const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Calls F<S, D, KV8>::run(args...) for the dtypes and head size given at run time.
+template <template <class, int, bool> class F, class... Args>
+auto dispatch(int kv_dtype, int io_dtype, int head_dim, Args&&... args)
+    -> decltype(F<F16, 64, false>::run(args...)) {
+    const bool kv8 = kv_dtype == KV_DTYPE_FP8_E4M3;
+    if (io_dtype == KV_DTYPE_F16) {
+        if (head_dim == 64) return kv8 ? F<F16, 64, true>::run(args...) : F<F16, 64, false>::run(args...);
+        return kv8 ? F<F16, 128, true>::run(args...) : F<F16, 128, false>::run(args...);
+    }
+    if (head_dim == 64) return kv8 ? F<BF16, 64, true>::run(args...) : F<BF16, 64, false>::run(args...);
+    return kv8 ? F<BF16, 128, true>::run(args...) : F<BF16, 128, false>::run(args...);
+}
+
+template <class S, int D, bool KV8> struct TargetWaves {
+    static int64_t run() { return group_target_waves<S, D, KV8>(); }
+};
+template <class S, int D, bool KV8> struct Launch {
+    static hipError_t run(int group, const DecodeArgs& a, hipStream_t stream) {
+        return launch_t<S, D, KV8>(group, a, stream);
+    }
+};
+
 }  // namespace
 
-static Plan plan_mfma(int dtype, int group, int head_dim, const DecodeArgs& a) {
+static Plan plan_mfma(int kv_dtype, int io_dtype, int group, int head_dim, const DecodeArgs& a) {
     const int stage = group * (head_dim + 4) * static_cast<int>(sizeof(float));
-    int64_t target = 0;
-    if (dtype == KV_DTYPE_F16) target = head_dim == 64 ? group_target_waves<F16, 64>() : group_target_waves<F16, 128>();
-    else target = head_dim == 64 ? group_target_waves<BF16, 64>() : group_target_waves<BF16, 128>();
+    const int64_t target = dispatch<TargetWaves>(kv_dtype, io_dtype, head_dim);
     return make_plan(a, stage, true, target);
 }
 
-int partition_chunk_mfma(int dtype, int group, int head_dim, const DecodeArgs& a) {
-    return plan_mfma(dtype, group, head_dim, a).chunk;
+int partition_chunk_mfma(int kv_dtype, int io_dtype, int group, int head_dim, const DecodeArgs& a) {
+    return plan_mfma(kv_dtype, io_dtype, group, head_dim, a).chunk;
 }
 
-int group_waves_mfma(int dtype, int group, int head_dim, const DecodeArgs& a) {
-    return plan_mfma(dtype, group, head_dim, a).group_waves;
+int group_waves_mfma(int kv_dtype, int io_dtype, int group, int head_dim, const DecodeArgs& a) {
+    return plan_mfma(kv_dtype, io_dtype, group, head_dim, a).group_waves;
 }
 
-hipError_t launch_partitions_mfma(int dtype, int head_dim, int group, const DecodeArgs& a,
-                                  hipStream_t stream) {
+hipError_t launch_partitions_mfma(int kv_dtype, int io_dtype, int head_dim, int group,
+                                  const DecodeArgs& a, hipStream_t stream) {
     if (group < 1 || group > 16) return hipErrorInvalidValue;
-    if (dtype == KV_DTYPE_F16) {
-        if (head_dim == 64) return launch_t<F16, 64>(group, a, stream);
-        if (head_dim == 128) return launch_t<F16, 128>(group, a, stream);
-    } else if (dtype == KV_DTYPE_BF16) {
-        if (head_dim == 64) return launch_t<BF16, 64>(group, a, stream);
-        if (head_dim == 128) return launch_t<BF16, 128>(group, a, stream);
-    }
-    return hipErrorInvalidValue;
+    if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
+    if (io_dtype != KV_DTYPE_F16 && io_dtype != KV_DTYPE_BF16) return hipErrorInvalidValue;
+    return dispatch<Launch>(kv_dtype, io_dtype, head_dim, group, a, stream);
 }
 
 }  // namespace pkv

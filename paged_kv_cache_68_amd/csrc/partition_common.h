@@ -106,7 +106,7 @@ struct BlockWalk {
                 const int j = jb + js * k;
                 valid = min(a.tile_tokens, it.L - j * a.tile_tokens);
                 const int row = (j & ((1 << a.tiles_log2) - 1)) * a.tile_tokens;
-                off = (static_cast<size_t>(t) * a.block_size + row) * static_cast<size_t>(row_bytes / 2);
+                off = (static_cast<size_t>(t) * a.block_size + row) * static_cast<size_t>(row_bytes);
             }
         }
         // everything here is wave-uniform; say so, or the resource would be rebuilt

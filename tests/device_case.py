@@ -10,15 +10,20 @@ import torch
 import paged_kv_cache_68_amd as pk
 from workloads import DecodeCase
 
-TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.uint8}
 
 
 def to_dev(bits: np.ndarray, dtype: str, device="cuda"):
+    """Host bit patterns (uint16, or uint8 E4M3 codes) -> device tensor of that type."""
+    if dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint8)).to(device)
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
     return t.view(TORCH_DT[dtype])
 
 
 def to_host_bits(t) -> np.ndarray:
+    if t.dtype == torch.uint8:
+        return t.detach().contiguous().cpu().numpy()
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
@@ -30,19 +35,19 @@ class DeviceCase:
         self.case = case
         self.cfg = cfg
         if case.where == "host":
-            self.pool = pk.KVPool(1, cfg.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.dtype,
-                                  block_size=cfg.block_size,
+            self.pool = pk.KVPool(1, cfg.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.kv,
+                                  block_size=cfg.block_size, io_dtype=cfg.dtype,
                                   device=device)
-            self.pool.k_cache(0).copy_(to_dev(case.k_pool, cfg.dtype, device))
-            self.pool.v_cache(0).copy_(to_dev(case.v_pool, cfg.dtype, device))
+            self.pool.k_cache(0).copy_(to_dev(case.k_pool, cfg.kv, device))
+            self.pool.v_cache(0).copy_(to_dev(case.v_pool, cfg.kv, device))
         else:
             # device-generated pools: adopt their memory as a one-layer pool
             k, v = case.k_pool, case.v_pool
             assert v.data_ptr() == k.data_ptr() + k.numel() * k.element_size()
             mem = torch.empty(0, dtype=torch.uint8, device=k.device).set_(k.untyped_storage())
             case.k_pool = case.v_pool = None
-            self.pool = pk.KVPool(1, cfg.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.dtype,
-                                  block_size=cfg.block_size,
+            self.pool = pk.KVPool(1, cfg.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.kv,
+                                  block_size=cfg.block_size, io_dtype=cfg.dtype,
                                   base=mem)
         self.query = to_dev(case.query, cfg.dtype, device)
         self.new_key = to_dev(case.new_key, cfg.dtype, device)

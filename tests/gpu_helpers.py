@@ -18,9 +18,12 @@ def oracle_after_write(case: DecodeCase):
     cfg = case.cfg
     kp = case.k_pool.copy()
     vp = case.v_pool.copy()
-    oracle.scatter(kp, vp, case.new_key, case.new_value, case.slot_mapping, cfg.block_size)
+    key, value = case.new_key, case.new_value
+    if cfg.kv == "fp8":               # the cache write of an FP8 pool rounds to E4M3
+        key, value = oracle.quantize_fp8(key, cfg.dtype), oracle.quantize_fp8(value, cfg.dtype)
+    oracle.scatter(kp, vp, key, value, case.slot_mapping, cfg.block_size)
     ref = oracle.paged_decode(case.query, kp, vp, case.block_tables, case.lengths, cfg.scale,
-                              cfg.block_size, cfg.dtype)
+                              cfg.block_size, cfg.kv, q_dtype=cfg.dtype)
     return ref, kp, vp
 
 
@@ -32,7 +35,7 @@ def oracle_for_seqs(dc: DeviceCase, seqs):
         kb, vb, table = dc.blocks_of(b)
         out.append(oracle.paged_decode_seq(dc.case.query[b], kb, vb, table,
                                            int(dc.case.lengths[b]), cfg.scale, cfg.block_size,
-                                           cfg.dtype))
+                                           cfg.kv, q_dtype=cfg.dtype))
     return np.stack(out)
 
 

@@ -44,12 +44,28 @@ def test_status_strings():
     (24, 2, 64, "f16", 12288),      # Qwen2.5-0.5B, 12 KiB / token
     (32, 8, 128, "bf16", 131072),   # Llama-3-8B, 128 KiB / token
     (80, 64, 128, "f16", 2621440),  # Llama-2-70B
+    (32, 8, 128, "fp8", 65536),     # Llama-3-8B with one-byte keys and values
 ])
 def test_pool_bytes_closed_form(layers, hkv, d, dtype, per_token):
     desc = pk.make_desc(layers, 1000, hkv, d, dtype)
+    b = 1 if dtype == "fp8" else 2
     assert pk.kv_bytes_per_token(desc) == per_token
-    assert pk.kv_bytes_per_token(desc) == oracle.kv_bytes_per_token(layers, hkv, d, 2)
-    assert pk.kv_pool_bytes(desc) == oracle.kv_pool_bytes(layers, hkv, d, 2, 1000, 16)
+    assert pk.kv_bytes_per_token(desc) == oracle.kv_bytes_per_token(layers, hkv, d, b)
+    assert pk.kv_pool_bytes(desc) == oracle.kv_pool_bytes(layers, hkv, d, b, 1000, 16)
+
+
+def test_fp8_pool_needs_a_16_bit_io_type():
+    desc = pk.make_desc(1, 64, 2, 64, "fp8", io_dtype="f16")
+    assert pk.kv_pool_bytes(desc) == 64 * 16 * 2 * 64 * 2
+    for bad in (2, 7, -1):
+        desc.io_dtype = bad
+        assert pk.kv_pool_bytes(desc) == 0
+        h = ctypes.c_void_p()
+        assert _lib.lib().kv_pool_create(ctypes.byref(desc), FAKE_BASE, 1 << 30, ctypes.byref(h)) == _lib.KV_ERR_UNSUPPORTED
+    # a 16-bit pool ignores io_dtype
+    desc = pk.make_desc(1, 64, 2, 64, "f16")
+    desc.io_dtype = 7
+    assert pk.kv_pool_bytes(desc) == 64 * 16 * 2 * 64 * 2 * 2
 
 
 @pytest.mark.parametrize("field,value,status", [

@@ -24,21 +24,29 @@ class DecodeConfig:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    dtype: str            # "f16" or "bf16": storage type of Q, K, V and the output
+    dtype: str            # "f16" or "bf16": Q, new K / V and the output; K / V storage
+                          # too unless kv_dtype is set
     block_size: int
     num_blocks: int       # physical blocks in the pool (one layer)
     batch: int
     lengths: str          # recipe name, see gen.draw_lengths
     partition_size: int   # tokens per split-context partition
     description: str
+    kv_dtype: str = ""    # storage of K and V when it differs from ``dtype``: "fp8" (E4M3)
 
     @property
     def group(self) -> int:
         return self.num_q_heads // self.num_kv_heads
 
     @property
+    def kv(self) -> str:
+        """Storage type of K and V ("f16", "bf16" or "fp8")."""
+        return self.kv_dtype or self.dtype
+
+    @property
     def elem_bytes(self) -> int:
-        return 2
+        """Bytes per stored K / V element."""
+        return 1 if self.kv == "fp8" else 2
 
     @property
     def scale(self) -> float:

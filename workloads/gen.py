@@ -14,7 +14,8 @@ table) is described here by:
 
 16-bit values are kept as uint16 bit patterns on the host so that fp16 and bf16 can
 be handled the same way and compared bit for bit.  Values are i.i.d. N(0, 1) drawn in
-fp32 and rounded to the storage type with round-to-nearest-even.
+fp32 and rounded to the storage type with round-to-nearest-even.  FP8 (E4M3) pools hold
+uint8 codes, drawn the same way and rounded by torch's float8_e4m3fn conversion.
 
 Slots nobody may read (unused blocks, positions >= L-1 of a last block) can be
 poisoned with NaN, so a reader that touches them shows up as NaN in its output.
@@ -43,7 +44,11 @@ def bits_dtype_name(dtype: str) -> str:
 
 
 def nan_bits(dtype: str) -> int:
-    return {"f16": 0x7E00, "bf16": 0x7FC0}[dtype]
+    return {"f16": 0x7E00, "bf16": 0x7FC0, "fp8": 0x7F}[dtype]
+
+
+def _np_storage(dtype: str):
+    return np.uint8 if dtype == "fp8" else np.uint16
 
 
 def round_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -134,17 +139,21 @@ def _stale_mask(cfg, lens, tables):
 
 
 def _host_values(shape, rng, dtype):
-    return round_to_bits(rng.standard_normal(size=shape, dtype=np.float32), dtype)
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if dtype == "fp8":
+        import torch  # E4M3 rounding of the drawn values (input data only)
+        return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return round_to_bits(x, dtype)
 
 
 def _make_scattered_host(cfg, rng, lens, poison):
     bs, H, d = cfg.block_size, cfg.num_kv_heads, cfg.head_dim
     tables, used = _scattered_tables(cfg, lens, rng)
-    fill = nan_bits(cfg.dtype) if poison else 0
+    fill = nan_bits(cfg.kv) if poison else 0
     pools = []
     for _ in range(2):   # K then V
-        pool = np.full((cfg.num_blocks, bs, H, d), fill, dtype=np.uint16)
-        pool[used] = _host_values((len(used), bs, H, d), rng, cfg.dtype)
+        pool = np.full((cfg.num_blocks, bs, H, d), fill, dtype=_np_storage(cfg.kv))
+        pool[used] = _host_values((len(used), bs, H, d), rng, cfg.kv)
         pools.append(pool)
     return tables, used, pools
 
@@ -159,9 +168,9 @@ def _make_shared_prefix_host(cfg, rng, poison):
     """
     bs, H, d = cfg.block_size, cfg.num_kv_heads, cfg.head_dim
     nb = cfg.num_blocks
-    fill = nan_bits(cfg.dtype) if poison else 0
-    kp = np.full((nb, bs, H, d), fill, dtype=np.uint16)
-    vp = np.full((nb, bs, H, d), fill, dtype=np.uint16)
+    fill = nan_bits(cfg.kv) if poison else 0
+    kp = np.full((nb, bs, H, d), fill, dtype=_np_storage(cfg.kv))
+    vp = np.full((nb, bs, H, d), fill, dtype=_np_storage(cfg.kv))
     free = deque(int(x) for x in rng.permutation(nb))
     ref = np.zeros(nb, dtype=np.int64)
 
@@ -171,8 +180,8 @@ def _make_shared_prefix_host(cfg, rng, poison):
     # prefix tokens (the parent's prompt)
     for j, blk in enumerate(prefix):
         n_valid = min(bs, SHARED_PREFIX_TOKENS - j * bs)
-        kp[blk, :n_valid] = _host_values((n_valid, H, d), rng, cfg.dtype)
-        vp[blk, :n_valid] = _host_values((n_valid, H, d), rng, cfg.dtype)
+        kp[blk, :n_valid] = _host_values((n_valid, H, d), rng, cfg.kv)
+        vp[blk, :n_valid] = _host_values((n_valid, H, d), rng, cfg.kv)
     # fork: every child copies the parent's table; counts rise by forks-1
     tables = [list(prefix) for _ in range(SHARED_FORKS)]
     ref[prefix] += SHARED_FORKS - 1
@@ -200,8 +209,8 @@ def _make_shared_prefix_host(cfg, rng, poison):
                 tables[b].append(blk)
             if t < L - 1:
                 blk = tables[b][j]
-                kp[blk, o] = _host_values((H, d), rng, cfg.dtype)
-                vp[blk, o] = _host_values((H, d), rng, cfg.dtype)
+                kp[blk, o] = _host_values((H, d), rng, cfg.kv)
+                vp[blk, o] = _host_values((H, d), rng, cfg.kv)
     width = max(len(t) for t in tables)
     tab = np.full((SHARED_FORKS, width), -1, dtype=np.int32)
     for b, t in enumerate(tables):
@@ -244,8 +253,8 @@ def make_case(cfg: DecodeConfig, where: str = "host", poison: bool = True,
         kp, vp = pools
         if poison:
             for blk, o in _stale_mask(cfg, lens, tables):
-                kp[blk, o] = nan_bits(cfg.dtype)
-                vp[blk, o] = nan_bits(cfg.dtype)
+                kp[blk, o] = nan_bits(cfg.kv)
+                vp[blk, o] = nan_bits(cfg.kv)
     else:
         kp, vp = _device_pools(cfg, lens, tables, used, poison, device)
 
@@ -274,7 +283,7 @@ def truncate(case: DecodeCase, batch: int) -> DecodeCase:
 def _device_pools(cfg, lens, tables, used, poison, device):
     import torch  # device inputs only
 
-    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[cfg.kv]
     bs, H, d = cfg.block_size, cfg.num_kv_heads, cfg.head_dim
     dev = torch.device(device if device is not None else "cuda")
     gen = torch.Generator(device=dev)
@@ -291,7 +300,6 @@ def _device_pools(cfg, lens, tables, used, poison, device):
                                     dtype=torch.float32).to(tdt)
         pools.append(pool)
     if poison:
-        nan = float("nan")
         mask = torch.ones(cfg.num_blocks, dtype=torch.bool, device=dev)
         mask[torch.as_tensor(used, device=dev)] = False
         idx = torch.nonzero(mask).flatten()
@@ -299,7 +307,10 @@ def _device_pools(cfg, lens, tables, used, poison, device):
         sb = torch.as_tensor([s[0] for s in stale], device=dev, dtype=torch.long)
         so = torch.as_tensor([s[1] for s in stale], device=dev, dtype=torch.long)
         for pool in pools:
+            # NaN bit patterns written through an integer view of the storage
+            ints = pool.view(torch.uint8) if cfg.kv == "fp8" else pool.view(torch.int16)
+            nan = nan_bits(cfg.kv)              # < 0x8000: fits the int16 view as is
             if idx.numel():
-                pool.index_fill_(0, idx, nan)
-            pool[sb, so] = nan
+                ints.index_fill_(0, idx, nan)
+            ints[sb, so] = nan
     return pools[0], pools[1]
