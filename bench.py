@@ -37,19 +37,22 @@ PARTITION_KERNEL = "pa_partition"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
-def algorithmic_bytes(lens, hq, hkv, d, elem, block_size=16):
+def algorithmic_bytes(lens, hq, hkv, d, kv_elem, io_elem=2, block_size=16):
     """Bytes the method must move for one step (K+V of every context token, the table
-    entries and length read, Q in and O out), and the partition kernel's share."""
+    entries and length read, Q in and O out), and the partition kernel's share.
+    kv_elem: bytes per stored K / V element (1 for FP8); io_elem: bytes per query /
+    output / new key element."""
     lens = np.asarray(lens, dtype=np.int64)
-    kv = int(np.sum(2 * lens * hkv * d * elem))
+    kv = int(np.sum(2 * lens * hkv * d * kv_elem))
     table = int(np.sum(4 * ((lens + block_size - 1) // block_size)))
     nlen = 4 * len(lens)
-    q = len(lens) * hq * d * elem
-    o = len(lens) * hq * d * elem
+    q = len(lens) * hq * d * io_elem
+    o = len(lens) * hq * d * io_elem
+    write = len(lens) * (2 * hkv * d * (io_elem + kv_elem) + 8)
     return {"kv": kv, "table": table, "lens": nlen, "q": q, "o": o,
             "partition_kernel": kv + table + nlen + q,
-            "write": len(lens) * (2 * hkv * d * elem * 2 + 8),
-            "step": kv + table + nlen + q + o + len(lens) * (2 * hkv * d * elem * 2 + 8)}
+            "write": write,
+            "step": kv + table + nlen + q + o + write}
 
 
 def kernel_source_hash() -> str:
@@ -90,7 +93,7 @@ def cpu_baseline(dc, budget_s: float):
             kb, vb, table = dc.blocks_of(b)
             t0 = time.perf_counter()
             ref = oracle.paged_decode_seq(dc.case.query[b], kb, vb, table, int(dc.case.lengths[b]),
-                                          cfg.scale, cfg.block_size, cfg.dtype)
+                                          cfg.scale, cfg.block_size, cfg.kv, q_dtype=cfg.dtype)
             t_total += time.perf_counter() - t0
             max_err = max(max_err, float(np.max(np.abs(oracle.to_f64(out_bits[b], cfg.dtype) - ref))))
             done += 1
@@ -204,6 +207,8 @@ def main(argv=None):
     ap.add_argument("--block-size", type=int, default=None,
                     help="rebuild the workload with this block size (8, 16, 32, 64); the pool "
                          "keeps the same number of token slots")
+    ap.add_argument("--kv-dtype", choices=["fp8"], default=None,
+                    help="store keys and values as FP8 (E4M3) instead of the workload's type")
     ap.add_argument("--cow", choices=sorted(COW_WORKLOADS),
                     help="time the copy-on-write block copy on this workload instead")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
@@ -253,11 +258,14 @@ def main(argv=None):
         B = args.block_size
         cfg = dataclasses.replace(cfg, block_size=B, num_blocks=cfg.num_blocks * cfg.block_size // B,
                                   name=f"{cfg.name}_b{B}")
+    if args.kv_dtype:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, kv_dtype=args.kv_dtype, name=f"{cfg.name}_{args.kv_dtype}kv")
     print(f"[bench] building {cfg.name} on the device", file=sys.stderr, flush=True)
     case = make_case(cfg, where="device" if cfg.index in (3, 5) else "host", poison=False)
     dc = DeviceCase(case)
-    elem = 2
-    nbytes = algorithmic_bytes(case.lengths, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, elem)
+    nbytes = algorithmic_bytes(case.lengths, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                               cfg.elem_bytes, 2, cfg.block_size)
     stream = torch.cuda.current_stream()
 
     def step(ev_a=None, ev_b=None):
@@ -303,7 +311,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": cfg.dtype if cfg.kv == cfg.dtype else f"{cfg.kv} kv, {cfg.dtype} q/out",
         "data": "synthetic",
         "config": {
             "workload": cfg.name,

@@ -91,7 +91,6 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
     constexpr int W = kWavesPerGroup;
     constexpr int NQK = D / 32;    // score MFMAs per block
     constexpr int EPL = D / 16;    // value MFMAs per block = V elements per lane per token
-    using VRow = typename std::conditional<EPL == 8, uint4, uint2>::type;
     using Buf = KVBuf<KV8, NQK, EPL>;
 
     const int lane = threadIdx.x & 63;
@@ -195,17 +194,13 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
             return buf.k[i];
         }
     };
-    auto v_row = [&](const Buf& buf, int r) -> VRow {
+    // dword q (16-bit elements 2q, 2q+1) of V row r, widened just before it is used
+    auto v_word = [&](const Buf& buf, int r, int q) -> uint32_t {
         if constexpr (KV8) {
-            if constexpr (EPL == 8) {
-                const uint2 lo = fp8x4_to<S>(buf.v[r].x);
-                const uint2 hi = fp8x4_to<S>(buf.v[r].y);
-                return make_uint4(lo.x, lo.y, hi.x, hi.y);
-            } else {
-                return fp8x4_to<S>(buf.v[r]);
-            }
+            const uint32_t w = reinterpret_cast<const uint32_t*>(&buf.v[r])[q / 2];
+            return (q & 1) ? S::template from_fp8x2<true>(w) : S::template from_fp8x2<false>(w);
         } else {
-            return buf.v[r];
+            return reinterpret_cast<const uint32_t*>(&buf.v[r])[q];
         }
     };
 
@@ -261,15 +256,12 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
         const uint2 pt = make_uint2(S::pack2(pr[0], pr[1]), S::pack2(pr[2], pr[3]));
         // V^T operand of element e: (tok 4c, 4c+1 | 4c+2, 4c+3) at element EPL*n + e;
         // rows past the valid tokens were loaded as zeros
-        VRow vr[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vr[r] = v_row(buf, r);
 #pragma unroll
         for (int q = 0; q < EPL / 2; ++q) {
-            const uint32_t w0 = reinterpret_cast<const uint32_t*>(&vr[0])[q];
-            const uint32_t w1 = reinterpret_cast<const uint32_t*>(&vr[1])[q];
-            const uint32_t w2 = reinterpret_cast<const uint32_t*>(&vr[2])[q];
-            const uint32_t w3 = reinterpret_cast<const uint32_t*>(&vr[3])[q];
+            const uint32_t w0 = v_word(buf, 0, q);
+            const uint32_t w1 = v_word(buf, 1, q);
+            const uint32_t w2 = v_word(buf, 2, q);
+            const uint32_t w3 = v_word(buf, 3, q);
             const uint2 even = make_uint2(lo_halves(w0, w1), lo_halves(w2, w3));
             const uint2 odd = make_uint2(hi_halves(w0, w1), hi_halves(w2, w3));
             acc[2 * q] = S::mfma_k16(even, pt, acc[2 * q]);
