@@ -41,7 +41,8 @@ __all__ = [
     "kv_pool_bytes", "block_bytes", "locate",
     "physical_address", "scatter", "copy_blocks", "gather", "attention_contiguous", "softmax_weights",
     "paged_decode", "paged_decode_seq", "online_decode_seq", "partition_partials",
-    "combine_partials", "partitioned_decode_seq", "brute_force_seq",
+    "combine_partials", "partitioned_decode_seq", "brute_force_seq", "paged_prefill_seq",
+    "paged_prefill", "prefill_flops",
 ]
 
 
@@ -353,3 +354,59 @@ def brute_force_seq(q, keys, values, scale):
             row.append(math.fsum(ex[t] * values[t][kv][i] for t in range(len(keys))) / z)
         out.append(row)
     return out
+
+
+# ---------------------------------------------------------------- multi-token queries (prefill)
+
+def paged_prefill_seq(q_bits, k_pool_bits, v_pool_bits, table, length, scale, block_size, dtype,
+                      q_dtype=None):
+    """The n = len(q_bits) newest tokens of one sequence attend over the sequence's paged
+    K/V, causally: token i sits at position p = length - n + i and its query heads see
+    positions [0, p] only.  Their own keys and values are already in the pool.
+
+    A prompt (or a chunk of one) processed in parallel, as "PagedAttention: Treating KV
+    Memory Like Virtual Memory" ("Prefill is the other shape of the request": chunks of
+    a prompt cut to the step's token budget) and "PagedAttention and Virtual Memory
+    Management" (prefill processes the prompt in parallel) describe it; each row is
+    the attention of P2 "Reading through the table" over the first p + 1 positions.
+    Tokens with p < 0 (more queries than the length holds) get zero output.
+    q_bits: [n, Hq, d].  Returns fp64 [n, Hq, d].
+    """
+    n = len(q_bits)
+    qf = to_f64(q_bits, q_dtype or dtype)
+    kc = to_f64(gather(k_pool_bits, table, length, block_size), dtype)
+    vc = to_f64(gather(v_pool_bits, table, length, block_size), dtype)
+    out = np.zeros(qf.shape, dtype=np.float64)
+    for i in range(n):
+        p = int(length) - n + i
+        if p >= 0:
+            out[i] = attention_contiguous(qf[i], kc[:p + 1], vc[:p + 1], scale)
+    return out
+
+
+def paged_prefill(query_bits, query_start, k_pool_bits, v_pool_bits, block_tables, lengths, scale,
+                  block_size, dtype, q_dtype=None, seqs=None) -> np.ndarray:
+    """A batch of chunks: sequence b's queries are rows [query_start[b], query_start[b+1])
+    of ``query_bits`` ([T, Hq, d]).  Returns fp64 [T, Hq, d] (rows of skipped sequences
+    are zero)."""
+    out = np.zeros(np.asarray(query_bits).shape, dtype=np.float64)
+    idx = range(len(lengths)) if seqs is None else seqs
+    for b in idx:
+        a, e = int(query_start[b]), int(query_start[b + 1])
+        if e > a:
+            out[a:e] = paged_prefill_seq(query_bits[a:e], k_pool_bits, v_pool_bits, block_tables[b],
+                                         int(lengths[b]), scale, block_size, dtype, q_dtype)
+    return out
+
+
+def prefill_flops(query_lens, lengths, num_q_heads, head_dim) -> int:
+    """Multiply-adds x 2 of the causal attention above: a query at position p costs
+    (p + 1) * d for q.K and as many for P.V, per query head."""
+    total = 0
+    for n, L in zip(query_lens, lengths):
+        n, L = int(n), int(L)
+        first = max(0, L - n)                   # position of the first query (clamped)
+        # sum over p in [first, L) of (p + 1)
+        total += (L * (L + 1) - first * (first + 1)) // 2
+    return 4 * total * num_q_heads * head_dim
+
