@@ -291,6 +291,33 @@ kv_status_t kv_bm_ref_count(const kv_block_manager_t* bm, int32_t block, int32_t
 kv_status_t kv_bm_free_list(const kv_block_manager_t* bm, int32_t* blocks, int32_t cap,
                             int32_t* num);
 
+/* Multi-token (prefill / chunked-prefill) attention for one layer: each sequence has a
+ * chunk of new tokens whose keys and values are already in the pool (reshape_and_cache),
+ * and each of them attends causally over the sequence's paged keys and values
+ * ("PagedAttention: Treating KV Memory Like Virtual Memory", "Prefill is the other shape
+ * of the request": a prompt processed in parallel, cut into chunks to a step's token
+ * budget; "PagedAttention and Virtual Memory Management": the prefill phase processes the
+ * prompt in parallel).
+ *  query, out   : [T][num_q_heads][head_dim], io dtype; the chunks of all sequences packed
+ *                 one after another.
+ *  query_start  : [batch + 1] int32 device, non-decreasing, query_start[0] = 0: sequence
+ *                 b's queries are rows [query_start[b], query_start[b+1]), n_b of them.
+ *  max_query_len: an upper bound on every n_b (host value; sizes the launch).  Queries
+ *                 past it are not computed.
+ *  context_lens : [batch] int32, length L_b including the chunk: query i of sequence b is
+ *                 at position p = L_b - n_b + i and reads positions [0, p].  A query with
+ *                 p < 0 gets a zero output.
+ *  block_tables, max_blocks_per_seq, num_q_heads, scale: as for paged_attention_decode.
+ * Arithmetic as in decode (fp32 scores, softmax and accumulation; the output rounded to
+ * the io dtype).  No workspace.  Errors: KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED (group
+ * size), KV_ERR_HIP.  batch == 0 or max_query_len == 0 is a no-op. */
+kv_status_t paged_attention_prefill(const kv_pool_t* pool, int32_t layer, void* out,
+                                    const void* query, const int32_t* query_start,
+                                    int32_t max_query_len, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                    int32_t batch, int32_t num_q_heads, float scale,
+                                    hipStream_t stream);
+
 /* Test hook: copy each sequence's K and V, through its block table, into contiguous
  * buffers ("Why AI servers waste memory, and how paging fixes it", "Reading through
  * the table").  k_out, v_out: [batch][max_blocks_per_seq * B][num_kv_heads][head_dim]

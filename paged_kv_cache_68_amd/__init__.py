@@ -22,7 +22,7 @@ __all__ = [
     "KVPool", "kv_pool_bytes", "kv_bytes_per_token", "reshape_and_cache",
     "paged_attention_workspace_bytes", "paged_attention_decode", "paged_attention_partitions",
     "paged_attention_reduce", "kv_pool_gather", "make_desc", "PagedKVError",
-    "BlockManager", "OutOfBlocks", "copy_blocks",
+    "BlockManager", "OutOfBlocks", "copy_blocks", "paged_attention_prefill",
 ]
 
 BLOCK_SIZE = 16
@@ -217,6 +217,20 @@ def paged_attention_reduce(pool, layer, out, query, block_tables, context_lens, 
                            partition_size=0, workspace=None, stream=None):
     _decode_call("paged_attention_reduce", pool, layer, out, query, block_tables, context_lens,
                  scale, partition_size, workspace, stream)
+
+
+def paged_attention_prefill(pool: KVPool, layer: int, out, query, query_start, max_query_len,
+                            block_tables, context_lens, scale=None, stream=None) -> None:
+    """Causal attention of each sequence's chunk of new tokens (rows
+    [query_start[b], query_start[b+1]) of ``query``) over its paged K/V."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(pool.head_dim)
+    batch = int(context_lens.shape[0])
+    check(lib().paged_attention_prefill(pool.handle, int(layer), _ptr(out), _ptr(query),
+                                        _ptr(query_start), int(max_query_len), _ptr(block_tables),
+                                        int(block_tables.shape[1]), _ptr(context_lens), batch,
+                                        int(query.shape[1]), float(scale), _stream(stream)),
+          "paged_attention_prefill")
 
 
 def kv_pool_gather(pool: KVPool, layer: int, block_tables, context_lens, k_out, v_out,

@@ -79,6 +79,8 @@ SIGNATURES = {
     "paged_attention_reduce": (_i32, _DECODE_ARGS),
     "kv_pool_gather": (_i32, [_pool, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
     "kv_copy_blocks": (_i32, [_pool, _vp, _i32, _vp]),
+    "paged_attention_prefill": (_i32, [_pool, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32,
+                                       _f32, _vp]),
     "kv_bm_create": (_i32, [_i32, _i32, ctypes.POINTER(_bm)]),
     "kv_bm_destroy": (_i32, [_bm]),
     "kv_bm_add_request": (_i32, [_bm, _i64]),

@@ -348,6 +348,47 @@ kv_status_t paged_attention_partitions(const kv_pool_t* pool, int32_t layer, voi
                        workspace_bytes, stream);
 }
 
+kv_status_t paged_attention_prefill(const kv_pool_t* pool, int32_t layer, void* out,
+                                    const void* query, const int32_t* query_start,
+                                    int32_t max_query_len, const int32_t* block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                    int32_t batch, int32_t num_q_heads, float scale,
+                                    hipStream_t stream) {
+    if (!pool) return KV_ERR_INVALID_ARG;
+    const kv_pool_desc_t& d = pool->desc;
+    if (layer < 0 || layer >= d.num_layers || batch < 0 || max_query_len < 0 || num_q_heads < 1)
+        return KV_ERR_INVALID_ARG;
+    if (num_q_heads % d.num_kv_heads != 0) return KV_ERR_UNSUPPORTED;
+    const int32_t group = num_q_heads / d.num_kv_heads;
+    if (group > pkv::kMaxGroup) return KV_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return KV_ERR_INVALID_ARG;
+    if (batch == 0 || max_query_len == 0) return KV_OK;
+    if (max_blocks_per_seq < 1) return KV_ERR_INVALID_ARG;
+    if (!out || !query || !query_start || !block_tables || !context_lens) return KV_ERR_INVALID_ARG;
+    if (!aligned(out) || !aligned(query) || !aligned(query_start, 4) || !aligned(block_tables, 4) ||
+        !aligned(context_lens, 4))
+        return KV_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(max_blocks_per_seq) * d.block_size > INT32_MAX) return KV_ERR_INVALID_ARG;
+    const int64_t rows = static_cast<int64_t>(max_query_len) * group;
+    const int64_t row_tiles = ceil_div(rows, pkv::prefill_rows_per_group());
+    if (row_tiles > INT32_MAX || static_cast<int64_t>(batch) * d.num_kv_heads * row_tiles > INT32_MAX)
+        return KV_ERR_INVALID_ARG;
+    DecodeShape shape;
+    shape.group = group;
+    shape.part_blocks = 1;
+    shape.num_parts = 1;
+    pkv::PrefillArgs pa;
+    pa.a = make_args(pool, layer, out, query, block_tables, max_blocks_per_seq, context_lens,
+                     batch, num_q_heads, scale, nullptr, shape);
+    pa.a.stream_loads = 0;       // keys are re-read by every row tile of a sequence
+    pa.qstart = query_start;
+    pa.group = group;
+    pa.row_tiles = static_cast<int32_t>(row_tiles);
+    return pkv::launch_prefill(d.dtype, io_dtype(d), d.head_dim, pa, stream) == hipSuccess
+               ? KV_OK
+               : KV_ERR_HIP;
+}
+
 kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* out,
                                    const void* query, const int32_t* block_tables,
                                    int32_t max_blocks_per_seq, const int32_t* context_lens,

@@ -53,6 +53,15 @@ struct DecodeArgs {
     int32_t stream_loads;    // 1: K/V loads carry the non-temporal hint
 };
 
+// Multi-token (prefill) attention: the decode arguments (queries and outputs are
+// [T][Hq][D], packed over the batch) plus where each sequence's queries start.
+struct PrefillArgs {
+    DecodeArgs a;
+    const int32_t* qstart;   // [B + 1]: sequence b's queries are rows [qstart[b], qstart[b+1])
+    int32_t group;           // query heads per KV head
+    int32_t row_tiles;       // work-groups per (sequence, KV head)
+};
+
 // A call that can touch more K/V bytes than this streams them past the last-level cache
 // (256 MB Infinity Cache on MI355X): they could not stay cached until the next step
 // anyway.  Smaller working sets (a few sequences, a shared prefix, a small pool) keep
@@ -73,6 +82,10 @@ int partition_chunk_mfma(int kv_dtype, int io_dtype, int group, int head_dim, co
 // Waves per work-group of the matrix-core kernel's group plan for this batch (0: not used).
 int group_waves_mfma(int kv_dtype, int io_dtype, int group, int head_dim, const DecodeArgs& a);
 hipError_t launch_reduce(int io_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
+// (token, head) rows one prefill work-group covers.
+int prefill_rows_per_group();
+hipError_t launch_prefill(int kv_dtype, int io_dtype, int head_dim, const PrefillArgs& pa,
+                          hipStream_t stream);
 // New tokens' rows ([T][row_elems] in io_dtype) into their slots: a bit copy for a
 // 16-bit pool, E4M3 rounding for an FP8 pool.
 hipError_t launch_reshape_and_cache(const void* key, const void* value, const int64_t* slots,

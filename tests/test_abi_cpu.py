@@ -199,3 +199,29 @@ def test_gather_argument_checks():
     assert lib.kv_pool_gather(h, 0, A, 0, A, 4, A, A, None) == E.KV_ERR_INVALID_ARG
     assert lib.kv_pool_gather(h, 0, A, 3, A, 4, A + 8, A, None) == E.KV_ERR_INVALID_ARG
     lib.kv_pool_destroy(h)
+
+
+def test_prefill_argument_checks():
+    desc, h = _borrowed_pool(layers=2, nb=64, hkv=2, d=64)
+    lib = _lib.lib()
+    E = _lib
+
+    def call(**kw):
+        a = dict(layer=0, out=A, query=A, qs=A, maxq=16, tables=A, max_blocks=3, lens=A, batch=4,
+                 hq=14, scale=0.125)
+        a.update(kw)
+        return lib.paged_attention_prefill(h, a["layer"], a["out"], a["query"], a["qs"], a["maxq"],
+                                           a["tables"], a["max_blocks"], a["lens"], a["batch"],
+                                           a["hq"], a["scale"], None)
+    assert call(batch=0) == E.KV_OK and call(maxq=0) == E.KV_OK          # no-ops
+    assert call(batch=-1) == E.KV_ERR_INVALID_ARG
+    assert call(maxq=-1) == E.KV_ERR_INVALID_ARG
+    assert call(layer=2) == E.KV_ERR_INVALID_ARG
+    assert call(qs=None) == E.KV_ERR_INVALID_ARG
+    assert call(qs=A + 2) == E.KV_ERR_INVALID_ARG
+    assert call(out=A + 8) == E.KV_ERR_INVALID_ARG
+    assert call(hq=15) == E.KV_ERR_UNSUPPORTED
+    assert call(hq=34) == E.KV_ERR_UNSUPPORTED
+    assert call(max_blocks=0) == E.KV_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == E.KV_ERR_INVALID_ARG
+    lib.kv_pool_destroy(h)

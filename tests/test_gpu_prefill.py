@@ -1,0 +1,171 @@
+"""GPU parity of multi-token (prefill / chunked-prefill) paged attention against the
+oracle: packed chunks of several sequences, causal rows over paged K/V, every block size,
+16-bit and FP8 pools, GQA groups 1..16, chunks longer than one work-group, empty chunks
+and chunks with more queries than positions."""
+
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import paged_kv_cache_68_amd as pk  # noqa: E402
+from workloads import nan_bits, round_to_bits  # noqa: E402
+
+from .gpu_helpers import TOL, max_abs_err, to_dev, to_host_bits  # noqa: E402
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+# Bits of the significand rounding of each io type: a round-to-nearest result is within
+# 2^-s of the exact value, relatively.
+SIG = {"bf16": 8, "f16": 11}
+
+
+def _check(got_bits, ref, qs, tables, lens, vp, B, kv, io, hkv):
+    """|got - ref| <= TOL + 2^-s (|ref| + max |v| over the row's keys), per element.
+
+    The decode tolerance TOL covers outputs that average many tokens.  A prefill row near
+    the start of a sequence averages a handful of values and can be as large as they are;
+    rounding the output to the io type costs up to 2^-s |o|, and rounding the softmax
+    weights to the io type for the matrix-core product costs up to 2^-s sum_t w_t |v_t|
+    <= 2^-s max_t |v_t|."""
+    got = oracle.to_f64(got_bits, io)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    hq = got.shape[1]
+    g = hq // hkv
+    bound = np.full(got.shape, TOL[io])
+    for b in range(len(lens)):
+        a, e = int(qs[b]), int(qs[b + 1])
+        L = int(lens[b])
+        if e == a or L == 0:
+            continue
+        vc = np.abs(oracle.to_f64(oracle.gather(vp, tables[b], L, B), kv)).max(axis=2)   # [L, Hkv]
+        run = np.maximum.accumulate(vc, axis=0)
+        for i in range(e - a):
+            pos = L - (e - a) + i
+            if pos >= 0:
+                vm = np.repeat(run[pos], g)                                           # [Hq]
+                bound[a + i] = TOL[io] + 2.0 ** -SIG[io] * (np.abs(ref[a + i]) + vm[:, None])
+    err = np.abs(got - ref)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), (worst, float(err[worst]), float(bound[worst]))
+
+
+def _case(chunks, B, hq, hkv, d, io, kv, seed):
+    """chunks: list of (n, L).  Scattered pool (NaN in unused slots), packed queries."""
+    rng = np.random.default_rng(seed)
+    lens = np.array([L for _, L in chunks], dtype=np.int32)
+    ns = [n for n, _ in chunks]
+    qs = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    need = int(sum(-(-int(L) // B) for L in lens))
+    nb = need + 8
+    perm = rng.permutation(nb)
+    W = max(1, max(-(-int(L) // B) for L in lens))
+    tables = np.full((len(lens), W), -1, dtype=np.int32)
+    pos = 0
+    for b, L in enumerate(lens):
+        m = -(-int(L) // B)
+        tables[b, :m] = perm[pos:pos + m]
+        pos += m
+    store = np.uint8 if kv == "fp8" else np.uint16
+    kp = np.full((nb, B, hkv, d), nan_bits(kv), dtype=store)
+    vp = np.full((nb, B, hkv, d), nan_bits(kv), dtype=store)
+    used = perm[:need]
+    if kv == "fp8":
+        for p_ in (kp, vp):
+            mag = rng.integers(0x20, 0x41, (need, B, hkv, d), dtype=np.uint8)
+            p_[used] = mag | (rng.integers(0, 2, (need, B, hkv, d), dtype=np.uint8) << 7)
+    else:
+        kp[used] = round_to_bits(rng.standard_normal((need, B, hkv, d), dtype=np.float32), kv)
+        vp[used] = round_to_bits(rng.standard_normal((need, B, hkv, d), dtype=np.float32), kv)
+    # stale slots past each length stay NaN
+    for b, L in enumerate(lens):
+        if L % B:
+            kp[tables[b, L // B], L % B:] = nan_bits(kv)
+            vp[tables[b, L // B], L % B:] = nan_bits(kv)
+    q = round_to_bits(rng.standard_normal((int(qs[-1]), hq, d), dtype=np.float32), io)
+    return lens, qs, tables, kp, vp, q, nb
+
+
+def _run(B, lens, qs, tables, kp, vp, q, nb, hkv, d, io, kv):
+    pool = pk.KVPool(1, nb, hkv, d, kv, block_size=B, io_dtype=io)
+    pool.k_cache(0).copy_(to_dev(kp, kv))
+    pool.v_cache(0).copy_(to_dev(vp, kv))
+    qd = to_dev(q, io)
+    out = torch.full_like(qd, 7.0)
+    maxq = int(np.max(np.diff(qs))) if len(qs) > 1 else 0
+    pk.paged_attention_prefill(pool, 0, out, qd, torch.from_numpy(qs).cuda(), maxq,
+                               torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                               scale=1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    return to_host_bits(out)
+
+
+CHUNKS = [(1, 1), (1, 100), (17, 17), (40, 100), (200, 700), (513, 513), (64, 2000), (0, 50),
+          (5, 3), (33, 33)]
+
+
+@pytest.mark.parametrize("B", [16, 8, 32])
+@pytest.mark.parametrize("hq,hkv,d,io,kv", [
+    (32, 8, 128, "bf16", "bf16"), (14, 2, 64, "f16", "f16"), (8, 8, 128, "f16", "f16"),
+    (32, 2, 128, "bf16", "bf16"), (32, 8, 128, "bf16", "fp8"), (14, 2, 64, "f16", "fp8"),
+])
+def test_prefill_matches_oracle(B, hq, hkv, d, io, kv):
+    _say(f"prefill B={B} hq={hq} hkv={hkv} d={d} io={io} kv={kv}")
+    lens, qs, tables, kp, vp, q, nb = _case(CHUNKS, B, hq, hkv, d, io, kv, seed=100 + B)
+    got = _run(B, lens, qs, tables, kp, vp, q, nb, hkv, d, io, kv)
+    ref = oracle.paged_prefill(q, qs, kp, vp, tables, lens, 1.0 / math.sqrt(d), B, kv, q_dtype=io)
+    _check(got, ref, qs, tables, lens, vp, B, kv, io, hkv)
+    # the (5, 3) chunk: its first two queries sit before position 0 -> zeros
+    a = int(qs[8])
+    assert not got[a:a + 2].any()
+
+
+def test_whole_prompt_of_the_measured_prefix():
+    """One 2,407-token prompt (151 blocks) prefilled in one chunk, Qwen2.5-0.5B heads."""
+    lens, qs, tables, kp, vp, q, nb = _case([(2407, 2407)], 16, 14, 2, 64, "f16", "f16", seed=7)
+    got = _run(16, lens, qs, tables, kp, vp, q, nb, 2, 64, "f16", "f16")
+    rows = [0, 1, 15, 16, 500, 1203, 2047, 2406]
+    ref = np.stack([oracle.paged_prefill_seq(q[:r + 1][-1:], kp, vp, tables[0], r + 1, 1 / 8.0, 16, "f16")[0]
+                    for r in rows])
+    sub_qs = np.arange(len(rows) + 1)
+    _check(got[rows], ref, sub_qs, np.repeat(tables, len(rows), axis=0), np.array(rows) + 1,
+           vp, 16, "f16", "f16", 2)
+
+
+def test_deterministic_and_independent_of_block_placement():
+    chunks = [(300, 900), (77, 77), (128, 3000)]
+    lens, qs, tables, kp, vp, q, nb = _case(chunks, 16, 32, 8, 128, "bf16", "bf16", seed=9)
+    out = _run(16, lens, qs, tables, kp, vp, q, nb, 8, 128, "bf16", "bf16")
+    again = _run(16, lens, qs, tables, kp, vp, q, nb, 8, 128, "bf16", "bf16")
+    assert np.array_equal(out, again)
+    pi = np.random.default_rng(10).permutation(nb)
+    kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+    kp2[pi] = kp
+    vp2[pi] = vp
+    t2 = np.where(tables >= 0, pi[np.maximum(tables, 0)], -1).astype(np.int32)
+    assert np.array_equal(_run(16, lens, qs, t2, kp2, vp2, q, nb, 8, 128, "bf16", "bf16"), out)
+
+
+def test_single_token_chunks_match_decode_within_tolerance():
+    """n = 1 is a decode step: both kernels agree with the oracle (and so with each other)."""
+    chunks = [(1, 5), (1, 700), (1, 4100)]
+    lens, qs, tables, kp, vp, q, nb = _case(chunks, 16, 32, 8, 128, "bf16", "bf16", seed=11)
+    pre = _run(16, lens, qs, tables, kp, vp, q, nb, 8, 128, "bf16", "bf16")
+    pool = pk.KVPool(1, nb, 8, 128, "bf16")
+    pool.k_cache(0).copy_(to_dev(kp, "bf16"))
+    pool.v_cache(0).copy_(to_dev(vp, "bf16"))
+    qd = to_dev(q, "bf16")
+    out = torch.empty_like(qd)
+    pk.paged_attention_decode(pool, 0, out, qd, torch.from_numpy(tables).cuda(),
+                              torch.from_numpy(lens).cuda(), scale=1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    dec = oracle.to_f64(to_host_bits(out), "bf16")
+    assert np.max(np.abs(oracle.to_f64(pre, "bf16") - dec)) <= 2 * TOL["bf16"]
