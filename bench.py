@@ -198,6 +198,103 @@ def bench_cow(args, name):
     return 0
 
 
+# Multi-token (prefill) attention workloads: chunks of new tokens attending causally over
+# their sequences' paged K/V (the keys and values of the chunk already in the pool).
+PREFILL_WORKLOADS = {
+    # one 2,407-token prompt (151 blocks) in one chunk, Qwen2.5-0.5B heads, fp16
+    "qwen05b_prompt_2407": {"hq": 14, "hkv": 2, "d": 64, "dtype": "f16", "chunks": [(2407, 2407)]},
+    # a chunked-prefill step of 8,192 tokens: 4 sequences each computing positions
+    # 6,144 .. 8,191 of an 8,192-token prompt, Llama-3-8B heads, bf16
+    "llama3_8b_chunked_prefill_4x2048_ctx8192": {"hq": 32, "hkv": 8, "d": 128, "dtype": "bf16",
+                                                 "chunks": [(2048, 8192)] * 4},
+}
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}     # MI355X dense matrix-core peak
+
+
+def bench_prefill(args, name):
+    import torch
+    import oracle
+    import paged_kv_cache_68_amd as pk
+
+    w = PREFILL_WORKLOADS[name]
+    hq, hkv, d, dt = w["hq"], w["hkv"], w["d"], w["dtype"]
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    ns = [n for n, _ in w["chunks"]]
+    lens = np.array([L for _, L in w["chunks"]], dtype=np.int32)
+    qs = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    nblk = [-(-int(L) // 16) for L in lens]
+    nb = sum(nblk) + 64
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = np.full((len(lens), max(nblk)), -1, dtype=np.int32)
+    pos = 0
+    for b, m in enumerate(nblk):
+        tables[b, :m] = perm[pos:pos + m]
+        pos += m
+    pool = pk.KVPool(1, nb, hkv, d, dt)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    for c in (pool.k_cache(0), pool.v_cache(0)):
+        c.copy_(torch.randn(c.shape, generator=gen, device="cuda", dtype=torch.float32).to(tdt))
+    q = torch.randn((int(qs[-1]), hq, d), generator=gen, device="cuda", dtype=torch.float32).to(tdt)
+    out = torch.empty_like(q)
+    qs_d = torch.from_numpy(qs).cuda()
+    tab_d = torch.from_numpy(tables).cuda()
+    lens_d = torch.from_numpy(lens).cuda()
+    maxq = max(ns)
+    stream = torch.cuda.current_stream()
+    scale = 1.0 / math.sqrt(d)
+    run = lambda: pk.paged_attention_prefill(pool, 0, out, q, qs_d, maxq, tab_d, lens_d, scale, stream)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev_a[i].record(stream)
+        run()
+        ev_b[i].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
+    flops = oracle.prefill_flops(ns, lens, hq, d)
+    tflops = flops / (k_ms * 1e-3) / 1e12
+    tokens = int(qs[-1])
+    result = {
+        "metric": "paged prefill attention: query tokens/s and achieved TFLOP/s (% of MI355X dense matrix-core peak)",
+        "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": name, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "block_size": 16,
+                   "chunks": [list(c) for c in w["chunks"]], "query_tokens": tokens},
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill_mfma", "achieved": tflops,
+                     "peak": PEAK_MFMA_TFLOPS[dt], "unit": "TFLOP/s", "frac": tflops / PEAK_MFMA_TFLOPS[dt],
+                     "traffic": None, "algorithmic_flops_per_launch": flops, "avg_launch_us": k_ms * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on the last 8 query rows of the first sequence (the costliest ones)
+        from tests.device_case import to_host_bits
+        kb = to_host_bits(pool.k_cache(0))
+        vb = to_host_bits(pool.v_cache(0))
+        qb = to_host_bits(q)
+        n0, L0 = w["chunks"][0]
+        rows = 8
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            ref = oracle.paged_prefill_seq(qb[n0 - rows:n0], kb, vb, tables[0], L0, scale, 16, dt)
+            t_cpu = time.perf_counter() - t0
+        got = oracle.to_f64(to_host_bits(out)[n0 - rows:n0], dt)
+        result["cpu_baseline"] = {"value": rows / t_cpu, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"the last {rows} query rows of sequence 0 ({t_cpu:.1f} s)",
+                                  "max_abs_err_vs_gpu": float(np.max(np.abs(got - ref)))}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +306,8 @@ def main(argv=None):
                          "keeps the same number of token slots")
     ap.add_argument("--kv-dtype", choices=["fp8"], default=None,
                     help="store keys and values as FP8 (E4M3) instead of the workload's type")
+    ap.add_argument("--prefill", choices=sorted(PREFILL_WORKLOADS),
+                    help="time multi-token (prefill) attention on this workload instead")
     ap.add_argument("--cow", choices=sorted(COW_WORKLOADS),
                     help="time the copy-on-write block copy on this workload instead")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
@@ -251,6 +350,8 @@ def main(argv=None):
 
     if args.cow:
         return bench_cow(args, args.cow)
+    if args.prefill:
+        return bench_prefill(args, args.prefill)
 
     cfg = config_by_name(args.config)
     if args.block_size and args.block_size != cfg.block_size:
