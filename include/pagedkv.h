@@ -318,6 +318,63 @@ kv_status_t paged_attention_prefill(const kv_pool_t* pool, int32_t layer, void* 
                                     int32_t batch, int32_t num_q_heads, float scale,
                                     hipStream_t stream);
 
+/* ------------------------------------------------------------------ prefix cache
+ * Host-side automatic prefix caching on a block pool: which physical blocks a new request
+ * can reuse because an earlier one computed the same prefix ("PagedAttention: Treating
+ * KV Memory Like Virtual Memory", "A separate mechanism: automatic prefix caching"; "2.1
+ * PagedAttention", section 9, BlockPool / KVCacheManager).
+ *  - A block is hashed when it fills: 64-bit FNV-1a over the little-endian bytes of the
+ *    previous block's hash (0 before the first block), the block's token ids (int32) and,
+ *    for a request's first block only, the request's 64-bit salt.  The hashes form a
+ *    chain, so a hit means agreement from the first token; a match ends on a block
+ *    boundary.  A block whose hash is already cached (the same prefix in another block)
+ *    stays uncached.
+ *  - A hit copies nothing: the block's count rises, and a free cached block leaves the
+ *    free queue.  Finishing lowers the counts of the request's blocks, last block first;
+ *    blocks that reach zero return to the free queue with their hash, hash-less ones at
+ *    the head (reused first, in that order) and cached ones at the tail (evicted last).
+ *    Taking a cached free block for new data evicts its hash.
+ *  - Every call checks everything before changing anything.  Host memory only; not
+ *    thread-safe.  Shared blocks are full, so nothing is ever written into a shared
+ *    block and no copy-on-write copy is needed. */
+typedef struct kv_prefix_cache kv_prefix_cache_t;
+
+/* num_blocks blocks of block_size token slots; the free queue starts as 0 .. n-1. */
+kv_status_t kv_pc_create(int32_t num_blocks, int32_t block_size, kv_prefix_cache_t** out);
+kv_status_t kv_pc_destroy(kv_prefix_cache_t* pc);
+
+/* Start request rid with prompt[0..n): the leading full blocks of the prompt found in the
+ * cache become its first blocks; *found_tokens is their token count (a multiple of
+ * block_size).  The rest of the prompt is added with kv_pc_append.  KV_ERR_INVALID_ARG if
+ * rid exists. */
+kv_status_t kv_pc_add_request(kv_prefix_cache_t* pc, int64_t rid, const int32_t* prompt,
+                              int32_t n, uint64_t salt, int32_t* found_tokens);
+
+/* Slots (block * block_size + offset) for the request's next n tokens, whose ids are
+ * tokens[0..n); blocks that fill up are hashed and cached.  KV_ERR_OUT_OF_BLOCKS if the
+ * free queue cannot cover them (nothing changed). */
+kv_status_t kv_pc_append(kv_prefix_cache_t* pc, int64_t rid, const int32_t* tokens, int32_t n,
+                         int64_t* slots, int64_t slots_cap);
+kv_status_t kv_pc_free_request(kv_prefix_cache_t* pc, int64_t rid);
+
+/* Views. */
+kv_status_t kv_pc_get_length(const kv_prefix_cache_t* pc, int64_t rid, int32_t* length);
+kv_status_t kv_pc_get_table(const kv_prefix_cache_t* pc, int64_t rid, int32_t* table, int32_t cap,
+                            int32_t* num);
+/* Tables ([n][max_blocks], -1 padded) and lengths of rids, as paged_attention_* read them. */
+kv_status_t kv_pc_export(const kv_prefix_cache_t* pc, const int64_t* rids, int32_t n,
+                         int32_t max_blocks, int32_t* tables, int32_t* lengths);
+int32_t kv_pc_num_free(const kv_prefix_cache_t* pc);
+int32_t kv_pc_num_cached(const kv_prefix_cache_t* pc);
+/* The free queue, head first. */
+kv_status_t kv_pc_free_queue(const kv_prefix_cache_t* pc, int32_t* blocks, int32_t cap, int32_t* num);
+/* Count, cached flag and hash (0 if uncached) of a block; outputs may be NULL. */
+kv_status_t kv_pc_block_info(const kv_prefix_cache_t* pc, int32_t block, int32_t* ref_count,
+                             int32_t* is_cached, uint64_t* hash);
+/* The chain hash of one block (first != 0: the request's first block, salt mixed in). */
+uint64_t kv_pc_hash_block(uint64_t prev, const int32_t* tokens, int32_t n, int32_t first,
+                          uint64_t salt);
+
 /* Test hook: copy each sequence's K and V, through its block table, into contiguous
  * buffers ("Why AI servers waste memory, and how paging fixes it", "Reading through
  * the table").  k_out, v_out: [batch][max_blocks_per_seq * B][num_kv_heads][head_dim]

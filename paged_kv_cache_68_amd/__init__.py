@@ -22,7 +22,8 @@ __all__ = [
     "KVPool", "kv_pool_bytes", "kv_bytes_per_token", "reshape_and_cache",
     "paged_attention_workspace_bytes", "paged_attention_decode", "paged_attention_partitions",
     "paged_attention_reduce", "kv_pool_gather", "make_desc", "PagedKVError",
-    "BlockManager", "OutOfBlocks", "copy_blocks", "paged_attention_prefill",
+    "BlockManager", "OutOfBlocks", "copy_blocks", "paged_attention_prefill", "PrefixCache",
+    "hash_block",
 ]
 
 BLOCK_SIZE = 16
@@ -243,3 +244,4 @@ def kv_pool_gather(pool: KVPool, layer: int, block_tables, context_lens, k_out, 
 
 
 from .block_manager import BlockManager, OutOfBlocks, copy_blocks  # noqa: E402
+from .prefix_cache import PrefixCache, hash_block  # noqa: E402

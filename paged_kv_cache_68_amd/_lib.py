@@ -93,6 +93,19 @@ SIGNATURES = {
     "kv_bm_num_free": (_i32, [_bm]),
     "kv_bm_ref_count": (_i32, [_bm, _i32, _pi32]),
     "kv_bm_free_list": (_i32, [_bm, _vp, _i32, _pi32]),
+    "kv_pc_create": (_i32, [_i32, _i32, ctypes.POINTER(_bm)]),
+    "kv_pc_destroy": (_i32, [_bm]),
+    "kv_pc_add_request": (_i32, [_bm, _i64, _vp, _i32, ctypes.c_uint64, _pi32]),
+    "kv_pc_append": (_i32, [_bm, _i64, _vp, _i32, _vp, _i64]),
+    "kv_pc_free_request": (_i32, [_bm, _i64]),
+    "kv_pc_get_length": (_i32, [_bm, _i64, _pi32]),
+    "kv_pc_get_table": (_i32, [_bm, _i64, _vp, _i32, _pi32]),
+    "kv_pc_export": (_i32, [_bm, _vp, _i32, _i32, _vp, _vp]),
+    "kv_pc_num_free": (_i32, [_bm]),
+    "kv_pc_num_cached": (_i32, [_bm]),
+    "kv_pc_free_queue": (_i32, [_bm, _vp, _i32, _pi32]),
+    "kv_pc_block_info": (_i32, [_bm, _i32, _pi32, _pi32, ctypes.POINTER(ctypes.c_uint64)]),
+    "kv_pc_hash_block": (ctypes.c_uint64, [ctypes.c_uint64, _vp, _i32, _i32, ctypes.c_uint64]),
 }
 
 
