@@ -7,4 +7,4 @@ product path.
 """
 
 from .oracle import *  # noqa: F401,F403
-from .block_manager import BlockManager, OutOfBlocks  # noqa: F401
+from .block_manager import BlockManager, OutOfBlocks, move_requests  # noqa: F401

@@ -31,6 +31,23 @@ Readings (listed in DESIGN.md as well):
   it was before the batch (the pages' check-before-mutate rule, applied to the batch).
 * Free walks the request's table front to back (P2 "The real implementation"),
   so blocks freed together join the free list in table order (P2's example, step 7).
+
+Swap (``move_requests``), from [P3] section 6 (swapping policy: a second pool of
+blocks in host memory; the victim's blocks are copied there, the freed GPU blocks go
+back to the active pool, and on resume the blocks are copied back and decoding goes
+on where it stopped) and [P4] "2.1 PagedAttention" (preemption: swap moves the cache
+to CPU memory and back instead of recomputing it).  Readings:
+* The host pool is a second manager of the same kind; a swap moves a set of requests
+  from one manager to the other (out: device to host; in: host to device).
+* Every distinct block the moved tables name gets one new block in the destination,
+  taken from its free list in first-seen order (requests in the order given, each
+  table front to back); a block the moved requests share stays shared there, with
+  the same count.  The (src, dst) pairs are the copies to make.
+* The source then drops the moved requests as ``free`` does, request after request,
+  table front to back.  A block still named by a request that stays behind keeps
+  its contents and its remaining references; its copy goes along anyway.
+* All or nothing: unknown or repeated ids, or an id the destination already has,
+  change nothing; so does a destination free list shorter than the distinct blocks.
 """
 
 from __future__ import annotations
@@ -38,7 +55,7 @@ from __future__ import annotations
 import copy as _copy
 from collections import deque
 
-__all__ = ["OutOfBlocks", "BlockManager"]
+__all__ = ["OutOfBlocks", "BlockManager", "move_requests"]
 
 
 class OutOfBlocks(Exception):
@@ -180,3 +197,35 @@ class BlockManager:
         for block in range(self.num_blocks):
             in_free = block in free_set
             assert in_free == (counts[block] == 0), f"block {block} lost or double-booked"
+
+
+def move_requests(src: BlockManager, dst: BlockManager, rids):
+    """Move requests from ``src`` to ``dst`` (swap out or in).  Returns the block
+    copies [(src block, dst block), ...] to make; raises OutOfBlocks (nothing changed)
+    if ``dst`` has too few free blocks, KeyError for a bad id."""
+    rids = list(rids)
+    if len(set(rids)) != len(rids):
+        raise KeyError("a request id is repeated")
+    for rid in rids:
+        if rid not in src.tables:
+            raise KeyError(f"unknown request {rid!r}")
+        if rid in dst.tables:
+            raise KeyError(f"request {rid!r} exists in the destination")
+    if src.block_size != dst.block_size:
+        raise ValueError("block sizes differ")
+    order = []                                   # distinct source blocks, first seen first
+    for rid in rids:
+        for block in src.tables[rid]:
+            if block not in order:
+                order.append(block)
+    if len(order) > dst.num_free():
+        raise OutOfBlocks(rids)
+    new = {block: dst.free_list.popleft() for block in order}
+    for rid in rids:
+        dst.tables[rid] = [new[b] for b in src.tables[rid]]
+        dst.lengths[rid] = src.lengths[rid]
+        for b in dst.tables[rid]:
+            dst.ref_count[b] += 1
+    for rid in rids:
+        src.free(rid)
+    return [(b, new[b]) for b in order]

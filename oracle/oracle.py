@@ -39,7 +39,7 @@ import numpy as np
 __all__ = [
     "to_f64", "fp8_to_f64", "encode_fp8", "quantize_fp8", "FP8_MAX", "kv_bytes_per_token",
     "kv_pool_bytes", "block_bytes", "locate",
-    "physical_address", "scatter", "copy_blocks", "gather", "attention_contiguous", "softmax_weights",
+    "physical_address", "scatter", "copy_blocks", "swap_blocks", "gather", "attention_contiguous", "softmax_weights",
     "paged_decode", "paged_decode_seq", "online_decode_seq", "partition_partials",
     "combine_partials", "partitioned_decode_seq", "brute_force_seq", "paged_prefill_seq",
     "paged_prefill", "prefill_flops",
@@ -174,6 +174,18 @@ def copy_blocks(pool: np.ndarray, copies) -> None:
     """
     for src, dst, rows in copies:
         pool[int(dst), :int(rows)] = pool[int(src), :int(rows)]
+
+
+def swap_blocks(src_pool: np.ndarray, dst_pool: np.ndarray, pairs) -> None:
+    """Swap copies between two pools of the same block shape (device and host), in
+    place: for each (src, dst), every token row of block src of ``src_pool`` is copied
+    into block dst of ``dst_pool``   [P3 section 6, swapping: the victim's physical
+    blocks go to a block pool in host memory, and come back the same way].  ``src_pool``
+    and ``dst_pool`` are one K or V cache each, block index first.  A pure copy of the
+    stored bits, pairs applied in order.
+    """
+    for src, dst in pairs:
+        dst_pool[int(dst)] = src_pool[int(src)]
 
 
 def gather(pool: np.ndarray, table, length: int, block_size: int) -> np.ndarray:
