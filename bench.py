@@ -55,10 +55,15 @@ def algorithmic_bytes(lens, hq, hkv, d, kv_elem, io_elem=2, block_size=16):
             "step": kv + table + nlen + q + o + write}
 
 
+# the sources that decide the decode partition kernel's code and launch shape
+DECODE_SOURCES = ("api.cpp", "device_common.h", "internal.h", "paged_decode.hip",
+                  "paged_decode_mfma.hip", "partition_common.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_68_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in DECODE_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -198,6 +203,122 @@ def bench_cow(args, name):
     return 0
 
 
+# Swap workloads (kv_swap_blocks): preempting one request by copying its blocks to a pool
+# in pinned host memory and back, Llama-3-8B pool geometry over all 32 layers (8 KV heads
+# x 128, bf16: 32 KiB per block per layer for K and for V).  The victim's device blocks
+# are scattered over the pool, as an allocation history leaves them; its host blocks are
+# the front of a fresh host free list.
+SWAP_WORKLOADS = {
+    # one 8,192-token request: 512 blocks, 1 GiB each way
+    "llama3_8b_swap_8192_tokens": {"layers": 32, "dev_blocks": 4096, "host_blocks": 1024,
+                                   "tokens": 8192},
+    # a 2,407-token request: 151 blocks, 302 MiB each way
+    "llama3_8b_swap_2407_tokens": {"layers": 32, "dev_blocks": 4096, "host_blocks": 1024,
+                                   "tokens": 2407},
+}
+PEAK_HOST_LINK_GBPS = 64.0     # PCIe 5.0 x16, one direction (MI355X host interface)
+
+
+def bench_swap(args, name):
+    import torch
+    import paged_kv_cache_68_amd as pk
+
+    w = SWAP_WORKLOADS[name]
+    hkv, d, B = 8, 128, 16
+    dev = pk.KVPool(w["layers"], w["dev_blocks"], hkv, d, "bf16")
+    host = pk.KVPool(w["layers"], w["host_blocks"], hkv, d, "bf16", host=True)
+    dev.memory.view(torch.int16).random_(-30000, 30000)
+    # the block managers' moves give the pairs: the victim's table is a scattered set
+    dev_m, host_m = pk.BlockManager(w["dev_blocks"], B), pk.BlockManager(w["host_blocks"], B)
+    rng = np.random.default_rng(5)
+    filler = int(rng.integers(w["dev_blocks"] // 4, w["dev_blocks"] // 2))
+    dev_m.add_request(1)
+    dev_m.append_batch([1], [filler * B])
+    dev_m.add_request(0)
+    for _ in range(w["tokens"]):                      # interleaved growth scatters blocks
+        dev_m.append_batch([0, 1])
+    out_pairs = dev_m.move_to(host_m, [0])
+    in_pairs = host_m.move_to(dev_m, [0])
+    n = int(out_pairs.shape[0])
+    block_bytes = B * hkv * d * 2
+    nbytes = n * block_bytes * 2 * w["layers"]       # one way: each byte crosses the link once
+    out_d = torch.from_numpy(np.ascontiguousarray(out_pairs)).cuda()
+    in_d = torch.from_numpy(np.ascontiguousarray(in_pairs)).cuda()
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pk.swap_blocks(dev, host, out_d, stream)
+        pk.swap_blocks(host, dev, in_d, stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        pk.swap_blocks(dev, host, out_d, stream)
+        ev[i][1].record(stream)
+        pk.swap_blocks(host, dev, in_d, stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    out_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    in_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    out_gbps = nbytes / (out_ms * 1e-3) / 1e9
+    in_gbps = nbytes / (in_ms * 1e-3) / 1e9
+    # the runtime copy (hipMemcpyAsync through torch) of one contiguous stretch of the
+    # same size, for context
+    stretch_dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stretch_host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    for _ in range(2):
+        stretch_host.copy_(stretch_dev, non_blocking=True)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record(stream)
+    stretch_host.copy_(stretch_dev, non_blocking=True)
+    e[1].record(stream)
+    stretch_dev.copy_(stretch_host, non_blocking=True)
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    dma = {"d2h_GBps": nbytes / (e[0].elapsed_time(e[1]) * 1e-3) / 1e9,
+           "h2d_GBps": nbytes / (e[1].elapsed_time(e[2]) * 1e-3) / 1e9}
+    del stretch_dev, stretch_host
+    value = 2 * nbytes / ((out_ms + in_ms) * 1e-3) / 1e9
+    result = {
+        "metric": "swap out + in of one request's blocks (kv_swap_blocks): host-link GB/s, "
+                  "bytes moved each way",
+        "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "blocks": n, "bytes_each_way": nbytes, **w},
+        "swap_out": {"GBps": out_gbps, "avg_launch_us": out_ms * 1e3},
+        "swap_in": {"GBps": in_gbps, "avg_launch_us": in_ms * 1e3},
+        "contiguous_memcpy_same_bytes": dma,
+        "roofline": {"bound": "host-link", "kernel": "swap_copy", "achieved": value,
+                     "peak": PEAK_HOST_LINK_GBPS, "unit": "GB/s",
+                     "frac": value / PEAK_HOST_LINK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": (out_ms + in_ms) / 2 * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        # the oracle's block copies between host arrays of two layers' K and V, scaled
+        src = np.zeros((w["dev_blocks"], B, hkv, d), dtype=np.uint16)
+        dst = np.zeros((w["host_blocks"], B, hkv, d), dtype=np.uint16)
+        pr = [tuple(int(x) for x in p) for p in out_pairs.tolist()]
+        sample_layers = 2
+        t0 = time.perf_counter()
+        for _ in range(2 * sample_layers):
+            oracle.swap_blocks(src, dst, pr)
+        t_cpu = (time.perf_counter() - t0) * w["layers"] / sample_layers
+        result["cpu_baseline"] = {"value": nbytes / t_cpu / 1e9, "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"swap-out copies of {sample_layers} of {w['layers']} "
+                                            "layers (K and V) between host arrays, scaled to all "
+                                            "layers"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 # Multi-token (prefill) attention workloads: chunks of new tokens attending causally over
 # their sequences' paged K/V (the keys and values of the chunk already in the pool).
 PREFILL_WORKLOADS = {
@@ -310,6 +431,8 @@ def main(argv=None):
                     help="time multi-token (prefill) attention on this workload instead")
     ap.add_argument("--cow", choices=sorted(COW_WORKLOADS),
                     help="time the copy-on-write block copy on this workload instead")
+    ap.add_argument("--swap", choices=sorted(SWAP_WORKLOADS),
+                    help="time swap-out and swap-in block copies on this workload instead")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -350,6 +473,8 @@ def main(argv=None):
 
     if args.cow:
         return bench_cow(args, args.cow)
+    if args.swap:
+        return bench_swap(args, args.swap)
     if args.prefill:
         return bench_prefill(args, args.prefill)
 

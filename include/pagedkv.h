@@ -118,6 +118,26 @@ size_t kv_pool_bytes(const kv_pool_desc_t* desc);
 kv_status_t kv_pool_create(const kv_pool_desc_t* desc, void* device_base, size_t base_bytes,
                            kv_pool_t** out);
 
+/* A pool in pinned host memory with the same layout as a device pool: the "auxiliary
+ * physical block pool in CPU host memory" that swapped-out blocks go to ("PagedAttention
+ * and Virtual Memory Management", section 6, swapping policy).  Only kv_swap_blocks,
+ * kv_pool_get_desc, kv_pool_layer_ptrs (host addresses) and kv_pool_destroy accept it;
+ * the attention and cache-write calls return KV_ERR_INVALID_ARG for it.
+ *  host_base == NULL : the library allocates kv_pool_bytes(desc) bytes of pinned,
+ *                      device-mapped host memory (hipHostMalloc) and frees it in
+ *                      kv_pool_destroy.
+ *  host_base != NULL : the caller's pinned host memory (allocated pinned, e.g.
+ *                      hipHostMalloc), borrowed; 256-byte aligned, base_bytes >=
+ *                      kv_pool_bytes(desc); KV_ERR_INVALID_ARG if HIP does not know it
+ *                      as host memory mapped for the current device.
+ * The contents are not initialised. */
+kv_status_t kv_host_pool_create(const kv_pool_desc_t* desc, void* host_base, size_t base_bytes,
+                                kv_pool_t** out);
+
+/* 1 if the pool lives in host memory (kv_host_pool_create), 0 if on the device, -1 for
+ * NULL. */
+int32_t kv_pool_is_host(const kv_pool_t* pool);
+
 /* Destroy a handle; frees the pool memory only if the library allocated it.
  * NULL is accepted and ignored.  The caller must ensure no enqueued work still uses it. */
 kv_status_t kv_pool_destroy(kv_pool_t* pool);
@@ -227,6 +247,24 @@ kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* o
 kv_status_t kv_copy_blocks(kv_pool_t* pool, const int32_t* copies, int32_t num_copies,
                            hipStream_t stream);
 
+/* Swap copies: for every pair (src block, dst block) of pairs[0..num_pairs), all B rows
+ * of block src of every layer's K and V in pool src are copied to block dst of pool dst
+ * ("PagedAttention and Virtual Memory Management", section 6, swapping policy: device
+ * to host on preemption, host to device on resume).  The pools have the same
+ * num_layers, block_size, num_kv_heads, head_dim and dtype (num_blocks may differ); one
+ * or both may be host pools.  Bytes are copied unchanged.
+ *  pairs : [num_pairs][2] int32 in device memory (or pinned host memory), as
+ *          kv_bm_move writes them.  Destination blocks must be distinct; a pair naming a
+ *          block outside its pool is skipped.  src and dst must not be the same pool.
+ * One kernel launch on `stream`, asynchronous: the caller keeps the pairs and both
+ * pools alive until the stream reaches it.  The kernel runs on a fixed number of
+ * work-groups (far fewer than the CUs) so decode kernels on other streams keep the
+ * rest of the chip.
+ * Errors: KV_ERR_INVALID_ARG (null or equal pools, shapes that differ, num_pairs < 0,
+ * null or misaligned pairs), KV_ERR_HIP (launch failed). */
+kv_status_t kv_swap_blocks(const kv_pool_t* src, kv_pool_t* dst, const int32_t* pairs,
+                           int32_t num_pairs, hipStream_t stream);
+
 /* ------------------------------------------------------------------ block manager
  * Host-side bookkeeping that decides where tokens go: a free list of physical blocks,
  * a reference count per block and a block table per request ("Why AI servers waste
@@ -290,6 +328,24 @@ kv_status_t kv_bm_ref_count(const kv_block_manager_t* bm, int32_t block, int32_t
 /* The free list, front first. */
 kv_status_t kv_bm_free_list(const kv_block_manager_t* bm, int32_t* blocks, int32_t cap,
                             int32_t* num);
+
+/* Swap: move requests rids[0..n) from manager src to manager dst -- out to a manager of
+ * host blocks, or back in to the device's ("PagedAttention and Virtual Memory
+ * Management", section 6, swapping policy: the victim's blocks go to a block pool in
+ * host memory, the GPU blocks return to the free list, and on resume they come back).
+ * Every distinct block the moved tables name gets one block of dst, taken from the
+ * front of dst's free list in first-seen order (requests in the order given, tables
+ * front to back); blocks the moved requests share stay shared in dst with the same
+ * counts.  Then src drops the requests as kv_bm_free_request does.  A block that a
+ * request left in src still names keeps its references there (its copy goes along).
+ *  pairs : [*num_pairs][2] int32 out, (src block, dst block) in first-seen order -- the
+ *          copies kv_swap_blocks must make.  pairs_cap >= the total table length of the
+ *          moved requests is always enough.
+ * All or nothing: KV_ERR_OUT_OF_BLOCKS if dst's free list is shorter than the distinct
+ * blocks; KV_ERR_INVALID_ARG for an unknown or repeated id, an id dst already has,
+ * different block sizes, src == dst or too small a pairs buffer; nothing changes. */
+kv_status_t kv_bm_move(kv_block_manager_t* src, kv_block_manager_t* dst, const int64_t* rids,
+                       int32_t n, int32_t* pairs, int32_t pairs_cap, int32_t* num_pairs);
 
 /* Multi-token (prefill / chunked-prefill) attention for one layer: each sequence has a
  * chunk of new tokens whose keys and values are already in the pool (reshape_and_cache),

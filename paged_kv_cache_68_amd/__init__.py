@@ -23,7 +23,7 @@ __all__ = [
     "paged_attention_workspace_bytes", "paged_attention_decode", "paged_attention_partitions",
     "paged_attention_reduce", "kv_pool_gather", "make_desc", "PagedKVError",
     "BlockManager", "OutOfBlocks", "copy_blocks", "paged_attention_prefill", "PrefixCache",
-    "hash_block",
+    "hash_block", "swap_blocks",
 ]
 
 BLOCK_SIZE = 16
@@ -94,8 +94,9 @@ class KVPool:
     """
 
     def __init__(self, num_layers, num_blocks, num_kv_heads, head_dim, dtype,
-                 block_size=BLOCK_SIZE, device=None, base=None, io_dtype=None):
+                 block_size=BLOCK_SIZE, device=None, base=None, io_dtype=None, host=False):
         torch = _torch()
+        self.host = bool(host)
         self.desc = make_desc(num_layers, num_blocks, num_kv_heads, head_dim, dtype, block_size,
                               io_dtype)
         nbytes = kv_pool_bytes(self.desc)
@@ -105,13 +106,29 @@ class KVPool:
             check(lib().kv_pool_create(ctypes.byref(self.desc), None, 0, ctypes.byref(h)),
                   "kv_pool_create")
             raise PagedKVError(KV_ERR_INVALID_ARG, "kv_pool_create")
+        self.dtype = _torch_dtype(self.desc.dtype)            # stored K / V elements
+        self.io_dtype = _torch_dtype(self.desc.io_dtype)      # queries, outputs, new K / V
+        h = ctypes.c_void_p()
+        if self.host:
+            # pinned host memory for swapped-out blocks: the library's own allocation
+            # (or the caller's pinned CPU tensor); ``memory`` is a CPU view of it, valid
+            # while the pool lives
+            ptr, size = (None, 0) if base is None else (base.data_ptr(),
+                                                        base.numel() * base.element_size())
+            check(lib().kv_host_pool_create(ctypes.byref(self.desc), ptr, size, ctypes.byref(h)),
+                  "kv_host_pool_create")
+            self.handle = h
+            if base is None:
+                k0 = ctypes.c_void_p()
+                check(lib().kv_pool_layer_ptrs(h, 0, ctypes.byref(k0), None), "kv_pool_layer_ptrs")
+                base = torch.frombuffer((ctypes.c_uint8 * nbytes).from_address(k0.value),
+                                        dtype=torch.uint8)
+            self.memory = base
+            return
         if base is None:
             dev = torch.device(device if device is not None else "cuda")
             base = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.memory = base
-        self.dtype = _torch_dtype(self.desc.dtype)            # stored K / V elements
-        self.io_dtype = _torch_dtype(self.desc.io_dtype)      # queries, outputs, new K / V
-        h = ctypes.c_void_p()
         check(lib().kv_pool_create(ctypes.byref(self.desc), base.data_ptr(),
                                    base.numel() * base.element_size(), ctypes.byref(h)),
               "kv_pool_create")
@@ -148,6 +165,8 @@ class KVPool:
 
     def close(self):
         if getattr(self, "handle", None) is not None and self.handle.value:
+            if self.host:
+                self.memory = None          # a view of memory the library frees next
             check(lib().kv_pool_destroy(self.handle), "kv_pool_destroy")
             self.handle = None
 
@@ -243,5 +262,5 @@ def kv_pool_gather(pool: KVPool, layer: int, block_tables, context_lens, k_out, 
           "kv_pool_gather")
 
 
-from .block_manager import BlockManager, OutOfBlocks, copy_blocks  # noqa: E402
+from .block_manager import BlockManager, OutOfBlocks, copy_blocks, swap_blocks  # noqa: E402
 from .prefix_cache import PrefixCache, hash_block  # noqa: E402

@@ -79,6 +79,9 @@ SIGNATURES = {
     "paged_attention_reduce": (_i32, _DECODE_ARGS),
     "kv_pool_gather": (_i32, [_pool, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
     "kv_copy_blocks": (_i32, [_pool, _vp, _i32, _vp]),
+    "kv_host_pool_create": (_i32, [ctypes.POINTER(KVPoolDesc), _vp, _sz, ctypes.POINTER(_pool)]),
+    "kv_pool_is_host": (_i32, [_pool]),
+    "kv_swap_blocks": (_i32, [_pool, _pool, _vp, _i32, _vp]),
     "paged_attention_prefill": (_i32, [_pool, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32,
                                        _f32, _vp]),
     "kv_bm_create": (_i32, [_i32, _i32, ctypes.POINTER(_bm)]),
@@ -93,6 +96,7 @@ SIGNATURES = {
     "kv_bm_num_free": (_i32, [_bm]),
     "kv_bm_ref_count": (_i32, [_bm, _i32, _pi32]),
     "kv_bm_free_list": (_i32, [_bm, _vp, _i32, _pi32]),
+    "kv_bm_move": (_i32, [_bm, _bm, _vp, _i32, _vp, _i32, _pi32]),
     "kv_pc_create": (_i32, [_i32, _i32, ctypes.POINTER(_bm)]),
     "kv_pc_destroy": (_i32, [_bm]),
     "kv_pc_add_request": (_i32, [_bm, _i64, _vp, _i32, ctypes.c_uint64, _pi32]),

@@ -11,7 +11,7 @@ import numpy as np
 
 from ._lib import KV_ERR_OUT_OF_BLOCKS, PagedKVError, check, lib
 
-__all__ = ["BlockManager", "OutOfBlocks", "copy_blocks"]
+__all__ = ["BlockManager", "OutOfBlocks", "copy_blocks", "swap_blocks"]
 
 
 class OutOfBlocks(PagedKVError):
@@ -104,6 +104,18 @@ class BlockManager:
         check(lib().kv_bm_ref_count(self.handle, int(block), ctypes.byref(v)), "kv_bm_ref_count")
         return v.value
 
+    def move_to(self, dst: "BlockManager", rids):
+        """Swap: move requests to manager ``dst`` (device to host, or back).  Returns the
+        copies as int32 (src block, dst block) pairs [k, 2] for ``swap_blocks``."""
+        r = np.ascontiguousarray(np.asarray(rids, dtype=np.int64))
+        n = r.shape[0]
+        cap = sum(len(self.table(int(x))) for x in r) if n else 0
+        pairs = np.empty((max(cap, 1), 2), dtype=np.int32)
+        got = ctypes.c_int32()
+        _check(lib().kv_bm_move(self.handle, dst.handle, _p(r) if n else None, n, _p(pairs), cap,
+                                ctypes.byref(got)), "kv_bm_move")
+        return pairs[:got.value]
+
     def free_list(self):
         buf = np.empty(self.num_blocks, dtype=np.int32)
         got = ctypes.c_int32()
@@ -119,3 +131,13 @@ def copy_blocks(pool, copies, stream=None) -> None:
     n = int(copies.shape[0])
     check(lib().kv_copy_blocks(pool.handle, copies.data_ptr() if n else None, n, _stream(stream)),
           "kv_copy_blocks")
+
+
+def swap_blocks(src_pool, dst_pool, pairs, stream=None) -> None:
+    """Swap copies: every layer's K and V of block pairs[i, 0] of ``src_pool`` go to block
+    pairs[i, 1] of ``dst_pool`` (one of them a host pool).  ``pairs`` is an int32 device
+    tensor [k, 2] (or a pinned CPU tensor)."""
+    from . import _stream
+    n = int(pairs.shape[0])
+    check(lib().kv_swap_blocks(src_pool.handle, dst_pool.handle, pairs.data_ptr() if n else None,
+                               n, _stream(stream)), "kv_swap_blocks")

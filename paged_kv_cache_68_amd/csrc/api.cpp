@@ -71,7 +71,7 @@ kv_status_t check_decode(const kv_pool_t* pool, int32_t layer, void* out, const 
                          const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                          float scale, int32_t partition_size, void* workspace,
                          size_t workspace_bytes, DecodeShape* shape) {
-    if (!pool) return KV_ERR_INVALID_ARG;
+    if (!pool || pool->host) return KV_ERR_INVALID_ARG;
     const kv_pool_desc_t& d = pool->desc;
     if (layer < 0 || layer >= d.num_layers) return KV_ERR_INVALID_ARG;
     if (batch < 0) return KV_ERR_INVALID_ARG;
@@ -153,7 +153,8 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     const size_t block_bytes = static_cast<size_t>(d.block_size) * a.row_bytes * 2;
     const size_t reach = block_bytes * std::min<size_t>(static_cast<size_t>(batch) * max_blocks,
                                                        static_cast<size_t>(d.num_blocks));
-    a.stream_loads = reach > pkv::kStreamThresholdBytes ? 1 : 0;
+    a.streamed = reach > pkv::kStreamThresholdBytes ? 1 : 0;
+    a.stream_loads = a.streamed;
     const char* st = getenv("PAGEDKV_STREAM");
     if (st && (st[0] == '0' || st[0] == '1')) a.stream_loads = st[0] - '0';
     return a;
@@ -236,6 +237,8 @@ kv_status_t kv_pool_create(const kv_pool_desc_t* desc, void* device_base, size_t
     p->desc = *desc;
     p->cache_bytes = cache_bytes(desc);
     p->owned = 0;
+    p->host = 0;
+    p->host_base = nullptr;
     p->device = -1;
     if (hipGetDevice(&p->device) != hipSuccess) {
         (void)hipGetLastError();
@@ -261,10 +264,73 @@ kv_status_t kv_pool_create(const kv_pool_desc_t* desc, void* device_base, size_t
     return KV_OK;
 }
 
+kv_status_t kv_host_pool_create(const kv_pool_desc_t* desc, void* host_base, size_t base_bytes,
+                                kv_pool_t** out) {
+    if (!out) return KV_ERR_INVALID_ARG;
+    const kv_status_t st = check_desc(desc);
+    if (st != KV_OK) return st;
+    const size_t need = kv_pool_bytes(desc);
+    if (host_base && (!aligned(host_base, 256) || base_bytes < need)) return KV_ERR_INVALID_ARG;
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) {
+        (void)hipGetLastError();
+        return KV_ERR_HIP;
+    }
+    void* host = host_base;
+    int owned = 0;
+    if (!host) {
+        if (hipHostMalloc(&host, need, hipHostMallocDefault) != hipSuccess || !host) {
+            (void)hipGetLastError();
+            return KV_ERR_OUT_OF_MEMORY;
+        }
+        owned = 1;
+    } else {
+        // the kernels reach the memory through its device mapping: it must be pinned
+        // host memory HIP knows, and both ends of the range must map
+        hipPointerAttribute_t attr;
+        if (hipPointerGetAttributes(&attr, host_base) != hipSuccess ||
+            attr.type != hipMemoryTypeHost) {
+            (void)hipGetLastError();
+            return KV_ERR_INVALID_ARG;
+        }
+        void* last = nullptr;
+        if (hipHostGetDevicePointer(&last, static_cast<char*>(host_base) + need - 1, 0) !=
+                hipSuccess || !last) {
+            (void)hipGetLastError();
+            return KV_ERR_INVALID_ARG;
+        }
+    }
+    void* dev = nullptr;
+    if (hipHostGetDevicePointer(&dev, host, 0) != hipSuccess || !dev) {
+        (void)hipGetLastError();
+        if (owned) (void)hipHostFree(host);
+        return KV_ERR_INVALID_ARG;
+    }
+    kv_pool_t* p = new (std::nothrow) kv_pool_t;
+    if (!p) {
+        if (owned) (void)hipHostFree(host);
+        return KV_ERR_OUT_OF_MEMORY;
+    }
+    p->desc = *desc;
+    p->cache_bytes = cache_bytes(desc);
+    p->owned = owned;
+    p->host = 1;
+    p->host_base = static_cast<char*>(host);
+    p->base = static_cast<char*>(dev);
+    p->device = device;
+    *out = p;
+    return KV_OK;
+}
+
+int32_t kv_pool_is_host(const kv_pool_t* pool) { return pool ? pool->host : -1; }
+
 kv_status_t kv_pool_destroy(kv_pool_t* pool) {
     if (!pool) return KV_OK;
     kv_status_t st = KV_OK;
-    if (pool->owned && hipFree(pool->base) != hipSuccess) st = KV_ERR_HIP;
+    if (pool->owned) {
+        const hipError_t e = pool->host ? hipHostFree(pool->host_base) : hipFree(pool->base);
+        if (e != hipSuccess) st = KV_ERR_HIP;
+    }
     delete pool;
     return st;
 }
@@ -278,7 +344,8 @@ kv_status_t kv_pool_get_desc(const kv_pool_t* pool, kv_pool_desc_t* desc) {
 kv_status_t kv_pool_layer_ptrs(const kv_pool_t* pool, int32_t layer, void** k_cache,
                                void** v_cache) {
     if (!pool || layer < 0 || layer >= pool->desc.num_layers) return KV_ERR_INVALID_ARG;
-    char* kc = pool->base + static_cast<size_t>(2 * layer) * pool->cache_bytes;
+    char* kc = (pool->host ? pool->host_base : pool->base) +
+               static_cast<size_t>(2 * layer) * pool->cache_bytes;
     if (k_cache) *k_cache = kc;
     if (v_cache) *v_cache = kc + pool->cache_bytes;
     return KV_OK;
@@ -286,7 +353,7 @@ kv_status_t kv_pool_layer_ptrs(const kv_pool_t* pool, int32_t layer, void** k_ca
 
 kv_status_t reshape_and_cache(kv_pool_t* pool, int32_t layer, const void* key, const void* value,
                               const int64_t* slot_mapping, int32_t num_tokens, hipStream_t stream) {
-    if (!pool || layer < 0 || layer >= pool->desc.num_layers || num_tokens < 0)
+    if (!pool || pool->host || layer < 0 || layer >= pool->desc.num_layers || num_tokens < 0)
         return KV_ERR_INVALID_ARG;
     if (num_tokens == 0) return KV_OK;
     if (!key || !value || !slot_mapping) return KV_ERR_INVALID_ARG;
@@ -302,7 +369,7 @@ kv_status_t reshape_and_cache(kv_pool_t* pool, int32_t layer, const void* key, c
 
 kv_status_t kv_copy_blocks(kv_pool_t* pool, const int32_t* copies, int32_t num_copies,
                            hipStream_t stream) {
-    if (!pool || num_copies < 0) return KV_ERR_INVALID_ARG;
+    if (!pool || pool->host || num_copies < 0) return KV_ERR_INVALID_ARG;
     if (num_copies == 0) return KV_OK;
     if (!copies || !aligned(copies, 4)) return KV_ERR_INVALID_ARG;
     const kv_pool_desc_t& d = pool->desc;
@@ -310,6 +377,25 @@ kv_status_t kv_copy_blocks(kv_pool_t* pool, const int32_t* copies, int32_t num_c
         pool->base, copies, num_copies, d.num_layers, d.num_blocks, d.block_size,
         d.num_kv_heads * d.head_dim * static_cast<int32_t>(elem_bytes(d)), pool->cache_bytes,
         stream);
+    return e == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+kv_status_t kv_swap_blocks(const kv_pool_t* src, kv_pool_t* dst, const int32_t* pairs,
+                           int32_t num_pairs, hipStream_t stream) {
+    if (!src || !dst || src == dst || num_pairs < 0) return KV_ERR_INVALID_ARG;
+    const kv_pool_desc_t& a = src->desc;
+    const kv_pool_desc_t& b = dst->desc;
+    if (a.num_layers != b.num_layers || a.block_size != b.block_size ||
+        a.num_kv_heads != b.num_kv_heads || a.head_dim != b.head_dim || a.dtype != b.dtype)
+        return KV_ERR_INVALID_ARG;
+    if (num_pairs == 0) return KV_OK;
+    if (!pairs || !aligned(pairs, 8)) return KV_ERR_INVALID_ARG;
+    const size_t block_bytes = static_cast<size_t>(a.block_size) * a.num_kv_heads * a.head_dim *
+                               elem_bytes(a);
+    const hipError_t e = pkv::launch_swap_blocks(src->base, dst->base, pairs, num_pairs,
+                                                 a.num_layers, a.num_blocks, b.num_blocks,
+                                                 block_bytes, src->cache_bytes, dst->cache_bytes,
+                                                 stream);
     return e == hipSuccess ? KV_OK : KV_ERR_HIP;
 }
 
@@ -354,7 +440,7 @@ kv_status_t paged_attention_prefill(const kv_pool_t* pool, int32_t layer, void* 
                                     int32_t max_blocks_per_seq, const int32_t* context_lens,
                                     int32_t batch, int32_t num_q_heads, float scale,
                                     hipStream_t stream) {
-    if (!pool) return KV_ERR_INVALID_ARG;
+    if (!pool || pool->host) return KV_ERR_INVALID_ARG;
     const kv_pool_desc_t& d = pool->desc;
     if (layer < 0 || layer >= d.num_layers || batch < 0 || max_query_len < 0 || num_q_heads < 1)
         return KV_ERR_INVALID_ARG;
@@ -381,6 +467,7 @@ kv_status_t paged_attention_prefill(const kv_pool_t* pool, int32_t layer, void* 
     pa.a = make_args(pool, layer, out, query, block_tables, max_blocks_per_seq, context_lens,
                      batch, num_q_heads, scale, nullptr, shape);
     pa.a.stream_loads = 0;       // keys are re-read by every row tile of a sequence
+    pa.a.streamed = 0;
     pa.qstart = query_start;
     pa.group = group;
     pa.row_tiles = static_cast<int32_t>(row_tiles);
@@ -403,7 +490,8 @@ kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* o
 kv_status_t kv_pool_gather(const kv_pool_t* pool, int32_t layer, const int32_t* block_tables,
                            int32_t max_blocks_per_seq, const int32_t* context_lens,
                            int32_t batch, void* k_out, void* v_out, hipStream_t stream) {
-    if (!pool || layer < 0 || layer >= pool->desc.num_layers || batch < 0) return KV_ERR_INVALID_ARG;
+    if (!pool || pool->host || layer < 0 || layer >= pool->desc.num_layers || batch < 0)
+        return KV_ERR_INVALID_ARG;
     if (batch == 0) return KV_OK;
     if (max_blocks_per_seq < 1 || batch > 65535 ||
         max_blocks_per_seq > 0x7fffffff / pool->desc.block_size)

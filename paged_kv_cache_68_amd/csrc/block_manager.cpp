@@ -255,6 +255,57 @@ kv_status_t kv_bm_export(const kv_block_manager_t* m, const int64_t* rids, int32
     return KV_OK;
 }
 
+kv_status_t kv_bm_move(kv_block_manager_t* src, kv_block_manager_t* dst, const int64_t* rids,
+                       int32_t n, int32_t* pairs, int32_t pairs_cap, int32_t* num_pairs) {
+    if (!src || !dst || src == dst || n < 0 || (n > 0 && !rids) || !num_pairs ||
+        src->block_size != dst->block_size)
+        return KV_ERR_INVALID_ARG;
+    // check everything first: ids known here, new there, not repeated; room for the pairs
+    std::unordered_map<int32_t, int32_t> fresh;          // source block -> destination block
+    std::vector<int32_t> order;                          // distinct source blocks, first seen
+    try {
+        std::unordered_map<int64_t, int> seen;
+        for (int32_t i = 0; i < n; ++i) {
+            auto it = src->requests.find(rids[i]);
+            if (it == src->requests.end() || dst->requests.count(rids[i]) || seen[rids[i]]++)
+                return KV_ERR_INVALID_ARG;
+            for (int32_t b : it->second.table)
+                if (fresh.emplace(b, -1).second) order.push_back(b);
+        }
+        dst->requests.reserve(dst->requests.size() + n);
+    } catch (...) {
+        return KV_ERR_OUT_OF_MEMORY;
+    }
+    const int32_t need = static_cast<int32_t>(order.size());
+    if (need > 0 && (!pairs || pairs_cap < need)) return KV_ERR_INVALID_ARG;
+    if (need > dst->num_free) return KV_ERR_OUT_OF_BLOCKS;
+    // the destination's requests first (copies of the tables, so nothing below can fail)
+    std::vector<kv_block_manager::Request> moved;
+    try {
+        moved.reserve(n);
+        for (int32_t i = 0; i < n; ++i) moved.push_back(src->requests.find(rids[i])->second);
+    } catch (...) {
+        return KV_ERR_OUT_OF_MEMORY;
+    }
+    for (int32_t k = 0; k < need; ++k) {
+        const int32_t b = dst->take();
+        dst->refs[b] = 0;                               // counted from the tables below
+        fresh[order[k]] = b;
+        pairs[2 * k + 0] = order[k];
+        pairs[2 * k + 1] = b;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        for (int32_t& b : moved[i].table) {
+            b = fresh[b];
+            ++dst->refs[b];
+        }
+        dst->requests.emplace(rids[i], std::move(moved[i]));
+    }
+    for (int32_t i = 0; i < n; ++i) kv_bm_free_request(src, rids[i]);
+    *num_pairs = need;
+    return KV_OK;
+}
+
 int32_t kv_bm_num_free(const kv_block_manager_t* m) { return m ? m->num_free : -1; }
 
 kv_status_t kv_bm_ref_count(const kv_block_manager_t* m, int32_t block, int32_t* count) {

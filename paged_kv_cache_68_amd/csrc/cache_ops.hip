@@ -8,6 +8,8 @@
 // a bit copy with 16-byte (dwordx4) accesses; into an FP8 pool each value is rounded to
 // E4M3 on the way.  The block copy and the gather are bit copies.
 
+#include <stdlib.h>
+
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -119,7 +121,72 @@ __global__ __launch_bounds__(256) void cow_copy(uint4* __restrict__ base,
     for (int ch = threadIdx.x; ch < n; ch += blockDim.x) to[ch] = from[ch];
 }
 
+// Swap copies between two pools of the same block shape, one or both in pinned host
+// memory reached through its device mapping ("PagedAttention and Virtual Memory
+// Management", section 6, swapping policy).  pairs[i] = (src block, dst block); every
+// layer's K and V block is one contiguous stretch of block_chunks 16-byte chunks.
+// Items are (tensor, pair) stretches, numbered pair-fastest so neighbouring items of one
+// tensor follow the pair list (a run of consecutive blocks stays one run of addresses on
+// the host link).  A fixed, small grid walks the items: the host link, not the CUs, is
+// the limit, and the rest of the chip stays free for decode.  Each thread keeps kUnroll
+// loads in flight before it stores, to cover the host link's latency.  A pair naming a
+// block outside its pool is skipped.
+constexpr int kSwapThreads = 256;
+constexpr int kSwapUnroll = 4;
+
+__global__ __launch_bounds__(kSwapThreads) void swap_copy(
+    const uint4* __restrict__ src, uint4* __restrict__ dst, const int2* __restrict__ pairs,
+    int32_t num_pairs, int64_t items, int32_t src_blocks, int32_t dst_blocks,
+    int32_t block_chunks, size_t src_cache_chunks, size_t dst_cache_chunks) {
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int64_t tensor = it / num_pairs;
+        const int2 pr = pairs[it - tensor * num_pairs];
+        if (static_cast<unsigned>(pr.x) >= static_cast<unsigned>(src_blocks) ||
+            static_cast<unsigned>(pr.y) >= static_cast<unsigned>(dst_blocks))
+            continue;
+        const uint4* from = src + tensor * src_cache_chunks + static_cast<size_t>(pr.x) * block_chunks;
+        uint4* to = dst + tensor * dst_cache_chunks + static_cast<size_t>(pr.y) * block_chunks;
+        for (int c0 = threadIdx.x; c0 < block_chunks; c0 += kSwapThreads * kSwapUnroll) {
+            uint4 r[kSwapUnroll];
+#pragma unroll
+            for (int u = 0; u < kSwapUnroll; ++u) {
+                const int c = c0 + u * kSwapThreads;
+                if (c < block_chunks) r[u] = from[c];
+            }
+#pragma unroll
+            for (int u = 0; u < kSwapUnroll; ++u) {
+                const int c = c0 + u * kSwapThreads;
+                if (c < block_chunks) to[c] = r[u];
+            }
+        }
+    }
+}
+
 }  // namespace
+
+int swap_groups() {
+    static const int groups = [] {
+        const char* e = getenv("PAGEDKV_SWAP_GROUPS");
+        const int v = e ? atoi(e) : 0;
+        return v > 0 && v <= 65535 ? v : kDefaultSwapGroups;
+    }();
+    return groups;
+}
+
+hipError_t launch_swap_blocks(const char* src, char* dst, const int32_t* pairs, int32_t num_pairs,
+                              int32_t num_layers, int32_t src_blocks, int32_t dst_blocks,
+                              size_t block_bytes, size_t src_cache_bytes, size_t dst_cache_bytes,
+                              hipStream_t stream) {
+    if (num_pairs <= 0) return hipSuccess;
+    const int64_t items = static_cast<int64_t>(num_pairs) * 2 * num_layers;
+    const int64_t groups = items < swap_groups() ? items : swap_groups();
+    hipLaunchKernelGGL(swap_copy, dim3(static_cast<unsigned>(groups)), dim3(kSwapThreads), 0,
+                       stream, reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst),
+                       reinterpret_cast<const int2*>(pairs), num_pairs, items, src_blocks,
+                       dst_blocks, static_cast<int32_t>(block_bytes / 16), src_cache_bytes / 16,
+                       dst_cache_bytes / 16);
+    return hipGetLastError();
+}
 
 hipError_t launch_copy_blocks(char* base, const int32_t* copies, int32_t num_copies,
                               int32_t num_layers, int32_t num_blocks, int32_t block_size,

@@ -10,9 +10,11 @@
 
 struct kv_pool {
     kv_pool_desc_t desc;
-    char* base;          // device address of layer 0's K cache
-    int owned;           // 1 if the library allocated `base`
-    int device;          // HIP device the pool lives on
+    char* base;          // device address of layer 0's K cache (device view of a host pool)
+    char* host_base;     // host address of a host pool, else nullptr
+    int owned;           // 1 if the library allocated the memory
+    int host;            // 1 for a pool in pinned host memory
+    int device;          // HIP device the pool lives on (mapped for, if host)
     size_t cache_bytes;  // bytes of one layer's K (or V) cache
 };
 
@@ -20,6 +22,7 @@ namespace pkv {
 
 constexpr int kBlockSize = 16;          // default tokens per physical block (the VALU kernel's)
 constexpr int kTile = 16;               // tokens per matrix-core tile
+constexpr int kDefaultSwapGroups = 64;  // work-groups of a swap copy (host-link bound)
 constexpr int kMaxTilesPerWave = 256;   // a wave holds one table entry per tile in 4 VGPRs
 constexpr int kDefaultPartition = 512;  // tokens per split-context partition
 constexpr int kMaxPartition = 4096;     // at most 256 tiles of 16 tokens per wave
@@ -51,6 +54,8 @@ struct DecodeArgs {
     float scale_log2;        // scale * log2(e): scores are kept in base-2 units
     int32_t xcd_chunk;       // work-groups per XCD chunk in the launch renumbering
     int32_t stream_loads;    // 1: K/V loads carry the non-temporal hint
+    int32_t streamed;        // 1: the call reaches more K/V bytes than the last-level
+                             // cache holds (the plan's input; the hint can be overridden)
 };
 
 // Multi-token (prefill) attention: the decode arguments (queries and outputs are
@@ -94,6 +99,10 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, const in
                                     int io_dtype, hipStream_t stream);
 // base: layer 0's K cache; the 2 * num_layers caches follow each other, cache_bytes
 // apart; rows of row_bytes bytes.
+hipError_t launch_swap_blocks(const char* src, char* dst, const int32_t* pairs, int32_t num_pairs,
+                              int32_t num_layers, int32_t src_blocks, int32_t dst_blocks,
+                              size_t block_bytes, size_t src_cache_bytes, size_t dst_cache_bytes,
+                              hipStream_t stream);
 hipError_t launch_copy_blocks(char* base, const int32_t* copies, int32_t num_copies,
                               int32_t num_layers, int32_t num_blocks, int32_t block_size,
                               int32_t row_bytes, size_t cache_bytes, hipStream_t stream);

@@ -372,7 +372,7 @@ struct Plan {
 // walks at most 256 tiles (its table entries sit in four registers) and every wave's
 // LDS stage stays within 64 KiB.
 //  * Long sequences streamed from HBM (at least two waves per (sequence, KV head), and
-//    more bytes than the last-level cache holds, see stream_loads): work-groups of 8
+//    more bytes than the last-level cache holds, see streamed): work-groups of 8
 //    waves spanning as many KV heads as make about 1 KiB of each token row (4 heads of
 //    128 bf16 / fp16 values, 8 of FP8), i.e. whole contiguous stretches of the row
 //    instead of separate 128- or 256-byte pieces fetched by unrelated work-groups; the
@@ -402,7 +402,7 @@ inline Plan make_plan(const DecodeArgs& a, int stage_bytes, bool group_capable,
     const int64_t per_head = target_waves / seqheads;     // waves per (sequence, KV head)
     int heads, chunk, ppw;
     int64_t slots;
-    if (per_head >= 2 && a.stream_loads) {
+    if (per_head >= 2 && a.streamed) {
         const int head_bytes = a.row_bytes / a.num_kv_heads;
         heads = 1;
         while (heads * 2 <= 8 && a.num_kv_heads % (heads * 2) == 0 && heads * 2 * head_bytes <= 1024)
