@@ -9,17 +9,24 @@
 // prompt in parallel) describe it.
 //
 // Mapping.  The (token, query head) pairs of one (sequence, KV head) form n * G rows,
-// head fastest; rows share the KV head's keys and values.  The decode kernel's matrix-
-// core tile is reused with its 16 columns filled by 16 rows instead of G heads:
-//   scores  S^T[16 keys][16 rows] = K[16 keys][D] . Q^T[D][16 rows]   (16x16x32 MFMA)
-//   values  O^T[D][16 rows]      += V^T[D][16 keys] . P^T[16 keys][16 rows] (16x16x16)
-// with a causal mask per column (key position <= the row's position) and a running max
-// and sum per column.  Each wave owns NC column blocks (16 NC rows) so that every key /
-// value tile it loads feeds NC products; a work-group of 4 waves covers 64 NC rows.
-// A wave walks the key tiles from position 0 up to its last row's position; a column
-// block whose rows all end before a tile skips that tile's products.  The keys of the
-// 4 waves of a work-group are the same, so the second to fourth reads of a tile mostly
-// hit the compute unit's cache.
+// head fastest; rows share the KV head's keys and values.  A work-group of W waves owns
+// 32 W consecutive rows, each wave two column blocks of 16 rows, and walks the keys
+// from position 0 to its last row's position in stages of 32 keys:
+//  * the work-group's threads fetch a stage's keys and values through the block table
+//    (one 16-byte LDS chunk of 8 values per thread and tensor at a time; E4M3 codes are
+//    widened here, once per work-group) into one of two LDS buffers, while the waves
+//    compute on the other;
+//  * scores  S^T[16 keys][16 rows] = K . Q^T     (16x16x32 MFMA, two per stage and k-chunk)
+//  * values  O^T[16 d][16 rows]   += V^T . P^T   (16x16x32 MFMA over the stage's 32 keys)
+//    the P^T operand is the score tile's own register layout (key slot 8c + j of the
+//    product is key 4c + j of the first 16 and 16 + 4c + j - 4 of the second), and the
+//    V^T operand takes the same slots from eight 16-byte LDS reads per lane;
+//  * online softmax per column (base 2) with a lazy rescale: the running maximum is
+//    raised only when a score passes it by more than 2^8, so the weights stay below 256
+//    and the accumulator is rescaled rarely; a stage that lies wholly before every row of
+//    a column block needs no causal mask.
+// Keys past the sequence's length (and table entries outside the pool) are staged as
+// zeros, so masked weights never meet stale memory.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -31,27 +38,58 @@
 namespace pkv {
 namespace {
 
-template <bool KV8, int NQK, int EPL> struct PBuf;
-template <int NQK, int EPL> struct PBuf<false, NQK, EPL> {
-    uint4 k[NQK];
-    typename std::conditional<EPL == 8, uint4, uint2>::type v[4];
+// Row-pair lane swaps (gfx950 v_permlane16_swap / v_permlane32_swap) of one value with
+// itself: a = the value of the even row (or the lower half), b = that of the odd row (or
+// the upper half), in every lane of the pair.  The second operand is passed through an
+// empty asm statement so that the compiler cannot treat the two operands as one value:
+// it would otherwise fold the second result into the first.
+struct pair_f {
+    float a, b;
 };
-template <int NQK, int EPL> struct PBuf<true, NQK, EPL> {
-    uint4 k[NQK / 2];
-    typename std::conditional<EPL == 8, uint2, uint32_t>::type v[4];
-};
+__device__ __forceinline__ pair_f swap16(float x) {
+    uint32_t y = __builtin_bit_cast(uint32_t, x);
+    asm volatile("" : "+v"(y));
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), y, false, false);
+    return {__builtin_bit_cast(float, static_cast<uint32_t>(r[0])), __builtin_bit_cast(float, static_cast<uint32_t>(r[1]))};
+}
+__device__ __forceinline__ pair_f swap32(float x) {
+    uint32_t y = __builtin_bit_cast(uint32_t, x);
+    asm volatile("" : "+v"(y));
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), y, false, false);
+    return {__builtin_bit_cast(float, static_cast<uint32_t>(r[0])), __builtin_bit_cast(float, static_cast<uint32_t>(r[1]))};
+}
 
-template <class S, int D, int NC, bool KV8>
-__global__ __launch_bounds__(256) void pa_prefill_mfma(PrefillArgs pa) {
+constexpr int kPfKeys = 32;         // keys per LDS stage
+constexpr int kPfWaves = 4;         // waves per work-group
+constexpr int kPfRowsPerWave = 32;  // two 16-row column blocks
+
+template <class S, int D, int W, bool KV8>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void pa_prefill_mfma(PrefillArgs pa) {
     const DecodeArgs& a = pa.a;
-    constexpr int NQK = D / 32;
-    constexpr int EPL = D / 16;
-    using Buf = PBuf<KV8, NQK, EPL>;
-    constexpr int kRowsPerWave = 16 * NC;
-    constexpr int kRowsPerGroup = 4 * kRowsPerWave;
+    constexpr int NC = 2;
+    constexpr int KT = kPfKeys;
+    constexpr int NQK = D / 32;                  // k-chunks of the score product
+    constexpr int DB = D / 16;                   // 16-row d-blocks of the value product
+    // LDS bytes per staged key row: the padding spreads the rows over the banks for the
+    // key reads (16 rows, one 16-byte chunk each) and the value transpose reads (8 rows,
+    // 32 bytes each, per half wave)
+    constexpr int ROWB_K = D * 2 + 16;
+    constexpr int ROWB_V = D * 2 + 32;
+    constexpr int CPR = D / 8;                   // 16-byte LDS chunks per key row
+    constexpr int CHUNKS = KT * CPR;             // chunks per tensor and stage
+    constexpr int THREADS = 64 * W;
+    constexpr int PER_T = (CHUNKS + THREADS - 1) / THREADS;
+    constexpr int EB = KV8 ? 1 : 2;              // bytes per stored element
+    constexpr int STAGE_K = KT * ROWB_K;
+    constexpr int STAGE_V = KT * ROWB_V;
+    using Raw = typename std::conditional<KV8, uint2, uint4>::type;
 
-    const int lane = threadIdx.x & 63;
-    const int wave = uniform(threadIdx.x >> 6);
+    __shared__ __align__(16) uint8_t lds_k[2][STAGE_K];
+    __shared__ __align__(16) uint8_t lds_v[2][STAGE_V];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
     const int n = lane & 15;
     const int c = lane >> 4;
     const int G = pa.group;
@@ -66,8 +104,15 @@ __global__ __launch_bounds__(256) void pa_prefill_mfma(PrefillArgs pa) {
     const int nq = pa.qstart[b + 1] - q0;
     const int L = clamped_length(a, b);
     const int rows = nq * G;
-    const int row_base = rt * kRowsPerGroup + wave * kRowsPerWave;
-    if (rt * kRowsPerGroup >= rows) return;          // the whole work-group is past the chunk
+    const int group_row0 = rt * kPfRowsPerWave * W;
+    if (group_row0 >= rows) return;              // the whole work-group is past the chunk
+    const int row_base = group_row0 + wave * kPfRowsPerWave;
+    // a negative scale is applied as a positive one to negated keys (exact, done while
+    // staging), so that the running maximum of the raw scores is that of the scaled ones
+    // (a zero scale runs as 1e-30: every weight is then exactly 1, as it should be, and
+    // masked scores stay -inf instead of becoming 0 * inf)
+    const float sl2 = fmaxf(fabsf(a.scale_log2), 1e-30f);
+    const bool negate_keys = a.scale_log2 < 0.f;
 
     // this lane's column in each block: row -> (token, head), position, Q^T operand
     int qpos[NC];
@@ -84,13 +129,14 @@ __global__ __launch_bounds__(256) void pa_prefill_mfma(PrefillArgs pa) {
         const size_t qrow = (static_cast<size_t>(q0 + t) * a.num_q_heads + kvh * G + g) * D;
 #pragma unroll
         for (int i = 0; i < NQK; ++i) {
-            const int e0 = KV8 ? c * (D / 4) + 8 * i : 8 * (4 * i + c);
-            qv[cb][i] = qpos[cb] >= 0 ? *reinterpret_cast<const uint4*>(a.q + qrow + e0)
+            qv[cb][i] = qpos[cb] >= 0 ? *reinterpret_cast<const uint4*>(a.q + qrow + 32 * i + 8 * c)
                                       : make_uint4(0, 0, 0, 0);
         }
     }
-    // last position of each column block and of the wave (wave-uniform)
+    // first and last position of each column block (wave-uniform): rows are in token
+    // order, so the block's first row has its smallest position
     int last[NC];
+    int first[NC];
     int wave_last = -1;
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
@@ -99,176 +145,230 @@ __global__ __launch_bounds__(256) void pa_prefill_mfma(PrefillArgs pa) {
         for (int off = 1; off < 64; off <<= 1) x = max(x, __shfl_xor(x, off));
         last[cb] = uniform(x);
         wave_last = max(wave_last, last[cb]);
+        const int r0 = row_base + cb * 16;
+        first[cb] = r0 < rows ? L - nq + r0 / G : -1;
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    // the work-group's last position: its last row's
+    const int group_rows_end = min(rows, group_row0 + kPfRowsPerWave * W);
+    const int group_last = L - nq + (group_rows_end - 1) / G;
+    const int nstages = group_last >= 0 ? group_last / KT + 1 : 0;
+    const int wave_stages = wave_last >= 0 ? wave_last / KT + 1 : 0;
 
-    f32x4_t acc[NC][EPL];
+    f32x4_t acc[NC][DB];
     float m[NC], l[NC];
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
         m[cb] = -INFINITY;
         l[cb] = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[cb][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < DB; ++e) acc[cb][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int row_bytes = a.row_bytes;
-    constexpr int EB = KV8 ? 1 : 2;
-    const int koff = KV8 ? kvh * D + c * (D / 4) + n * row_bytes : (kvh * D + 8 * c) * 2 + n * row_bytes;
-    const int voff = (kvh * D + EPL * n) * EB + 4 * c * row_bytes;
-    const int addr_x32 = (lane ^ 32) * 4;
+    // ---- staging: global (through the table) -> registers -> LDS.  Thread chunk u is
+    // key (tid + u THREADS) / CPR of the stage, 8 values at part (tid + u THREADS) % CPR.
+    const int* table = a.tables + static_cast<size_t>(b) * a.max_blocks;
+    const int bshift = __builtin_ctz(a.block_size);
+    const uint32_t block_bytes = static_cast<uint32_t>(a.block_size * a.row_bytes);
+    Raw rk[PER_T], rv[PER_T];
+    int tb[PER_T];                               // table entries of the stage being fetched
 
-    auto load = [&](__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, Buf& buf) {
-        if constexpr (KV8) {
+    auto fetch_table = [&](int j) {
 #pragma unroll
-            for (int i = 0; i < NQK / 2; ++i) buf.k[i] = load16(rk, koff + 16 * i);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if constexpr (EPL == 8) buf.v[r] = load8(rv, voff + r * row_bytes);
-                else buf.v[r] = load4(rv, voff + r * row_bytes);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NQK; ++i) buf.k[i] = load16(rk, koff + 64 * i);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if constexpr (EPL == 8) buf.v[r] = load16(rv, voff + r * row_bytes);
-                else buf.v[r] = load8(rv, voff + r * row_bytes);
-            }
+        for (int u = 0; u < PER_T; ++u) {
+            const int q = tid + u * THREADS;
+            const int pos = j * KT + q / CPR;
+            tb[u] = (q < CHUNKS && pos < L) ? table[pos >> bshift] : -1;
         }
     };
-    auto k_operand = [&](const Buf& buf, int i) -> uint4 {
+    auto fetch = [&](int j) {
+#pragma unroll
+        for (int u = 0; u < PER_T; ++u) {
+            const int q = tid + u * THREADS;
+            const int pos = j * KT + q / CPR;
+            const int blk = tb[u];
+            const bool ok = q < CHUNKS && static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
+            // an entry outside the pool (or past the length) reads block 0 and stages zeros
+            const uint32_t inner = static_cast<uint32_t>((pos & (a.block_size - 1)) * a.row_bytes +
+                                                         (kvh * D + (q % CPR) * 8) * EB);
+            const size_t off = static_cast<size_t>(ok ? static_cast<uint32_t>(blk) : 0u) * block_bytes + inner;
+            const Raw xk = *reinterpret_cast<const Raw*>(a.k + off);
+            const Raw xv = *reinterpret_cast<const Raw*>(a.v + off);
+            rk[u] = ok ? xk : Raw{};
+            rv[u] = ok ? xv : Raw{};
+        }
+    };
+    auto widen = [&](const Raw& x) -> uint4 {
         if constexpr (KV8) {
-            const uint32_t* w = reinterpret_cast<const uint32_t*>(buf.k) + 2 * i;
-            const uint2 lo = fp8x4_to<S>(w[0]);
-            const uint2 hi = fp8x4_to<S>(w[1]);
+            const uint2 lo = fp8x4_to<S>(x.x);
+            const uint2 hi = fp8x4_to<S>(x.y);
             return make_uint4(lo.x, lo.y, hi.x, hi.y);
         } else {
-            return buf.k[i];
+            return x;
         }
     };
-    auto v_word = [&](const Buf& buf, int r, int q) -> uint32_t {
-        if constexpr (KV8) {
-            const uint32_t w = reinterpret_cast<const uint32_t*>(&buf.v[r])[q / 2];
-            return (q & 1) ? S::template from_fp8x2<true>(w) : S::template from_fp8x2<false>(w);
-        } else {
-            return reinterpret_cast<const uint32_t*>(&buf.v[r])[q];
-        }
-    };
-
-    Item it;
-    it.b = b;
-    it.kvh = kvh;
-    it.L = L;
-    BlockWalk walk;
-
-    auto process = [&](int k, int valid, const Buf& buf) {
-        const int tpos = (walk.jb + k) * a.tile_tokens;     // position of the tile's first key
-        uint4 kop[NQK];
+    auto stage_store = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < NQK; ++i) kop[i] = k_operand(buf, i);
-        uint2 pt[NC];
-        bool live[NC];
+        for (int u = 0; u < PER_T; ++u) {
+            const int q = tid + u * THREADS;
+            if (q < CHUNKS) {
+                uint4 kx = widen(rk[u]);
+                if (negate_keys) {
+                    kx.x ^= 0x80008000u;
+                    kx.y ^= 0x80008000u;
+                    kx.z ^= 0x80008000u;
+                    kx.w ^= 0x80008000u;
+                }
+                *reinterpret_cast<uint4*>(&lds_k[buf][(q / CPR) * ROWB_K + (q % CPR) * 16]) = kx;
+                *reinterpret_cast<uint4*>(&lds_v[buf][(q / CPR) * ROWB_V + (q % CPR) * 16]) = widen(rv[u]);
+            }
+        }
+    };
+
+    // ---- one stage of 32 keys for this wave.  Both column blocks always run: a block
+    // whose rows all precede the stage gets only masked scores, zero weights and no
+    // change, and the straight-line code lets the LDS reads run ahead of the products.
+    // V^T operands come from LDS transpose reads: in each 16-lane group, source lane s
+    // reads 4 values of key slot s / 4 at d offset 4 (s % 4), and lane n receives the
+    // 4 slots' values of d row n.
+    const int tr_key = 4 * c + (n >> 2);         // key of this lane's transpose source slot
+    const int tr_d = 4 * (n & 3);
+    auto max_across_c = [](float x) {            // over the 4 lanes of a column (lane ^ 16, ^ 32)
+        const pair_f r = swap16(x);
+        x = __builtin_fmaxf(r.a, r.b);
+        const pair_f t = swap32(x);
+        return __builtin_fmaxf(t.a, t.b);
+    };
+    auto compute = [&](int j, int buf) {
+        const int tpos = j * KT;
+        const uint8_t* kl = lds_k[buf];
+        const uint8_t* vl = lds_v[buf];
+        uint4 kop[2][NQK];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < NQK; ++i)
+                kop[st][i] = *reinterpret_cast<const uint4*>(kl + (st * 16 + n) * ROWB_K + (32 * i + 8 * c) * 2);
+        // V^T operand of d-block e: slots 8c .. 8c + 3 are keys 4c .. 4c + 3, slots
+        // 8c + 4 .. 8c + 7 keys 16 + 4c .. 16 + 4c + 3
+        uint4 vop[DB];
+#pragma unroll
+        for (int e = 0; e < DB; ++e) {
+            typedef short v4i16 __attribute__((ext_vector_type(4)));
+            typedef v4i16 __attribute__((address_space(3))) lds_v4i16;
+            const uint8_t* p0 = vl + tr_key * ROWB_V + (16 * e + tr_d) * 2;
+            const uint8_t* p1 = p0 + 16 * ROWB_V;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(__attribute__((address_space(3))) const uint8_t*)(p0));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(__attribute__((address_space(3))) const uint8_t*)(p1));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo);
+            const uint2 h2 = __builtin_bit_cast(uint2, hi);
+            vop[e] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+        }
+        f32x4_t sc[NC][2];
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < NQK; ++i) x = S::mfma_k32(kop[st][i], qv[cb][i], x);
+                sc[cb][st] = x;
+            }
+        uint4 pop[NC];
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb) {
-            live[cb] = last[cb] >= tpos;                     // wave-uniform
-            pt[cb] = make_uint2(0, 0);
-            if (!live[cb]) continue;
-            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+            float sv[8];
 #pragma unroll
-            for (int i = 0; i < NQK; ++i) s = S::mfma_k32(kop[i], qv[cb][i], s);
-            float sr[4];
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int kr = 4 * c + r;
-                sr[r] = (kr < valid && tpos + kr <= qpos[cb]) ? s[r] * a.scale_log2 : -INFINITY;
+                for (int r = 0; r < 4; ++r) sv[4 * st + r] = sc[cb][st][r];
+            if (first[cb] < tpos + KT - 1) {                 // wave-uniform: some key after a row
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int key = (k < 4) ? 4 * c + k : 16 + 4 * c + (k - 4);
+                    if (tpos + key > qpos[cb]) sv[k] = -INFINITY;
+                }
             }
-            float mb = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
-            mb = fmaxf(mb, xor16(mb));
-            mb = fmaxf(mb, xor32(mb, addr_x32));
-            const float mn = fmaxf(m[cb], mb);
-            const float mu = (mn == -INFINITY) ? 0.f : mn;
-            const float alpha = fast_exp2(m[cb] - mu);
-            float pr[4];
+            float mb = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(sv[0], sv[1]), sv[2]),
+                                       __builtin_fmaxf(__builtin_fmaxf(sv[3], sv[4]), sv[5]));
+            mb = __builtin_fmaxf(mb, __builtin_fmaxf(sv[6], sv[7]));
+            mb = max_across_c(mb);
+            const float mbs = mb * sl2;                      // -inf stays -inf
+            if (__any(mbs > m[cb] + 8.f)) {
+                const float mn = __builtin_fmaxf(m[cb], mbs);
+                const float mu = (mn == -INFINITY) ? 0.f : mn;
+                const float alpha = fast_exp2(m[cb] - mu);   // 0 while nothing was seen
+                l[cb] *= alpha;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sr[r] - mu);
-            l[cb] = l[cb] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-            m[cb] = mn;
-            if (__any(alpha != 1.f)) {
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[cb][e] *= alpha;
+                for (int e = 0; e < DB; ++e) acc[cb][e] *= alpha;
+                m[cb] = mn;
             }
-            pt[cb] = make_uint2(S::pack2(pr[0], pr[1]), S::pack2(pr[2], pr[3]));
+            const float mu = (m[cb] == -INFINITY) ? 0.f : m[cb];
+            float pr[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) pr[k] = fast_exp2(fmaf(sv[k], sl2, -mu));
+            l[cb] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+            pop[cb] = make_uint4(S::pack2(pr[0], pr[1]), S::pack2(pr[2], pr[3]),
+                                 S::pack2(pr[4], pr[5]), S::pack2(pr[6], pr[7]));
         }
-        // V^T operand words, shared by the column blocks
 #pragma unroll
-        for (int q = 0; q < EPL / 2; ++q) {
-            const uint32_t w0 = v_word(buf, 0, q);
-            const uint32_t w1 = v_word(buf, 1, q);
-            const uint32_t w2 = v_word(buf, 2, q);
-            const uint32_t w3 = v_word(buf, 3, q);
-            const uint2 even = make_uint2(lo_halves(w0, w1), lo_halves(w2, w3));
-            const uint2 odd = make_uint2(hi_halves(w0, w1), hi_halves(w2, w3));
+        for (int e = 0; e < DB; ++e)
 #pragma unroll
-            for (int cb = 0; cb < NC; ++cb) {
-                if (!live[cb]) continue;
-                acc[cb][2 * q] = S::mfma_k16(even, pt[cb], acc[cb][2 * q]);
-                acc[cb][2 * q + 1] = S::mfma_k16(odd, pt[cb], acc[cb][2 * q + 1]);
-            }
-        }
+            for (int cb = 0; cb < NC; ++cb) acc[cb][e] = S::mfma_k32(vop[e], pop[cb], acc[cb][e]);
     };
 
-    // tiles 0 .. (wave_last / T), in stretches of at most 256 (one table entry per lane
-    // per tile held in four registers)
-    const int ntiles = wave_last >= 0 ? wave_last / a.tile_tokens + 1 : 0;
-    for (int j0 = 0; j0 < ntiles; j0 += kMaxTilesPerWave) {
-        const int j1 = min(ntiles, j0 + kMaxTilesPerWave);
-        walk.init_range(a, it, j0, j1, lane);
-        __builtin_amdgcn_s_waitcnt(0);
-        if constexpr (D == 128) walk_blocks3<Buf>(a, it, walk, row_bytes, load, process);
-        else walk_blocks<Buf>(a, it, walk, row_bytes, load, process);
+    // ---- pipeline: fetch stage j + 1 while computing stage j
+    if (nstages > 0) {
+        fetch_table(0);
+        fetch(0);
+        stage_store(0);
+        if (nstages > 1) fetch_table(1);
+    }
+    for (int j = 0; j < nstages; ++j) {
+        if (j + 1 < nstages) {
+            fetch(j + 1);
+            if (j + 2 < nstages) fetch_table(j + 2);
+        }
+        __syncthreads();                         // stage j is in LDS buffer j & 1
+        if (j < wave_stages) compute(j, j & 1);
+        if (j + 1 < nstages) stage_store((j + 1) & 1);   // its last readers passed the barrier
     }
 
-    // normalise and write: lane (c, n) holds elements [c D/4, (c+1) D/4) of its row
+    // normalise and write: lane (n, c) holds elements 16 e + 4 c + rr of row n
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
-        float lt = l[cb] + xor16(l[cb]);
-        lt += xor32(lt, addr_x32);
+        const pair_f r16 = swap16(l[cb]);
+        float lt = r16.a + r16.b;
+        const pair_f r32 = swap32(lt);
+        lt = r32.a + r32.b;
         const int r = row_base + cb * 16 + n;
         if (r >= rows) continue;
         const int t = tok[cb];
         const int g = r - t * G;
         const float inv = (qpos[cb] >= 0 && lt > 0.f) ? 1.f / lt : 0.f;
-        uint16_t* dst = a.out + (static_cast<size_t>(q0 + t) * a.num_q_heads + kvh * G + g) * D + c * (D / 4);
-        // acc[cb][e][rr] is element EPL (4c + rr) + e of the row
+        uint16_t* dst = a.out + (static_cast<size_t>(q0 + t) * a.num_q_heads + kvh * G + g) * D + 4 * c;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            uint32_t w[EPL / 2];
-#pragma unroll
-            for (int e = 0; e < EPL; e += 2)
-                w[e / 2] = S::pack2(acc[cb][e][rr] * inv, acc[cb][e + 1][rr] * inv);
-            if constexpr (EPL == 8)
-                *reinterpret_cast<uint4*>(dst + EPL * rr) = make_uint4(w[0], w[1], w[2], w[3]);
-            else
-                *reinterpret_cast<uint2*>(dst + EPL * rr) = make_uint2(w[0], w[1]);
-        }
+        for (int e = 0; e < DB; ++e)
+            *reinterpret_cast<uint2*>(dst + 16 * e) =
+                make_uint2(S::pack2(acc[cb][e][0] * inv, acc[cb][e][1] * inv),
+                           S::pack2(acc[cb][e][2] * inv, acc[cb][e][3] * inv));
     }
 }
 
 template <class S, int D, bool KV8>
 hipError_t launch_prefill_t(const PrefillArgs& pa, hipStream_t stream) {
-    constexpr int NC = 2;
     const int64_t wgs = static_cast<int64_t>(pa.a.batch) * pa.a.num_kv_heads * pa.row_tiles;
     if (wgs <= 0) return hipSuccess;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((pa_prefill_mfma<S, D, NC, KV8>), dim3(static_cast<unsigned>(wgs)), dim3(256),
-                       0, stream, pa);
+    hipLaunchKernelGGL((pa_prefill_mfma<S, D, kPfWaves, KV8>), dim3(static_cast<unsigned>(wgs)),
+                       dim3(64 * kPfWaves), 0, stream, pa);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int prefill_rows_per_group() { return 4 * 16 * 2; }
+int prefill_rows_per_group() { return kPfWaves * kPfRowsPerWave; }
 
 hipError_t launch_prefill(int kv_dtype, int io_dtype, int head_dim, const PrefillArgs& pa,
                           hipStream_t stream) {
