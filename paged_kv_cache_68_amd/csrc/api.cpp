@@ -456,7 +456,8 @@ kv_status_t paged_attention_prefill(const kv_pool_t* pool, int32_t layer, void* 
         return KV_ERR_INVALID_ARG;
     if (static_cast<int64_t>(max_blocks_per_seq) * d.block_size > INT32_MAX) return KV_ERR_INVALID_ARG;
     const int64_t rows = static_cast<int64_t>(max_query_len) * group;
-    const int64_t row_tiles = ceil_div(rows, pkv::prefill_rows_per_group());
+    const int waves = pkv::prefill_waves_for(static_cast<int64_t>(batch) * d.num_kv_heads, rows);
+    const int64_t row_tiles = ceil_div(rows, 32 * waves);
     if (row_tiles > INT32_MAX || static_cast<int64_t>(batch) * d.num_kv_heads * row_tiles > INT32_MAX)
         return KV_ERR_INVALID_ARG;
     DecodeShape shape;
@@ -471,6 +472,8 @@ kv_status_t paged_attention_prefill(const kv_pool_t* pool, int32_t layer, void* 
     pa.qstart = query_start;
     pa.group = group;
     pa.row_tiles = static_cast<int32_t>(row_tiles);
+    pa.waves = waves;
+    pa.buffer_bytes = pool->cache_bytes < (size_t(1) << 31) ? static_cast<int32_t>(pool->cache_bytes) : 0;
     return pkv::launch_prefill(d.dtype, io_dtype(d), d.head_dim, pa, stream) == hipSuccess
                ? KV_OK
                : KV_ERR_HIP;

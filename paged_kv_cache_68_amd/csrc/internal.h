@@ -65,6 +65,9 @@ struct PrefillArgs {
     const int32_t* qstart;   // [B + 1]: sequence b's queries are rows [qstart[b], qstart[b+1])
     int32_t group;           // query heads per KV head
     int32_t row_tiles;       // work-groups per (sequence, KV head)
+    int32_t waves;           // waves per work-group (4 or 8); 32 rows each
+    int32_t buffer_bytes;    // > 0: one layer's K (and V) cache spans this many bytes, small
+                             // enough for 32-bit buffer offsets; 0: 64-bit addresses
 };
 
 // A call that can touch more K/V bytes than this streams them past the last-level cache
@@ -88,7 +91,9 @@ int partition_chunk_mfma(int kv_dtype, int io_dtype, int group, int head_dim, co
 int group_waves_mfma(int kv_dtype, int io_dtype, int group, int head_dim, const DecodeArgs& a);
 hipError_t launch_reduce(int io_dtype, int head_dim, const DecodeArgs& a, hipStream_t stream);
 // (token, head) rows one prefill work-group covers.
-int prefill_rows_per_group();
+// waves per work-group for a prefill launch of `seq_heads` (sequence, KV head) pairs of
+// up to `rows` rows each
+int prefill_waves_for(int64_t seq_heads, int64_t rows);
 hipError_t launch_prefill(int kv_dtype, int io_dtype, int head_dim, const PrefillArgs& pa,
                           hipStream_t stream);
 // New tokens' rows ([T][row_elems] in io_dtype) into their slots: a bit copy for a

@@ -30,6 +30,7 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdlib.h>
 
 #include <type_traits>
 
@@ -60,7 +61,6 @@ __device__ __forceinline__ pair_f swap32(float x) {
 }
 
 constexpr int kPfKeys = 32;         // keys per LDS stage
-constexpr int kPfWaves = 4;         // waves per work-group
 constexpr int kPfRowsPerWave = 32;  // two 16-row column blocks
 
 template <class S, int D, int W, bool KV8>
@@ -171,6 +171,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const uint32_t block_bytes = static_cast<uint32_t>(a.block_size * a.row_bytes);
     Raw rk[PER_T], rv[PER_T];
     int tb[PER_T];                               // table entries of the stage being fetched
+    const __amdgpu_buffer_rsrc_t rsrc_k = make_rsrc(a.k, pa.buffer_bytes);
+    const __amdgpu_buffer_rsrc_t rsrc_v = make_rsrc(a.v, pa.buffer_bytes);
 
     auto fetch_table = [&](int j) {
 #pragma unroll
@@ -187,14 +189,27 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             const int pos = j * KT + q / CPR;
             const int blk = tb[u];
             const bool ok = q < CHUNKS && static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
-            // an entry outside the pool (or past the length) reads block 0 and stages zeros
             const uint32_t inner = static_cast<uint32_t>((pos & (a.block_size - 1)) * a.row_bytes +
                                                          (kvh * D + (q % CPR) * 8) * EB);
-            const size_t off = static_cast<size_t>(ok ? static_cast<uint32_t>(blk) : 0u) * block_bytes + inner;
-            const Raw xk = *reinterpret_cast<const Raw*>(a.k + off);
-            const Raw xv = *reinterpret_cast<const Raw*>(a.v + off);
-            rk[u] = ok ? xk : Raw{};
-            rv[u] = ok ? xv : Raw{};
+            if (pa.buffer_bytes > 0) {
+                // an entry outside the pool (or past the length) reads past the buffer's
+                // end, which returns zeros
+                const uint32_t off = ok ? static_cast<uint32_t>(blk) * block_bytes + inner : 0x80000000u;
+                if constexpr (KV8) {
+                    rk[u] = load8(rsrc_k, static_cast<int>(off));
+                    rv[u] = load8(rsrc_v, static_cast<int>(off));
+                } else {
+                    rk[u] = load16(rsrc_k, static_cast<int>(off));
+                    rv[u] = load16(rsrc_v, static_cast<int>(off));
+                }
+            } else {
+                // an entry outside the pool (or past the length) reads block 0 and stages zeros
+                const size_t off = static_cast<size_t>(ok ? static_cast<uint32_t>(blk) : 0u) * block_bytes + inner;
+                const Raw xk = *reinterpret_cast<const Raw*>(a.k + off);
+                const Raw xv = *reinterpret_cast<const Raw*>(a.v + off);
+                rk[u] = ok ? xk : Raw{};
+                rv[u] = ok ? xv : Raw{};
+            }
         }
     };
     auto widen = [&](const Raw& x) -> uint4 {
@@ -361,14 +376,31 @@ hipError_t launch_prefill_t(const PrefillArgs& pa, hipStream_t stream) {
     const int64_t wgs = static_cast<int64_t>(pa.a.batch) * pa.a.num_kv_heads * pa.row_tiles;
     if (wgs <= 0) return hipSuccess;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((pa_prefill_mfma<S, D, kPfWaves, KV8>), dim3(static_cast<unsigned>(wgs)),
-                       dim3(64 * kPfWaves), 0, stream, pa);
+    if (pa.waves == 8)
+        hipLaunchKernelGGL((pa_prefill_mfma<S, D, 8, KV8>), dim3(static_cast<unsigned>(wgs)),
+                           dim3(64 * 8), 0, stream, pa);
+    else
+        hipLaunchKernelGGL((pa_prefill_mfma<S, D, 4, KV8>), dim3(static_cast<unsigned>(wgs)),
+                           dim3(64 * 4), 0, stream, pa);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int prefill_rows_per_group() { return kPfWaves * kPfRowsPerWave; }
+// 8 waves (256 rows, one work-group per CU) share each staged K/V tile between twice as
+// many rows and halve each thread's staging work; 4 waves (128 rows, two work-groups per
+// CU) keep twice as many work-groups for launches too small to fill the chip with 8.
+// PAGEDKV_PREFILL_WAVES=4|8 forces the choice.
+int prefill_waves_for(int64_t seq_heads, int64_t rows) {
+    static const int forced = [] {
+        const char* e = getenv("PAGEDKV_PREFILL_WAVES");
+        const int v = e ? atoi(e) : 0;
+        return (v == 4 || v == 8) ? v : 0;
+    }();
+    if (forced) return forced;
+    const int64_t cus = device_cus() > 0 ? device_cus() : 256;
+    return seq_heads * ((rows + 255) / 256) >= 2 * cus ? 8 : 4;
+}
 
 hipError_t launch_prefill(int kv_dtype, int io_dtype, int head_dim, const PrefillArgs& pa,
                           hipStream_t stream) {
