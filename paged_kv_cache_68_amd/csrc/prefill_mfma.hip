@@ -392,12 +392,9 @@ hipError_t launch_prefill_t(const PrefillArgs& pa, hipStream_t stream) {
 // CU) keep twice as many work-groups for launches too small to fill the chip with 8.
 // PAGEDKV_PREFILL_WAVES=4|8 forces the choice.
 int prefill_waves_for(int64_t seq_heads, int64_t rows) {
-    static const int forced = [] {
-        const char* e = getenv("PAGEDKV_PREFILL_WAVES");
-        const int v = e ? atoi(e) : 0;
-        return (v == 4 || v == 8) ? v : 0;
-    }();
-    if (forced) return forced;
+    const char* e = getenv("PAGEDKV_PREFILL_WAVES");
+    const int forced = e ? atoi(e) : 0;
+    if (forced == 4 || forced == 8) return forced;
     const int64_t cus = device_cus() > 0 ? device_cus() : 256;
     return seq_heads * ((rows + 255) / 256) >= 2 * cus ? 8 : 4;
 }

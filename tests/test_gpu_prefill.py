@@ -169,3 +169,37 @@ def test_single_token_chunks_match_decode_within_tolerance():
     torch.cuda.synchronize()
     dec = oracle.to_f64(to_host_bits(out), "bf16")
     assert np.max(np.abs(oracle.to_f64(pre, "bf16") - dec)) <= 2 * TOL["bf16"]
+
+
+def test_chunked_prefill_step_full_size_sampled():
+    """The measured chunked-prefill step at its full size: 4 sequences, each computing
+    positions 6,144 .. 8,191 of an 8,192-token prompt, Llama-3-8B heads, bf16 (8-wave
+    work-groups).  Sampled rows of every sequence against the oracle."""
+    _say("prefill full size 4 x 2048 at 8192, hq=32 hkv=8 d=128 bf16")
+    chunks = [(2048, 8192)] * 4
+    lens, qs, tables, kp, vp, q, nb = _case(chunks, 16, 32, 8, 128, "bf16", "bf16", seed=12)
+    got = _run(16, lens, qs, tables, kp, vp, q, nb, 8, 128, "bf16", "bf16")
+    picks, ref, sub_lens, sub_tables = [], [], [], []
+    for b in range(4):
+        for i in (0, 1, 255, 256, 1024, 2047):
+            r = int(qs[b]) + i
+            pos = 8192 - 2048 + i
+            picks.append(r)
+            ref.append(oracle.paged_prefill_seq(q[r:r + 1], kp, vp, tables[b], pos + 1,
+                                                1 / math.sqrt(128), 16, "bf16")[0])
+            sub_lens.append(pos + 1)
+            sub_tables.append(tables[b])
+    _check(got[picks], np.stack(ref), np.arange(len(picks) + 1), np.stack(sub_tables),
+           np.array(sub_lens), vp, 16, "bf16", "bf16", 8)
+
+
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_both_work_group_shapes(waves, kv, monkeypatch):
+    """4- and 8-wave work-groups (forced) give oracle results on the mixed chunk set."""
+    monkeypatch.setenv("PAGEDKV_PREFILL_WAVES", waves)
+    _say(f"prefill waves={waves} kv={kv}")
+    lens, qs, tables, kp, vp, q, nb = _case(CHUNKS, 16, 32, 8, 128, "bf16", kv, seed=300)
+    got = _run(16, lens, qs, tables, kp, vp, q, nb, 8, 128, "bf16", kv)
+    ref = oracle.paged_prefill(q, qs, kp, vp, tables, lens, 1.0 / math.sqrt(128), 16, kv, q_dtype="bf16")
+    _check(got, ref, qs, tables, lens, vp, 16, kv, "bf16", 8)
