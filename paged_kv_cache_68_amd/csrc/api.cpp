@@ -155,6 +155,8 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
                                                        static_cast<size_t>(d.num_blocks));
     a.streamed = reach > pkv::kStreamThresholdBytes ? 1 : 0;
     a.stream_loads = a.streamed;
+    // (a margin below 2 GiB leaves room for an offset that is past the end but still fits)
+    a.layer_bytes = pool->cache_bytes <= 0x7FF00000u ? static_cast<int32_t>(pool->cache_bytes) : 0;
     const char* st = getenv("PAGEDKV_STREAM");
     if (st && (st[0] == '0' || st[0] == '1')) a.stream_loads = st[0] - '0';
     return a;

@@ -56,6 +56,8 @@ struct DecodeArgs {
     int32_t stream_loads;    // 1: K/V loads carry the non-temporal hint
     int32_t streamed;        // 1: the call reaches more K/V bytes than the last-level
                              // cache holds (the plan's input; the hint can be overridden)
+    int32_t layer_bytes;     // bytes of this layer's K (and V) cache if at most 0x7FF00000,
+                             // else 0: lets a wave address any block with 32-bit offsets
 };
 
 // Multi-token (prefill) attention: the decode arguments (queries and outputs are

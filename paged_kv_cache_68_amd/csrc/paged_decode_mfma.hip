@@ -84,9 +84,95 @@ template <int NQK, int EPL> struct KVBuf<true, NQK, EPL> {       // E4M3 codes
     typename std::conditional<EPL == 8, uint2, uint32_t>::type v[4];
 };
 
-template <class S, int D, int MODE, bool NT, bool KV8>
+// 8-token blocks, two per 16-row tile.  With B = 8 a tile of one block fills half of the
+// matrix-core tile; pairing blocks 2k and 2k + 1 of a wave's range fills it and halves
+// the walk.  Rows 0-7 of the tile come from the first block, rows 8-15 from the second,
+// so each lane addresses its own block: through one buffer resource over the whole
+// layer (32-bit offsets, hence layers up to 0x7FF00000 bytes), with an offset past its end for a
+// row that is not there (beyond the length or an entry outside the pool), which loads
+// zeros.  The tile's valid rows are still a prefix: the second block only holds tokens
+// when the first is full.
+struct PairLoc {
+    int off0, off1;      // byte offsets of the two blocks in the layer (-1: none)
+    int valid0, valid1;  // tokens in each
+};
+
+struct PairWalk {
+    int jb, j_end, nk;   // first tile (even), end, number of pairs
+    int tab0[4], tab1[4];
+
+    __device__ __forceinline__ void init_range(const DecodeArgs& a, const Item& it, int j_begin,
+                                               int j_stop, int lane) {
+        jb = j_begin;
+        j_end = j_stop;
+        nk = j_stop > j_begin ? (j_stop - j_begin + 1) / 2 : 0;
+        const int32_t* trow = a.tables + static_cast<size_t>(it.b) * a.max_blocks;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k = 64 * t + lane;
+            const int j = jb + 2 * k;
+            tab0[t] = (64 * t < nk && k < nk) ? trow[j] : -1;
+            tab1[t] = (64 * t < nk && k < nk && j + 1 < j_stop) ? trow[j + 1] : -1;
+        }
+    }
+
+    __device__ __forceinline__ int at(const DecodeArgs& a, const Item& it, int k, PairLoc& loc) const {
+        int t0 = -1, t1 = -1;
+        if (k < nk) {
+            const int kk = k & 63;
+            t0 = k < 64 ? __builtin_amdgcn_readlane(tab0[0], kk)
+               : k < 128 ? __builtin_amdgcn_readlane(tab0[1], kk)
+               : k < 192 ? __builtin_amdgcn_readlane(tab0[2], kk)
+                         : __builtin_amdgcn_readlane(tab0[3], kk);
+            t1 = k < 64 ? __builtin_amdgcn_readlane(tab1[0], kk)
+               : k < 128 ? __builtin_amdgcn_readlane(tab1[1], kk)
+               : k < 192 ? __builtin_amdgcn_readlane(tab1[2], kk)
+                         : __builtin_amdgcn_readlane(tab1[3], kk);
+        }
+        const int j = jb + 2 * k;
+        const int block_bytes = 8 * a.row_bytes;
+        const bool ok0 = static_cast<unsigned>(t0) < static_cast<unsigned>(a.num_blocks);
+        const bool ok1 = static_cast<unsigned>(t1) < static_cast<unsigned>(a.num_blocks);
+        loc.valid0 = uniform(ok0 ? max(0, min(8, it.L - 8 * j)) : 0);
+        loc.valid1 = uniform(ok1 && loc.valid0 == 8 ? max(0, min(8, it.L - 8 * (j + 1))) : 0);
+        loc.off0 = uniform(ok0 ? t0 * block_bytes : -1);
+        loc.off1 = uniform(ok1 ? t1 * block_bytes : -1);
+        return loc.valid0 + loc.valid1;
+    }
+};
+
+// walk_blocks3's schedule over tile pairs
+template <class Buf, class Load, class Process>
+__device__ __forceinline__ void walk_pairs3(const DecodeArgs& a, const Item& it, const PairWalk& w,
+                                            Load load, Process process) {
+    Buf b0, b1, b2;
+    PairLoc loc;
+    int v0 = w.at(a, it, 0, loc);
+    load(loc, b0);
+    int v1 = w.at(a, it, 1, loc);
+    load(loc, b1);
+    for (int k = 0; k < w.nk; k += 3) {
+        const int v2 = w.at(a, it, k + 2, loc);
+        load(loc, b2);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k, v0, b0);
+        if (k + 1 >= w.nk) break;
+        v0 = w.at(a, it, k + 3, loc);
+        load(loc, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k + 1, v1, b1);
+        if (k + 2 >= w.nk) break;
+        v1 = w.at(a, it, k + 4, loc);
+        load(loc, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        process(k + 2, v2, b2);
+    }
+}
+
+template <class S, int D, int MODE, bool NT, bool KV8, bool PAIR = false>
 __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, int n_items,
                                                          int per_item, int ppw, int heads) {
+    static_assert(!PAIR || MODE == kGroup, "paired 8-token blocks only in the group plan");
     constexpr bool SPLIT = MODE == kSplit;
     constexpr int W = kWavesPerGroup;
     constexpr int NQK = D / 32;    // score MFMAs per block
@@ -276,7 +362,47 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
     // three register sets for every head size: with d = 64 a block's loads are small and
     // a wave's walk is latency-bound, so the third set pays (Qwen serving batch of 256:
     // 15.0 -> 13.9 us); a fourth does not
-    walk_blocks3<Buf>(a, it, walk, row_bytes, load, process);
+    if constexpr (PAIR) {
+        PairWalk pw;
+        pw.init_range(a, it, it.j0, it.j1, lane);
+        const __amdgpu_buffer_rsrc_t lk = make_rsrc(a.k, a.layer_bytes);
+        const __amdgpu_buffer_rsrc_t lv = make_rsrc(a.v, a.layer_bytes);
+        // K row n of the tile: row n & 7 of block n >> 3; V rows 4c + r: block c >> 1
+        const int krow = (n & 7) * row_bytes + (koff - n * row_bytes);
+        const int vrow = 4 * (c & 1) * row_bytes + (voff - 4 * c * row_bytes);
+        constexpr int kFar = 0x7FF80000;         // past any layer reached this way: loads zeros
+        auto load_pair = [&](const PairLoc& loc, Buf& buf) {
+            const bool k_first = n < 8;
+            const int kb = k_first ? loc.off0 : loc.off1;
+            const int kv = k_first ? loc.valid0 : loc.valid1;
+            const int ko = (kb >= 0 && (n & 7) < kv) ? kb + krow : kFar;
+            const bool v_first = c < 2;
+            const int vb = v_first ? loc.off0 : loc.off1;
+            const int vv = v_first ? loc.valid0 : loc.valid1;
+            if constexpr (KV8) {
+#pragma unroll
+                for (int i = 0; i < NQK / 2; ++i) buf.k[i] = load16<NT>(lk, ko + 16 * i);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int vo = (vb >= 0 && 4 * (c & 1) + r < vv) ? vb + vrow + r * row_bytes : kFar;
+                    if constexpr (EPL == 8) buf.v[r] = load8<NT>(lv, vo);
+                    else buf.v[r] = load4<NT>(lv, vo);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NQK; ++i) buf.k[i] = load16<NT>(lk, ko + 64 * i);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int vo = (vb >= 0 && 4 * (c & 1) + r < vv) ? vb + vrow + r * row_bytes : kFar;
+                    if constexpr (EPL == 8) buf.v[r] = load16<NT>(lv, vo);
+                    else buf.v[r] = load8<NT>(lv, vo);
+                }
+            }
+        };
+        walk_pairs3<Buf>(a, it, pw, load_pair, process);
+    } else {
+        walk_blocks3<Buf>(a, it, walk, row_bytes, load, process);
+    }
 
     if constexpr (MODE == kGroup) {
         flush(it.p);
@@ -331,8 +457,12 @@ hipError_t launch_t(int group, const DecodeArgs& a, hipStream_t stream) {
         DecodeArgs g = a;
         g.xcd_chunk = 0;
         const int64_t wgs = static_cast<int64_t>(a.batch) * (a.num_kv_heads / pl.heads) * pl.chunks;
-        auto kernel = a.stream_loads ? pa_partition_mfma<S, D, kGroup, true, KV8>
-                                     : pa_partition_mfma<S, D, kGroup, false, KV8>;
+        // 8-token blocks go two to a tile when one resource can reach the whole layer
+        const bool pair = a.block_size == 8 && a.layer_bytes > 0 && !getenv_is0("PAGEDKV_PAIR");
+        auto kernel = pair ? (a.stream_loads ? pa_partition_mfma<S, D, kGroup, true, KV8, true>
+                                             : pa_partition_mfma<S, D, kGroup, false, KV8, true>)
+                           : (a.stream_loads ? pa_partition_mfma<S, D, kGroup, true, KV8>
+                                             : pa_partition_mfma<S, D, kGroup, false, KV8>);
         hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(64 * pl.group_waves),
                            pl.group_waves * stage, stream, g, group, static_cast<int>(wgs),
                            pl.chunk, pl.ppw, pl.heads);

@@ -346,6 +346,12 @@ inline int device_cus() {
     return cus;
 }
 
+// True when the variable is set to a value starting with '0' (a tuning switch turned off).
+inline bool getenv_is0(const char* name) {
+    const char* e = getenv(name);
+    return e && e[0] == '0';
+}
+
 inline int env_int(const char* name, int fallback) {
     const char* e = getenv(name);
     return (e && atoi(e) > 0) ? atoi(e) : fallback;

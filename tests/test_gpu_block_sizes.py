@@ -156,3 +156,30 @@ def test_copy_blocks_block_size_64():
         want = h.copy()
         oracle.copy_blocks(want, copies.tolist())
         assert np.array_equal(g, want)
+
+
+GROUP_PLANS = [
+    {},
+    {"PAGEDKV_SPLIT": "0", "PAGEDKV_GROUP_HEADS": "2", "PAGEDKV_GROUP_SLOTS": "2", "PAGEDKV_GROUP_PPW": "1"},
+    {"PAGEDKV_SPLIT": "0", "PAGEDKV_GROUP_HEADS": "1", "PAGEDKV_GROUP_SLOTS": "4", "PAGEDKV_GROUP_PPW": "2"},
+]
+
+
+@pytest.mark.parametrize("pair", ["1", "0"])
+@pytest.mark.parametrize("plan", range(len(GROUP_PLANS)))
+@pytest.mark.parametrize("part", [8, 16, 64, 512])
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(32, 8, 128, "bf16"), (14, 2, 64, "f16")])
+def test_block_size_8_paired_tiles(pair, plan, part, hq, hkv, d, dtype, monkeypatch):
+    """8-token blocks walked two to a 16-row tile (and, with PAGEDKV_PAIR=0, one): lengths
+    ending in either half of a pair, pairs that straddle partitions (8- and 16-token
+    partitions), padded tables and NaN in every stale slot, against the oracle."""
+    for k, v in GROUP_PLANS[plan].items():
+        monkeypatch.setenv(k, v)
+    monkeypatch.setenv("PAGEDKV_PAIR", pair)
+    _say(f"paired 8-token blocks pair={pair} plan={GROUP_PLANS[plan]} part={part} hq={hq} {dtype}")
+    lens = [1, 7, 8, 9, 15, 16, 17, 23, 24, 25, 511, 513, 1000, 2047, 0]
+    lens, tables, kp, vp, q, nb = _case(lens, 8, hq, hkv, d, dtype, seed=77)
+    out = _run(8, lens, tables, kp, vp, q, nb, hkv, d, dtype, part)
+    ref = oracle.paged_decode(q, kp, vp, tables, lens, 1.0 / np.sqrt(d), 8, dtype)
+    assert max_abs_err(out, ref, dtype) <= TOL[dtype]
+    assert not out[14].any()
