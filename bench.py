@@ -216,7 +216,8 @@ SWAP_WORKLOADS = {
     "llama3_8b_swap_2407_tokens": {"layers": 32, "dev_blocks": 4096, "host_blocks": 1024,
                                    "tokens": 2407},
 }
-PEAK_HOST_LINK_GBPS = 64.0     # PCIe 5.0 x16, one direction (MI355X host interface)
+PEAK_HOST_LINK_GBPS = 64.0
+LLC_BYTES = 256 << 20          # MI355X Infinity Cache     # PCIe 5.0 x16, one direction (MI355X host interface)
 
 
 def bench_swap(args, name):
@@ -433,6 +434,9 @@ def main(argv=None):
                     help="time the copy-on-write block copy on this workload instead")
     ap.add_argument("--swap", choices=sorted(SWAP_WORKLOADS),
                     help="time swap-out and swap-in block copies on this workload instead")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each step after evicting the last-level cache (done by "
+                         "default when the step's working set fits in it)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -562,6 +566,36 @@ def main(argv=None):
             "avg_launch_us": part_ms * 1e3,
         },
     }
+    # A working set smaller than the 256 MB Infinity Cache is served from it when steps
+    # run back to back.  For such workloads also time each step cold: a 512 MiB write
+    # between steps evicts the cache, and HIP events bracket the step alone.
+    tabs = dc.tables[dc.tables >= 0]
+    footprint = int(torch.unique(tabs).numel()) * cfg.block_size * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes * 2
+    if footprint < LLC_BYTES or args.cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.fill_(i & 0xFF)
+            ev[i][0].record(stream)
+            pk.reshape_and_cache(dc.pool, 0, dc.new_key, dc.new_value, dc.slots, stream)
+            pk.paged_attention_partitions(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
+                                          cfg.partition_size, dc.workspace, stream)
+            ev[i][1].record(stream)
+            pk.paged_attention_reduce(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
+                                      cfg.partition_size, dc.workspace, stream)
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        step_us = float(np.median([e[0].elapsed_time(e[2]) for e in ev])) * 1e3
+        result["cold_cache"] = {
+            "how": "512 MiB write between steps; median of HIP-event step times (write + partitions + reduce)",
+            "unique_kv_bytes": footprint,
+            "us_per_step": step_us,
+            "seqs_per_s": cfg.batch / (step_us * 1e-6),
+            "step_hbm_gbps": nbytes["step"] / (step_us * 1e-6) / 1e9,
+            "step_frac_of_peak": nbytes["step"] / (step_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+            "unique_kv_gbps": footprint / (step_us * 1e-6) / 1e9,
+        }
+        del flush
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(dc, args.cpu_budget)
