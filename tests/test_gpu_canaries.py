@@ -1,0 +1,127 @@
+"""Guard bands: every entry point writes only where it should.  Outputs, workspaces and
+pools sit inside larger buffers whose margins hold a byte pattern; after decode (every
+plan), prefill, cache writes with skipped slots, copy-on-write copies and swap copies the
+margins are unchanged, and decode leaves the pool's bytes unchanged."""
+
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_cache_68_amd as pk  # noqa: E402
+from workloads import nan_bits, round_to_bits  # noqa: E402
+
+from .gpu_helpers import to_dev  # noqa: E402
+
+GUARD = 4096
+PATTERN = 0xA5
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+class Guarded:
+    """nbytes of device memory with GUARD bytes of PATTERN on each side."""
+
+    def __init__(self, nbytes):
+        self.n = int(nbytes)
+        self.buf = torch.full((self.n + 2 * GUARD,), PATTERN, dtype=torch.uint8, device="cuda")
+        self.mem = self.buf[GUARD:GUARD + self.n]
+
+    def view(self, dtype, shape):
+        return self.mem.view(dtype).view(*shape)
+
+    def intact(self):
+        torch.cuda.synchronize()
+        return bool((self.buf[:GUARD] == PATTERN).all()) and bool((self.buf[GUARD + self.n:] == PATTERN).all())
+
+
+def _pool(nb, hkv, d, dtype, B=16, layers=1, host=False, seed=0):
+    desc = pk.make_desc(layers, nb, hkv, d, dtype, B)
+    g = Guarded(pk.kv_pool_bytes(desc))
+    pool = pk.KVPool(layers, nb, hkv, d, dtype, block_size=B, base=g.mem)
+    rng = np.random.default_rng(seed)
+    for layer in range(layers):
+        for which in (pool.k_cache, pool.v_cache):
+            bits = round_to_bits(rng.standard_normal(tuple(which(layer).shape), dtype=np.float32), dtype)
+            bits[:, :, 0, 0] = nan_bits(dtype)       # NaN scattered through the pool
+            which(layer).copy_(to_dev(bits, dtype))
+    return g, pool
+
+
+PLANS = [{}, {"PAGEDKV_SPLIT": "1"}, {"PAGEDKV_SPLIT": "0", "PAGEDKV_GROUP": "0"},
+         {"PAGEDKV_SPLIT": "0", "PAGEDKV_GROUP_HEADS": "2", "PAGEDKV_GROUP_SLOTS": "2", "PAGEDKV_GROUP_PPW": "1"},
+         {"PAGEDKV_KERNEL": "valu"}]
+
+
+@pytest.mark.parametrize("plan", range(len(PLANS)))
+def test_decode_writes_only_out_and_workspace(plan, monkeypatch):
+    for k, v in PLANS[plan].items():
+        monkeypatch.setenv(k, v)
+    _say(f"canaries decode plan {PLANS[plan]}")
+    hq, hkv, d, dt = 32, 8, 128, "bf16"
+    gp, pool = _pool(300, hkv, d, dt)
+    before = gp.mem.clone()
+    lens = torch.tensor([1, 17, 600, 2000, 0, 3000], dtype=torch.int32, device="cuda")
+    mb = 200
+    tables = torch.randperm(300, device="cuda", dtype=torch.int64)[:6 * mb // 4].int()
+    tables = torch.cat([tables, torch.full((6 * mb - tables.numel(),), -1, dtype=torch.int32, device="cuda")]).view(6, mb)
+    lens = torch.minimum(lens, (tables >= 0).sum(1).int() * 16)
+    q = torch.randn(6, hq, d, device="cuda").to(torch.bfloat16)
+    go = Guarded(q.numel() * 2)
+    out = go.view(torch.bfloat16, q.shape)
+    wsb = pk.paged_attention_workspace_bytes(6, hq, d, mb, 16, 256)
+    gw = Guarded(max(wsb, 16))
+    pk.paged_attention_decode(pool, 0, out, q, tables, lens, partition_size=256,
+                              workspace=gw.mem[:wsb] if wsb else None)
+    assert go.intact() and gw.intact() and gp.intact()
+    assert torch.equal(gp.mem, before)
+    assert torch.isfinite(out[:4].float()).all() and not out[4].any()
+
+
+def test_cache_write_skips_negative_and_out_of_range_slots():
+    _say("canaries reshape_and_cache")
+    gp, pool = _pool(8, 2, 64, "f16")
+    before_k = pool.k_cache(0).clone()
+    slots = torch.tensor([-1, 0, 127, 128, 5000, -7, 64], dtype=torch.int64, device="cuda")
+    key = torch.randn(7, 2, 64, device="cuda").half()
+    value = torch.randn(7, 2, 64, device="cuda").half()
+    pk.reshape_and_cache(pool, 0, key, value, slots)
+    assert gp.intact()
+    k = pool.k_cache(0).reshape(128, 2, 64).view(torch.int16)           # bits (the pool holds NaN)
+    kin = key.view(torch.int16)
+    assert torch.equal(k[0], kin[1]) and torch.equal(k[127], kin[2]) and torch.equal(k[64], kin[6])
+    untouched = [s for s in range(128) if s not in (0, 127, 64)]
+    assert torch.equal(k[untouched], before_k.reshape(128, 2, 64).view(torch.int16)[untouched])
+
+
+def test_prefill_writes_only_out():
+    _say("canaries prefill")
+    hq, hkv, d = 14, 2, 64
+    gp, pool = _pool(64, hkv, d, "f16")
+    before = gp.mem.clone()
+    qs = torch.tensor([0, 40, 41, 241], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([100, 1, 300], dtype=torch.int32, device="cuda")
+    tables = torch.arange(60, dtype=torch.int32, device="cuda").view(3, 20)
+    q = torch.randn(241, hq, d, device="cuda").half()
+    go = Guarded(q.numel() * 2)
+    out = go.view(torch.float16, q.shape)
+    pk.paged_attention_prefill(pool, 0, out, q, qs, 200, tables, lens, scale=1 / math.sqrt(d))
+    assert go.intact() and gp.intact() and torch.equal(gp.mem, before)
+
+
+def test_block_copies_stay_inside_the_pools():
+    _say("canaries copy_blocks / swap_blocks")
+    gp, pool = _pool(32, 2, 64, "f16", layers=2)
+    copies = torch.tensor([[0, 31, 16], [31, 0, 5], [3, 4, 16]], dtype=torch.int32, device="cuda")
+    pk.copy_blocks(pool, copies)
+    assert gp.intact()
+    gd, dst = _pool(8, 2, 64, "f16", layers=2, seed=1)
+    pairs = torch.tensor([[0, 7], [31, 0], [5, 8], [40, 1]], dtype=torch.int32, device="cuda")
+    pk.swap_blocks(pool, dst, pairs)
+    assert gd.intact() and gp.intact()
