@@ -42,6 +42,18 @@
  *    infinities to +-448 and writes NaN as S.1111.111.
  *  - Results depend only on logical token positions: the output is bit-identical
  *    under any relabelling of physical blocks, and run-to-run deterministic.
+ *  - Device data is trusted on the fast path: block ids past a sequence's length are
+ *    never read, an id outside the pool reads as zeros, a length past the table is
+ *    clamped, a negative or out-of-range slot writes nothing, and duplicate slots give
+ *    an unspecified one of the values.  Checked mode (environment PAGEDKV_CHECK=1, read
+ *    per call) validates on the device first, then waits for the stream and returns
+ *    KV_ERR_INVALID_ARG, with nothing written, if a used table entry names no block of
+ *    the pool, a length lies outside [0, max_blocks * block_size], a slot is out of
+ *    range or repeated (reshape_and_cache), or query offsets are decreasing or a chunk
+ *    exceeds max_query_len (paged_attention_prefill).  It synchronises, so it is for
+ *    debugging: it is not meant for graph capture, and on its first use per device it
+ *    allocates a small status buffer (and a slot bitmap) that lives until the process
+ *    ends.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include <hip/hip_runtime_api.h>
@@ -162,6 +163,76 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     return a;
 }
 
+// ---- checked mode (PAGEDKV_CHECK=1, read per call): validation pre-passes on the
+// caller's stream, then a wait and a read of the status word.  Per device the library
+// keeps a status word and a bitmap of slots (grown on demand) until the process ends.
+bool checked_mode() {
+    const char* e = getenv("PAGEDKV_CHECK");
+    return e && e[0] == '1';
+}
+
+struct CheckBuffers {
+    uint32_t* status = nullptr;
+    uint32_t* seen = nullptr;
+    int64_t seen_words = 0;
+};
+
+std::mutex g_check_mutex;
+CheckBuffers g_check[64];
+
+// The device's buffers, with room for `slots` bits; nullptr on failure.
+CheckBuffers* check_buffers(int64_t slots) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_check_mutex);
+    CheckBuffers& cb = g_check[dev];
+    if (!cb.status && hipMalloc(reinterpret_cast<void**>(&cb.status), sizeof(uint32_t)) != hipSuccess) {
+        (void)hipGetLastError();
+        cb.status = nullptr;
+        return nullptr;
+    }
+    const int64_t words = (slots + 31) / 32;
+    if (words > cb.seen_words) {
+        if (cb.seen && hipFree(cb.seen) != hipSuccess) (void)hipGetLastError();
+        cb.seen = nullptr;
+        cb.seen_words = 0;
+        if (hipMalloc(reinterpret_cast<void**>(&cb.seen), static_cast<size_t>(words) * 4) != hipSuccess) {
+            (void)hipGetLastError();
+            cb.seen = nullptr;
+            return nullptr;
+        }
+        cb.seen_words = words;
+    }
+    return &cb;
+}
+
+// Clear the status word, run `launch(status, seen)`, wait, and map the result.
+template <class Launch>
+kv_status_t run_check(int64_t slots, hipStream_t stream, Launch launch) {
+    CheckBuffers* cb = check_buffers(slots);
+    if (!cb) return KV_ERR_OUT_OF_MEMORY;
+    uint32_t word = 0;
+    if (pkv::launch_clear_word(cb->status, stream) != hipSuccess ||
+        launch(cb->status, cb->seen) != hipSuccess ||
+        hipMemcpyAsync(&word, cb->status, sizeof(word), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return KV_ERR_HIP;
+    }
+    return word ? KV_ERR_INVALID_ARG : KV_OK;
+}
+
+kv_status_t check_tables_on_device(const kv_pool_t* pool, const int32_t* tables, int32_t max_blocks,
+                                   const int32_t* lens, int32_t batch, hipStream_t stream) {
+    return run_check(0, stream, [&](uint32_t* status, uint32_t*) {
+        return pkv::launch_check_tables(tables, max_blocks, lens, batch, pool->desc.num_blocks,
+                                        pool->desc.block_size, status, stream);
+    });
+}
+
 enum Phase { kBoth = 3, kPartitions = 1, kReduce = 2 };
 
 kv_status_t decode_impl(int phases, const kv_pool_t* pool, int32_t layer, void* out,
@@ -175,6 +246,10 @@ kv_status_t decode_impl(int phases, const kv_pool_t* pool, int32_t layer, void* 
                                   workspace_bytes, &s);
     if (st != KV_OK) return st;
     if (batch == 0) return KV_OK;
+    if (checked_mode() && (phases & kPartitions)) {
+        st = check_tables_on_device(pool, block_tables, max_blocks, context_lens, batch, stream);
+        if (st != KV_OK) return st;
+    }
     const pkv::DecodeArgs a = make_args(pool, layer, out, query, block_tables, max_blocks,
                                         context_lens, batch, num_q_heads, scale, workspace, s);
     if (phases & kPartitions) {
@@ -363,6 +438,12 @@ kv_status_t reshape_and_cache(kv_pool_t* pool, int32_t layer, const void* key, c
     const kv_pool_desc_t& d = pool->desc;
     char* kc = pool->base + static_cast<size_t>(2 * layer) * pool->cache_bytes;
     const int64_t num_slots = static_cast<int64_t>(d.num_blocks) * d.block_size;
+    if (checked_mode()) {
+        const kv_status_t st = run_check(num_slots, stream, [&](uint32_t* status, uint32_t* seen) {
+            return pkv::launch_check_slots(slot_mapping, num_tokens, num_slots, seen, status, stream);
+        });
+        if (st != KV_OK) return st;
+    }
     const hipError_t e = pkv::launch_reshape_and_cache(
         key, value, slot_mapping, num_tokens, kc, kc + pool->cache_bytes, num_slots,
         d.num_kv_heads * d.head_dim, d.dtype, io_dtype(d), stream);
@@ -462,6 +543,15 @@ kv_status_t paged_attention_prefill(const kv_pool_t* pool, int32_t layer, void* 
     const int64_t row_tiles = ceil_div(rows, 32 * waves);
     if (row_tiles > INT32_MAX || static_cast<int64_t>(batch) * d.num_kv_heads * row_tiles > INT32_MAX)
         return KV_ERR_INVALID_ARG;
+    if (checked_mode()) {
+        kv_status_t st = check_tables_on_device(pool, block_tables, max_blocks_per_seq, context_lens,
+                                                batch, stream);
+        if (st == KV_OK)
+            st = run_check(0, stream, [&](uint32_t* status, uint32_t*) {
+                return pkv::launch_check_query_start(query_start, batch, max_query_len, status, stream);
+            });
+        if (st != KV_OK) return st;
+    }
     DecodeShape shape;
     shape.group = group;
     shape.part_blocks = 1;

@@ -106,6 +106,16 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, const in
                                     int io_dtype, hipStream_t stream);
 // base: layer 0's K cache; the 2 * num_layers caches follow each other, cache_bytes
 // apart; rows of row_bytes bytes.
+// checked mode (PAGEDKV_CHECK=1): validation pre-passes, each or-ing bits into *status
+hipError_t launch_check_tables(const int32_t* tables, int32_t max_blocks, const int32_t* lens,
+                               int32_t batch, int32_t num_blocks, int32_t block_size,
+                               uint32_t* status, hipStream_t stream);
+hipError_t launch_check_slots(const int64_t* slots, int32_t n, int64_t num_slots, uint32_t* seen,
+                              uint32_t* status, hipStream_t stream);
+hipError_t launch_check_query_start(const int32_t* qs, int32_t batch, int32_t max_query_len,
+                                    uint32_t* status, hipStream_t stream);
+hipError_t launch_clear_word(uint32_t* w, hipStream_t stream);
+
 hipError_t launch_swap_blocks(const char* src, char* dst, const int32_t* pairs, int32_t num_pairs,
                               int32_t num_layers, int32_t src_blocks, int32_t dst_blocks,
                               size_t block_bytes, size_t src_cache_bytes, size_t dst_cache_bytes,
