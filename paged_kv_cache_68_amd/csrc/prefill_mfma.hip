@@ -155,11 +155,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int wave_stages = wave_last >= 0 ? wave_last / KT + 1 : 0;
 
     f32x4_t acc[NC][DB];
-    float m[NC], l[NC];
+    f32x4_t lacc[NC];                            // running sums of the weights (4 equal rows)
+    float m[NC];
+    const uint32_t one2 = S::pack2(1.f, 1.f);
+    const uint4 ones = make_uint4(one2, one2, one2, one2);
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
         m[cb] = -INFINITY;
-        l[cb] = 0.f;
+        lacc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < DB; ++e) acc[cb][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -305,27 +308,31 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                     if (tpos + key > qpos[cb]) sv[k] = -INFINITY;
                 }
             }
+            // this lane's maximum; the column's (over the four c-lanes) is needed only when
+            // some score passes the running maximum by more than 2^8
             float mb = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(sv[0], sv[1]), sv[2]),
                                        __builtin_fmaxf(__builtin_fmaxf(sv[3], sv[4]), sv[5]));
             mb = __builtin_fmaxf(mb, __builtin_fmaxf(sv[6], sv[7]));
-            mb = max_across_c(mb);
-            const float mbs = mb * sl2;                      // -inf stays -inf
-            if (__any(mbs > m[cb] + 8.f)) {
+            if (__any(mb * sl2 > m[cb] + 8.f)) {
+                const float mbs = max_across_c(mb) * sl2;    // -inf stays -inf
                 const float mn = __builtin_fmaxf(m[cb], mbs);
                 const float mu = (mn == -INFINITY) ? 0.f : mn;
                 const float alpha = fast_exp2(m[cb] - mu);   // 0 while nothing was seen
-                l[cb] *= alpha;
 #pragma unroll
                 for (int e = 0; e < DB; ++e) acc[cb][e] *= alpha;
+                lacc[cb] *= alpha;
                 m[cb] = mn;
             }
             const float mu = (m[cb] == -INFINITY) ? 0.f : m[cb];
             float pr[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) pr[k] = fast_exp2(fmaf(sv[k], sl2, -mu));
-            l[cb] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
             pop[cb] = make_uint4(S::pack2(pr[0], pr[1]), S::pack2(pr[2], pr[3]),
                                  S::pack2(pr[4], pr[5]), S::pack2(pr[6], pr[7]));
+            // the column sums of the weights, on the matrix cores: an all-ones A operand
+            // puts sum_k P[k][n] in every row of column n (the same rounded weights the
+            // value product uses)
+            lacc[cb] = S::mfma_k32(ones, pop[cb], lacc[cb]);
         }
 #pragma unroll
         for (int e = 0; e < DB; ++e)
@@ -353,10 +360,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // normalise and write: lane (n, c) holds elements 16 e + 4 c + rr of row n
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
-        const pair_f r16 = swap16(l[cb]);
-        float lt = r16.a + r16.b;
-        const pair_f r32 = swap32(lt);
-        lt = r32.a + r32.b;
+        const float lt = lacc[cb][0];
         const int r = row_base + cb * 16 + n;
         if (r >= rows) continue;
         const int t = tok[cb];
