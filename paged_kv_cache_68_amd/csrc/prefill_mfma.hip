@@ -20,11 +20,13 @@
 //  * values  O^T[16 d][16 rows]   += V^T . P^T   (16x16x32 MFMA over the stage's 32 keys)
 //    the P^T operand is the score tile's own register layout (key slot 8c + j of the
 //    product is key 4c + j of the first 16 and 16 + 4c + j - 4 of the second), and the
-//    V^T operand takes the same slots from eight 16-byte LDS reads per lane;
+//    V^T operand takes the same slots from LDS transpose reads (ds_read_b64_tr_b16);
 //  * online softmax per column (base 2) with a lazy rescale: the running maximum is
 //    raised only when a score passes it by more than 2^8, so the weights stay below 256
-//    and the accumulator is rescaled rarely; a stage that lies wholly before every row of
-//    a column block needs no causal mask.
+//    and the accumulator is rescaled rarely; each lane checks its own scores and the
+//    column maximum is formed only then; the weight sums come from one more MFMA with an
+//    all-ones operand; a stage that lies wholly before every row of a wave needs no
+//    causal mask.
 // Keys past the sequence's length (and table entries outside the pool) are staged as
 // zeros, so masked weights never meet stale memory.
 
