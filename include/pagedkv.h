@@ -224,6 +224,27 @@ kv_status_t paged_attention_decode(const kv_pool_t* pool, int32_t layer, void* o
                                    int32_t partition_size, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
+/* One decode step with the cache write folded in: new_key[b] and new_value[b]
+ * ([batch][num_kv_heads][head_dim], io dtype, 16-byte aligned) are the key and value of
+ * the token at position context_lens[b] - 1 of sequence b; each is written (rounded to
+ * E4M3 for an FP8 pool) into the slot that position has through the table, block
+ * table[b][(L-1) / B], offset (L-1) mod B, and then attention runs as in
+ * paged_attention_decode.  This is reshape_and_cache with slot_mapping[b] taken from the
+ * table, followed by paged_attention_decode, in fewer launches: the matrix-core kernel
+ * writes each new row from the wave that then reads it ("Why AI servers waste memory,
+ * and how paging fixes it", "The real implementation": the append writes slot `offset`
+ * of the last block, then the token is read through the table).  A sequence of length 0,
+ * or whose table entry for position L - 1 names no block of the pool, writes nothing.
+ * Same arguments, results and errors as paged_attention_decode otherwise; the pool's
+ * bytes after the call equal those after reshape_and_cache with that slot mapping. */
+kv_status_t paged_attention_decode_append(const kv_pool_t* pool, int32_t layer, void* out,
+                                          const void* query, const void* new_key,
+                                          const void* new_value, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t batch, int32_t num_q_heads, float scale,
+                                          int32_t partition_size, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
+
 /* The two phases of paged_attention_decode, for callers that time or schedule them
  * separately; same arguments.  paged_attention_partitions writes the final output of
  * every sequence whose partitions it could combine by itself and partial results for
@@ -236,6 +257,16 @@ kv_status_t paged_attention_partitions(const kv_pool_t* pool, int32_t layer, voi
                                        int32_t batch, int32_t num_q_heads, float scale,
                                        int32_t partition_size, void* workspace,
                                        size_t workspace_bytes, hipStream_t stream);
+/* The first phase of paged_attention_decode_append (write the new tokens, partitions);
+ * paged_attention_reduce is its second phase. */
+kv_status_t paged_attention_partitions_append(const kv_pool_t* pool, int32_t layer, void* out,
+                                              const void* query, const void* new_key,
+                                              const void* new_value, const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq,
+                                              const int32_t* context_lens, int32_t batch,
+                                              int32_t num_q_heads, float scale,
+                                              int32_t partition_size, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream);
 kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* out,
                                    const void* query, const int32_t* block_tables,
                                    int32_t max_blocks_per_seq, const int32_t* context_lens,

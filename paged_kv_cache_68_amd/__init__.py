@@ -23,7 +23,7 @@ __all__ = [
     "paged_attention_workspace_bytes", "paged_attention_decode", "paged_attention_partitions",
     "paged_attention_reduce", "kv_pool_gather", "make_desc", "PagedKVError",
     "BlockManager", "OutOfBlocks", "copy_blocks", "paged_attention_prefill", "PrefixCache",
-    "hash_block", "swap_blocks",
+    "hash_block", "swap_blocks", "paged_attention_decode_append", "paged_attention_partitions_append",
 ]
 
 BLOCK_SIZE = 16
@@ -225,6 +225,39 @@ def paged_attention_decode(pool: KVPool, layer: int, out, query, block_tables, c
     _decode_call("paged_attention_decode", pool, layer, out, query, block_tables, context_lens,
                  scale, partition_size, workspace, stream)
     return out
+
+
+def _append_call(fn_name, pool, layer, out, query, new_key, new_value, block_tables,
+                 context_lens, scale, partition_size, workspace, stream):
+    batch, hq, d = (int(x) for x in query.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None and fn_name == "paged_attention_decode_append":
+        workspace = alloc_workspace(pool, batch, hq, block_tables.shape[1], partition_size)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(getattr(lib(), fn_name)(pool.handle, int(layer), _ptr(out), _ptr(query), _ptr(new_key),
+                                  _ptr(new_value), _ptr(block_tables), int(block_tables.shape[1]),
+                                  _ptr(context_lens), batch, hq, float(scale), int(partition_size),
+                                  _ptr(workspace), ws_bytes, _stream(stream)),
+          fn_name)
+
+
+def paged_attention_decode_append(pool: KVPool, layer: int, out, query, new_key, new_value,
+                                  block_tables, context_lens, scale=None, partition_size=0,
+                                  workspace=None, stream=None):
+    """Write new_key[b] / new_value[b] ([B, Hkv, D]) at position context_lens[b] - 1 of
+    each sequence (slot through its table), then decode: reshape_and_cache + decode in
+    fewer launches."""
+    _append_call("paged_attention_decode_append", pool, layer, out, query, new_key, new_value,
+                 block_tables, context_lens, scale, partition_size, workspace, stream)
+    return out
+
+
+def paged_attention_partitions_append(pool, layer, out, query, new_key, new_value, block_tables,
+                                      context_lens, scale=None, partition_size=0, workspace=None,
+                                      stream=None):
+    _append_call("paged_attention_partitions_append", pool, layer, out, query, new_key, new_value,
+                 block_tables, context_lens, scale, partition_size, workspace, stream)
 
 
 def paged_attention_partitions(pool, layer, out, query, block_tables, context_lens, scale=None,

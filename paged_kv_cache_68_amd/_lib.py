@@ -63,6 +63,7 @@ _i64 = ctypes.c_int64
 _pi32 = ctypes.POINTER(ctypes.c_int32)
 
 _DECODE_ARGS = [_pool, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _sz, _vp]
+_APPEND_ARGS = [_pool, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _vp, _sz, _vp]
 
 SIGNATURES = {
     "kv_status_string": (ctypes.c_char_p, [_i32]),
@@ -75,6 +76,8 @@ SIGNATURES = {
     "reshape_and_cache": (_i32, [_pool, _i32, _vp, _vp, _vp, _i32, _vp]),
     "paged_attention_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "paged_attention_decode": (_i32, _DECODE_ARGS),
+    "paged_attention_decode_append": (_i32, _APPEND_ARGS),
+    "paged_attention_partitions_append": (_i32, _APPEND_ARGS),
     "paged_attention_partitions": (_i32, _DECODE_ARGS),
     "paged_attention_reduce": (_i32, _DECODE_ARGS),
     "kv_pool_gather": (_i32, [_pool, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),

@@ -127,6 +127,8 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     a.tables = block_tables;
     a.lens = context_lens;
     a.out = static_cast<uint16_t*>(out);
+    a.new_k = nullptr;
+    a.new_v = nullptr;
     const size_t n = static_cast<size_t>(batch) * num_q_heads * s.num_parts;
     a.ws_acc = static_cast<float*>(workspace);
     a.ws_ml = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
@@ -239,7 +241,8 @@ kv_status_t decode_impl(int phases, const kv_pool_t* pool, int32_t layer, void* 
                         const void* query, const int32_t* block_tables, int32_t max_blocks,
                         const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                         float scale, int32_t partition_size, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+                        size_t workspace_bytes, hipStream_t stream,
+                        const void* new_key = nullptr, const void* new_value = nullptr) {
     DecodeShape s;
     kv_status_t st = check_decode(pool, layer, out, query, block_tables, max_blocks, context_lens,
                                   batch, num_q_heads, scale, partition_size, workspace,
@@ -250,8 +253,10 @@ kv_status_t decode_impl(int phases, const kv_pool_t* pool, int32_t layer, void* 
         st = check_tables_on_device(pool, block_tables, max_blocks, context_lens, batch, stream);
         if (st != KV_OK) return st;
     }
-    const pkv::DecodeArgs a = make_args(pool, layer, out, query, block_tables, max_blocks,
-                                        context_lens, batch, num_q_heads, scale, workspace, s);
+    pkv::DecodeArgs a = make_args(pool, layer, out, query, block_tables, max_blocks,
+                                  context_lens, batch, num_q_heads, scale, workspace, s);
+    a.new_k = static_cast<const uint16_t*>(new_key);
+    a.new_v = static_cast<const uint16_t*>(new_value);
     if (phases & kPartitions) {
         if (pkv::launch_partitions(pool->desc.dtype, io_dtype(pool->desc), pool->desc.head_dim,
                                    s.group, a, stream) !=
@@ -569,6 +574,35 @@ kv_status_t paged_attention_prefill(const kv_pool_t* pool, int32_t layer, void* 
     return pkv::launch_prefill(d.dtype, io_dtype(d), d.head_dim, pa, stream) == hipSuccess
                ? KV_OK
                : KV_ERR_HIP;
+}
+
+kv_status_t paged_attention_decode_append(const kv_pool_t* pool, int32_t layer, void* out,
+                                          const void* query, const void* new_key,
+                                          const void* new_value, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t batch, int32_t num_q_heads, float scale,
+                                          int32_t partition_size, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+    if (batch > 0 && (!new_key || !new_value || !aligned(new_key) || !aligned(new_value)))
+        return KV_ERR_INVALID_ARG;
+    return decode_impl(kBoth, pool, layer, out, query, block_tables, max_blocks_per_seq,
+                       context_lens, batch, num_q_heads, scale, partition_size, workspace,
+                       workspace_bytes, stream, new_key, new_value);
+}
+
+kv_status_t paged_attention_partitions_append(const kv_pool_t* pool, int32_t layer, void* out,
+                                              const void* query, const void* new_key,
+                                              const void* new_value, const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq,
+                                              const int32_t* context_lens, int32_t batch,
+                                              int32_t num_q_heads, float scale,
+                                              int32_t partition_size, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream) {
+    if (batch > 0 && (!new_key || !new_value || !aligned(new_key) || !aligned(new_value)))
+        return KV_ERR_INVALID_ARG;
+    return decode_impl(kPartitions, pool, layer, out, query, block_tables, max_blocks_per_seq,
+                       context_lens, batch, num_q_heads, scale, partition_size, workspace,
+                       workspace_bytes, stream, new_key, new_value);
 }
 
 kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* out,

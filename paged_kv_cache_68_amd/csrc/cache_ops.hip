@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
+#include "partition_common.h"
 
 namespace pkv {
 namespace {
@@ -65,6 +66,35 @@ __global__ __launch_bounds__(256) void rc_quantize(const uint4* __restrict__ key
     for (int32_t ch = threadIdx.x; ch < row_chunks; ch += blockDim.x) {
         kd[ch] = to_fp8x8<S>(ks[ch]);
         vd[ch] = to_fp8x8<S>(vs[ch]);
+    }
+}
+
+// The new token of sequence b (position L - 1) into the slot its table gives it, all KV
+// heads: one work-group per sequence, lanes over the row's 32-bit words (two values).
+// A sequence of length 0, or whose table entry names no block of the pool, writes
+// nothing.  FP8 pools take the row rounded to E4M3 as in rc_quantize.
+template <class S, bool KV8>
+__global__ __launch_bounds__(256) void append_kv(DecodeArgs a) {
+    const int b = blockIdx.x;
+    const int L = clamped_length(a, b);
+    if (L == 0) return;
+    const int last = L - 1;
+    const int blk = a.tables[static_cast<size_t>(b) * a.max_blocks + last / a.block_size];
+    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) return;
+    const size_t slot = static_cast<size_t>(blk) * a.block_size + last % a.block_size;
+    const int words = a.row_bytes / (KV8 ? 2 : 4);          // 32-bit words of the input row
+    const uint32_t* ks = reinterpret_cast<const uint32_t*>(a.new_k) + static_cast<size_t>(b) * words;
+    const uint32_t* vs = reinterpret_cast<const uint32_t*>(a.new_v) + static_cast<size_t>(b) * words;
+    uint8_t* kd = const_cast<uint8_t*>(a.k) + slot * a.row_bytes;
+    uint8_t* vd = const_cast<uint8_t*>(a.v) + slot * a.row_bytes;
+    for (int w = threadIdx.x; w < words; w += blockDim.x) {
+        if constexpr (KV8) {
+            reinterpret_cast<uint16_t*>(kd)[w] = static_cast<uint16_t>(fp8x2_from(S::lo(ks[w]), S::hi(ks[w])));
+            reinterpret_cast<uint16_t*>(vd)[w] = static_cast<uint16_t>(fp8x2_from(S::lo(vs[w]), S::hi(vs[w])));
+        } else {
+            reinterpret_cast<uint32_t*>(kd)[w] = ks[w];
+            reinterpret_cast<uint32_t*>(vd)[w] = vs[w];
+        }
     }
 }
 
@@ -163,6 +193,15 @@ __global__ __launch_bounds__(kSwapThreads) void swap_copy(
 }
 
 }  // namespace
+
+hipError_t launch_append_kv(int kv_dtype, int io_dtype, const DecodeArgs& a, hipStream_t stream) {
+    if (a.batch <= 0 || !a.new_k) return hipSuccess;
+    const bool kv8 = kv_dtype == KV_DTYPE_FP8_E4M3;
+    auto kernel = io_dtype == KV_DTYPE_F16 ? (kv8 ? append_kv<F16, true> : append_kv<F16, false>)
+                                           : (kv8 ? append_kv<BF16, true> : append_kv<BF16, false>);
+    hipLaunchKernelGGL(kernel, dim3(a.batch), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
 
 int swap_groups() {
     static const int groups = [] {

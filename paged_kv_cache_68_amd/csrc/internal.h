@@ -39,6 +39,9 @@ struct DecodeArgs {
     const int32_t* tables;   // [B][max_blocks]
     const int32_t* lens;     // [B]
     uint16_t* out;           // [B][Hq][D]
+    const uint16_t* new_k;   // [B][Hkv][D] io type, or null: the token at position L - 1 of
+    const uint16_t* new_v;   // each sequence, written into its slot (found through the
+                             // table) before it is read, in the same launch
     float* ws_acc;           // [B][Hkv][P][G][D]  unnormalised accumulators
     float* ws_ml;            // [B][Hkv][P][G][2]  (running max in log2 units, running sum)
     int32_t batch;
@@ -120,6 +123,9 @@ hipError_t launch_swap_blocks(const char* src, char* dst, const int32_t* pairs, 
                               int32_t num_layers, int32_t src_blocks, int32_t dst_blocks,
                               size_t block_bytes, size_t src_cache_bytes, size_t dst_cache_bytes,
                               hipStream_t stream);
+// the new tokens of a decode step (DecodeArgs::new_k / new_v) into the slots of position
+// L - 1, found through the tables: for kernels that do not write them themselves
+hipError_t launch_append_kv(int kv_dtype, int io_dtype, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(char* base, const int32_t* copies, int32_t num_copies,
                               int32_t num_layers, int32_t num_blocks, int32_t block_size,
                               int32_t row_bytes, size_t cache_bytes, hipStream_t stream);

@@ -377,12 +377,16 @@ hipError_t launch_partitions(int kv_dtype, int io_dtype, int head_dim, int group
                              const DecodeArgs& a, hipStream_t stream) {
     if (kernel_choice(kv_dtype, io_dtype, head_dim, group, a) == 1)
         return launch_partitions_mfma(kv_dtype, io_dtype, head_dim, group, a, stream);
+    // the VALU kernel does not write new tokens itself: a small launch does it first
+    if (a.new_k && launch_append_kv(kv_dtype, io_dtype, a, stream) != hipSuccess) return hipGetLastError();
+    DecodeArgs v = a;
+    v.new_k = v.new_v = nullptr;
     if (kv_dtype == KV_DTYPE_F16) {
-        if (head_dim == 64) return launch_part_g<F16, 64>(group, a, stream);
-        if (head_dim == 128) return launch_part_g<F16, 128>(group, a, stream);
+        if (head_dim == 64) return launch_part_g<F16, 64>(group, v, stream);
+        if (head_dim == 128) return launch_part_g<F16, 128>(group, v, stream);
     } else if (kv_dtype == KV_DTYPE_BF16) {
-        if (head_dim == 64) return launch_part_g<BF16, 64>(group, a, stream);
-        if (head_dim == 128) return launch_part_g<BF16, 128>(group, a, stream);
+        if (head_dim == 64) return launch_part_g<BF16, 64>(group, v, stream);
+        if (head_dim == 128) return launch_part_g<BF16, 128>(group, v, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -169,6 +169,35 @@ __device__ __forceinline__ void walk_pairs3(const DecodeArgs& a, const Item& it,
     }
 }
 
+// The decode step's new token (position L - 1) of KV head kvh into the slot its table
+// entry gives it: written by the wave that reads that tile, before its walk, and waited
+// for, so the wave's own loads of the tile see it (no other wave reads the tile; the
+// L1 of this compute unit holds no copy of it, as nothing read it in this launch).
+template <class S, int D, bool KV8>
+__device__ __forceinline__ void append_token(const DecodeArgs& a, int b, int kvh, int L, int lane) {
+    const int last = L - 1;
+    const int blk = a.tables[static_cast<size_t>(b) * a.max_blocks + last / a.block_size];
+    if (static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) && lane < D / 2) {
+        const size_t slot = static_cast<size_t>(blk) * a.block_size + last % a.block_size;
+        const size_t src = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * (D / 2) + lane;
+        const uint32_t kw = reinterpret_cast<const uint32_t*>(a.new_k)[src];
+        const uint32_t vw = reinterpret_cast<const uint32_t*>(a.new_v)[src];
+        if constexpr (KV8) {
+            const size_t dst = slot * a.row_bytes + kvh * D + 2 * lane;
+            *reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(a.k) + dst) =
+                static_cast<uint16_t>(fp8x2_from(S::lo(kw), S::hi(kw)));
+            *reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(a.v) + dst) =
+                static_cast<uint16_t>(fp8x2_from(S::lo(vw), S::hi(vw)));
+        } else {
+            const size_t dst = slot * a.row_bytes + (kvh * D + 2 * lane) * 2;
+            *reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(a.k) + dst) = kw;
+            *reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(a.v) + dst) = vw;
+        }
+    }
+    // the stores complete before any load below is issued
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <class S, int D, int MODE, bool NT, bool KV8, bool PAIR = false>
 __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, int n_items,
                                                          int per_item, int ppw, int heads) {
@@ -358,6 +387,13 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
             if ((j + 1) % a.part_blocks == 0 || k + 1 == walk.nk) flush(j / a.part_blocks);
         }
     };
+
+    if (a.new_k) {                                   // wave-uniform
+        const int jl = (it.L - 1) / a.tile_tokens;   // the tile holding position L - 1
+        bool mine = it.L > 0 && jl >= it.j0 && jl < it.j1;
+        if constexpr (SPLIT) mine = mine && (jl - it.j0) % W == wave;
+        if (mine) append_token<S, D, KV8>(a, it.b, it.kvh, it.L, lane);
+    }
 
     // three register sets for every head size: with d = 64 a block's loads are small and
     // a wave's walk is latency-bound, so the third set pays (Qwen serving batch of 256:
