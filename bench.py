@@ -216,8 +216,8 @@ SWAP_WORKLOADS = {
     "llama3_8b_swap_2407_tokens": {"layers": 32, "dev_blocks": 4096, "host_blocks": 1024,
                                    "tokens": 2407},
 }
-PEAK_HOST_LINK_GBPS = 64.0
-LLC_BYTES = 256 << 20          # MI355X Infinity Cache     # PCIe 5.0 x16, one direction (MI355X host interface)
+PEAK_HOST_LINK_GBPS = 64.0     # PCIe 5.0 x16, one direction (MI355X host interface)
+LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 
 
 def bench_swap(args, name):
@@ -434,6 +434,9 @@ def main(argv=None):
                     help="time the copy-on-write block copy on this workload instead")
     ap.add_argument("--swap", choices=sorted(SWAP_WORKLOADS),
                     help="time swap-out and swap-in block copies on this workload instead")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="launch reshape_and_cache on its own instead of folding the cache "
+                         "write into the partition kernel")
     ap.add_argument("--cold", action="store_true",
                     help="also time each step after evicting the last-level cache (done by "
                          "default when the step's working set fits in it)")
@@ -497,13 +500,31 @@ def main(argv=None):
     nbytes = algorithmic_bytes(case.lengths, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
                                cfg.elem_bytes, 2, cfg.block_size)
     stream = torch.cuda.current_stream()
+    # Every workload writes each sequence's new token at position L - 1, so the cache write
+    # can ride in the partition kernel (paged_attention_partitions_append); check that the
+    # slot mapping is exactly that, else (or with --separate-write) launch it on its own.
+    B = cfg.block_size
+    table_slots = np.array([case.block_tables[b, (L - 1) // B] * B + (L - 1) % B if L > 0 else -1
+                            for b, L in enumerate(case.lengths)], dtype=np.int64)
+    fused = not args.separate_write and np.array_equal(table_slots, case.slot_mapping.astype(np.int64))
+    if fused:
+        # no slot index is read: the table entry the kernel reads anyway names the slot
+        nbytes["write"] -= 8 * cfg.batch
+        nbytes["step"] -= 8 * cfg.batch
+        nbytes["partition_kernel"] += nbytes["write"]
 
     def step(ev_a=None, ev_b=None):
-        pk.reshape_and_cache(dc.pool, 0, dc.new_key, dc.new_value, dc.slots, stream)
+        if not fused:
+            pk.reshape_and_cache(dc.pool, 0, dc.new_key, dc.new_value, dc.slots, stream)
         if ev_a is not None:
             ev_a.record(stream)
-        pk.paged_attention_partitions(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
-                                      cfg.partition_size, dc.workspace, stream)
+        if fused:
+            pk.paged_attention_partitions_append(dc.pool, 0, dc.out, dc.query, dc.new_key, dc.new_value,
+                                                 dc.tables, dc.lens, cfg.scale, cfg.partition_size,
+                                                 dc.workspace, stream)
+        else:
+            pk.paged_attention_partitions(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
+                                          cfg.partition_size, dc.workspace, stream)
         if ev_b is not None:
             ev_b.record(stream)
         pk.paged_attention_reduce(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
@@ -550,7 +571,8 @@ def main(argv=None):
             "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
             "block_size": cfg.block_size, "pool_blocks": cfg.num_blocks,
             "partition_size": cfg.partition_size, "accumulate": "f32",
-            "step": "reshape_and_cache + paged_attention (partitions + reduce)",
+            "step": ("paged_attention_partitions_append (cache write folded in) + reduce" if fused
+                     else "reshape_and_cache + paged_attention (partitions + reduce)"),
         },
         "step_hbm_gbps": nbytes["step"] / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": nbytes["step"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
@@ -577,12 +599,7 @@ def main(argv=None):
         for i in range(args.steps):
             flush.fill_(i & 0xFF)
             ev[i][0].record(stream)
-            pk.reshape_and_cache(dc.pool, 0, dc.new_key, dc.new_value, dc.slots, stream)
-            pk.paged_attention_partitions(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
-                                          cfg.partition_size, dc.workspace, stream)
-            ev[i][1].record(stream)
-            pk.paged_attention_reduce(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
-                                      cfg.partition_size, dc.workspace, stream)
+            step()
             ev[i][2].record(stream)
         torch.cuda.synchronize()
         step_us = float(np.median([e[0].elapsed_time(e[2]) for e in ev])) * 1e3
