@@ -11,13 +11,15 @@
 // Mapping.  The (token, query head) pairs of one (sequence, KV head) form n * G rows,
 // head fastest; rows share the KV head's keys and values.  A work-group of W waves owns
 // 32 W consecutive rows, each wave two column blocks of 16 rows, and walks the keys
-// from position 0 to its last row's position in stages of 32 keys:
+// from position 0 to its last row's position in stages of 64 keys (one barrier per
+// stage; fewer barriers keep the waves from falling into step with each other), each
+// computed as two runs of 32:
 //  * the work-group's threads fetch a stage's keys and values through the block table
 //    (one 16-byte LDS chunk of 8 values per thread and tensor at a time; E4M3 codes are
 //    widened here, once per work-group) into one of two LDS buffers, while the waves
 //    compute on the other;
-//  * scores  S^T[16 keys][16 rows] = K . Q^T     (16x16x32 MFMA, two per stage and k-chunk)
-//  * values  O^T[16 d][16 rows]   += V^T . P^T   (16x16x32 MFMA over the stage's 32 keys)
+//  * scores  S^T[16 keys][16 rows] = K . Q^T     (16x16x32 MFMA, two per run and k-chunk)
+//  * values  O^T[16 d][16 rows]   += V^T . P^T   (16x16x32 MFMA over the run's 32 keys)
 //    the P^T operand is the score tile's own register layout (key slot 8c + j of the
 //    product is key 4c + j of the first 16 and 16 + 4c + j - 4 of the second), and the
 //    V^T operand takes the same slots from LDS transpose reads (ds_read_b64_tr_b16);
@@ -25,7 +27,7 @@
 //    raised only when a score passes it by more than 2^8, so the weights stay below 256
 //    and the accumulator is rescaled rarely; each lane checks its own scores and the
 //    column maximum is formed only then; the weight sums come from one more MFMA with an
-//    all-ones operand; a stage that lies wholly before every row of a wave needs no
+//    all-ones operand; a run that lies wholly before every row of a wave needs no
 //    causal mask.
 // Keys past the sequence's length (and table entries outside the pool) are staged as
 // zeros, so masked weights never meet stale memory.
@@ -62,14 +64,15 @@ __device__ __forceinline__ pair_f swap32(float x) {
     return {__builtin_bit_cast(float, static_cast<uint32_t>(r[0])), __builtin_bit_cast(float, static_cast<uint32_t>(r[1]))};
 }
 
-constexpr int kPfKeys = 32;         // keys per LDS stage
 constexpr int kPfRowsPerWave = 32;  // two 16-row column blocks
+
+constexpr int kPfRuns = 2;          // 32-key runs per LDS stage (one barrier per stage)
 
 template <class S, int D, int W, bool KV8>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void pa_prefill_mfma(PrefillArgs pa) {
     const DecodeArgs& a = pa.a;
     constexpr int NC = 2;
-    constexpr int KT = kPfKeys;
+    constexpr int KT = 32 * kPfRuns;             // keys per LDS stage
     constexpr int NQK = D / 32;                  // k-chunks of the score product
     constexpr int DB = D / 16;                   // 16-row d-blocks of the value product
     // LDS bytes per staged key row: the padding spreads the rows over the banks for the
@@ -244,8 +247,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     };
 
-    // ---- one stage of 32 keys for this wave.  Both column blocks always run: a block
-    // whose rows all precede the stage gets only masked scores, zero weights and no
+    // ---- one run of 32 keys for this wave.  Both column blocks always run: a block
+    // whose rows all precede the run gets only masked scores, zero weights and no
     // change, and the straight-line code lets the LDS reads run ahead of the products.
     // V^T operands come from LDS transpose reads: in each 16-lane group, source lane s
     // reads 4 values of key slot s / 4 at d offset 4 (s % 4), and lane n receives the
@@ -258,10 +261,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const pair_f t = swap32(x);
         return __builtin_fmaxf(t.a, t.b);
     };
-    auto compute = [&](int j, int buf) {
-        const int tpos = j * KT;
-        const uint8_t* kl = lds_k[buf];
-        const uint8_t* vl = lds_v[buf];
+    auto compute_half = [&](int tpos, const uint8_t* kl, const uint8_t* vl) {
         uint4 kop[2][NQK];
 #pragma unroll
         for (int st = 0; st < 2; ++st)
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sv[4 * st + r] = sc[cb][st][r];
-            if (first[cb] < tpos + KT - 1) {                 // wave-uniform: some key after a row
+            if (first[cb] < tpos + 31) {                     // wave-uniform: some key after a row
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const int key = (k < 4) ? 4 * c + k : 16 + 4 * c + (k - 4);
@@ -340,6 +340,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int e = 0; e < DB; ++e)
 #pragma unroll
             for (int cb = 0; cb < NC; ++cb) acc[cb][e] = S::mfma_k32(vop[e], pop[cb], acc[cb][e]);
+    };
+    // one stage: its 32-key runs in turn, up to this wave's last position
+    auto compute = [&](int j, int buf) {
+#pragma unroll
+        for (int h = 0; h < kPfRuns; ++h) {
+            const int tpos = j * KT + 32 * h;
+            if (h > 0 && tpos > wave_last) break;           // wave-uniform
+            compute_half(tpos, lds_k[buf] + 32 * h * ROWB_K, lds_v[buf] + 32 * h * ROWB_V);
+        }
     };
 
     // ---- pipeline: fetch stage j + 1 while computing stage j
