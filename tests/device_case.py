@@ -76,6 +76,17 @@ class DeviceCase:
         self.write()
         return self.decode()
 
+    def step_append(self):
+        """The step with the cache write folded into the partition kernel (each sequence's
+        new token goes to position L - 1), then the reduce: the launches bench.py times."""
+        pk.paged_attention_partitions_append(self.pool, 0, self.out, self.query, self.new_key,
+                                             self.new_value, self.tables, self.lens,
+                                             self.cfg.scale, self.cfg.partition_size,
+                                             self.workspace)
+        pk.paged_attention_reduce(self.pool, 0, self.out, self.query, self.tables, self.lens,
+                                  self.cfg.scale, self.cfg.partition_size, self.workspace)
+        return self.out
+
     def blocks_of(self, b: int):
         """Host bits of sequence b's blocks (K, V) and the matching relabelled table."""
         L = int(self.case.lengths[b])

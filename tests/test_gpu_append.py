@@ -14,9 +14,10 @@ torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
 import paged_kv_cache_68_amd as pk  # noqa: E402
-from workloads import nan_bits, round_to_bits  # noqa: E402
+from workloads import config_by_name, make_case, nan_bits, round_to_bits  # noqa: E402
 
-from .gpu_helpers import TOL, max_abs_err, to_dev, to_host_bits  # noqa: E402
+from .gpu_helpers import (TOL, DeviceCase, max_abs_err, oracle_for_seqs, to_dev,  # noqa: E402
+                          to_host_bits)
 
 
 def _say(msg):
@@ -126,3 +127,35 @@ def test_append_phases_and_unwritable_entries():
         s = int(slots[bi])
         expect[s // 16, s % 16] = nk[bi]
     assert np.array_equal(written, expect)
+
+
+@pytest.mark.parametrize("cfg_idx,seqs", [
+    (3, [0, 17, 63]),
+    (5, None),
+])
+def test_append_full_size_sampled(cfg_idx, seqs):
+    """The launches the benchmark times (partitions_append + reduce) on the full-size
+    workloads: sampled sequences against the oracle on the bytes the GPU holds, each
+    sampled sequence's new rows bit-equal to its inputs, and the whole output bit-equal to
+    reshape_and_cache + decode run afterwards (which rewrites the same rows)."""
+    cfg = config_by_name(cfg_idx)
+    case = make_case(cfg, where="device")
+    B = cfg.block_size
+    table_slots = np.array([case.block_tables[b, (L - 1) // B] * B + (L - 1) % B
+                            for b, L in enumerate(case.lengths)], dtype=np.int64)
+    assert np.array_equal(table_slots, case.slot_mapping.astype(np.int64))
+    dc = DeviceCase(case)
+    if seqs is None:   # shortest, longest and a spread of the others
+        order = np.argsort(case.lengths)
+        seqs = sorted({int(order[0]), int(order[-1]), *[int(x) for x in order[::64]]})
+    _say(f"append step {cfg.name} (sampled {seqs})")
+    out = to_host_bits(dc.step_append()).copy()
+    for b in seqs:
+        s = int(table_slots[b])
+        assert np.array_equal(to_host_bits(dc.pool.k_cache(0)[s // B, s % B]), case.new_key[b])
+        assert np.array_equal(to_host_bits(dc.pool.v_cache(0)[s // B, s % B]), case.new_value[b])
+    ref = oracle_for_seqs(dc, seqs)
+    err = max_abs_err(out[seqs], ref, cfg.dtype)
+    _say(f"{cfg.name}: max abs err {err:.3e}")
+    assert err <= TOL[cfg.dtype]
+    assert np.array_equal(to_host_bits(dc.step()), out)
