@@ -235,6 +235,10 @@ kv_status_t paged_attention_decode(const kv_pool_t* pool, int32_t layer, void* o
  * and how paging fixes it", "The real implementation": the append writes slot `offset`
  * of the last block, then the token is read through the table).  A sequence of length 0,
  * or whose table entry for position L - 1 names no block of the pool, writes nothing.
+ * The slots of position L - 1 must be pairwise distinct over the batch, as for
+ * reshape_and_cache: a block that several sequences share (before its copy-on-write
+ * copy, kv_copy_blocks) may hold the new token of at most one of them, else the result
+ * is undefined.
  * Same arguments, results and errors as paged_attention_decode otherwise; the pool's
  * bytes after the call equal those after reshape_and_cache with that slot mapping. */
 kv_status_t paged_attention_decode_append(const kv_pool_t* pool, int32_t layer, void* out,
