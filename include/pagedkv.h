@@ -49,7 +49,8 @@
  *    per call) validates on the device first, then waits for the stream and returns
  *    KV_ERR_INVALID_ARG, with nothing written, if a used table entry names no block of
  *    the pool, a length lies outside [0, max_blocks * block_size], a slot is out of
- *    range or repeated (reshape_and_cache), or query offsets are decreasing or a chunk
+ *    range or repeated (reshape_and_cache; for the decode calls that write the new
+ *    tokens, the slots of position L - 1), or query offsets are decreasing or a chunk
  *    exceeds max_query_len (paged_attention_prefill).  It synchronises, so it is for
  *    debugging: it is not meant for graph capture, and on its first use per device it
  *    allocates a small status buffer (and a slot bitmap) that lives until the process

@@ -252,6 +252,15 @@ kv_status_t decode_impl(int phases, const kv_pool_t* pool, int32_t layer, void* 
     if (checked_mode() && (phases & kPartitions)) {
         st = check_tables_on_device(pool, block_tables, max_blocks, context_lens, batch, stream);
         if (st != KV_OK) return st;
+        if (new_key) {
+            const int64_t slots = static_cast<int64_t>(pool->desc.num_blocks) * pool->desc.block_size;
+            st = run_check(slots, stream, [&](uint32_t* status, uint32_t* seen) {
+                return pkv::launch_check_append_slots(block_tables, max_blocks, context_lens, batch,
+                                                      pool->desc.num_blocks, pool->desc.block_size,
+                                                      seen, status, stream);
+            });
+            if (st != KV_OK) return st;
+        }
     }
     pkv::DecodeArgs a = make_args(pool, layer, out, query, block_tables, max_blocks,
                                   context_lens, batch, num_q_heads, scale, workspace, s);

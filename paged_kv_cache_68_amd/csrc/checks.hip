@@ -59,6 +59,26 @@ __global__ __launch_bounds__(256) void check_slots(const int64_t* __restrict__ s
     if (atomicOr(seen + (s >> 5), bit) & bit) atomicOr(status, kDuplicateSlot);
 }
 
+// the decode-with-append slots: position L - 1 of each sequence, through its table; two
+// sequences whose new tokens land in one slot find its bit already set (lengths and
+// block ids are check_tables' part)
+__global__ __launch_bounds__(256) void check_append_slots(const int32_t* __restrict__ tables,
+                                                          int32_t max_blocks,
+                                                          const int32_t* __restrict__ lens,
+                                                          int32_t batch, int32_t num_blocks,
+                                                          int32_t block_size, uint32_t* seen,
+                                                          uint32_t* status) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= batch) return;
+    const int L = lens[b];
+    if (L <= 0 || static_cast<int64_t>(L) > static_cast<int64_t>(max_blocks) * block_size) return;
+    const int blk = tables[static_cast<size_t>(b) * max_blocks + (L - 1) / block_size];
+    if (static_cast<unsigned>(blk) >= static_cast<unsigned>(num_blocks)) return;
+    const int64_t s = static_cast<int64_t>(blk) * block_size + (L - 1) % block_size;
+    const uint32_t bit = 1u << (s & 31);
+    if (atomicOr(seen + (s >> 5), bit) & bit) atomicOr(status, kDuplicateSlot);
+}
+
 __global__ __launch_bounds__(256) void check_query_start(const int32_t* __restrict__ qs, int32_t batch,
                                                          int32_t max_query_len, uint32_t* status) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
@@ -86,6 +106,18 @@ hipError_t launch_check_slots(const int64_t* slots, int32_t n, int64_t num_slots
                        dim3(256), 0, stream, seen, words);
     hipLaunchKernelGGL(check_slots, dim3((n + 255) / 256), dim3(256), 0, stream, slots, n, num_slots,
                        seen, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_check_append_slots(const int32_t* tables, int32_t max_blocks, const int32_t* lens,
+                                     int32_t batch, int32_t num_blocks, int32_t block_size,
+                                     uint32_t* seen, uint32_t* status, hipStream_t stream) {
+    if (batch <= 0) return hipSuccess;
+    const int64_t words = (static_cast<int64_t>(num_blocks) * block_size + 31) / 32;
+    hipLaunchKernelGGL(clear_words, dim3(static_cast<unsigned>(std::min<int64_t>((words + 255) / 256, 4096))),
+                       dim3(256), 0, stream, seen, words);
+    hipLaunchKernelGGL(check_append_slots, dim3((batch + 255) / 256), dim3(256), 0, stream, tables,
+                       max_blocks, lens, batch, num_blocks, block_size, seen, status);
     return hipGetLastError();
 }
 

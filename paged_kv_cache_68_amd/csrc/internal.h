@@ -115,6 +115,10 @@ hipError_t launch_check_tables(const int32_t* tables, int32_t max_blocks, const 
                                uint32_t* status, hipStream_t stream);
 hipError_t launch_check_slots(const int64_t* slots, int32_t n, int64_t num_slots, uint32_t* seen,
                               uint32_t* status, hipStream_t stream);
+// (decode with the cache write folded in) the slots of position L - 1 are distinct
+hipError_t launch_check_append_slots(const int32_t* tables, int32_t max_blocks, const int32_t* lens,
+                                     int32_t batch, int32_t num_blocks, int32_t block_size,
+                                     uint32_t* seen, uint32_t* status, hipStream_t stream);
 hipError_t launch_check_query_start(const int32_t* qs, int32_t batch, int32_t max_query_len,
                                     uint32_t* status, hipStream_t stream);
 hipError_t launch_clear_word(uint32_t* w, hipStream_t stream);

@@ -91,3 +91,33 @@ def test_bad_query_offsets_are_rejected(monkeypatch):
                                        2, tables, lens, scale=1 / math.sqrt(64))
     torch.cuda.synchronize()
     assert bool((out == 3.0).all())
+
+
+def test_append_with_shared_last_slot_is_rejected(monkeypatch):
+    """Two sequences whose position L - 1 falls in the same slot (a shared block before
+    its copy) are rejected by the decode-with-append calls before anything is written;
+    distinct slots pass and give the fast path's bits."""
+    _say("checked mode: decode_append with a shared last slot")
+    pool, lens, tables, q = _setup()
+    key = torch.randn(3, 2, 64, device="cuda").half()
+    val = torch.randn(3, 2, 64, device="cuda").half()
+    ref_pool, _, _, _ = _setup()
+    ref_pool.memory.copy_(pool.memory)
+    out0 = pk.paged_attention_decode_append(ref_pool, 0, torch.empty_like(q), q, key, val, tables, lens)
+    monkeypatch.setenv("PAGEDKV_CHECK", "1")
+    out1 = pk.paged_attention_decode_append(pool, 0, torch.empty_like(q), q, key, val, tables, lens)
+    torch.cuda.synchronize()
+    assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(pool.memory, ref_pool.memory)
+    # sequence 0 (length 5, block 0) and sequence 2 cut to length 5 over the same block 0
+    lens2 = lens.clone()
+    lens2[2] = 5
+    tables2 = tables.clone()
+    tables2[2, 0] = 0
+    before = pool.memory.clone()
+    out = torch.full_like(q, 3.0)
+    with pytest.raises(pk.PagedKVError):
+        pk.paged_attention_decode_append(pool, 0, out, q, key, val, tables2, lens2)
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())
+    assert torch.equal(pool.memory, before)
