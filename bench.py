@@ -333,6 +333,79 @@ PREFILL_WORKLOADS = {
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}     # MI355X dense matrix-core peak
 
 
+# Prefix-cache workloads (host bookkeeping, the kv_pc_* calls): admitting requests whose
+# prompts share a prefix, then decode steps that append one token to each.
+PREFIX_WORKLOADS = {
+    # 64 requests of a 4,103-token prompt whose first 4,096 tokens (256 blocks) are the
+    # same, then 256 decode steps of the 64 (Llama-3-8B-sized pool of 16-token blocks)
+    "shared_prompt_64x4103_256_steps": {"requests": 64, "shared": 4096, "private": 7,
+                                        "steps": 256, "blocks": 40960, "block_size": 16},
+}
+
+
+def bench_prefix_cache(args, name):
+    """Host-side: the library's prefix cache through its Python binding (each call's
+    marshalling included), and the oracle's for context on a smaller share."""
+    import paged_kv_cache_68_amd as pk
+
+    w = PREFIX_WORKLOADS[name]
+    B, R = w["block_size"], w["requests"]
+    rng = np.random.default_rng(11)
+    shared = rng.integers(0, 128000, w["shared"], dtype=np.int32)
+    prompts = [np.concatenate([shared, rng.integers(0, 128000, w["private"], dtype=np.int32)])
+               for _ in range(R)]
+    steps_tokens = rng.integers(0, 128000, (w["steps"], R), dtype=np.int32)
+
+    def run(cache_cls, requests, steps, export):
+        pc = cache_cls(w["blocks"], B)
+        t0 = time.perf_counter()
+        found = []
+        for r in range(requests):
+            f = pc.add_request(r, prompts[r])
+            found.append(f)
+            pc.append(r, prompts[r][f:])
+        t_admit = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        rids = list(range(requests))
+        for s in range(steps):
+            pc.append_step(rids, steps_tokens[s])
+            if export:
+                pc.export(list(range(requests)), -(-(w["shared"] + w["private"] + steps) // B))
+        t_steps = time.perf_counter() - t0
+        return found, t_admit, t_steps
+
+    found, t_admit, t_steps = run(pk.PrefixCache, R, w["steps"], True)
+    assert found[0] == 0 and all(f == w["shared"] for f in found[1:]), found[:4]
+    hashed = w["shared"] + w["private"] + R * w["private"]      # tokens that were hashed or checked
+    result = {
+        "metric": "prefix cache (kv_pc_*): host us per admitted request and per decode step of "
+                  "the batch",
+        "value": t_steps * 1e6 / w["steps"], "unit": "us per decode step (append_step of 64 + export)",
+        "n_gpus": 0, "steps": w["steps"], "warmup": 0, "ms_per_step": t_steps * 1e3 / w["steps"],
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": name, **w},
+        "admit_us_per_request": t_admit * 1e6 / R,
+        "prompt_tokens_per_s_admitted": R * (w["shared"] + w["private"]) / t_admit,
+        "found_tokens": {"first": found[0], "others": found[1]},
+        "roofline": None,
+        "note": "host bookkeeping off the GPU path; each call crosses the Python binding "
+                f"(a few us of marshalling per call); {hashed} distinct prompt tokens",
+    }
+    if not args.no_cpu_baseline:
+        import oracle.prefix_cache as opc
+        sample_steps = 32
+        _, o_admit, o_steps = run(opc.PrefixCache, R, sample_steps, False)
+        result["cpu_baseline"] = {"value": o_steps * 1e6 / sample_steps,
+                                  "unit": "us per decode step (append_step of 64, no export)",
+                                  "admit_us_per_request": o_admit * 1e6 / R, "cores": 1,
+                                  "kind": "oracle", "sample": f"{sample_steps} of {w['steps']} steps"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def bench_prefill(args, name):
     import torch
     import oracle
@@ -432,6 +505,8 @@ def main(argv=None):
                     help="time multi-token (prefill) attention on this workload instead")
     ap.add_argument("--cow", choices=sorted(COW_WORKLOADS),
                     help="time the copy-on-write block copy on this workload instead")
+    ap.add_argument("--prefix-cache", choices=sorted(PREFIX_WORKLOADS), default=None,
+                    help="host prefix-cache workload instead of the decode step")
     ap.add_argument("--swap", choices=sorted(SWAP_WORKLOADS),
                     help="time swap-out and swap-in block copies on this workload instead")
     ap.add_argument("--separate-write", action="store_true",
@@ -452,6 +527,9 @@ def main(argv=None):
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(each GPU would run its own share of sequences independently).", file=sys.stderr)
         return 2
+
+    if args.prefix_cache:          # host bookkeeping only
+        return bench_prefix_cache(args, args.prefix_cache)
 
     import torch
     import paged_kv_cache_68_amd as pk

@@ -459,6 +459,13 @@ kv_status_t kv_pc_add_request(kv_prefix_cache_t* pc, int64_t rid, const int32_t*
  * free queue cannot cover them (nothing changed). */
 kv_status_t kv_pc_append(kv_prefix_cache_t* pc, int64_t rid, const int32_t* tokens, int32_t n,
                          int64_t* slots, int64_t slots_cap);
+/* One decode step: token tokens[i] for request rids[i], i < n, the n requests distinct;
+ * slots[i] receives its slot.  The same as kv_pc_append of one token to each request in
+ * order, in one call, checked as a whole first: KV_ERR_INVALID_ARG for an unknown or
+ * repeated id, KV_ERR_OUT_OF_BLOCKS if the requests whose last block is full need more
+ * blocks than are free; nothing changes then.  n == 0 is a no-op. */
+kv_status_t kv_pc_append_step(kv_prefix_cache_t* pc, const int64_t* rids, const int32_t* tokens,
+                              int32_t n, int64_t* slots);
 kv_status_t kv_pc_free_request(kv_prefix_cache_t* pc, int64_t rid);
 
 /* Views. */

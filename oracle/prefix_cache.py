@@ -162,6 +162,18 @@ class PrefixCache:
                     self.hash[blk] = h
         return slots
 
+    def append_step(self, rids, tokens):
+        """A decode step: token tokens[i] for request rids[i], the requests distinct;
+        appending one token to each in turn, after checking the whole step first (the
+        requests whose last block is full each need a block).  All or nothing."""
+        rids = [int(r) for r in rids]
+        if len(set(rids)) != len(rids) or any(r not in self.lengths for r in rids):
+            raise ValueError("unknown or repeated request")
+        need = sum(1 for r in rids if self.lengths[r] % self.block_size == 0)
+        if need > len(self.free):
+            raise OutOfBlocks(need)
+        return [self.append(r, [t])[0] for r, t in zip(rids, tokens)]
+
     def free_request(self, rid):
         table = self.tables.pop(rid)
         self._release(list(reversed(table)))

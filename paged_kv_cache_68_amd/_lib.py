@@ -104,6 +104,7 @@ SIGNATURES = {
     "kv_pc_destroy": (_i32, [_bm]),
     "kv_pc_add_request": (_i32, [_bm, _i64, _vp, _i32, ctypes.c_uint64, _pi32]),
     "kv_pc_append": (_i32, [_bm, _i64, _vp, _i32, _vp, _i64]),
+    "kv_pc_append_step": (_i32, [_bm, _vp, _vp, _i32, _vp]),
     "kv_pc_free_request": (_i32, [_bm, _i64]),
     "kv_pc_get_length": (_i32, [_bm, _i64, _pi32]),
     "kv_pc_get_table": (_i32, [_bm, _i64, _vp, _i32, _pi32]),

@@ -26,8 +26,10 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <unordered_map>
+#include <unordered_set>
 #include <vector>
 
 #include "pagedkv.h"
@@ -115,7 +117,39 @@ struct kv_prefix_cache {
         ref[b] = 1;
         return b;
     }
+    // the request's next token: its slot; a block that fills up is hashed and cached (if
+    // the hash is new; a failed insertion only leaves the block uncached).  The caller
+    // has checked that a free block is there if one is needed and reserved the vectors.
+    int64_t append_one(Request& r, int32_t token) {
+        const int32_t B = block_size;
+        const int32_t off = r.length % B;
+        if (off == 0) r.table.push_back(take());
+        const int32_t blk = r.table.back();
+        r.partial.push_back(token);
+        ++r.length;
+        if (off + 1 == B) {
+            const bool first = r.length == B;
+            const uint64_t h = chain_hash(r.last_hash, r.partial.data(), B, first, r.salt);
+            r.last_hash = h;
+            r.partial.clear();
+            if (!hashed[blk] && cached.find(h) == cached.end()) {
+                try {
+                    cached.emplace(h, blk);
+                    hash[blk] = h;
+                    hashed[blk] = 1;
+                } catch (...) {
+                }
+            }
+        }
+        return static_cast<int64_t>(blk) * B + off;
+    }
 };
+
+// room for `size` entries, growing the capacity geometrically (appends one block at a
+// time stay amortised O(1)); may throw before anything else changes
+void grow(std::vector<int32_t>& v, size_t size) {
+    if (size > v.capacity()) v.reserve(std::max(size, 2 * v.capacity()));
+}
 
 extern "C" {
 
@@ -192,30 +226,43 @@ kv_status_t kv_pc_append(kv_prefix_cache_t* pc, int64_t rid, const int32_t* toke
     const int64_t want = (static_cast<int64_t>(r.length) + n + B - 1) / B;
     if (want - have > pc->num_free) return KV_ERR_OUT_OF_BLOCKS;
     try {
-        r.table.reserve(static_cast<size_t>(want));
+        grow(r.table, static_cast<size_t>(want));
         r.partial.reserve(static_cast<size_t>(B));
     } catch (...) {
         return KV_ERR_OUT_OF_MEMORY;
     }
-    for (int32_t i = 0; i < n; ++i) {
-        const int32_t off = r.length % B;
-        if (off == 0) r.table.push_back(pc->take());
-        const int32_t blk = r.table.back();
-        slots[i] = static_cast<int64_t>(blk) * B + off;
-        r.partial.push_back(tokens[i]);
-        ++r.length;
-        if (off + 1 == B) {              // the block is full: hash it, cache it if new
-            const bool first = r.length == B;
-            const uint64_t h = chain_hash(r.last_hash, r.partial.data(), B, first, r.salt);
-            r.last_hash = h;
-            r.partial.clear();
-            if (!pc->hashed[blk] && pc->cached.find(h) == pc->cached.end()) {
-                pc->cached.emplace(h, blk);
-                pc->hash[blk] = h;
-                pc->hashed[blk] = 1;
+    for (int32_t i = 0; i < n; ++i) slots[i] = pc->append_one(r, tokens[i]);
+    return KV_OK;
+}
+
+kv_status_t kv_pc_append_step(kv_prefix_cache_t* pc, const int64_t* rids, const int32_t* tokens,
+                              int32_t n, int64_t* slots) {
+    if (!pc || n < 0) return KV_ERR_INVALID_ARG;
+    if (n == 0) return KV_OK;
+    if (!rids || !tokens || !slots) return KV_ERR_INVALID_ARG;
+    const int32_t B = pc->block_size;
+    std::vector<kv_prefix_cache::Request*> rs;
+    int64_t need = 0;
+    try {
+        rs.reserve(static_cast<size_t>(n));
+        std::unordered_set<int64_t> seen;
+        seen.reserve(static_cast<size_t>(n));
+        for (int32_t i = 0; i < n; ++i) {
+            auto it = pc->requests.find(rids[i]);
+            if (it == pc->requests.end() || !seen.insert(rids[i]).second) return KV_ERR_INVALID_ARG;
+            auto& r = it->second;
+            if (r.length % B == 0) {
+                ++need;
+                grow(r.table, r.table.size() + 1);
             }
+            r.partial.reserve(static_cast<size_t>(B));
+            rs.push_back(&r);
         }
+    } catch (...) {
+        return KV_ERR_OUT_OF_MEMORY;
     }
+    if (need > pc->num_free) return KV_ERR_OUT_OF_BLOCKS;
+    for (int32_t i = 0; i < n; ++i) slots[i] = pc->append_one(*rs[i], tokens[i]);
     return KV_OK;
 }
 

@@ -57,6 +57,19 @@ class PrefixCache:
                                   _p(slots), int(t.size)), "kv_pc_append")
         return slots[:t.size]
 
+    def append_step(self, rids, tokens):
+        """One decode step: token tokens[i] for the distinct requests rids[i]; their slots.
+        All or nothing."""
+        r = np.ascontiguousarray(np.asarray(rids, dtype=np.int64))
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        if r.shape != t.shape or r.ndim != 1:
+            raise ValueError("rids and tokens must be 1-D of the same length")
+        slots = np.empty(max(1, r.size), dtype=np.int64)
+        _check(lib().kv_pc_append_step(self.handle, _p(r) if r.size else None,
+                                       _p(t) if t.size else None, int(r.size), _p(slots)),
+               "kv_pc_append_step")
+        return slots[:r.size]
+
     def free_request(self, rid: int) -> None:
         check(lib().kv_pc_free_request(self.handle, int(rid)), "kv_pc_free_request")
 

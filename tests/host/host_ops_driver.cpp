@@ -149,8 +149,27 @@ static void prefix_cache_trace(uint32_t seed) {
     std::set<int64_t> live;
     int64_t next = 0;
     for (int step = 0; step < 2000; ++step) {
-        const int op = rng() % 4;
-        if (op == 0) {
+        const int op = rng() % 5;
+        if (op == 4 && !live.empty()) {       // a decode step over a subset (and a bad one)
+            std::vector<int64_t> rids;
+            for (int64_t r : live)
+                if (rng() % 2) rids.push_back(r);
+            std::vector<int32_t> toks(rids.size());
+            for (auto& t : toks) t = rng() % 20;
+            std::vector<int64_t> slots(rids.size() + 1);
+            const kv_status_t st = kv_pc_append_step(pc, rids.empty() ? nullptr : rids.data(),
+                                                     toks.empty() ? nullptr : toks.data(),
+                                                     (int32_t)rids.size(), slots.data());
+            CHECK(st == KV_OK || st == KV_ERR_OUT_OF_BLOCKS);
+            if (st == KV_OK)
+                for (size_t i = 0; i < rids.size(); ++i) CHECK(slots[i] >= 0 && slots[i] < (int64_t)nb * B);
+            if (!rids.empty()) {
+                rids.push_back(rids[0]);          // repeated id: rejected, nothing changes
+                toks.push_back(0);
+                CHECK(kv_pc_append_step(pc, rids.data(), toks.data(), (int32_t)rids.size(),
+                                        slots.data()) == KV_ERR_INVALID_ARG);
+            }
+        } else if (op == 0) {
             std::vector<int32_t> prompt = stems[rng() % stems.size()];
             const int extra = rng() % (2 * B);
             for (int i = 0; i < extra; ++i) prompt.push_back(rng() % 20);

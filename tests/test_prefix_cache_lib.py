@@ -56,7 +56,24 @@ def test_random_operations_match_the_oracle(seed):
     stems = [[rng.randrange(30) for _ in range(rng.randrange(0, 6 * B))] for _ in range(5)]
     live, nxt = [], 0
     for _ in range(500):
-        op = rng.choice(["add", "append", "append", "free"] if live else ["add"])
+        op = rng.choice(["add", "append", "append", "step", "free"] if live else ["add"])
+        if op == "step":                     # one token for a random subset of the requests
+            rids = rng.sample(live, rng.randrange(1, len(live) + 1))
+            toks = [rng.randrange(30) for _ in rids]
+            try:
+                want = ora.append_step(rids, toks)
+            except OracleOut:
+                want = None
+            if want is None:
+                before = _state(lib_pc, ora, live)[0]
+                with pytest.raises(pk.OutOfBlocks):
+                    lib_pc.append_step(rids, toks)
+                assert _state(lib_pc, ora, live)[0] == before
+            else:
+                assert lib_pc.append_step(rids, toks).tolist() == want
+            a, b = _state(lib_pc, ora, live)
+            assert a == b
+            continue
         if op == "add":
             prompt = rng.choice(stems) + [rng.randrange(30) for _ in range(rng.randrange(0, 2 * B))]
             salt = rng.choice([0, 0, 5])
@@ -107,3 +124,15 @@ def test_export_and_argument_checks():
         pc.free_request(9)                   # unknown
     with pytest.raises(pk.PagedKVError):
         pc.export([3], 1)                    # table longer than the width
+
+
+def test_append_step_argument_checks():
+    pc = pk.PrefixCache(16, 4)
+    pc.add_request(1, [1, 2, 3])
+    pc.add_request(2, [4, 5])
+    assert pc.append_step([], []).tolist() == []
+    for rids in ([1, 1], [1, 7]):
+        with pytest.raises(pk.PagedKVError):
+            pc.append_step(rids, [0] * len(rids))
+    assert pc.length(1) == 0 and pc.length(2) == 0     # nothing was appended
+    assert pc.append_step([2, 1], [9, 8]).tolist() == [0 * 4 + 0, 1 * 4 + 0]

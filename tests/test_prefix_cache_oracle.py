@@ -138,3 +138,34 @@ def test_random_operations_keep_invariants(seed):
         else:
             pc.free_request(live.pop(rng.randrange(len(live))))
         pc.check_invariants()
+
+
+def test_decode_step_equals_one_token_appends_in_order():
+    """append_step is appending one token to each request in turn; a step that needs more
+    blocks than are free, or names a request twice, changes nothing."""
+    import copy
+    rng = random.Random(7)
+    pc = PrefixCache(12, 4)
+    for rid, n in enumerate([4, 6, 3, 8]):       # lengths 4 and 8 end on a full block
+        pc.add_request(rid, [rng.randrange(9) for _ in range(n)])
+        pc.append(rid, [rng.randrange(9) for _ in range(n)])
+    ref = copy.deepcopy(pc)
+    toks = [11, 12, 13, 14]
+    slots = pc.append_step([3, 0, 2, 1], toks)
+    want = [ref.append(r, [t])[0] for r, t in zip([3, 0, 2, 1], toks)]
+    assert slots == want
+    assert pc.tables == ref.tables and pc.lengths == ref.lengths and pc.free == ref.free
+    assert pc.tokens == ref.tokens and pc.cached == ref.cached and pc.ref == ref.ref
+    with pytest.raises(ValueError):
+        pc.append_step([0, 0], [1, 2])
+    with pytest.raises(ValueError):
+        pc.append_step([9], [1])
+    # drain the free list, then a step needing a block fails as a whole
+    while pc.free:
+        pc.append(0, [1] * (4 - pc.lengths[0] % 4))
+    before = copy.deepcopy(pc)
+    need_block = [r for r in pc.lengths if pc.lengths[r] % 4 == 0]
+    assert need_block
+    with pytest.raises(OutOfBlocks):
+        pc.append_step(sorted(pc.lengths), [5] * len(pc.lengths))
+    assert pc.tables == before.tables and pc.lengths == before.lengths and pc.tokens == before.tokens
