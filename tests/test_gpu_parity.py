@@ -336,3 +336,58 @@ def test_streaming_loads_give_identical_bits(group, monkeypatch):
     assert np.array_equal(outs[0], outs[1])
     ref = oracle.paged_decode(q, kp, vp, tables, lens, cfg.scale, 16, "bf16")
     assert max_abs_err(outs[1], ref, "bf16") <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ long contexts
+
+@pytest.mark.parametrize("plan", [{}, {"PAGEDKV_GROUP": "0"}, {"PAGEDKV_SPLIT": "1"}])
+def test_long_context_128k(plan, monkeypatch):
+    """A 131,072-token sequence (256 partitions of 512, more than the in-kernel merge
+    takes, so the reduce combines many chunks) beside 70,001-, 4,095- and 1-token ones;
+    Llama-3-8B heads, bf16, on each launch plan; the folded cache write gives the same
+    bits as the separate one."""
+    for k, v in plan.items():
+        monkeypatch.setenv(k, v)
+    _say(f"long context 128k plan={plan}")
+    hq, hkv, d, B = 32, 8, 128, 16
+    lens = np.array([131072, 70001, 4095, 1], dtype=np.int32)
+    nblk = [-(-int(L) // B) for L in lens]
+    nb = sum(nblk) + 8
+    rng = np.random.default_rng(1280)
+    perm = rng.permutation(nb)
+    W = max(nblk)
+    tables = np.full((len(lens), W), -1, dtype=np.int32)
+    pos = 0
+    for b, m in enumerate(nblk):
+        tables[b, :m] = perm[pos:pos + m]
+        pos += m
+    pool = pk.KVPool(1, nb, hkv, d, "bf16")
+    gen = torch.Generator(device="cuda").manual_seed(1280)
+    for cache in (pool.k_cache(0), pool.v_cache(0)):
+        cache.copy_(torch.randn(cache.shape, generator=gen, device="cuda").to(torch.bfloat16))
+    q = torch.randn(len(lens), hq, d, generator=gen, device="cuda").to(torch.bfloat16)
+    t_d, l_d = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    scale = 1.0 / math.sqrt(d)
+    out = pk.paged_attention_decode(pool, 0, torch.empty_like(q), q, t_d, l_d, scale=scale)
+    torch.cuda.synchronize()
+    got = to_host_bits(out)
+    q_bits = to_host_bits(q)
+    for b in range(len(lens)):
+        ids = torch.from_numpy(tables[b, :nblk[b]].astype(np.int64)).cuda()
+        kb = to_host_bits(pool.k_cache(0).index_select(0, ids))
+        vb = to_host_bits(pool.v_cache(0).index_select(0, ids))
+        ref = oracle.paged_decode_seq(q_bits[b], kb, vb, np.arange(nblk[b]), int(lens[b]), scale, B, "bf16")
+        err = max_abs_err(got[b:b + 1], ref[None], "bf16")
+        _say(f"  seq {b} (L={lens[b]}): max abs err {err:.3e}")
+        assert err <= TOL["bf16"]
+    # the new token of each sequence written by the partition kernel: same bits as the
+    # separate write followed by the decode above (the rows written are the same)
+    nk = torch.randn(len(lens), hkv, d, generator=gen, device="cuda").to(torch.bfloat16)
+    nv = torch.randn(len(lens), hkv, d, generator=gen, device="cuda").to(torch.bfloat16)
+    slots = torch.from_numpy(np.array([tables[b, (L - 1) // B] * B + (L - 1) % B
+                                       for b, L in enumerate(lens)], dtype=np.int64)).cuda()
+    pk.reshape_and_cache(pool, 0, nk, nv, slots)
+    ref_out = pk.paged_attention_decode(pool, 0, torch.empty_like(q), q, t_d, l_d, scale=scale)
+    out2 = pk.paged_attention_decode_append(pool, 0, torch.empty_like(q), q, nk, nv, t_d, l_d, scale=scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(out2), to_host_bits(ref_out))
