@@ -426,11 +426,17 @@ def bench_prefill(args, name):
     for b, m in enumerate(nblk):
         tables[b, :m] = perm[pos:pos + m]
         pos += m
-    pool = pk.KVPool(1, nb, hkv, d, dt)
+    kv = args.kv_dtype or dt
+    pool = pk.KVPool(1, nb, hkv, d, kv, io_dtype=dt if kv == "fp8" else None)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(11)
     for c in (pool.k_cache(0), pool.v_cache(0)):
-        c.copy_(torch.randn(c.shape, generator=gen, device="cuda", dtype=torch.float32).to(tdt))
+        if kv == "fp8":   # E4M3 codes of magnitude 2^-4 .. 2, either sign
+            mag = torch.randint(0x20, 0x41, c.shape, generator=gen, device="cuda", dtype=torch.int32)
+            sign = torch.randint(0, 2, c.shape, generator=gen, device="cuda", dtype=torch.int32) << 7
+            c.copy_((mag | sign).to(torch.uint8))
+        else:
+            c.copy_(torch.randn(c.shape, generator=gen, device="cuda", dtype=torch.float32).to(tdt))
     q = torch.randn((int(qs[-1]), hq, d), generator=gen, device="cuda", dtype=torch.float32).to(tdt)
     out = torch.empty_like(q)
     qs_d = torch.from_numpy(qs).cuda()
@@ -460,8 +466,9 @@ def bench_prefill(args, name):
         "metric": "paged prefill attention: query tokens/s and achieved TFLOP/s (% of MI355X dense matrix-core peak)",
         "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": dt, "data": "synthetic",
-        "config": {"workload": name, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "block_size": 16,
+        "vs_baseline": None, "dtype": dt if kv == dt else f"{kv} kv, {dt} q/out", "data": "synthetic",
+        "config": {"workload": name if kv == dt else f"{name}_{kv}kv", "q_heads": hq, "kv_heads": hkv,
+                   "head_dim": d, "block_size": 16,
                    "chunks": [list(c) for c in w["chunks"]], "query_tokens": tokens},
         "roofline": {"bound": "mfma", "kernel": "pa_prefill_mfma", "achieved": tflops,
                      "peak": PEAK_MFMA_TFLOPS[dt], "unit": "TFLOP/s", "frac": tflops / PEAK_MFMA_TFLOPS[dt],
@@ -478,7 +485,7 @@ def bench_prefill(args, name):
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
-            ref = oracle.paged_prefill_seq(qb[n0 - rows:n0], kb, vb, tables[0], L0, scale, 16, dt)
+            ref = oracle.paged_prefill_seq(qb[n0 - rows:n0], kb, vb, tables[0], L0, scale, 16, kv, q_dtype=dt)
             t_cpu = time.perf_counter() - t0
         got = oracle.to_f64(to_host_bits(out)[n0 - rows:n0], dt)
         result["cpu_baseline"] = {"value": rows / t_cpu, "unit": "tokens/s", "cores": 1, "kind": "oracle",
