@@ -19,7 +19,7 @@ Sources (page title, then the section used):
      place, case 2 allocates p_new, copies the o token vectors already in p, drops
      R[p] by one, repoints the table and writes slot o of p_new).
 
-Readings (listed in DESIGN.md as well):
+Readings:
 * Fork follows P2: one child per call, +1 per block, and the parent keeps running;
   P3's k-way fork is the parent plus k - 1 such forks, which adds k - 1.
 * The copy made on a write into a shared block moves the o = length mod B rows the

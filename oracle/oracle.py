@@ -20,7 +20,7 @@ Sources (page title, then the section / equation / figure used):
      block-wise online-softmax decode, and the cross-block reduction formula),
      section 5 (the copy-on-write copy of the rows a shared block already holds).
 
-Readings where the pages are silent or garbled (each is listed in the design doc):
+Readings where the pages are silent or garbled:
 * GQA: query head h reads KV head h // G with G = Hq / Hkv (contiguous groups).
   The einsum pair in P3 section 4 would mix every query head with every KV head;
   that is taken as a transcription slip.

@@ -21,7 +21,7 @@ Sources (page title, then the section used):
      from the middle of the queue ("touch"); allocating a cached free block evicts its
      hash.
 
-Readings (listed in DESIGN.md as well):
+Readings:
 * Hash: 64-bit FNV-1a (offset basis 0xcbf29ce484222325, prime 0x100000001b3) over the
   little-endian bytes of the previous block's hash (0 before the first block), the
   block's token ids (4 bytes each) and, for the first block only, the 8-byte salt.
