@@ -445,7 +445,12 @@ def bench_prefill(args, name):
     maxq = max(ns)
     stream = torch.cuda.current_stream()
     scale = 1.0 / math.sqrt(d)
-    run = lambda: pk.paged_attention_prefill(pool, 0, out, q, qs_d, maxq, tab_d, lens_d, scale, stream)
+    # the split entry point: the planner splits each row tile's keys over several
+    # work-groups when the launch would leave the GPU idle (then a merge kernel follows)
+    ws = pk.alloc_prefill_workspace(pool, len(lens), hq, int(qs[-1]), maxq, tables.shape[1])
+    splits_used = bool(ws is not None)
+    run = lambda: pk.paged_attention_prefill_split(pool, 0, out, q, qs_d, maxq, tab_d, lens_d, scale,
+                                                   workspace=ws, stream=stream)
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -470,7 +475,9 @@ def bench_prefill(args, name):
         "config": {"workload": name if kv == dt else f"{name}_{kv}kv", "q_heads": hq, "kv_heads": hkv,
                    "head_dim": d, "block_size": 16,
                    "chunks": [list(c) for c in w["chunks"]], "query_tokens": tokens},
-        "roofline": {"bound": "mfma", "kernel": "pa_prefill_mfma", "achieved": tflops,
+        "roofline": {"bound": "mfma",
+                     "kernel": "pa_prefill_mfma + pa_prefill_merge (key range split)" if splits_used
+                     else "pa_prefill_mfma", "achieved": tflops,
                      "peak": PEAK_MFMA_TFLOPS[dt], "unit": "TFLOP/s", "frac": tflops / PEAK_MFMA_TFLOPS[dt],
                      "traffic": None, "algorithmic_flops_per_launch": flops, "avg_launch_us": k_ms * 1e3},
     }

@@ -422,6 +422,33 @@ kv_status_t paged_attention_prefill(const kv_pool_t* pool, int32_t layer, void* 
                                     int32_t batch, int32_t num_q_heads, float scale,
                                     hipStream_t stream);
 
+/* paged_attention_prefill for launches too small to fill the GPU (a single prompt with
+ * few KV heads, say): each row tile's key range is split over up to 8 work-groups, whose
+ * partial results (the per-row running maximum, weight sum and unnormalised weighted sum
+ * of values, in fp32) a second kernel combines with the rule that merges split-context
+ * partitions ("PagedAttention and Virtual Memory Management", section 4, the reduction
+ * across thread blocks).  The split count follows from the arguments below alone; with
+ * one split the call is paged_attention_prefill (same bits, no workspace used).
+ *  num_tokens : rows of query and out (query_start[batch] <= num_tokens); partial
+ *               results of rows past it are not written.
+ *  workspace  : device memory, 256-byte aligned, of at least
+ *               paged_attention_prefill_workspace_bytes(pool, batch, num_q_heads,
+ *               num_tokens, max_query_len, max_blocks_per_seq) bytes (0: none needed);
+ *               contents on entry do not matter; caller-owned, not retained.
+ * Results agree with paged_attention_prefill to rounding (the sums are taken in another
+ * order) and are deterministic.  Errors: as paged_attention_prefill, and
+ * KV_ERR_WORKSPACE for too small a workspace. */
+size_t paged_attention_prefill_workspace_bytes(const kv_pool_t* pool, int32_t batch,
+                                               int32_t num_q_heads, int32_t num_tokens,
+                                               int32_t max_query_len, int32_t max_blocks_per_seq);
+kv_status_t paged_attention_prefill_split(const kv_pool_t* pool, int32_t layer, void* out,
+                                          const void* query, const int32_t* query_start,
+                                          int32_t max_query_len, int32_t num_tokens,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t batch,
+                                          int32_t num_q_heads, float scale, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ prefix cache
  * Host-side automatic prefix caching on a block pool: which physical blocks a new request
  * can reuse because an earlier one computed the same prefix ("PagedAttention: Treating

@@ -24,6 +24,7 @@ __all__ = [
     "paged_attention_reduce", "kv_pool_gather", "make_desc", "PagedKVError",
     "BlockManager", "OutOfBlocks", "copy_blocks", "paged_attention_prefill", "PrefixCache",
     "hash_block", "swap_blocks", "paged_attention_decode_append", "paged_attention_partitions_append",
+    "paged_attention_prefill_split", "prefill_workspace_bytes", "alloc_prefill_workspace",
 ]
 
 BLOCK_SIZE = 16
@@ -284,6 +285,42 @@ def paged_attention_prefill(pool: KVPool, layer: int, out, query, query_start, m
                                         int(block_tables.shape[1]), _ptr(context_lens), batch,
                                         int(query.shape[1]), float(scale), _stream(stream)),
           "paged_attention_prefill")
+
+
+def prefill_workspace_bytes(pool: KVPool, batch, num_q_heads, num_tokens, max_query_len,
+                            max_blocks_per_seq) -> int:
+    """Workspace bytes paged_attention_prefill_split needs for these shapes (0: none)."""
+    return int(lib().paged_attention_prefill_workspace_bytes(pool.handle, int(batch), int(num_q_heads),
+                                                            int(num_tokens), int(max_query_len),
+                                                            int(max_blocks_per_seq)))
+
+
+def alloc_prefill_workspace(pool: KVPool, batch, num_q_heads, num_tokens, max_query_len,
+                            max_blocks_per_seq, device=None):
+    n = prefill_workspace_bytes(pool, batch, num_q_heads, num_tokens, max_query_len, max_blocks_per_seq)
+    if n == 0:
+        return None
+    torch = _torch()
+    return torch.empty(n, dtype=torch.uint8, device=device or pool.memory.device)
+
+
+def paged_attention_prefill_split(pool: KVPool, layer: int, out, query, query_start, max_query_len,
+                                  block_tables, context_lens, scale=None, workspace=None,
+                                  stream=None) -> None:
+    """paged_attention_prefill with each row tile's keys split over several work-groups
+    when the launch is too small to fill the GPU (partial results in ``workspace``)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(pool.head_dim)
+    batch = int(context_lens.shape[0])
+    num_tokens = int(query.shape[0])
+    nbytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    check(lib().paged_attention_prefill_split(pool.handle, int(layer), _ptr(out), _ptr(query),
+                                              _ptr(query_start), int(max_query_len), num_tokens,
+                                              _ptr(block_tables), int(block_tables.shape[1]),
+                                              _ptr(context_lens), batch, int(query.shape[1]),
+                                              float(scale), _ptr(workspace) if workspace is not None else None,
+                                              nbytes, _stream(stream)),
+          "paged_attention_prefill_split")
 
 
 def kv_pool_gather(pool: KVPool, layer: int, block_tables, context_lens, k_out, v_out,

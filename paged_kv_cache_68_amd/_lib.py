@@ -87,6 +87,9 @@ SIGNATURES = {
     "kv_swap_blocks": (_i32, [_pool, _pool, _vp, _i32, _vp]),
     "paged_attention_prefill": (_i32, [_pool, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32,
                                        _f32, _vp]),
+    "paged_attention_prefill_workspace_bytes": (_sz, [_pool, _i32, _i32, _i32, _i32, _i32]),
+    "paged_attention_prefill_split": (_i32, [_pool, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp,
+                                             _i32, _i32, _f32, _vp, _sz, _vp]),
     "kv_bm_create": (_i32, [_i32, _i32, ctypes.POINTER(_bm)]),
     "kv_bm_destroy": (_i32, [_bm]),
     "kv_bm_add_request": (_i32, [_bm, _i64]),

@@ -286,6 +286,123 @@ kv_status_t decode_impl(int phases, const kv_pool_t* pool, int32_t layer, void* 
     return KV_OK;
 }
 
+// The launch shape of a prefill call (host values only): waves per work-group, row tiles
+// per (sequence, KV head) and, for the split entry point, work-groups per row tile.
+struct PrefillPlan {
+    int32_t group = 0;
+    int waves = 4;
+    int64_t row_tiles = 0;
+    int splits = 1;
+};
+
+kv_status_t plan_prefill(const kv_pool_t* pool, int32_t batch, int32_t num_q_heads,
+                         int32_t max_query_len, int32_t max_blocks_per_seq, bool may_split,
+                         PrefillPlan* pl) {
+    const kv_pool_desc_t& d = pool->desc;
+    if (num_q_heads % d.num_kv_heads != 0) return KV_ERR_UNSUPPORTED;
+    pl->group = num_q_heads / d.num_kv_heads;
+    if (pl->group > pkv::kMaxGroup) return KV_ERR_UNSUPPORTED;
+    const int64_t rows = static_cast<int64_t>(max_query_len) * pl->group;
+    pl->waves = pkv::prefill_waves_for(static_cast<int64_t>(batch) * d.num_kv_heads, rows);
+    pl->row_tiles = ceil_div(rows, 32 * pl->waves);
+    pl->splits = 1;
+    if (!may_split || max_query_len == 0 || batch == 0) return KV_OK;
+    // split the key range when the row tiles leave resident work-groups idle: enough
+    // splits to fill them, at most kMaxPrefillSplits, and at least 4 stages of 64 keys each
+    const int64_t wgs = static_cast<int64_t>(batch) * d.num_kv_heads * pl->row_tiles;
+    int64_t resident = pkv::prefill_resident_groups(d.dtype, io_dtype(d), d.head_dim, pl->waves);
+    if (resident <= 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+        resident = cus;
+    }
+    const int64_t max_stages = ceil_div(static_cast<int64_t>(max_blocks_per_seq) * d.block_size, 64);
+    int64_t splits = wgs < resident ? ceil_div(resident, wgs) : 1;
+    splits = std::min<int64_t>({splits, pkv::kMaxPrefillSplits, std::max<int64_t>(1, max_stages / 4)});
+    const char* e = getenv("PAGEDKV_PREFILL_SPLITS");
+    if (e && atoi(e) >= 1) splits = std::min(atoi(e), pkv::kMaxPrefillSplits);
+    pl->splits = static_cast<int>(splits);
+    return KV_OK;
+}
+
+// bytes of the partial results: acc then (m, l), each 256-byte aligned
+size_t prefill_partial_bytes(int32_t num_tokens, int32_t num_q_heads, int32_t head_dim, int splits,
+                             size_t* ml_offset) {
+    const size_t parts = static_cast<size_t>(num_tokens) * num_q_heads * splits;
+    const size_t acc = (parts * head_dim * 4 + 255) & ~size_t(255);
+    if (ml_offset) *ml_offset = acc;
+    return acc + ((parts * 8 + 255) & ~size_t(255));
+}
+
+kv_status_t prefill_impl(const kv_pool_t* pool, int32_t layer, void* out, const void* query,
+                         const int32_t* query_start, int32_t max_query_len, int32_t num_tokens,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                         float scale, bool may_split, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    if (!pool || pool->host) return KV_ERR_INVALID_ARG;
+    const kv_pool_desc_t& d = pool->desc;
+    if (layer < 0 || layer >= d.num_layers || batch < 0 || max_query_len < 0 || num_q_heads < 1)
+        return KV_ERR_INVALID_ARG;
+    if (num_q_heads % d.num_kv_heads != 0) return KV_ERR_UNSUPPORTED;
+    if (num_q_heads / d.num_kv_heads > pkv::kMaxGroup) return KV_ERR_UNSUPPORTED;
+    if (!(scale == scale)) return KV_ERR_INVALID_ARG;
+    if (batch == 0 || max_query_len == 0) return KV_OK;
+    if (max_blocks_per_seq < 1) return KV_ERR_INVALID_ARG;
+    if (!out || !query || !query_start || !block_tables || !context_lens) return KV_ERR_INVALID_ARG;
+    if (!aligned(out) || !aligned(query) || !aligned(query_start, 4) || !aligned(block_tables, 4) ||
+        !aligned(context_lens, 4))
+        return KV_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(max_blocks_per_seq) * d.block_size > INT32_MAX) return KV_ERR_INVALID_ARG;
+    PrefillPlan pl;
+    kv_status_t st = plan_prefill(pool, batch, num_q_heads, max_query_len, max_blocks_per_seq,
+                                  may_split, &pl);
+    if (st != KV_OK) return st;
+    if (pl.row_tiles > INT32_MAX ||
+        static_cast<int64_t>(batch) * d.num_kv_heads * pl.row_tiles * pl.splits > INT32_MAX)
+        return KV_ERR_INVALID_ARG;
+    size_t ml_offset = 0;
+    if (pl.splits > 1) {
+        if (num_tokens < 1) return KV_ERR_INVALID_ARG;
+        if (prefill_partial_bytes(num_tokens, num_q_heads, d.head_dim, pl.splits, &ml_offset) > workspace_bytes)
+            return KV_ERR_WORKSPACE;
+        if (!workspace || !aligned(workspace, 256)) return KV_ERR_INVALID_ARG;
+    }
+    if (checked_mode()) {
+        st = check_tables_on_device(pool, block_tables, max_blocks_per_seq, context_lens, batch, stream);
+        if (st == KV_OK)
+            st = run_check(0, stream, [&](uint32_t* status, uint32_t*) {
+                return pkv::launch_check_query_start(query_start, batch, max_query_len, status, stream);
+            });
+        if (st != KV_OK) return st;
+    }
+    DecodeShape shape;
+    shape.group = pl.group;
+    shape.part_blocks = 1;
+    shape.num_parts = 1;
+    pkv::PrefillArgs pa;
+    pa.a = make_args(pool, layer, out, query, block_tables, max_blocks_per_seq, context_lens,
+                     batch, num_q_heads, scale, nullptr, shape);
+    pa.a.stream_loads = 0;       // keys are re-read by every row tile of a sequence
+    pa.a.streamed = 0;
+    pa.qstart = query_start;
+    pa.group = pl.group;
+    pa.row_tiles = static_cast<int32_t>(pl.row_tiles);
+    pa.waves = pl.waves;
+    pa.buffer_bytes = pool->cache_bytes < (size_t(1) << 31) ? static_cast<int32_t>(pool->cache_bytes) : 0;
+    pa.splits = pl.splits;
+    pa.num_tokens = num_tokens;
+    pa.ws_acc = pl.splits > 1 ? static_cast<float*>(workspace) : nullptr;
+    pa.ws_ml = pl.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_offset) : nullptr;
+    return pkv::launch_prefill(d.dtype, io_dtype(d), d.head_dim, pa, stream) == hipSuccess
+               ? KV_OK
+               : KV_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -537,52 +654,34 @@ kv_status_t paged_attention_prefill(const kv_pool_t* pool, int32_t layer, void* 
                                     int32_t max_blocks_per_seq, const int32_t* context_lens,
                                     int32_t batch, int32_t num_q_heads, float scale,
                                     hipStream_t stream) {
-    if (!pool || pool->host) return KV_ERR_INVALID_ARG;
-    const kv_pool_desc_t& d = pool->desc;
-    if (layer < 0 || layer >= d.num_layers || batch < 0 || max_query_len < 0 || num_q_heads < 1)
-        return KV_ERR_INVALID_ARG;
-    if (num_q_heads % d.num_kv_heads != 0) return KV_ERR_UNSUPPORTED;
-    const int32_t group = num_q_heads / d.num_kv_heads;
-    if (group > pkv::kMaxGroup) return KV_ERR_UNSUPPORTED;
-    if (!(scale == scale)) return KV_ERR_INVALID_ARG;
-    if (batch == 0 || max_query_len == 0) return KV_OK;
-    if (max_blocks_per_seq < 1) return KV_ERR_INVALID_ARG;
-    if (!out || !query || !query_start || !block_tables || !context_lens) return KV_ERR_INVALID_ARG;
-    if (!aligned(out) || !aligned(query) || !aligned(query_start, 4) || !aligned(block_tables, 4) ||
-        !aligned(context_lens, 4))
-        return KV_ERR_INVALID_ARG;
-    if (static_cast<int64_t>(max_blocks_per_seq) * d.block_size > INT32_MAX) return KV_ERR_INVALID_ARG;
-    const int64_t rows = static_cast<int64_t>(max_query_len) * group;
-    const int waves = pkv::prefill_waves_for(static_cast<int64_t>(batch) * d.num_kv_heads, rows);
-    const int64_t row_tiles = ceil_div(rows, 32 * waves);
-    if (row_tiles > INT32_MAX || static_cast<int64_t>(batch) * d.num_kv_heads * row_tiles > INT32_MAX)
-        return KV_ERR_INVALID_ARG;
-    if (checked_mode()) {
-        kv_status_t st = check_tables_on_device(pool, block_tables, max_blocks_per_seq, context_lens,
-                                                batch, stream);
-        if (st == KV_OK)
-            st = run_check(0, stream, [&](uint32_t* status, uint32_t*) {
-                return pkv::launch_check_query_start(query_start, batch, max_query_len, status, stream);
-            });
-        if (st != KV_OK) return st;
-    }
-    DecodeShape shape;
-    shape.group = group;
-    shape.part_blocks = 1;
-    shape.num_parts = 1;
-    pkv::PrefillArgs pa;
-    pa.a = make_args(pool, layer, out, query, block_tables, max_blocks_per_seq, context_lens,
-                     batch, num_q_heads, scale, nullptr, shape);
-    pa.a.stream_loads = 0;       // keys are re-read by every row tile of a sequence
-    pa.a.streamed = 0;
-    pa.qstart = query_start;
-    pa.group = group;
-    pa.row_tiles = static_cast<int32_t>(row_tiles);
-    pa.waves = waves;
-    pa.buffer_bytes = pool->cache_bytes < (size_t(1) << 31) ? static_cast<int32_t>(pool->cache_bytes) : 0;
-    return pkv::launch_prefill(d.dtype, io_dtype(d), d.head_dim, pa, stream) == hipSuccess
-               ? KV_OK
-               : KV_ERR_HIP;
+    return prefill_impl(pool, layer, out, query, query_start, max_query_len, 0, block_tables,
+                        max_blocks_per_seq, context_lens, batch, num_q_heads, scale, false,
+                        nullptr, 0, stream);
+}
+
+size_t paged_attention_prefill_workspace_bytes(const kv_pool_t* pool, int32_t batch,
+                                               int32_t num_q_heads, int32_t num_tokens,
+                                               int32_t max_query_len, int32_t max_blocks_per_seq) {
+    if (!pool || batch < 1 || num_q_heads < 1 || num_tokens < 1 || max_query_len < 1 ||
+        max_blocks_per_seq < 1)
+        return 0;
+    PrefillPlan pl;
+    if (plan_prefill(pool, batch, num_q_heads, max_query_len, max_blocks_per_seq, true, &pl) != KV_OK ||
+        pl.splits <= 1)
+        return 0;
+    return prefill_partial_bytes(num_tokens, num_q_heads, pool->desc.head_dim, pl.splits, nullptr);
+}
+
+kv_status_t paged_attention_prefill_split(const kv_pool_t* pool, int32_t layer, void* out,
+                                          const void* query, const int32_t* query_start,
+                                          int32_t max_query_len, int32_t num_tokens,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t batch,
+                                          int32_t num_q_heads, float scale, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+    return prefill_impl(pool, layer, out, query, query_start, max_query_len, num_tokens,
+                        block_tables, max_blocks_per_seq, context_lens, batch, num_q_heads, scale,
+                        true, workspace, workspace_bytes, stream);
 }
 
 kv_status_t paged_attention_decode_append(const kv_pool_t* pool, int32_t layer, void* out,

@@ -73,6 +73,10 @@ struct PrefillArgs {
     int32_t waves;           // waves per work-group (4 or 8); 32 rows each
     int32_t buffer_bytes;    // > 0: one layer's K (and V) cache spans this many bytes, small
                              // enough for 32-bit buffer offsets; 0: 64-bit addresses
+    int32_t splits;          // work-groups sharing each row tile's key range (1: none)
+    int32_t num_tokens;      // (splits > 1) rows of the query: bounds the partial results
+    float* ws_acc;           // (splits > 1) [num_tokens * num_q_heads][splits][D]
+    float* ws_ml;            // (splits > 1) [num_tokens * num_q_heads][splits][2]: (m, l)
 };
 
 // A call that can touch more K/V bytes than this streams them past the last-level cache
@@ -101,6 +105,9 @@ hipError_t launch_reduce(int io_dtype, int head_dim, const DecodeArgs& a, hipStr
 int prefill_waves_for(int64_t seq_heads, int64_t rows);
 hipError_t launch_prefill(int kv_dtype, int io_dtype, int head_dim, const PrefillArgs& pa,
                           hipStream_t stream);
+// work-groups of a prefill launch with `waves` waves each that the GPU holds at once
+int64_t prefill_resident_groups(int kv_dtype, int io_dtype, int head_dim, int waves);
+constexpr int kMaxPrefillSplits = 8;
 // New tokens' rows ([T][row_elems] in io_dtype) into their slots: a bit copy for a
 // 16-bit pool, E4M3 rounding for an FP8 pool.
 hipError_t launch_reshape_and_cache(const void* key, const void* value, const int64_t* slots,

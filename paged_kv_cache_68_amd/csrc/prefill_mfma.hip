@@ -36,6 +36,7 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "partition_common.h"
@@ -68,7 +69,10 @@ constexpr int kPfRowsPerWave = 32;  // two 16-row column blocks
 
 constexpr int kPfRuns = 2;          // 32-key runs per LDS stage (one barrier per stage)
 
-template <class S, int D, int W, bool KV8>
+// SPLIT: pa.splits work-groups share each row tile's key stages, each taking an equal
+// run of them and writing its rows' unnormalised partial results (acc, m, l) for
+// pa_prefill_merge to combine.
+template <class S, int D, int W, bool KV8, bool SPLIT>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void pa_prefill_mfma(PrefillArgs pa) {
     const DecodeArgs& a = pa.a;
     constexpr int NC = 2;
@@ -99,10 +103,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int c = lane >> 4;
     const int G = pa.group;
 
-    // work-group -> (sequence, KV head, row tile); the heaviest row tiles (latest
+    // work-group -> (sequence, KV head, row tile[, split]); the heaviest row tiles (latest
     // positions, most keys) are numbered first
-    const int rt = pa.row_tiles - 1 - static_cast<int>(blockIdx.x % pa.row_tiles);
-    const int rest = static_cast<int>(blockIdx.x / pa.row_tiles);
+    const int split = SPLIT ? static_cast<int>(blockIdx.x % pa.splits) : 0;
+    const int tile_id = SPLIT ? static_cast<int>(blockIdx.x / pa.splits) : static_cast<int>(blockIdx.x);
+    const int rt = pa.row_tiles - 1 - tile_id % pa.row_tiles;
+    const int rest = tile_id / pa.row_tiles;
     const int kvh = rest % a.num_kv_heads;
     const int b = rest / a.num_kv_heads;
     const int q0 = pa.qstart[b];
@@ -351,21 +357,49 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     };
 
-    // ---- pipeline: fetch stage j + 1 while computing stage j
-    if (nstages > 0) {
-        fetch_table(0);
-        fetch(0);
-        stage_store(0);
-        if (nstages > 1) fetch_table(1);
+    // ---- this work-group's stages [j_lo, j_hi): all of them, or its split's equal run
+    int j_lo = 0, j_hi = nstages;
+    if constexpr (SPLIT) {
+        const int per = (nstages + pa.splits - 1) / pa.splits;
+        j_lo = min(nstages, split * per);
+        j_hi = min(nstages, j_lo + per);
     }
-    for (int j = 0; j < nstages; ++j) {
-        if (j + 1 < nstages) {
+    // ---- pipeline: fetch stage j + 1 while computing stage j
+    if (j_lo < j_hi) {
+        fetch_table(j_lo);
+        fetch(j_lo);
+        stage_store(j_lo & 1);
+        if (j_lo + 1 < j_hi) fetch_table(j_lo + 1);
+    }
+    for (int j = j_lo; j < j_hi; ++j) {
+        if (j + 1 < j_hi) {
             fetch(j + 1);
-            if (j + 2 < nstages) fetch_table(j + 2);
+            if (j + 2 < j_hi) fetch_table(j + 2);
         }
         __syncthreads();                         // stage j is in LDS buffer j & 1
         if (j < wave_stages) compute(j, j & 1);
-        if (j + 1 < nstages) stage_store((j + 1) & 1);   // its last readers passed the barrier
+        if (j + 1 < j_hi) stage_store((j + 1) & 1);      // its last readers passed the barrier
+    }
+
+    if constexpr (SPLIT) {
+        // partial results: lane (n, c) holds elements 16 e + 4 c + rr of row n; (m, l) as
+        // the running maximum (base-2 units, -inf if no key was seen) and weight sum
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
+            const int r = row_base + cb * 16 + n;
+            if (r >= rows) continue;
+            const int t = tok[cb];
+            if (q0 + t >= pa.num_tokens) continue;
+            const int g = r - t * G;
+            const int64_t part = (static_cast<int64_t>(q0 + t) * a.num_q_heads + kvh * G + g) * pa.splits + split;
+            float* dst = pa.ws_acc + part * D + 4 * c;
+#pragma unroll
+            for (int e = 0; e < DB; ++e)
+                *reinterpret_cast<float4*>(dst + 16 * e) =
+                    make_float4(acc[cb][e][0], acc[cb][e][1], acc[cb][e][2], acc[cb][e][3]);
+            if (c == 0) *reinterpret_cast<float2*>(pa.ws_ml + 2 * part) = make_float2(m[cb], lacc[cb][0]);
+        }
+        return;
     }
 
     // normalise and write: lane (n, c) holds elements 16 e + 4 c + rr of row n
@@ -386,18 +420,116 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
 }
 
+// Combines a split launch's partial results: O = sum_s w_s acc_s / sum_s w_s l_s with
+// w_s = 2^(m_s - max m), summed in ascending s (deterministic).  The work-groups mirror
+// the main kernel's row tiles (each tile's rows in groups of 16), so exactly the rows it
+// computed are written; 16 lanes per row, D / 16 elements per lane, all of a row's
+// partial results loaded at once.
+template <class S, int D>
+__global__ __launch_bounds__(256) void pa_prefill_merge(PrefillArgs pa) {
+    constexpr int PER = D / 16;
+    const DecodeArgs& a = pa.a;
+    const int G = pa.group;
+    const int subs = 2 * pa.waves;               // 16-row groups per row tile
+    const int sub = static_cast<int>(blockIdx.x % subs);
+    const int tile_id = static_cast<int>(blockIdx.x / subs);
+    const int rt = pa.row_tiles - 1 - tile_id % pa.row_tiles;
+    const int rest = tile_id / pa.row_tiles;
+    const int kvh = rest % a.num_kv_heads;
+    const int b = rest / a.num_kv_heads;
+    const int q0 = pa.qstart[b];
+    const int rows = (pa.qstart[b + 1] - q0) * G;
+    const int tile_rows = 32 * pa.waves;
+    const int r = rt * tile_rows + sub * 16 + static_cast<int>(threadIdx.x >> 4);
+    if (r >= min(rows, (rt + 1) * tile_rows)) return;
+    const int t = r / G;
+    if (q0 + t >= pa.num_tokens) return;
+    const int g = r - t * G;
+    const int64_t row = static_cast<int64_t>(q0 + t) * a.num_q_heads + kvh * G + g;
+    const int l16 = threadIdx.x & 15;
+    const int S_ = pa.splits;
+    const float2* ml = reinterpret_cast<const float2*>(pa.ws_ml) + row * S_;
+    const float* acc = pa.ws_acc + row * S_ * D + PER * l16;
+    float2 v[kMaxPrefillSplits];
+    float x[kMaxPrefillSplits][PER];
+#pragma unroll
+    for (int s = 0; s < kMaxPrefillSplits; ++s) {
+        if (s < S_) {
+            v[s] = ml[s];
+#pragma unroll
+            for (int e = 0; e < PER; e += 4) {
+                const float4 q = *reinterpret_cast<const float4*>(acc + s * D + e);
+                x[s][e] = q.x;
+                x[s][e + 1] = q.y;
+                x[s][e + 2] = q.z;
+                x[s][e + 3] = q.w;
+            }
+        }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxPrefillSplits; ++s)
+        if (s < S_) M = fmaxf(M, v[s].x);
+    float A[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) A[e] = 0.f;
+    float lsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxPrefillSplits; ++s) {
+        if (s < S_) {
+            const float w = (v[s].x == -INFINITY) ? 0.f : fast_exp2(v[s].x - M);
+            lsum += w * v[s].y;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) A[e] = fmaf(w, x[s][e], A[e]);
+        }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    uint32_t packed[PER / 2];
+#pragma unroll
+    for (int e = 0; e < PER; e += 2) packed[e / 2] = S::pack2(A[e] * inv, A[e + 1] * inv);
+    uint16_t* dst = a.out + row * D + PER * l16;
+    if constexpr (PER == 8) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    } else {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+    }
+}
+
+template <class S, int D, bool KV8, bool SPLIT>
+void launch_main(const PrefillArgs& pa, unsigned grid, hipStream_t stream) {
+    if (pa.waves == 8)
+        hipLaunchKernelGGL((pa_prefill_mfma<S, D, 8, KV8, SPLIT>), dim3(grid), dim3(64 * 8), 0, stream, pa);
+    else
+        hipLaunchKernelGGL((pa_prefill_mfma<S, D, 4, KV8, SPLIT>), dim3(grid), dim3(64 * 4), 0, stream, pa);
+}
+
 template <class S, int D, bool KV8>
 hipError_t launch_prefill_t(const PrefillArgs& pa, hipStream_t stream) {
     const int64_t wgs = static_cast<int64_t>(pa.a.batch) * pa.a.num_kv_heads * pa.row_tiles;
     if (wgs <= 0) return hipSuccess;
-    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-    if (pa.waves == 8)
-        hipLaunchKernelGGL((pa_prefill_mfma<S, D, 8, KV8>), dim3(static_cast<unsigned>(wgs)),
-                           dim3(64 * 8), 0, stream, pa);
-    else
-        hipLaunchKernelGGL((pa_prefill_mfma<S, D, 4, KV8>), dim3(static_cast<unsigned>(wgs)),
-                           dim3(64 * 4), 0, stream, pa);
+    if (wgs * std::max(pa.splits, 2 * pa.waves) > 0x7fffffff) return hipErrorInvalidValue;
+    if (pa.splits > 1) {
+        launch_main<S, D, KV8, true>(pa, static_cast<unsigned>(wgs * pa.splits), stream);
+        hipLaunchKernelGGL((pa_prefill_merge<S, D>), dim3(static_cast<unsigned>(wgs * 2 * pa.waves)),
+                           dim3(256), 0, stream, pa);
+    } else {
+        launch_main<S, D, KV8, false>(pa, static_cast<unsigned>(wgs), stream);
+    }
     return hipGetLastError();
+}
+
+template <class S, int D, bool KV8>
+int64_t resident_groups_t(int waves) {
+    int dev = 0, cus = 0, blocks = 0;
+    const void* k = waves == 8 ? reinterpret_cast<const void*>(&pa_prefill_mfma<S, D, 8, KV8, true>)
+                               : reinterpret_cast<const void*>(&pa_prefill_mfma<S, D, 4, KV8, true>);
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, 64 * waves, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return static_cast<int64_t>(cus) * blocks;
 }
 
 }  // namespace
@@ -412,6 +544,18 @@ int prefill_waves_for(int64_t seq_heads, int64_t rows) {
     if (forced == 4 || forced == 8) return forced;
     const int64_t cus = device_cus() > 0 ? device_cus() : 256;
     return seq_heads * ((rows + 255) / 256) >= 2 * cus ? 8 : 4;
+}
+
+int64_t prefill_resident_groups(int kv_dtype, int io_dtype, int head_dim, int waves) {
+    const bool kv8 = kv_dtype == KV_DTYPE_FP8_E4M3;
+    if (io_dtype == KV_DTYPE_F16) {
+        if (head_dim == 64) return kv8 ? resident_groups_t<F16, 64, true>(waves) : resident_groups_t<F16, 64, false>(waves);
+        if (head_dim == 128) return kv8 ? resident_groups_t<F16, 128, true>(waves) : resident_groups_t<F16, 128, false>(waves);
+    } else if (io_dtype == KV_DTYPE_BF16) {
+        if (head_dim == 64) return kv8 ? resident_groups_t<BF16, 64, true>(waves) : resident_groups_t<BF16, 64, false>(waves);
+        if (head_dim == 128) return kv8 ? resident_groups_t<BF16, 128, true>(waves) : resident_groups_t<BF16, 128, false>(waves);
+    }
+    return 0;
 }
 
 hipError_t launch_prefill(int kv_dtype, int io_dtype, int head_dim, const PrefillArgs& pa,

@@ -203,3 +203,89 @@ def test_both_work_group_shapes(waves, kv, monkeypatch):
     got = _run(16, lens, qs, tables, kp, vp, q, nb, 8, 128, "bf16", kv)
     ref = oracle.paged_prefill(q, qs, kp, vp, tables, lens, 1.0 / math.sqrt(128), 16, kv, q_dtype="bf16")
     _check(got, ref, qs, tables, lens, vp, 16, kv, "bf16", 8)
+
+
+# ------------------------------------------------------------------ key-range splits
+
+def _run_split(B, lens, qs, tables, kp, vp, q, nb, hkv, d, io, kv, seed_out=7.0):
+    pool = pk.KVPool(1, nb, hkv, d, kv, block_size=B, io_dtype=io)
+    pool.k_cache(0).copy_(to_dev(kp, kv))
+    pool.v_cache(0).copy_(to_dev(vp, kv))
+    qd = to_dev(q, io)
+    out = torch.full_like(qd, seed_out)
+    maxq = int(np.max(np.diff(qs))) if len(qs) > 1 else 0
+    ws = pk.alloc_prefill_workspace(pool, len(lens), qd.shape[1], qd.shape[0], maxq, tables.shape[1])
+    if ws is not None:
+        ws.fill_(0xFF)                               # contents on entry must not matter
+    pk.paged_attention_prefill_split(pool, 0, out, qd, torch.from_numpy(qs).cuda(), maxq,
+                                     torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                                     scale=1.0 / math.sqrt(d), workspace=ws)
+    torch.cuda.synchronize()
+    return to_host_bits(out), ws
+
+
+@pytest.mark.parametrize("splits", ["2", "3", "8"])
+@pytest.mark.parametrize("B,hq,hkv,d,io,kv", [
+    (16, 32, 8, 128, "bf16", "bf16"), (16, 14, 2, 64, "f16", "f16"), (8, 32, 8, 128, "bf16", "fp8"),
+    (32, 8, 8, 128, "f16", "f16"),
+])
+def test_split_prefill_matches_oracle(splits, B, hq, hkv, d, io, kv, monkeypatch):
+    """Each row tile's keys split over 2, 3 or 8 work-groups (forced), partial results
+    merged by the second kernel: the oracle's answer, to the prefill bar."""
+    monkeypatch.setenv("PAGEDKV_PREFILL_SPLITS", splits)
+    _say(f"split prefill splits={splits} B={B} hq={hq} hkv={hkv} d={d} io={io} kv={kv}")
+    lens, qs, tables, kp, vp, q, nb = _case(CHUNKS, B, hq, hkv, d, io, kv, seed=900 + B + d)
+    got, ws = _run_split(B, lens, qs, tables, kp, vp, q, nb, hkv, d, io, kv)
+    assert ws is not None
+    ref = oracle.paged_prefill(q, qs, kp, vp, tables, lens, 1.0 / math.sqrt(d), B, kv, q_dtype=io)
+    # rows past max_query_len do not exist here; rows of empty chunks: none
+    _check(got, ref, qs, tables, lens, vp, B, kv, io, hkv)
+
+
+def test_split_of_one_is_the_plain_kernel(monkeypatch):
+    """With one split the split entry point runs the plain kernel: the same bits, and no
+    workspace is asked for."""
+    monkeypatch.setenv("PAGEDKV_PREFILL_SPLITS", "1")
+    _say("split prefill with one split")
+    lens, qs, tables, kp, vp, q, nb = _case(CHUNKS, 16, 32, 8, 128, "bf16", "bf16", seed=77)
+    got, ws = _run_split(16, lens, qs, tables, kp, vp, q, nb, 8, 128, "bf16", "bf16")
+    assert ws is None
+    plain = _run(16, lens, qs, tables, kp, vp, q, nb, 8, 128, "bf16", "bf16")
+    assert np.array_equal(got, plain)
+
+
+def test_split_prompt_of_2407_tokens(monkeypatch):
+    """One 2,407-token prompt with Qwen2.5-0.5B heads (2 KV heads: too few row tiles to fill
+    the GPU, so the planner splits): sampled rows against the oracle, all rows against
+    the plain kernel to the prefill bar, and a workspace one byte short is refused."""
+    monkeypatch.delenv("PAGEDKV_PREFILL_SPLITS", raising=False)
+    _say("split prefill: 2,407-token prompt")
+    B, hq, hkv, d, io = 16, 14, 2, 64, "f16"
+    lens, qs, tables, kp, vp, q, nb = _case([(2407, 2407)], B, hq, hkv, d, io, io, seed=2407)
+    pool = pk.KVPool(1, nb, hkv, d, io, block_size=B)
+    need = pk.prefill_workspace_bytes(pool, 1, hq, 2407, 2407, tables.shape[1])
+    assert need > 0, "the planner should split this launch"
+    got, _ = _run_split(B, lens, qs, tables, kp, vp, q, nb, hkv, d, io, io)
+    plain = _run(B, lens, qs, tables, kp, vp, q, nb, hkv, d, io, io)
+    # sampled rows against the oracle: row r is the last query of a sequence of r + 1 tokens
+    rows = np.array([0, 1, 2, 15, 16, 300, 1200, 2000, 2405, 2406])
+    ref_rows = np.stack([oracle.paged_prefill_seq(q[r:r + 1], kp, vp, tables[0], int(r) + 1,
+                                                  1.0 / math.sqrt(d), B, io)[0] for r in rows])
+    vv = oracle.to_f64(vp, io)
+    vmax = float(np.abs(vv[np.isfinite(vv)]).max())
+    g = oracle.to_f64(got[rows], io)
+    assert np.all(np.abs(g - ref_rows) <= TOL[io] + 2.0 ** -SIG[io] * (np.abs(ref_rows) + vmax))
+    # every row against the plain kernel: both within the bar of the same exact value
+    pb = oracle.to_f64(plain, io)
+    gb = oracle.to_f64(got, io)
+    assert np.all(np.abs(gb - pb) <= 2 * (TOL[io] + 2.0 ** -SIG[io] * (np.abs(pb) + vmax)))
+    # a workspace one byte short is refused before anything is enqueued
+    qd = to_dev(q, io)
+    out = torch.full_like(qd, 7.0)
+    short = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pk.PagedKVError):
+        pk.paged_attention_prefill_split(pool, 0, out, qd, torch.from_numpy(qs).cuda(), 2407,
+                                         torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                                         workspace=short)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
