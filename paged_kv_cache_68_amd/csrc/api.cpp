@@ -318,7 +318,7 @@ kv_status_t plan_prefill(const kv_pool_t* pool, int32_t batch, int32_t num_q_hea
             (void)hipGetLastError();
             cus = 256;
         }
-        resident = cus;
+        resident = 2 * static_cast<int64_t>(cus);     // no occupancy known: two per CU
     }
     const int64_t max_stages = ceil_div(static_cast<int64_t>(max_blocks_per_seq) * d.block_size, 64);
     int64_t splits = wgs < resident ? ceil_div(resident, wgs) : 1;

@@ -225,3 +225,31 @@ def test_prefill_argument_checks():
     assert call(max_blocks=0) == E.KV_ERR_INVALID_ARG
     assert call(scale=float("nan")) == E.KV_ERR_INVALID_ARG
     lib.kv_pool_destroy(h)
+
+
+def test_prefill_split_sizing_and_argument_checks():
+    """The split prefill's workspace size follows from the arguments (no device needed:
+    without one the planner assumes 256 compute units holding two work-groups each); bad
+    arguments and too small a workspace are refused before anything is enqueued."""
+    desc, h = _borrowed_pool(layers=1, nb=256, hkv=2, d=64, dtype="f16")
+    lib = _lib.lib()
+    # one 2,407-token prompt, 14 query heads: too few row tiles for the GPU, so a split
+    need = lib.paged_attention_prefill_workspace_bytes(h, 1, 14, 2407, 2407, 151)
+    assert need > 0 and need % 256 == 0
+    splits = need // ((2407 * 14 * (64 * 4 + 8)))
+    assert 2 <= splits <= 8
+    # nothing to compute, or a bad shape: no workspace
+    assert lib.paged_attention_prefill_workspace_bytes(h, 0, 14, 2407, 2407, 151) == 0
+    assert lib.paged_attention_prefill_workspace_bytes(h, 1, 13, 2407, 2407, 151) == 0
+    assert lib.paged_attention_prefill_workspace_bytes(None, 1, 14, 2407, 2407, 151) == 0
+    # a short prefix of a few tokens: nothing worth splitting (fewer than 8 stages)
+    assert lib.paged_attention_prefill_workspace_bytes(h, 1, 14, 8, 8, 1) == 0
+    args = dict(out=FAKE_BASE, q=FAKE_BASE, qs=FAKE_BASE, tab=FAKE_BASE, lens=FAKE_BASE)
+    call = lambda ws, wsb, nt=2407: lib.paged_attention_prefill_split(
+        h, 0, args["out"], args["q"], args["qs"], 2407, nt, args["tab"], 151, args["lens"], 1, 14,
+        0.125, ws, wsb, None)
+    assert call(FAKE_BASE, need - 1) == _lib.KV_ERR_WORKSPACE
+    assert call(None, need) == _lib.KV_ERR_INVALID_ARG
+    assert call(FAKE_BASE + 16, need) == _lib.KV_ERR_INVALID_ARG     # not 256-byte aligned
+    assert call(FAKE_BASE, need, nt=0) == _lib.KV_ERR_INVALID_ARG
+    assert lib.kv_pool_destroy(h) == _lib.KV_OK
