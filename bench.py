@@ -449,6 +449,8 @@ def bench_prefill(args, name):
     # work-groups when the launch would leave the GPU idle (then a merge kernel follows)
     ws = pk.alloc_prefill_workspace(pool, len(lens), hq, int(qs[-1]), maxq, tables.shape[1])
     splits_used = bool(ws is not None)
+    # work-groups per row tile: the workspace holds (acc, m, l) per row and split
+    splits = 1 if ws is None else int(ws.numel() // (int(qs[-1]) * hq * (4 * d + 8)))
     run = lambda: pk.paged_attention_prefill_split(pool, 0, out, q, qs_d, maxq, tab_d, lens_d, scale,
                                                    workspace=ws, stream=stream)
     for _ in range(args.warmup):
@@ -474,7 +476,8 @@ def bench_prefill(args, name):
         "vs_baseline": None, "dtype": dt if kv == dt else f"{kv} kv, {dt} q/out", "data": "synthetic",
         "config": {"workload": name if kv == dt else f"{name}_{kv}kv", "q_heads": hq, "kv_heads": hkv,
                    "head_dim": d, "block_size": 16,
-                   "chunks": [list(c) for c in w["chunks"]], "query_tokens": tokens},
+                   "chunks": [list(c) for c in w["chunks"]], "query_tokens": tokens,
+                   "key_range_splits": splits},
         "roofline": {"bound": "mfma",
                      "kernel": "pa_prefill_mfma + pa_prefill_merge (key range split)" if splits_used
                      else "pa_prefill_mfma", "achieved": tflops,
