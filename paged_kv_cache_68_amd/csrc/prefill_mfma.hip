@@ -79,10 +79,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int KT = 32 * kPfRuns;             // keys per LDS stage
     constexpr int NQK = D / 32;                  // k-chunks of the score product
     constexpr int DB = D / 16;                   // 16-row d-blocks of the value product
-    // LDS bytes per staged key row: the padding spreads the rows over the banks for the
-    // key reads (16 rows, one 16-byte chunk each) and the value transpose reads (8 rows,
-    // 32 bytes each, per half wave)
-    constexpr int ROWB_K = D * 2 + 16;
+    // LDS bytes per staged key and value row: the padding spreads the rows over the banks
+    // for the key reads (16 rows, one 16-byte chunk each) and the value transpose reads
+    // (8 rows, 32 bytes each, per half wave).  Measured on the kernel's own address
+    // patterns: with 32 bytes both read at the linear rate; 16 bytes cut the key reads to
+    // 58% of it, and unpadded value rows cut the transposing reads to a sixth
+    constexpr int ROWB_K = D * 2 + 32;
     constexpr int ROWB_V = D * 2 + 32;
     constexpr int CPR = D / 8;                   // 16-byte LDS chunks per key row
     constexpr int CHUNKS = KT * CPR;             // chunks per tensor and stage
