@@ -8,7 +8,7 @@ import ctypes
 import numpy as np
 
 from ._lib import check, lib
-from .block_manager import OutOfBlocks, _check
+from .block_manager import _check
 
 __all__ = ["PrefixCache", "hash_block"]
 

@@ -4,7 +4,6 @@ the same bits as the fast path."""
 
 import math
 
-import numpy as np
 import pytest
 
 pytestmark = pytest.mark.gpu

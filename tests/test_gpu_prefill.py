@@ -16,7 +16,7 @@ import oracle  # noqa: E402
 import paged_kv_cache_68_amd as pk  # noqa: E402
 from workloads import nan_bits, round_to_bits  # noqa: E402
 
-from .gpu_helpers import TOL, max_abs_err, to_dev, to_host_bits  # noqa: E402
+from .gpu_helpers import TOL, to_dev, to_host_bits  # noqa: E402
 
 
 def _say(msg):

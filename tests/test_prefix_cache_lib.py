@@ -4,7 +4,6 @@ on the pages' example and on random operations; failing calls change nothing."""
 
 import random
 
-import numpy as np
 import pytest
 
 from oracle.prefix_cache import OutOfBlocks as OracleOut
