@@ -84,10 +84,16 @@ def test_bad_query_offsets_are_rejected(monkeypatch):
     pool, lens, tables, q = _setup()
     monkeypatch.setenv("PAGEDKV_CHECK", "1")
     out = torch.full_like(q, 3.0)
+    monkeypatch.setenv("PAGEDKV_PREFILL_SPLITS", "2")      # the split entry point splits
+    ws = pk.alloc_prefill_workspace(pool, 3, q.shape[1], q.shape[0], 2, tables.shape[1])
+    assert ws is not None
     for qs in ([0, 2, 1, 3], [0, 3, 3, 3]):
+        qs_d = torch.tensor(qs, dtype=torch.int32, device="cuda")
         with pytest.raises(pk.PagedKVError):
-            pk.paged_attention_prefill(pool, 0, out, q, torch.tensor(qs, dtype=torch.int32, device="cuda"),
-                                       2, tables, lens, scale=1 / math.sqrt(64))
+            pk.paged_attention_prefill(pool, 0, out, q, qs_d, 2, tables, lens, scale=1 / math.sqrt(64))
+        with pytest.raises(pk.PagedKVError):
+            pk.paged_attention_prefill_split(pool, 0, out, q, qs_d, 2, tables, lens,
+                                             scale=1 / math.sqrt(64), workspace=ws)
     torch.cuda.synchronize()
     assert bool((out == 3.0).all())
 
