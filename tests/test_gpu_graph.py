@@ -1,0 +1,49 @@
+"""The decode step captured in a HIP graph (torch.cuda.graph): the launches the benchmark
+times -- the partition kernel with the new tokens written in, then the reduce -- enqueue
+no memset and no host synchronisation, so they capture; every replay, with the
+program's own eager work and synchronisations between replays, gives the eager bits."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_cache_68_amd as pk  # noqa: E402
+from workloads import config_by_name, make_case  # noqa: E402
+
+from .gpu_helpers import DeviceCase, to_host_bits  # noqa: E402
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("cfg_idx", [2, 3])
+def test_decode_step_in_a_graph(cfg_idx):
+    cfg = config_by_name(cfg_idx)
+    _say(f"graph capture: {cfg.name}")
+    case = make_case(cfg, where="host" if cfg_idx == 2 else "device", poison=False)
+    dc = DeviceCase(case)
+    eager = to_host_bits(dc.step_append()).copy()
+    pool_after = to_host_bits(dc.pool.k_cache(0)[:64]).copy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                 # warm-up on the capture stream
+        dc.step_append()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dc.step_append()
+    scratch = torch.empty(1 << 20, device="cuda")
+    for rep in range(4):
+        dc.out.fill_(7.0)
+        scratch.normal_()                          # the program's own work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(dc.out), eager), f"replay {rep}"
+        assert np.array_equal(to_host_bits(dc.pool.k_cache(0)[:64]), pool_after)
+    _say(f"  {cfg.name}: 4 replays equal the eager step")
