@@ -526,6 +526,8 @@ def main(argv=None):
                     help="host prefix-cache workload instead of the decode step")
     ap.add_argument("--swap", choices=sorted(SWAP_WORKLOADS),
                     help="time swap-out and swap-in block copies on this workload instead")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the decode step replayed from a HIP graph")
     ap.add_argument("--separate-write", action="store_true",
                     help="launch reshape_and_cache on its own instead of folding the cache "
                          "write into the partition kernel")
@@ -608,22 +610,23 @@ def main(argv=None):
         nbytes["step"] -= 8 * cfg.batch
         nbytes["partition_kernel"] += nbytes["write"]
 
-    def step(ev_a=None, ev_b=None):
+    def step(ev_a=None, ev_b=None, on=None):
+        st = stream if on is None else on
         if not fused:
-            pk.reshape_and_cache(dc.pool, 0, dc.new_key, dc.new_value, dc.slots, stream)
+            pk.reshape_and_cache(dc.pool, 0, dc.new_key, dc.new_value, dc.slots, st)
         if ev_a is not None:
-            ev_a.record(stream)
+            ev_a.record(st)
         if fused:
             pk.paged_attention_partitions_append(dc.pool, 0, dc.out, dc.query, dc.new_key, dc.new_value,
                                                  dc.tables, dc.lens, cfg.scale, cfg.partition_size,
-                                                 dc.workspace, stream)
+                                                 dc.workspace, st)
         else:
             pk.paged_attention_partitions(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
-                                          cfg.partition_size, dc.workspace, stream)
+                                          cfg.partition_size, dc.workspace, st)
         if ev_b is not None:
-            ev_b.record(stream)
+            ev_b.record(st)
         pk.paged_attention_reduce(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
-                                  cfg.partition_size, dc.workspace, stream)
+                                  cfg.partition_size, dc.workspace, st)
 
     for _ in range(args.warmup):
         step()
@@ -683,6 +686,33 @@ def main(argv=None):
             "avg_launch_us": part_ms * 1e3,
         },
     }
+    # --graph: also time the same step captured once in a HIP graph and replayed back to
+    # back (how a serving loop might run short steps; each replay checked against the
+    # eager output)
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(on=side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(on=torch.cuda.current_stream())   # the capture stream
+        ref = dc.out.clone()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        dc.out.fill_(7.0)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        assert torch.equal(dc.out.view(torch.int16), ref.view(torch.int16)), "graph replay differs"
+        result["graph_replay"] = {"us_per_step": g_ms * 1e3, "seqs_per_s": cfg.batch / (g_ms * 1e-3),
+                                  "how": "the step captured in one HIP graph, replayed back to back"}
+        del graph
     # A working set smaller than the 256 MB Infinity Cache is served from it when steps
     # run back to back.  For such workloads also time each step cold: a 512 MiB write
     # between steps evicts the cache, and HIP events bracket the step alone.
