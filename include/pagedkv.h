@@ -427,8 +427,10 @@ kv_status_t paged_attention_prefill(const kv_pool_t* pool, int32_t layer, void* 
  * partial results (the per-row running maximum, weight sum and unnormalised weighted sum
  * of values, in fp32) a second kernel combines with the rule that merges split-context
  * partitions ("PagedAttention and Virtual Memory Management", section 4, the reduction
- * across thread blocks).  The split count follows from the arguments below alone; with
- * one split the call is paged_attention_prefill (same bits, no workspace used).
+ * across thread blocks).  The split count follows from the arguments below and the
+ * current device (its compute units and the kernel's occupancy), so size the workspace
+ * with the same device current; with one split the call is paged_attention_prefill (same
+ * bits, no workspace used).
  *  num_tokens : rows of query and out (query_start[batch] <= num_tokens); partial
  *               results of rows past it are not written.
  *  workspace  : device memory, 256-byte aligned, of at least
