@@ -25,6 +25,7 @@ __all__ = [
     "BlockManager", "OutOfBlocks", "copy_blocks", "paged_attention_prefill", "PrefixCache",
     "hash_block", "swap_blocks", "paged_attention_decode_append", "paged_attention_partitions_append",
     "paged_attention_prefill_split", "prefill_workspace_bytes", "alloc_prefill_workspace",
+    "DecodeStep",
 ]
 
 BLOCK_SIZE = 16
@@ -86,6 +87,65 @@ def _stream(stream) -> int:
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+# ---------------------------------------------------------------- argument checks
+# The C ABI sees only addresses and counts, not buffer sizes, so a tensor of the wrong
+# type, shape or device would make the kernels read or write outside it.  Every entry
+# point below checks its tensors here first and raises ValueError on a mismatch, before
+# anything reaches the library.
+
+def _need(t, name, dtype=None, shape=None, ndim=None, device=None):
+    """Check that ``t`` is a dense tensor on ``device`` (a torch.device; None: any CUDA
+    device) with the given dtype and shape (None entries of ``shape`` match any size)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if device is None:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: expected a GPU tensor, got one on {t.device}")
+    elif t.device != device:
+        raise ValueError(f"{name}: expected a tensor on {device}, got one on {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dimensions, got shape {tuple(t.shape)}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(g) != w for g, w in zip(t.shape, shape)):
+            want = tuple("*" if w is None else w for w in shape)
+            raise ValueError(f"{name}: expected shape {want}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return t
+
+
+def _need_bytes(t, name, device):
+    """A raw device buffer (workspace): any dtype, contiguous, on ``device``."""
+    if t is None:
+        return None
+    return _need(t, name, device=device)
+
+
+def _check_decode_args(pool, out, query, block_tables, context_lens, new_key=None, new_value=None,
+                       workspace=None):
+    """Shapes of a decode call: query / out [B, Hq, D] in the pool's io dtype with D the
+    pool's head size and Hq a multiple of its KV heads; tables int32 [B, max_blocks];
+    lengths int32 [B]; new keys / values [B, Hkv, D]; all on the pool's device."""
+    dev = pool.device
+    _need(query, "query", pool.io_dtype, ndim=3, device=dev)
+    batch, hq, d = (int(x) for x in query.shape)
+    if d != pool.head_dim:
+        raise ValueError(f"query: head size {d} differs from the pool's {pool.head_dim}")
+    if hq < 1 or hq % pool.num_kv_heads:
+        raise ValueError(f"query: {hq} heads is not a multiple of the pool's {pool.num_kv_heads} KV heads")
+    _need(out, "out", pool.io_dtype, (batch, hq, d), device=dev)
+    _need(block_tables, "block_tables", _torch().int32, (batch, None), device=dev)
+    _need(context_lens, "context_lens", _torch().int32, (batch,), device=dev)
+    if new_key is not None or new_value is not None:
+        _need(new_key, "new_key", pool.io_dtype, (batch, pool.num_kv_heads, d), device=dev)
+        _need(new_value, "new_value", pool.io_dtype, (batch, pool.num_kv_heads, d), device=dev)
+    _need_bytes(workspace, "workspace", dev)
+    return batch, hq, int(block_tables.shape[1])
 
 
 class KVPool:
@@ -151,6 +211,18 @@ class KVPool:
     def head_dim(self):
         return self.desc.head_dim
 
+    @property
+    def block_size(self):
+        return self.desc.block_size
+
+    @property
+    def device(self):
+        """The GPU the pool lives on; the attention and cache-write calls need their
+        tensors there.  A host pool (swap target) has none and refuses those calls."""
+        if self.host:
+            raise ValueError("this pool is in host memory: only swap_blocks accepts it")
+        return self.memory.device
+
     def _cache(self, layer: int, which: int):
         per = self.desc.num_blocks * self.desc.block_size * self.desc.num_kv_heads * self.desc.head_dim
         flat = self.memory.view(self.dtype)
@@ -179,8 +251,15 @@ class KVPool:
 
 
 def reshape_and_cache(pool: KVPool, layer: int, key, value, slot_mapping, stream=None) -> None:
-    """Write key[i], value[i] ([T, Hkv, D]) into slot slot_mapping[i] (int64) of ``layer``."""
+    """Write key[i], value[i] ([T, Hkv, D], the pool's io dtype) into slot
+    slot_mapping[i] (int64 [T]) of ``layer``."""
+    torch = _torch()
+    dev = pool.device
+    _need(slot_mapping, "slot_mapping", torch.int64, ndim=1, device=dev)
     n = int(slot_mapping.shape[0])
+    row = (n, pool.num_kv_heads, pool.head_dim)
+    _need(key, "key", pool.io_dtype, row, device=dev)
+    _need(value, "value", pool.io_dtype, row, device=dev)
     check(lib().reshape_and_cache(pool.handle, int(layer), _ptr(key), _ptr(value),
                                   _ptr(slot_mapping), n, _stream(stream)),
           "reshape_and_cache")
@@ -203,17 +282,20 @@ def alloc_workspace(pool: KVPool, batch, num_q_heads, max_blocks_per_seq, partit
     return torch.empty(n, dtype=torch.uint8, device=device or pool.memory.device)
 
 
+def _nbytes(t) -> int:
+    return 0 if t is None else int(t.numel() * t.element_size())
+
+
 def _decode_call(fn_name, pool, layer, out, query, block_tables, context_lens, scale,
                  partition_size, workspace, stream):
-    batch, hq, d = (int(x) for x in query.shape)
-    max_blocks = int(block_tables.shape[1]) if block_tables.dim() == 2 else 0
+    batch, hq, max_blocks = _check_decode_args(pool, out, query, block_tables, context_lens,
+                                               workspace=workspace)
     if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        scale = 1.0 / math.sqrt(pool.head_dim)
     fn = getattr(lib(), fn_name)
     check(fn(pool.handle, int(layer), _ptr(out), _ptr(query), _ptr(block_tables), max_blocks,
              _ptr(context_lens), batch, hq, float(scale), int(partition_size), _ptr(workspace),
-             ws_bytes, _stream(stream)),
+             _nbytes(workspace), _stream(stream)),
           fn_name)
 
 
@@ -221,6 +303,7 @@ def paged_attention_decode(pool: KVPool, layer: int, out, query, block_tables, c
                            scale=None, partition_size=0, workspace=None, stream=None):
     """out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over the sequence's paged K/V."""
     if workspace is None:
+        _check_decode_args(pool, out, query, block_tables, context_lens)
         workspace = alloc_workspace(pool, query.shape[0], query.shape[1], block_tables.shape[1],
                                     partition_size)
     _decode_call("paged_attention_decode", pool, layer, out, query, block_tables, context_lens,
@@ -230,16 +313,18 @@ def paged_attention_decode(pool: KVPool, layer: int, out, query, block_tables, c
 
 def _append_call(fn_name, pool, layer, out, query, new_key, new_value, block_tables,
                  context_lens, scale, partition_size, workspace, stream):
-    batch, hq, d = (int(x) for x in query.shape)
+    if new_key is None or new_value is None:
+        raise ValueError(f"{fn_name}: new_key and new_value are required")
+    batch, hq, max_blocks = _check_decode_args(pool, out, query, block_tables, context_lens,
+                                               new_key, new_value, workspace)
     if scale is None:
-        scale = 1.0 / math.sqrt(d)
+        scale = 1.0 / math.sqrt(pool.head_dim)
     if workspace is None and fn_name == "paged_attention_decode_append":
-        workspace = alloc_workspace(pool, batch, hq, block_tables.shape[1], partition_size)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        workspace = alloc_workspace(pool, batch, hq, max_blocks, partition_size)
     check(getattr(lib(), fn_name)(pool.handle, int(layer), _ptr(out), _ptr(query), _ptr(new_key),
-                                  _ptr(new_value), _ptr(block_tables), int(block_tables.shape[1]),
+                                  _ptr(new_value), _ptr(block_tables), max_blocks,
                                   _ptr(context_lens), batch, hq, float(scale), int(partition_size),
-                                  _ptr(workspace), ws_bytes, _stream(stream)),
+                                  _ptr(workspace), _nbytes(workspace), _stream(stream)),
           fn_name)
 
 
@@ -273,17 +358,80 @@ def paged_attention_reduce(pool, layer, out, query, block_tables, context_lens, 
                  scale, partition_size, workspace, stream)
 
 
+class DecodeStep:
+    """One decode step prepared once for buffers a serving loop reuses: the tensors are
+    checked when the step is built, and each call is then a single call into the library
+    (paged_attention_decode_append when new keys / values are given, else
+    paged_attention_decode: partitions, and the reduce when some sequence needs one).
+
+    The step keeps the tensors' addresses, so the tensors must stay alive and keep their
+    storage (update their contents in place between calls).  Lengths and tables are read
+    on the device at each call, so they may change, within the shapes given here."""
+
+    def __init__(self, pool: KVPool, layer: int, out, query, block_tables, context_lens,
+                 new_key=None, new_value=None, scale=None, partition_size=0, workspace=None):
+        batch, hq, max_blocks = _check_decode_args(pool, out, query, block_tables, context_lens,
+                                                   new_key, new_value, workspace)
+        if (new_key is None) != (new_value is None):
+            raise ValueError("DecodeStep: give both new_key and new_value, or neither")
+        if workspace is None:
+            workspace = alloc_workspace(pool, batch, hq, max_blocks, partition_size)
+        if scale is None:
+            scale = 1.0 / math.sqrt(pool.head_dim)
+        # keep every buffer alive as long as the step
+        self._keep = (pool, out, query, block_tables, context_lens, new_key, new_value, workspace)
+        vp = ctypes.c_void_p
+        head = [pool.handle, ctypes.c_int32(int(layer)), vp(_ptr(out)), vp(_ptr(query))]
+        tail = [vp(_ptr(block_tables)), ctypes.c_int32(max_blocks), vp(_ptr(context_lens)),
+                ctypes.c_int32(batch), ctypes.c_int32(hq), ctypes.c_float(float(scale)),
+                ctypes.c_int32(int(partition_size)), vp(_ptr(workspace)),
+                ctypes.c_size_t(_nbytes(workspace))]
+        if new_key is not None:
+            self._fn = lib().paged_attention_decode_append
+            self._name = "paged_attention_decode_append"
+            self._args = head + [vp(_ptr(new_key)), vp(_ptr(new_value))] + tail
+        else:
+            self._fn = lib().paged_attention_decode
+            self._name = "paged_attention_decode"
+            self._args = head + tail
+        self.out = out
+
+    def __call__(self, stream=None):
+        st = self._fn(*self._args, _stream(stream))
+        if st:
+            check(st, self._name)
+        return self.out
+
+
+def _check_prefill_args(pool, out, query, query_start, block_tables, context_lens):
+    torch = _torch()
+    dev = pool.device
+    _need(query, "query", pool.io_dtype, ndim=3, device=dev)
+    tokens, hq, d = (int(x) for x in query.shape)
+    if d != pool.head_dim:
+        raise ValueError(f"query: head size {d} differs from the pool's {pool.head_dim}")
+    if hq < 1 or hq % pool.num_kv_heads:
+        raise ValueError(f"query: {hq} heads is not a multiple of the pool's {pool.num_kv_heads} KV heads")
+    _need(out, "out", pool.io_dtype, (tokens, hq, d), device=dev)
+    _need(context_lens, "context_lens", torch.int32, ndim=1, device=dev)
+    batch = int(context_lens.shape[0])
+    _need(query_start, "query_start", torch.int32, (batch + 1,), device=dev)
+    _need(block_tables, "block_tables", torch.int32, (batch, None), device=dev)
+    return batch, tokens, hq
+
+
 def paged_attention_prefill(pool: KVPool, layer: int, out, query, query_start, max_query_len,
                             block_tables, context_lens, scale=None, stream=None) -> None:
     """Causal attention of each sequence's chunk of new tokens (rows
-    [query_start[b], query_start[b+1]) of ``query``) over its paged K/V."""
+    [query_start[b], query_start[b+1]) of ``query``) over its paged K/V.  ``query_start``
+    must end at no more than the rows of ``query`` (it is read on the device)."""
+    batch, _, hq = _check_prefill_args(pool, out, query, query_start, block_tables, context_lens)
     if scale is None:
         scale = 1.0 / math.sqrt(pool.head_dim)
-    batch = int(context_lens.shape[0])
     check(lib().paged_attention_prefill(pool.handle, int(layer), _ptr(out), _ptr(query),
                                         _ptr(query_start), int(max_query_len), _ptr(block_tables),
                                         int(block_tables.shape[1]), _ptr(context_lens), batch,
-                                        int(query.shape[1]), float(scale), _stream(stream)),
+                                        hq, float(scale), _stream(stream)),
           "paged_attention_prefill")
 
 
@@ -309,23 +457,32 @@ def paged_attention_prefill_split(pool: KVPool, layer: int, out, query, query_st
                                   stream=None) -> None:
     """paged_attention_prefill with each row tile's keys split over several work-groups
     when the launch is too small to fill the GPU (partial results in ``workspace``)."""
+    batch, num_tokens, hq = _check_prefill_args(pool, out, query, query_start, block_tables,
+                                                context_lens)
+    _need_bytes(workspace, "workspace", pool.device)
     if scale is None:
         scale = 1.0 / math.sqrt(pool.head_dim)
-    batch = int(context_lens.shape[0])
-    num_tokens = int(query.shape[0])
-    nbytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     check(lib().paged_attention_prefill_split(pool.handle, int(layer), _ptr(out), _ptr(query),
                                               _ptr(query_start), int(max_query_len), num_tokens,
                                               _ptr(block_tables), int(block_tables.shape[1]),
-                                              _ptr(context_lens), batch, int(query.shape[1]),
-                                              float(scale), _ptr(workspace) if workspace is not None else None,
-                                              nbytes, _stream(stream)),
+                                              _ptr(context_lens), batch, hq,
+                                              float(scale), _ptr(workspace), _nbytes(workspace),
+                                              _stream(stream)),
           "paged_attention_prefill_split")
 
 
 def kv_pool_gather(pool: KVPool, layer: int, block_tables, context_lens, k_out, v_out,
                    stream=None) -> None:
+    """Test hook: k_out / v_out [B, max_blocks * block_size, Hkv, D] in the pool's storage
+    type receive each sequence's rows through its table (zeros past its length)."""
+    torch = _torch()
+    dev = pool.device
+    _need(context_lens, "context_lens", torch.int32, ndim=1, device=dev)
     batch = int(context_lens.shape[0])
+    _need(block_tables, "block_tables", torch.int32, (batch, None), device=dev)
+    rows = (batch, int(block_tables.shape[1]) * pool.block_size, pool.num_kv_heads, pool.head_dim)
+    _need(k_out, "k_out", pool.dtype, rows, device=dev)
+    _need(v_out, "v_out", pool.dtype, rows, device=dev)
     check(lib().kv_pool_gather(pool.handle, int(layer), _ptr(block_tables),
                                int(block_tables.shape[1]), _ptr(context_lens), batch, _ptr(k_out),
                                _ptr(v_out), _stream(stream)),

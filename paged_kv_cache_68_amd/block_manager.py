@@ -126,8 +126,10 @@ class BlockManager:
 
 def copy_blocks(pool, copies, stream=None) -> None:
     """Device copy-on-write copies for every layer: copies is an int32 device tensor
-    [k, 3] of (src, dst, rows)."""
-    from . import _stream
+    [k, 3] of (src, dst, rows) on the pool's device."""
+    import torch
+    from . import _need, _stream
+    _need(copies, "copies", torch.int32, (None, 3), device=pool.device)
     n = int(copies.shape[0])
     check(lib().kv_copy_blocks(pool.handle, copies.data_ptr() if n else None, n, _stream(stream)),
           "kv_copy_blocks")
@@ -135,9 +137,18 @@ def copy_blocks(pool, copies, stream=None) -> None:
 
 def swap_blocks(src_pool, dst_pool, pairs, stream=None) -> None:
     """Swap copies: every layer's K and V of block pairs[i, 0] of ``src_pool`` go to block
-    pairs[i, 1] of ``dst_pool`` (one of them a host pool).  ``pairs`` is an int32 device
-    tensor [k, 2] (or a pinned CPU tensor)."""
-    from . import _stream
+    pairs[i, 1] of ``dst_pool`` (one of them a host pool).  ``pairs`` is an int32 tensor
+    [k, 2] on the GPU, or in pinned host memory."""
+    import torch
+    from . import _need, _stream
+    if not isinstance(pairs, torch.Tensor):
+        raise ValueError(f"pairs: expected a torch.Tensor, got {type(pairs).__name__}")
+    if pairs.device.type == "cpu":
+        if not pairs.is_pinned():
+            raise ValueError("pairs: a host tensor must be in pinned memory")
+        _need(pairs, "pairs", torch.int32, (None, 2), device=pairs.device)
+    else:
+        _need(pairs, "pairs", torch.int32, (None, 2))
     n = int(pairs.shape[0])
     check(lib().kv_swap_blocks(src_pool.handle, dst_pool.handle, pairs.data_ptr() if n else None,
                                n, _stream(stream)), "kv_swap_blocks")

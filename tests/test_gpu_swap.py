@@ -95,8 +95,8 @@ def test_swap_device_to_device_and_skipped_pairs():
         assert np.array_equal(got, want)
     with pytest.raises(pk.PagedKVError):                 # shapes differ
         pk.swap_blocks(a, pk.KVPool(2, 12, 2, 128, "f16"), torch.from_numpy(pairs).cuda())
-    with pytest.raises(pk.PagedKVError):                 # decode does not take a host pool
-        h = pk.KVPool(1, 4, 2, 64, "f16", host=True)
+    h = pk.KVPool(1, 4, 2, 64, "f16", host=True)
+    with pytest.raises(ValueError, match="host memory"):  # decode does not take a host pool
         q = torch.zeros(1, 2, 64, dtype=torch.float16, device="cuda")
         pk.paged_attention_decode(h, 0, torch.empty_like(q), q,
                                   torch.zeros(1, 1, dtype=torch.int32, device="cuda"),
