@@ -398,10 +398,10 @@ kv_status_t kv_bm_move(kv_block_manager_t* src, kv_block_manager_t* dst, const i
 /* Multi-token (prefill / chunked-prefill) attention for one layer: each sequence has a
  * chunk of new tokens whose keys and values are already in the pool (reshape_and_cache),
  * and each of them attends causally over the sequence's paged keys and values
- * ("PagedAttention: Treating KV Memory Like Virtual Memory", "Prefill is the other shape
- * of the request": a prompt processed in parallel, cut into chunks to a step's token
- * budget; "PagedAttention and Virtual Memory Management": the prefill phase processes the
- * prompt in parallel).
+ * ("PagedAttention: Treating KV Memory Like Virtual Memory", section "What the allocator
+ * actually sees": besides one-token decode steps a request arrives as a prompt processed
+ * in parallel, or in pieces cut to a step's token budget; "PagedAttention and Virtual
+ * Memory Management": the prefill phase processes the prompt in parallel).
  *  query, out   : [T][num_q_heads][head_dim], io dtype; the chunks of all sequences packed
  *                 one after another.
  *  query_start  : [batch + 1] int32 device, non-decreasing, query_start[0] = 0: sequence

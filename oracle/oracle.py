@@ -377,9 +377,10 @@ def paged_prefill_seq(q_bits, k_pool_bits, v_pool_bits, table, length, scale, bl
     positions [0, p] only.  Their own keys and values are already in the pool.
 
     A prompt (or a chunk of one) processed in parallel, as "PagedAttention: Treating KV
-    Memory Like Virtual Memory" ("Prefill is the other shape of the request": chunks of
-    a prompt cut to the step's token budget) and "PagedAttention and Virtual Memory
-    Management" (prefill processes the prompt in parallel) describe it; each row is
+    Memory Like Virtual Memory", section "What the allocator actually sees" (a request
+    also comes as a whole prompt, or as pieces of one cut to the step's token budget),
+    and "PagedAttention and Virtual Memory Management" (prefill processes the prompt in
+    parallel) describe it; each row is
     the attention of P2 "Reading through the table" over the first p + 1 positions.
     Tokens with p < 0 (more queries than the length holds) get zero output.
     q_bits: [n, Hq, d].  Returns fp64 [n, Hq, d].

@@ -4,9 +4,10 @@
 // their keys and values are already in the pool.  Token i's query heads attend over
 // positions [0, L - n + i] of the sequence, read through its block table: a prompt (or a
 // chunk of one, cut to a step's token budget) processed in parallel, as "PagedAttention:
-// Treating KV Memory Like Virtual Memory" ("Prefill is the other shape of the request")
-// and "PagedAttention and Virtual Memory Management" (the prefill phase processes the
-// prompt in parallel) describe it.
+// Treating KV Memory Like Virtual Memory", section "What the allocator actually sees"
+// (besides one-token decode steps, a request also arrives as a whole prompt, or pieces
+// of one sized to the step's token budget), and "PagedAttention and Virtual Memory
+// Management" (the prefill phase processes the prompt in parallel) describe it.
 //
 // Mapping.  The (token, query head) pairs of one (sequence, KV head) form n * G rows,
 // head fastest; rows share the KV head's keys and values.  A work-group of W waves owns

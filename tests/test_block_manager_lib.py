@@ -19,8 +19,7 @@ GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "block
 
 
 def _state(m, rids):
-    return (m.free_list() if hasattr(m, "handle") else list(m.free_list),
-            [m.ref_count(b) if hasattr(m, "handle") else m.ref_count[b] for b in range(m.num_blocks)],
+    return (m.free_list(), [m.ref_count(b) for b in range(m.num_blocks)],
             {r: m.table(r) for r in rids}, {r: m.length(r) for r in rids})
 
 

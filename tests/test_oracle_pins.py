@@ -55,6 +55,28 @@ def test_address_example_from_page():
     assert addr == a["physical_block"] * a["block_bytes"] + a["offset"] * a["token_bytes"]
 
 
+@pytest.mark.parametrize("h", [1, 5, 7])
+def test_address_head_term_matches_the_pools_own_element_addresses(h):
+    """Addr_K(t) with a non-zero head ("PagedAttention and Virtual Memory Management",
+    section 4): for the Llama-3-8B layer layout [blocks][16][8 KV heads][128] in bf16
+    the oracle's address of (t, h) must be the address numpy itself gives element
+    [table[t // 16], t % 16, h, 0] of such an array, and the bytes there must be the
+    value planted at that element."""
+    nb, B, hkv, d = 96, 16, 8, 128
+    pool = np.zeros((nb, B, hkv, d), dtype=np.uint16)
+    table = [40, 3, 93, 17]
+    base = pool.__array_interface__["data"][0]
+    for t in (0, 15, 16, 38, 63):
+        blk, o = table[t // B], t % B
+        pool[blk, o, h, 0] = 1000 + t
+        addr = oracle.physical_address(t, B, table, B * hkv * d * 2, hkv * d * 2, head=h,
+                                       stride_head=d * 2, base=base)
+        assert addr == pool[blk, o, h, :].__array_interface__["data"][0]
+        assert addr - base == np.ravel_multi_index((blk, o, h, 0), pool.shape) * 2
+        flat = pool.reshape(-1).view(np.uint8)
+        assert int(flat[addr - base]) | (int(flat[addr - base + 1]) << 8) == 1000 + t
+
+
 def test_footprints_from_pages():
     g = _load("footprints.json")
     for ex in g["bytes_per_token"]:
@@ -264,61 +286,59 @@ def test_empty_sequence_is_zero():
 
 # ------------------------------------------------------------------ paged == contiguous
 
-class _FreeListManager:
-    """Free list from the front, one table per request, a new block when n % B == 0."""
+class _BumpPool:
+    """Blocks handed out in increasing id order, one table per request, a fresh block
+    whenever a request's length is a multiple of the block size; every slot starts as
+    a NaN bit pattern so a read of a slot nobody wrote would show."""
 
     def __init__(self, nb, bs, hkv, d):
-        self.bs = bs
-        self.free = list(range(nb))
+        self.bs, self.next_block = bs, 0
         self.k = np.full((nb, bs, hkv, d), 0x7E00, np.uint16)
         self.v = np.full((nb, bs, hkv, d), 0x7E00, np.uint16)
         self.tables, self.lens = {}, {}
 
-    def add(self, rid):
-        self.tables[rid], self.lens[rid] = [], 0
-
-    def append(self, rid, kbits, vbits):
-        n = self.lens[rid]
+    def write(self, rid, kbits, vbits):
+        n = self.lens.setdefault(rid, 0)
+        table = self.tables.setdefault(rid, [])
         if n % self.bs == 0:
-            self.tables[rid].append(self.free.pop(0))
-        blk = self.tables[rid][-1]
-        self.k[blk, n % self.bs] = kbits
-        self.v[blk, n % self.bs] = vbits
+            table.append(self.next_block)
+            self.next_block += 1
+        self.k[table[-1], n % self.bs] = kbits
+        self.v[table[-1], n % self.bs] = vbits
         self.lens[rid] = n + 1
 
 
-@pytest.mark.parametrize("bs", [1, 4, 16])
+@pytest.mark.parametrize("bs", [1, 2, 8, 16])
 def test_reading_through_table_equals_one_array(bs):
-    """Two requests grown in turn so their blocks interleave (the test the tutorial
-    describes in "Proof it works"), at block sizes 1, 4 and 16."""
+    """Requests grown in a shuffled order, so their blocks interleave in the pool
+    ("Why AI servers waste memory", "Proof it works": reading through the table gives
+    what one flat array per request gives), for three requests of 19, 6 and 11 tokens
+    at block sizes 1, 2, 8 and 16."""
     from workloads import round_to_bits
-    rng = np.random.default_rng(bs)
-    hkv, d = 1, 4
-    mgr = _FreeListManager(64, bs, hkv, d)
-    rows = {"x": ([], []), "y": ([], [])}
-    for rid in rows:
-        mgr.add(rid)
-    for i in range(13):
-        for rid, n in (("x", 13), ("y", 7)):
-            if i < n:
-                kb = round_to_bits(rng.standard_normal((hkv, d), dtype=np.float32), "f16")
-                vb = round_to_bits(rng.standard_normal((hkv, d), dtype=np.float32), "f16")
-                mgr.append(rid, kb, vb)
-                rows[rid][0].append(kb)
-                rows[rid][1].append(vb)
-    q = round_to_bits(rng.standard_normal((1, d), dtype=np.float32), "f16")
-    if bs in (1, 4):   # the two requests' blocks alternate in the pool
-        tx = mgr.tables["x"]
-        assert tx != list(range(tx[0], tx[0] + len(tx)))
-    for rid in rows:
-        kc = oracle.to_f64(np.stack(rows[rid][0]), "f16")
-        vc = oracle.to_f64(np.stack(rows[rid][1]), "f16")
+    rng = np.random.default_rng(900 + bs)
+    hkv, d = 2, 4
+    targets = {"r0": 19, "r1": 6, "r2": 11}
+    schedule = [rid for rid, n in targets.items() for _ in range(n)]
+    rng.shuffle(schedule)
+    pool = _BumpPool(64, bs, hkv, d)
+    flat = {rid: ([], []) for rid in targets}
+    for rid in schedule:
+        kb = round_to_bits(rng.standard_normal((hkv, d), dtype=np.float32), "f16")
+        vb = round_to_bits(rng.standard_normal((hkv, d), dtype=np.float32), "f16")
+        pool.write(rid, kb, vb)
+        flat[rid][0].append(kb)
+        flat[rid][1].append(vb)
+    if bs <= 2:       # the requests' blocks are not contiguous runs
+        assert any(t != list(range(t[0], t[0] + len(t))) for t in pool.tables.values())
+    q = round_to_bits(rng.standard_normal((hkv * 2, d), dtype=np.float32), "f16")
+    for rid, (ks, vs) in flat.items():
+        kc = oracle.to_f64(np.stack(ks), "f16")
+        vc = oracle.to_f64(np.stack(vs), "f16")
         contiguous = oracle.attention_contiguous(oracle.to_f64(q, "f16"), kc, vc, 0.5)
-        paged = oracle.paged_decode_seq(q, mgr.k, mgr.v, mgr.tables[rid], mgr.lens[rid], 0.5, bs, "f16")
+        paged = oracle.paged_decode_seq(q, pool.k, pool.v, pool.tables[rid], pool.lens[rid], 0.5, bs, "f16")
         assert np.max(np.abs(paged - contiguous)) <= 1e-15
         # gather returns exactly the rows written, in order
-        assert np.array_equal(oracle.gather(mgr.k, mgr.tables[rid], mgr.lens[rid], bs),
-                              np.stack(rows[rid][0]))
+        assert np.array_equal(oracle.gather(pool.k, pool.tables[rid], pool.lens[rid], bs), np.stack(ks))
 
 
 # ------------------------------------------------------------------ cache write

@@ -17,9 +17,9 @@ def _state(lib_pc, ora, rids):
     lib_s = (lib_pc.free_queue(), [lib_pc.block_info(b) for b in range(lib_pc.num_blocks)],
              {r: lib_pc.table(r) for r in rids}, {r: lib_pc.length(r) for r in rids},
              lib_pc.num_cached())
-    ora_s = (list(ora.free), [(ora.ref[b], ora.hash[b] is not None, ora.hash[b]) for b in range(ora.num_blocks)],
-             {r: list(ora.tables[r]) for r in rids}, {r: ora.lengths[r] for r in rids},
-             len(ora.cached))
+    ora_s = (ora.free_queue(), [(ora.ref_count(b), ora.block_hash_of(b) is not None, ora.block_hash_of(b))
+                                for b in range(ora.num_blocks)],
+             {r: ora.table(r) for r in rids}, {r: ora.length(r) for r in rids}, ora.num_cached())
     return lib_s, ora_s
 
 

@@ -17,8 +17,7 @@ def test_fnv1a_test_vectors():
 
 
 def _state(pc):
-    return (list(pc.free), list(pc.ref), list(pc.hash), dict(pc.cached),
-            {r: list(t) for r, t in pc.tables.items()}, dict(pc.lengths))
+    return pc.snapshot()
 
 
 def test_shared_prefix_of_2407_tokens_matches_150_blocks():
@@ -34,12 +33,12 @@ def test_shared_prefix_of_2407_tokens_matches_150_blocks():
         found.append(pc.add_request(r, prompt))
         pc.append(r, prompt[found[-1]:])
     assert found == [2400] * 15
-    shared = pc.tables[0][:150]
-    assert all(pc.tables[r][:150] == shared for r in range(16))
-    assert all(pc.ref[b] == 16 for b in shared)
-    tails = {pc.tables[r][150] for r in range(16)}
-    assert len(tails) == 16 and all(pc.ref[b] == 1 for b in tails)
-    assert pc.num_blocks - len(pc.free) == 150 + 16
+    shared = pc.table(0)[:150]
+    assert all(pc.table(r)[:150] == shared for r in range(16))
+    assert all(pc.ref_count(b) == 16 for b in shared)
+    tails = {pc.table(r)[150] for r in range(16)}
+    assert len(tails) == 16 and all(pc.ref_count(b) == 1 for b in tails)
+    assert pc.num_blocks - pc.num_free() == 150 + 16
     pc.check_invariants()
 
 
@@ -70,13 +69,14 @@ def test_finished_prefix_stays_findable_until_evicted():
     p = list(range(10))                    # blocks: 2 full (cached) + 1 partial
     pc.add_request(0, p)
     pc.append(0, p)
-    full = pc.tables[0][:2]
+    full = pc.table(0)[:2]
     pc.free_request(0)
-    assert all(pc.ref[b] == 0 and pc.hash[b] is not None for b in full)
+    assert all(pc.ref_count(b) == 0 and pc.block_hash_of(b) is not None for b in full)
     # hash-less partial block at the head, cached ones at the tail, last-walked first
-    assert pc.free[0] not in full and pc.free[-2:] == [full[1], full[0]]
+    q = pc.free_queue()
+    assert q[0] not in full and q[-2:] == [full[1], full[0]]
     assert pc.add_request(1, p) == 8        # warm: found, nothing computed
-    assert all(b not in pc.free and pc.ref[b] == 1 for b in full)
+    assert all(b not in pc.free_queue() and pc.ref_count(b) == 1 for b in full)
     pc.check_invariants()
 
 
@@ -86,15 +86,15 @@ def test_uncached_blocks_are_reused_first_and_cached_ones_oldest_first():
     for rid, p in (("a", pa), ("b", pb)):
         pc.add_request(rid, p)
         pc.append(rid, p)
-    a0, a1 = pc.tables["a"]
+    a0, a1 = pc.table("a")
     pc.free_request("a")                    # a's cached blocks join the tail first,
     pc.free_request("b")                    # each request's last block first
-    assert pc.free[:2] == [4, 5]            # the never-used (hash-less) blocks lead
-    assert pc.free[2:4] == [a1, a0] and len(pc.cached) == 4
+    assert pc.free_queue()[:2] == [4, 5]    # the never-used (hash-less) blocks lead
+    assert pc.free_queue()[2:4] == [a1, a0] and pc.num_cached() == 4
     pc.add_request("c", [9])
     pc.append("c", [9, 9, 9, 9, 9])         # 3 blocks: the 2 uncached ones, then a's tail block
-    assert pc.tables["c"] == [4, 5, a1] and pc.hash[a1] is None   # evicted; holds c's partial tail
-    assert len(pc.cached) == 4 - 1 + 2      # one evicted, c's two full blocks cached
+    assert pc.table("c") == [4, 5, a1] and pc.block_hash_of(a1) is None   # evicted; holds c's partial tail
+    assert pc.num_cached() == 4 - 1 + 2     # one evicted, c's two full blocks cached
     assert pc.add_request("d", pa) == 2     # a's head block survives, its tail does not
     assert pc.add_request("e", pb) == 4     # b's prefix is still there
 
@@ -154,18 +154,17 @@ def test_decode_step_equals_one_token_appends_in_order():
     slots = pc.append_step([3, 0, 2, 1], toks)
     want = [ref.append(r, [t])[0] for r, t in zip([3, 0, 2, 1], toks)]
     assert slots == want
-    assert pc.tables == ref.tables and pc.lengths == ref.lengths and pc.free == ref.free
-    assert pc.tokens == ref.tokens and pc.cached == ref.cached and pc.ref == ref.ref
+    assert pc.snapshot() == ref.snapshot()
     with pytest.raises(ValueError):
         pc.append_step([0, 0], [1, 2])
     with pytest.raises(ValueError):
         pc.append_step([9], [1])
     # drain the free list, then a step needing a block fails as a whole
-    while pc.free:
-        pc.append(0, [1] * (4 - pc.lengths[0] % 4))
-    before = copy.deepcopy(pc)
-    need_block = [r for r in pc.lengths if pc.lengths[r] % 4 == 0]
+    while pc.num_free():
+        pc.append(0, [1] * (4 - pc.length(0) % 4))
+    before = pc.snapshot()
+    need_block = [r for r in pc.requests() if pc.length(r) % 4 == 0]
     assert need_block
     with pytest.raises(OutOfBlocks):
-        pc.append_step(sorted(pc.lengths), [5] * len(pc.lengths))
-    assert pc.tables == before.tables and pc.lengths == before.lengths and pc.tokens == before.tokens
+        pc.append_step(sorted(pc.requests()), [5] * len(pc.requests()))
+    assert pc.snapshot() == before

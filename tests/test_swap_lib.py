@@ -22,7 +22,7 @@ def _lib_state(m, rids):
 
 
 def _ora_state(m, rids):
-    return (list(m.free_list), list(m.ref_count), {r: m.table(r) for r in rids},
+    return (m.free_list(), m.ref_counts(), {r: m.table(r) for r in rids},
             {r: m.length(r) for r in rids})
 
 

@@ -16,8 +16,7 @@ from oracle import BlockManager, OutOfBlocks, move_requests
 
 
 def _state(m):
-    return (list(m.free_list), list(m.ref_count), {r: list(t) for r, t in m.tables.items()},
-            dict(m.lengths))
+    return m.snapshot()
 
 
 def test_worked_example_by_hand():
@@ -33,10 +32,10 @@ def test_worked_example_by_hand():
     assert dev.table(0) == [0, 1, 2] and dev.table(1) == [3, 4]
     pairs = move_requests(dev, host, [0, 2])
     assert pairs == [(0, 0), (1, 1), (2, 2)]
-    assert list(dev.free_list) == [5, 6, 7, 0, 1, 2]
-    assert dev.ref_count[:5] == [0, 0, 0, 1, 1]
+    assert dev.free_list() == [5, 6, 7, 0, 1, 2]
+    assert dev.ref_counts()[:5] == [0, 0, 0, 1, 1]
     assert host.table(0) == host.table(2) == [0, 1, 2] and host.length(2) == 10
-    assert host.ref_count == [2, 2, 2, 0, 0, 0] and list(host.free_list) == [3, 4, 5]
+    assert host.ref_counts() == [2, 2, 2, 0, 0, 0] and host.free_list() == [3, 4, 5]
     # request 1 grows into the freed blocks: 5 + 7 = 12 tokens take blocks 5 then 6
     dev.append_batch([1], [7])
     assert dev.table(1) == [3, 4, 5]
@@ -44,7 +43,7 @@ def test_worked_example_by_hand():
     pairs = move_requests(host, dev, [2, 0])
     assert pairs == [(0, 6), (1, 7), (2, 0)]
     assert dev.table(0) == dev.table(2) == [6, 7, 0] and dev.length(0) == 10
-    assert list(host.free_list) == [3, 4, 5, 0, 1, 2]
+    assert host.free_list() == [3, 4, 5, 0, 1, 2]
     dev.check_invariants()
     host.check_invariants()
 
@@ -56,11 +55,11 @@ def test_partial_swap_of_a_shared_prefix():
     dev.add_request(0)
     dev.append_batch([0], [9])
     dev.fork(0, 1)
-    free_before = list(dev.free_list)
+    free_before = dev.free_list()
     pairs = move_requests(dev, host, [1])
     assert pairs == [(0, 0), (1, 1), (2, 2)]
-    assert list(dev.free_list) == free_before and dev.ref_count[:3] == [1, 1, 1]
-    assert host.ref_count[:3] == [1, 1, 1]
+    assert dev.free_list() == free_before and dev.ref_counts()[:3] == [1, 1, 1]
+    assert host.ref_counts()[:3] == [1, 1, 1]
 
 
 def test_failures_change_nothing():
@@ -103,8 +102,8 @@ def test_swap_blocks_copies_whole_blocks_bit_for_bit():
 
 def _read(m, store, rid):
     B = m.block_size
-    t = m.tables[rid]
-    return [int(store[t[p // B], p % B]) for p in range(m.lengths[rid])]
+    t = m.table(rid)
+    return [int(store[t[p // B], p % B]) for p in range(m.length(rid))]
 
 
 @pytest.mark.parametrize("seed", range(5))
