@@ -279,6 +279,35 @@ kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* o
                                    int32_t partition_size, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the scratch array the library keeps on each GPU for
+ * paged_attention_decode_noalloc (64 MiB). */
+#define PAGEDKV_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* paged_attention_decode for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same arguments
+ * without the workspace, the same kernels and the same output bits.  The fp32 partial
+ * results go to a scratch array of PAGEDKV_SCRATCH_BYTES that the library keeps in device
+ * memory, one per GPU, from the library's load until the process ends; the call itself
+ * allocates nothing.  Its device address is looked up on the first call on each device
+ * (that call must run with the device current, as every call must).
+ *  - The shape must need at most PAGEDKV_SCRATCH_BYTES of workspace
+ *    (paged_attention_workspace_bytes(...) <= PAGEDKV_SCRATCH_BYTES), else the call
+ *    returns KV_ERR_WORKSPACE and enqueues nothing.  For example 64 sequences x 8,192
+ *    tokens with 32 query heads of 128 need 17 MB; 512 sequences x 4,096 tokens with 64
+ *    heads of 128 need 136 MB and are refused.
+ *  - Every call on one GPU shares that GPU's array and leaves its partial results in it.
+ *    Nothing in it needs to start at zero.  Calls that overlap in time on one GPU (on
+ *    different streams, or from several threads without ordering) race on the array and
+ *    give undefined results: serialise them, e.g. on one stream.
+ *  - Checked mode (PAGEDKV_CHECK) does not apply: its passes allocate and synchronise.
+ * Errors: as paged_attention_decode, with KV_ERR_WORKSPACE for a shape beyond the array
+ * and KV_ERR_HIP if the array's address cannot be found. */
+kv_status_t paged_attention_decode_noalloc(const kv_pool_t* pool, int32_t layer, void* out,
+                                           const void* query, const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                           int32_t batch, int32_t num_q_heads, float scale,
+                                           int32_t partition_size, hipStream_t stream);
+
 /* Copy-on-write copies on the device, for every layer of the pool, K and V:
  *  copies : [num_copies][3] int32 device array of (src, dst, rows); the first `rows`
  *           token rows of physical block src are copied into block dst and the other

@@ -25,7 +25,7 @@ __all__ = [
     "BlockManager", "OutOfBlocks", "copy_blocks", "paged_attention_prefill", "PrefixCache",
     "hash_block", "swap_blocks", "paged_attention_decode_append", "paged_attention_partitions_append",
     "paged_attention_prefill_split", "prefill_workspace_bytes", "alloc_prefill_workspace",
-    "DecodeStep",
+    "DecodeStep", "paged_attention_decode_noalloc",
 ]
 
 BLOCK_SIZE = 16
@@ -356,6 +356,25 @@ def paged_attention_reduce(pool, layer, out, query, block_tables, context_lens, 
                            partition_size=0, workspace=None, stream=None):
     _decode_call("paged_attention_reduce", pool, layer, out, query, block_tables, context_lens,
                  scale, partition_size, workspace, stream)
+
+
+SCRATCH_BYTES = 64 << 20      # PAGEDKV_SCRATCH_BYTES
+
+
+def paged_attention_decode_noalloc(pool: KVPool, layer: int, out, query, block_tables, context_lens,
+                                   scale=None, partition_size=0, stream=None):
+    """paged_attention_decode with no workspace argument and no allocation: partial
+    results go to the library's per-GPU scratch array (SCRATCH_BYTES).  Shapes that
+    need more are refused (KV_ERR_WORKSPACE); calls that overlap on one GPU race."""
+    batch, hq, max_blocks = _check_decode_args(pool, out, query, block_tables, context_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(pool.head_dim)
+    check(lib().paged_attention_decode_noalloc(pool.handle, int(layer), _ptr(out), _ptr(query),
+                                               _ptr(block_tables), max_blocks, _ptr(context_lens),
+                                               batch, hq, float(scale), int(partition_size),
+                                               _stream(stream)),
+          "paged_attention_decode_noalloc")
+    return out
 
 
 class DecodeStep:

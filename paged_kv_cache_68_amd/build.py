@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libpagedkv.so"
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "block_manager.cpp", "prefix_cache.cpp", "cache_ops.hip", "paged_decode.hip", "paged_decode_mfma.hip", "prefill_mfma.hip", "checks.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "prefix_cache.cpp", "cache_ops.hip", "paged_decode.hip", "paged_decode_mfma.hip", "prefill_mfma.hip", "checks.hip", "scratch.hip"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -242,14 +242,15 @@ kv_status_t decode_impl(int phases, const kv_pool_t* pool, int32_t layer, void* 
                         const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                         float scale, int32_t partition_size, void* workspace,
                         size_t workspace_bytes, hipStream_t stream,
-                        const void* new_key = nullptr, const void* new_value = nullptr) {
+                        const void* new_key = nullptr, const void* new_value = nullptr,
+                        bool allow_checked = true) {
     DecodeShape s;
     kv_status_t st = check_decode(pool, layer, out, query, block_tables, max_blocks, context_lens,
                                   batch, num_q_heads, scale, partition_size, workspace,
                                   workspace_bytes, &s);
     if (st != KV_OK) return st;
     if (batch == 0) return KV_OK;
-    if (checked_mode() && (phases & kPartitions)) {
+    if (allow_checked && checked_mode() && (phases & kPartitions)) {
         st = check_tables_on_device(pool, block_tables, max_blocks, context_lens, batch, stream);
         if (st != KV_OK) return st;
         if (new_key) {
@@ -722,6 +723,31 @@ kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* o
     return decode_impl(kReduce, pool, layer, out, query, block_tables, max_blocks_per_seq,
                        context_lens, batch, num_q_heads, scale, partition_size, workspace,
                        workspace_bytes, stream);
+}
+
+kv_status_t paged_attention_decode_noalloc(const kv_pool_t* pool, int32_t layer, void* out,
+                                           const void* query, const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                           int32_t batch, int32_t num_q_heads, float scale,
+                                           int32_t partition_size, hipStream_t stream) {
+    if (!pool || pool->host) return KV_ERR_INVALID_ARG;
+    // SIZE_MAX: arguments the decode checks below refuse
+    const size_t need = batch > 0 ? paged_attention_workspace_bytes(batch, num_q_heads,
+                                                                    pool->desc.head_dim,
+                                                                    max_blocks_per_seq,
+                                                                    pool->desc.block_size,
+                                                                    partition_size)
+                                  : 0;
+    if (need != SIZE_MAX && need > PAGEDKV_SCRATCH_BYTES) return KV_ERR_WORKSPACE;
+    void* scratch = nullptr;
+    if (need > 0 && need != SIZE_MAX && pkv::scratch_for_current_device(&scratch) != hipSuccess) {
+        (void)hipGetLastError();
+        return KV_ERR_HIP;
+    }
+    // the checked-mode passes allocate and synchronise: not on this path
+    return decode_impl(kBoth, pool, layer, out, query, block_tables, max_blocks_per_seq,
+                       context_lens, batch, num_q_heads, scale, partition_size, scratch,
+                       scratch ? PAGEDKV_SCRATCH_BYTES : 0, stream, nullptr, nullptr, false);
 }
 
 kv_status_t kv_pool_gather(const kv_pool_t* pool, int32_t layer, const int32_t* block_tables,

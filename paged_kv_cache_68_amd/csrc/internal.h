@@ -137,6 +137,10 @@ hipError_t launch_swap_blocks(const char* src, char* dst, const int32_t* pairs, 
 // the new tokens of a decode step (DecodeArgs::new_k / new_v) into the slots of position
 // L - 1, found through the tables: for kernels that do not write them themselves
 hipError_t launch_append_kv(int kv_dtype, int io_dtype, const DecodeArgs& a, hipStream_t stream);
+// Bytes of the library's per-device scratch array (paged_attention_decode_noalloc).
+constexpr size_t kScratchBytes = PAGEDKV_SCRATCH_BYTES;
+// Device address of the current device's scratch array (looked up once per device).
+hipError_t scratch_for_current_device(void** ptr);
 hipError_t launch_copy_blocks(char* base, const int32_t* copies, int32_t num_copies,
                               int32_t num_layers, int32_t num_blocks, int32_t block_size,
                               int32_t row_bytes, size_t cache_bytes, hipStream_t stream);
