@@ -37,20 +37,33 @@ PARTITION_KERNEL = "pa_partition"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
-def algorithmic_bytes(lens, hq, hkv, d, kv_elem, io_elem=2, block_size=16):
+def unique_rows(lens, tables, block_size):
+    """Distinct (physical block, slot) token rows a step reads: sequences that share
+    blocks (forks of one prefix) read the shared rows once from HBM."""
+    rows = []
+    for b, L in enumerate(np.asarray(lens, dtype=np.int64).tolist()):
+        t = np.arange(L, dtype=np.int64)
+        rows.append(np.asarray(tables[b], dtype=np.int64)[t // block_size] * block_size + t % block_size)
+    return int(np.unique(np.concatenate(rows)).size) if rows else 0
+
+
+def algorithmic_bytes(lens, hq, hkv, d, kv_elem, io_elem=2, block_size=16, tables=None):
     """Bytes the method must move for one step (K+V of every context token, the table
     entries and length read, Q in and O out), and the partition kernel's share.
     kv_elem: bytes per stored K / V element (1 for FP8); io_elem: bytes per query /
-    output / new key element."""
+    output / new key element.  With ``tables``, ``kv_unique`` counts each distinct
+    token row once (the HBM bytes when sequences share blocks)."""
     lens = np.asarray(lens, dtype=np.int64)
     kv = int(np.sum(2 * lens * hkv * d * kv_elem))
+    kv_unique = kv if tables is None else 2 * unique_rows(lens, tables, block_size) * hkv * d * kv_elem
     table = int(np.sum(4 * ((lens + block_size - 1) // block_size)))
     nlen = 4 * len(lens)
     q = len(lens) * hq * d * io_elem
     o = len(lens) * hq * d * io_elem
     write = len(lens) * (2 * hkv * d * (io_elem + kv_elem) + 8)
-    return {"kv": kv, "table": table, "lens": nlen, "q": q, "o": o,
+    return {"kv": kv, "kv_unique": kv_unique, "table": table, "lens": nlen, "q": q, "o": o,
             "partition_kernel": kv + table + nlen + q,
+            "partition_kernel_unique": kv_unique + table + nlen + q,
             "write": write,
             "step": kv + table + nlen + q + o + write}
 
@@ -71,8 +84,10 @@ def kernel_source_hash() -> str:
 
 
 def load_traffic(workload: str):
-    """HBM bytes per launch of the partition kernel from committed rocprofv3 counter
-    runs (profiles/<kernel>_<workload>_traffic.json), if taken on the current source."""
+    """HBM bytes per launch of the partition kernel from a committed rocprofv3 counter
+    run (profiles/<kernel>_<workload>_traffic.json: TCC_EA0_RDREQ_DRAM_32B and
+    TCC_EA0_WRREQ_WRITE_DRAM_32B, requests to DRAM counted in 32-byte units, so bytes =
+    32 x count with no calibration), if taken on the current source."""
     path = os.path.join(PROFILE_DIR, f"{PARTITION_KERNEL}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -83,34 +98,112 @@ def load_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(dc, budget_s: float):
-    """Time the fp64 oracle on the host on as many sequences as fit in ``budget_s``."""
-    import oracle
+def host_cpu():
+    """Host facts recorded with the CPU baseline."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "nproc": len(os.sched_getaffinity(0)), "model": model}
+
+
+# Host cores the oracle may use: every one this process may run on, at most 16 (the
+# host share of one GPU on the measuring machines).
+MAX_ORACLE_WORKERS = 16
+
+
+def _oracle_worker_init():
     from threadpoolctl import threadpool_limits
+    global _BLAS_LIMIT
+    _BLAS_LIMIT = threadpool_limits(limits=1)    # one BLAS thread per worker
+
+
+def _oracle_task(task):
+    """One sequence of the sample, read from the arrays the parent left in ``folder``."""
+    import oracle
+    folder, i, L, scale, B, kv, qdt = task
+    kb = np.load(os.path.join(folder, f"k{i}.npy"), mmap_mode="r")
+    vb = np.load(os.path.join(folder, f"v{i}.npy"), mmap_mode="r")
+    q = np.load(os.path.join(folder, f"q{i}.npy"))
+    table = np.arange(kb.shape[0])
+    return i, oracle.paged_decode_seq(q, kb, vb, table, L, scale, B, kv, q_dtype=qdt)
+
+
+def oracle_pool():
+    """Worker processes for the CPU baseline, one per host core (at most 16), each with
+    one BLAS thread.  Started as fresh interpreters before this process touches the GPU,
+    so no worker ever holds GPU state."""
+    import multiprocessing as mp
+    workers = min(MAX_ORACLE_WORKERS, len(os.sched_getaffinity(0)))
+    return mp.get_context("spawn").Pool(workers, initializer=_oracle_worker_init)
+
+
+def cpu_baseline(dc, budget_s: float, pool=None, max_sample_bytes: int = 2 << 30):
+    """Time the fp64 oracle on the host's cores (``pool``: worker processes from
+    oracle_pool(), one BLAS thread each) on a bounded sample of the step: sequences
+    taken at an even stride until their K/V reach ``max_sample_bytes``, the sample
+    repeated until it is about ``budget_s`` seconds of CPU work.  Also checks the GPU
+    output on the sample."""
+    import shutil
+    import tempfile
+
+    import oracle
+    from tests.device_case import to_host_bits   # plumbing: device bytes -> host bits
 
     cfg = dc.cfg
-    order = list(range(cfg.batch))
-    done, t_total, max_err = 0, 0.0, 0.0
-    from tests.device_case import to_host_bits   # plumbing: device bytes -> host bits
+    lens = np.asarray(dc.case.lengths, dtype=np.int64)
+    row = cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes * 2
+    per_seq = np.maximum(lens, 1) * row
+    n_fit = int(np.searchsorted(np.cumsum(np.sort(per_seq)), max_sample_bytes, side="right"))
+    stride = max(1, -(-cfg.batch // max(1, n_fit)))
+    sample = list(range(0, cfg.batch, stride))
+    while len(sample) > 1 and int(per_seq[sample].sum()) > max_sample_bytes:
+        sample = sample[:-1]
     out_bits = to_host_bits(dc.out)
-    with threadpool_limits(limits=1):
-        for b in order:
-            kb, vb, table = dc.blocks_of(b)
+    folder = tempfile.mkdtemp(prefix="pkv_oracle_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    try:
+        for i in sample:
+            kb, vb, _ = dc.blocks_of(i)
+            np.save(os.path.join(folder, f"k{i}.npy"), kb)
+            np.save(os.path.join(folder, f"v{i}.npy"), vb)
+            np.save(os.path.join(folder, f"q{i}.npy"), dc.case.query[i])
+        tasks = [(folder, i, int(lens[i]), cfg.scale, cfg.block_size, cfg.kv, cfg.dtype) for i in sample]
+        own = pool is None
+        if own:
+            pool = oracle_pool()
+        try:
+            workers = pool._processes
+            # an untimed pass over the sample gives its CPU cost, hence the passes timed
             t0 = time.perf_counter()
-            ref = oracle.paged_decode_seq(dc.case.query[b], kb, vb, table, int(dc.case.lengths[b]),
-                                          cfg.scale, cfg.block_size, cfg.kv, q_dtype=cfg.dtype)
-            t_total += time.perf_counter() - t0
-            max_err = max(max_err, float(np.max(np.abs(oracle.to_f64(out_bits[b], cfg.dtype) - ref))))
-            done += 1
-            if t_total >= budget_s:
-                break
+            results = pool.map(_oracle_task, tasks, chunksize=1)
+            pass_cpu = (time.perf_counter() - t0) * min(workers, len(tasks))
+            repeats = max(1, int(round(budget_s / max(pass_cpu, 1e-3))))
+            t0 = time.perf_counter()
+            pool.map(_oracle_task, tasks * repeats, chunksize=1)
+            wall = time.perf_counter() - t0
+        finally:
+            if own:
+                pool.close()
+                pool.join()
+    finally:
+        shutil.rmtree(folder, ignore_errors=True)
+    max_err = 0.0
+    for i, ref in results:
+        max_err = max(max_err, float(np.max(np.abs(oracle.to_f64(out_bits[i], cfg.dtype) - ref))))
     return {
-        "value": done / t_total,
+        "value": len(tasks) * repeats / wall,
         "unit": "seqs/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{done} of {cfg.batch} sequences of one step (fp64 gather + softmax(qK^T)V, "
-                  f"BLAS limited to 1 thread), {t_total:.1f} s",
+        "sample": f"{len(tasks)} of {cfg.batch} sequences of one step (every {stride}th), "
+                  f"{repeats} pass(es), fp64 gather + softmax(qK^T)V, {workers} worker processes "
+                  f"with one BLAS thread each, {wall:.1f} s wall",
+        "host": host_cpu(),
         "max_abs_err_vs_gpu": max_err,
     }
 
@@ -218,6 +311,7 @@ SWAP_WORKLOADS = {
 }
 PEAK_HOST_LINK_GBPS = 64.0     # PCIe 5.0 x16, one direction (MI355X host interface)
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
+GRAPH_STEPS = 10               # decode steps per HIP graph in bench.py --graph
 
 
 def bench_swap(args, name):
@@ -534,7 +628,8 @@ def main(argv=None):
     ap.add_argument("--cold", action="store_true",
                     help="also time each step after evicting the last-level cache (done by "
                          "default when the step's working set fits in it)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle CPU work (summed over the worker processes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain copy of known size (the cache-write kernel copying "
@@ -550,6 +645,18 @@ def main(argv=None):
     if args.prefix_cache:          # host bookkeeping only
         return bench_prefix_cache(args, args.prefix_cache)
 
+    # the CPU baseline's worker processes start before anything here touches the GPU
+    decode_run = not (args.copy_calibration or args.cow or args.swap or args.prefill)
+    workers = oracle_pool() if decode_run and not args.no_cpu_baseline else None
+    try:
+        return _main_gpu(args, workers)
+    finally:
+        if workers is not None:
+            workers.close()
+            workers.join()
+
+
+def _main_gpu(args, workers):
     import torch
     import paged_kv_cache_68_amd as pk
     from workloads import config_by_name, make_case
@@ -595,7 +702,7 @@ def main(argv=None):
     case = make_case(cfg, where="device" if cfg.index in (3, 5) else "host", poison=False)
     dc = DeviceCase(case)
     nbytes = algorithmic_bytes(case.lengths, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
-                               cfg.elem_bytes, 2, cfg.block_size)
+                               cfg.elem_bytes, 2, cfg.block_size, tables=case.block_tables)
     stream = torch.cuda.current_stream()
     # Every workload writes each sequence's new token at position L - 1, so the cache write
     # can ride in the partition kernel (paged_attention_partitions_append); check that the
@@ -609,41 +716,53 @@ def main(argv=None):
         nbytes["write"] -= 8 * cfg.batch
         nbytes["step"] -= 8 * cfg.batch
         nbytes["partition_kernel"] += nbytes["write"]
+        nbytes["partition_kernel_unique"] += nbytes["write"]
 
-    def step(ev_a=None, ev_b=None, on=None):
+    # the step as a serving loop runs it: buffers checked once, one library call per step
+    # (partitions, then the reduce when some sequence needs one)
+    dstep = pk.DecodeStep(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens,
+                          new_key=dc.new_key if fused else None,
+                          new_value=dc.new_value if fused else None, scale=cfg.scale,
+                          partition_size=cfg.partition_size, workspace=dc.workspace)
+
+    def step(on=None, ev_a=None, ev_b=None):
         st = stream if on is None else on
         if not fused:
             pk.reshape_and_cache(dc.pool, 0, dc.new_key, dc.new_value, dc.slots, st)
-        if ev_a is not None:
-            ev_a.record(st)
-        if fused:
-            pk.paged_attention_partitions_append(dc.pool, 0, dc.out, dc.query, dc.new_key, dc.new_value,
-                                                 dc.tables, dc.lens, cfg.scale, cfg.partition_size,
-                                                 dc.workspace, st)
-        else:
-            pk.paged_attention_partitions(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
-                                          cfg.partition_size, dc.workspace, st)
-        if ev_b is not None:
-            ev_b.record(st)
-        pk.paged_attention_reduce(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens, cfg.scale,
-                                  cfg.partition_size, dc.workspace, st)
+        if ev_a is None:
+            dstep(st)
+            return
+        ev_a.record(st)
+        dstep.partitions(st)
+        ev_b.record(st)
+        dstep.reduce(st)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr, flush=True)
 
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # The K timed steps carry no events: on this stack a timing event is a marker the
+    # command processor serialises (about 4.5 us of GPU time each), which would lengthen
+    # short steps.  The partition kernel's own duration comes from K more steps with HIP
+    # events recorded around it on its stream.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(ev_a[i], ev_b[i])
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    part_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
-    achieved = nbytes["partition_kernel"] / (part_ms * 1e-3) / 1e9
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(ev_a=ev_a[i], ev_b=ev_b[i])
+    torch.cuda.synchronize()
+    part_times = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
+    part_ms = float(np.median(part_times))
+    # the kernel's HBM bytes: each distinct token row once (forks of a prefix share rows)
+    achieved = nbytes["partition_kernel_unique"] / (part_ms * 1e-3) / 1e9
+    effective = nbytes["partition_kernel"] / (part_ms * 1e-3) / 1e9
     seqs_per_s = cfg.batch / (ms_step * 1e-3)
     print(f"[bench] {ms_step * 1e3:.1f} us/step, partition kernel {part_ms * 1e3:.1f} us "
           f"= {achieved:.0f} GB/s", file=sys.stderr, flush=True)
@@ -682,37 +801,56 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": nbytes["partition_kernel"],
+            "algorithmic_bytes_per_launch": nbytes["partition_kernel_unique"],
             "avg_launch_us": part_ms * 1e3,
+            "launch_us_stat": f"median of {args.steps} HIP-event durations (mean "
+                              f"{np.mean(part_times) * 1e3:.1f} us), events on the kernel's stream "
+                              "in K steps run after the timed ones",
         },
     }
+    if nbytes["partition_kernel"] != nbytes["partition_kernel_unique"]:
+        # sequences share blocks: the roofline takes each distinct row once; the logical
+        # rate (every sequence's rows, as if each were read from HBM) is reported beside it
+        result["roofline"]["effective"] = {
+            "achieved": effective, "unit": "GB/s",
+            "logical_bytes_per_launch": nbytes["partition_kernel"],
+            "note": "every sequence's K/V rows counted, shared rows once per sequence",
+        }
     # --graph: also time the same step captured once in a HIP graph and replayed back to
     # back (how a serving loop might run short steps; each replay checked against the
     # eager output)
     if args.graph:
+        # the step captured in HIP graphs and replayed back to back, one step per graph
+        # and GRAPH_STEPS steps per graph: a graph launch costs a fixed amount of host and
+        # command-processor time on this stack, which a longer graph spreads over its steps
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             step(on=side)
         stream.wait_stream(side)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step(on=torch.cuda.current_stream())   # the capture stream
         ref = dc.out.clone()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        dc.out.fill_(7.0)
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        g_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        assert torch.equal(dc.out.view(torch.int16), ref.view(torch.int16)), "graph replay differs"
-        result["graph_replay"] = {"us_per_step": g_ms * 1e3, "seqs_per_s": cfg.batch / (g_ms * 1e-3),
-                                  "how": "the step captured in one HIP graph, replayed back to back"}
-        del graph
+        result["graph_replay"] = {"how": "the step captured in a HIP graph (n steps per graph), "
+                                         "graphs replayed back to back, every replay checked"}
+        for n in (1, GRAPH_STEPS):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(n):
+                    step(on=torch.cuda.current_stream())   # the capture stream
+            for _ in range(args.warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            dc.out.fill_(7.0)
+            reps = max(1, args.steps // n)
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                graph.replay()
+            torch.cuda.synchronize()
+            g_ms = (time.perf_counter() - t0) * 1e3 / (reps * n)
+            assert torch.equal(dc.out.view(torch.int16), ref.view(torch.int16)), "graph replay differs"
+            result["graph_replay"][f"{n}_steps_per_graph"] = {
+                "us_per_step": g_ms * 1e3, "seqs_per_s": cfg.batch / (g_ms * 1e-3)}
+            del graph
     # A working set smaller than the 256 MB Infinity Cache is served from it when steps
     # run back to back.  For such workloads also time each step cold: a 512 MiB write
     # between steps evicts the cache, and HIP events bracket the step alone.
@@ -740,7 +878,7 @@ def main(argv=None):
         del flush
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(dc, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(dc, args.cpu_budget, workers)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -98,6 +98,25 @@ def _ptr(t) -> Optional[int]:
 def _need(t, name, dtype=None, shape=None, ndim=None, device=None):
     """Check that ``t`` is a dense tensor on ``device`` (a torch.device; None: any CUDA
     device) with the given dtype and shape (None entries of ``shape`` match any size)."""
+    try:                      # fast path: everything as asked
+        if ((dtype is None or t.dtype == dtype) and t.is_contiguous() and
+                (t.is_cuda if device is None else
+                 (t.is_cuda and t.get_device() == device.index) if device.type == "cuda" else
+                 t.device == device)):
+            if shape is not None:
+                got = t.shape
+                if len(got) == len(shape) and all(w is None or g == w for g, w in zip(got, shape)):
+                    return t
+            elif ndim is None or t.dim() == ndim:
+                return t
+    except AttributeError:
+        pass
+    _explain(t, name, dtype, shape, ndim, device)
+    return t
+
+
+def _explain(t, name, dtype, shape, ndim, device):
+    """Raise ValueError naming what is wrong with ``t``."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
@@ -116,7 +135,7 @@ def _need(t, name, dtype=None, shape=None, ndim=None, device=None):
             raise ValueError(f"{name}: expected shape {want}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: expected a contiguous tensor")
-    return t
+    raise ValueError(f"{name}: not accepted")
 
 
 def _need_bytes(t, name, device):
@@ -126,11 +145,41 @@ def _need_bytes(t, name, device):
     return _need(t, name, device=device)
 
 
+def _decode_args_ok(pool, out, query, block_tables, context_lens, new_key, new_value, workspace):
+    """The common case in one expression: every tensor as _check_decode_args wants it."""
+    torch = _torch()
+    dt, i32 = pool.io_dtype, torch.int32
+    di = pool.device_index
+    b, hq, d = query.shape
+    ok = (query.dtype == dt and out.dtype == dt and d == pool.head_dim and hq > 0 and
+          hq % pool.num_kv_heads == 0 and out.shape == query.shape and
+          block_tables.dtype == i32 and context_lens.dtype == i32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == b and context_lens.dim() == 1 and context_lens.shape[0] == b and
+          query.get_device() == di and out.get_device() == di and block_tables.get_device() == di and
+          context_lens.get_device() == di and query.is_contiguous() and out.is_contiguous() and
+          block_tables.is_contiguous() and context_lens.is_contiguous())
+    if ok and (new_key is not None or new_value is not None):
+        row = (b, pool.num_kv_heads, d)
+        ok = (new_key.dtype == dt and new_value.dtype == dt and new_key.shape == row and
+              new_value.shape == row and new_key.get_device() == di and
+              new_value.get_device() == di and new_key.is_contiguous() and new_value.is_contiguous())
+    if ok and workspace is not None:
+        ok = workspace.get_device() == di and workspace.is_contiguous()
+    return ok
+
+
 def _check_decode_args(pool, out, query, block_tables, context_lens, new_key=None, new_value=None,
                        workspace=None):
     """Shapes of a decode call: query / out [B, Hq, D] in the pool's io dtype with D the
     pool's head size and Hq a multiple of its KV heads; tables int32 [B, max_blocks];
     lengths int32 [B]; new keys / values [B, Hkv, D]; all on the pool's device."""
+    try:
+        fast = _decode_args_ok(pool, out, query, block_tables, context_lens, new_key, new_value,
+                               workspace)
+    except (AttributeError, TypeError, ValueError):
+        fast = False
+    if fast:
+        return int(query.shape[0]), int(query.shape[1]), int(block_tables.shape[1])
     dev = pool.device
     _need(query, "query", pool.io_dtype, ndim=3, device=dev)
     batch, hq, d = (int(x) for x in query.shape)
@@ -214,6 +263,11 @@ class KVPool:
     @property
     def block_size(self):
         return self.desc.block_size
+
+    @property
+    def device_index(self):
+        """Index of the pool's GPU, as torch's get_device() gives it."""
+        return self.device.index
 
     @property
     def device(self):
@@ -380,19 +434,25 @@ def paged_attention_decode_noalloc(pool: KVPool, layer: int, out, query, block_t
 class DecodeStep:
     """One decode step prepared once for buffers a serving loop reuses: the tensors are
     checked when the step is built, and each call is then a single call into the library
+    with the arguments already converted.  ``step()`` runs the whole step
     (paged_attention_decode_append when new keys / values are given, else
-    paged_attention_decode: partitions, and the reduce when some sequence needs one).
+    paged_attention_decode); ``step.partitions()`` and ``step.reduce()`` run its two
+    phases (paged_attention_partitions[_append], paged_attention_reduce) for callers that
+    time or schedule them separately.
 
     The step keeps the tensors' addresses, so the tensors must stay alive and keep their
     storage (update their contents in place between calls).  Lengths and tables are read
-    on the device at each call, so they may change, within the shapes given here."""
+    on the device at each call, so they may change, within the shapes given here.
+    ``stream`` (a torch stream or a raw handle) fixes the stream; without it each call
+    uses torch's current stream."""
 
     def __init__(self, pool: KVPool, layer: int, out, query, block_tables, context_lens,
-                 new_key=None, new_value=None, scale=None, partition_size=0, workspace=None):
-        batch, hq, max_blocks = _check_decode_args(pool, out, query, block_tables, context_lens,
-                                                   new_key, new_value, workspace)
+                 new_key=None, new_value=None, scale=None, partition_size=0, workspace=None,
+                 stream=None):
         if (new_key is None) != (new_value is None):
             raise ValueError("DecodeStep: give both new_key and new_value, or neither")
+        batch, hq, max_blocks = _check_decode_args(pool, out, query, block_tables, context_lens,
+                                                   new_key, new_value, workspace)
         if workspace is None:
             workspace = alloc_workspace(pool, batch, hq, max_blocks, partition_size)
         if scale is None:
@@ -405,21 +465,34 @@ class DecodeStep:
                 ctypes.c_int32(batch), ctypes.c_int32(hq), ctypes.c_float(float(scale)),
                 ctypes.c_int32(int(partition_size)), vp(_ptr(workspace)),
                 ctypes.c_size_t(_nbytes(workspace))]
+        L = lib()
         if new_key is not None:
-            self._fn = lib().paged_attention_decode_append
-            self._name = "paged_attention_decode_append"
-            self._args = head + [vp(_ptr(new_key)), vp(_ptr(new_value))] + tail
+            rows = [vp(_ptr(new_key)), vp(_ptr(new_value))]
+            self._whole = ("paged_attention_decode_append", L.paged_attention_decode_append, head + rows + tail)
+            self._first = ("paged_attention_partitions_append", L.paged_attention_partitions_append,
+                           head + rows + tail)
         else:
-            self._fn = lib().paged_attention_decode
-            self._name = "paged_attention_decode"
-            self._args = head + tail
+            self._whole = ("paged_attention_decode", L.paged_attention_decode, head + tail)
+            self._first = ("paged_attention_partitions", L.paged_attention_partitions, head + tail)
+        self._second = ("paged_attention_reduce", L.paged_attention_reduce, head + tail)
+        self._stream = None if stream is None else vp(_stream(stream))
         self.out = out
 
-    def __call__(self, stream=None):
-        st = self._fn(*self._args, _stream(stream))
+    def _run(self, call, stream):
+        name, fn, args = call
+        st = fn(*args, self._stream if stream is None and self._stream is not None else _stream(stream))
         if st:
-            check(st, self._name)
+            check(st, name)
+
+    def __call__(self, stream=None):
+        self._run(self._whole, stream)
         return self.out
+
+    def partitions(self, stream=None):
+        self._run(self._first, stream)
+
+    def reduce(self, stream=None):
+        self._run(self._second, stream)
 
 
 def _check_prefill_args(pool, out, query, query_start, block_tables, context_lens):

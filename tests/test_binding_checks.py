@@ -42,7 +42,9 @@ def rec(monkeypatch):
 
 def fake_pool(device=CPU, hkv=2, d=64, io=torch.float16, store=torch.float16, bs=16):
     """The attributes the binding reads from a KVPool."""
-    return SimpleNamespace(handle=None, device=device, io_dtype=io, dtype=store, head_dim=d,
+    return SimpleNamespace(handle=None, device=device,
+                           device_index=-1 if device.type == "cpu" else device.index,
+                           io_dtype=io, dtype=store, head_dim=d,
                            num_kv_heads=hkv, block_size=bs, desc=SimpleNamespace(block_size=bs),
                            memory=torch.empty(0, device="meta"))
 
@@ -223,9 +225,9 @@ def test_decode_step_checks_once_and_calls_once(rec, monkeypatch):
             calls.append((self.name, len(args)))
             return 0
 
-    monkeypatch.setattr(pk, "lib", lambda: SimpleNamespace(
-        paged_attention_decode=Fn("paged_attention_decode"),
-        paged_attention_decode_append=Fn("paged_attention_decode_append")))
+    names = ["paged_attention_decode", "paged_attention_decode_append", "paged_attention_partitions",
+             "paged_attention_partitions_append", "paged_attention_reduce"]
+    monkeypatch.setattr(pk, "lib", lambda: SimpleNamespace(**{n: Fn(n) for n in names}))
     a = good_decode()
     ws = torch.empty(16, dtype=torch.uint8)
     step = pk.DecodeStep(fake_pool(), 0, a["out"], a["query"], a["block_tables"], a["context_lens"],
@@ -233,10 +235,14 @@ def test_decode_step_checks_once_and_calls_once(rec, monkeypatch):
     step()
     step()
     nk = torch.zeros(3, 2, 64, dtype=torch.float16)
-    pk.DecodeStep(fake_pool(), 0, a["out"], a["query"], a["block_tables"], a["context_lens"],
-                  new_key=nk, new_value=nk.clone(), workspace=ws)()
+    s2 = pk.DecodeStep(fake_pool(), 0, a["out"], a["query"], a["block_tables"], a["context_lens"],
+                       new_key=nk, new_value=nk.clone(), workspace=ws)
+    s2()
+    s2.partitions()
+    s2.reduce()
     assert calls == [("paged_attention_decode", 14), ("paged_attention_decode", 14),
-                     ("paged_attention_decode_append", 16)]
+                     ("paged_attention_decode_append", 16), ("paged_attention_partitions_append", 16),
+                     ("paged_attention_reduce", 14)]
     with pytest.raises(ValueError):
         pk.DecodeStep(fake_pool(), 0, a["out"], a["query"], a["block_tables"], a["context_lens"],
                       new_key=nk, workspace=ws)
