@@ -33,9 +33,12 @@
  *    element; "PagedAttention and Virtual Memory Management", section 1: b = 1 for
  *    FP8).  Queries, attention outputs and the new keys / values given to
  *    reshape_and_cache use the pool's io_dtype (fp16 or bf16; for 16-bit pools it is
- *    the pool's dtype).  Arithmetic is fp32: stored values are widened exactly, dot
- *    products, softmax and the P.V accumulation are fp32, and the output is rounded to
- *    the io type with round-to-nearest-even.
+ *    the pool's dtype).  Arithmetic: stored values are widened exactly; dot products and
+ *    the softmax are fp32; the softmax weights enter the P.V product on the matrix cores
+ *    as 16-bit operands, each weight split into a rounded part and its rounded remainder
+ *    (about 16 significand bits; prefill with fp16 io uses one fp16 part, 11 bits), with
+ *    the products accumulated in fp32; the output is rounded to the io type with
+ *    round-to-nearest-even.
  *  - FP8 E4M3: 1 sign, 4 exponent (bias 7) and 3 mantissa bits, no infinities,
  *    S.1111.111 is NaN, largest finite magnitude 448, no scale factor.  The cache write
  *    rounds to the nearest code (ties to even), saturates larger magnitudes and

@@ -88,6 +88,17 @@ struct BF16 {
     }
 };
 
+// Two fp32 values as a sum of two packed 16-bit parts of S: x = (RNE(a), RNE(b)) and
+// y = the rounded remainders (a - x.a, b - x.b), so that x + y carries about twice the
+// significand bits of one 16-bit value (relative error near 2^-18 for bf16, 2^-22 for
+// fp16, apart from fp16 underflow below 2^-24).  Used for the softmax weights of the
+// value product: x and y each go through the matrix cores, accumulating into one sum.
+template <class S>
+__device__ __forceinline__ uint2 split_pack2(float a, float b) {
+    const uint32_t hi = S::pack2(a, b);
+    return make_uint2(hi, S::pack2(a - S::lo(hi), b - S::hi(hi)));
+}
+
 // Four E4M3 codes (one dword, code i in byte i) -> four 16-bit values of S, in order.
 template <class S>
 __device__ __forceinline__ uint2 fp8x4_to(uint32_t w) {

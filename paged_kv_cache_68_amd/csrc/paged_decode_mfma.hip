@@ -368,7 +368,13 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
 #pragma unroll
             for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
         }
-        const uint2 pt = make_uint2(S::pack2(pr[0], pr[1]), S::pack2(pr[2], pr[3]));
+        // P^T operand as two 16-bit parts (rounded weights, then the rounded remainders):
+        // both go through the matrix cores, so the weights enter the value product with
+        // about 16 significand bits instead of the storage type's 8 or 11
+        const uint2 p01 = split_pack2<S>(pr[0], pr[1]);
+        const uint2 p23 = split_pack2<S>(pr[2], pr[3]);
+        const uint2 pt = make_uint2(p01.x, p23.x);
+        const uint2 ptl = make_uint2(p01.y, p23.y);
         // V^T operand of element e: (tok 4c, 4c+1 | 4c+2, 4c+3) at element EPL*n + e;
         // rows past the valid tokens were loaded as zeros
 #pragma unroll
@@ -381,6 +387,8 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
             const uint2 odd = make_uint2(hi_halves(w0, w1), hi_halves(w2, w3));
             acc[2 * q] = S::mfma_k16(even, pt, acc[2 * q]);
             acc[2 * q + 1] = S::mfma_k16(odd, pt, acc[2 * q + 1]);
+            acc[2 * q] = S::mfma_k16(even, ptl, acc[2 * q]);
+            acc[2 * q + 1] = S::mfma_k16(odd, ptl, acc[2 * q + 1]);
         }
         if constexpr (MODE == kItem) {     // last block of a partition: emit it
             const int j = walk.jb + k;

@@ -95,6 +95,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int STAGE_K = KT * ROWB_K;
     constexpr int STAGE_V = KT * ROWB_V;
     using Raw = typename std::conditional<KV8, uint2, uint4>::type;
+    constexpr bool kSplitWeights = std::is_same<S, BF16>::value;
 
     __shared__ __align__(16) uint8_t lds_k[2][STAGE_K];
     __shared__ __align__(16) uint8_t lds_v[2][STAGE_V];
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                 for (int i = 0; i < NQK; ++i) x = S::mfma_k32(kop[st][i], qv[cb][i], x);
                 sc[cb][st] = x;
             }
-        uint4 pop[NC];
+        uint4 pop[NC], pol[NC];                  // weights: rounded parts, remainders
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb) {
             float sv[8];
@@ -338,17 +339,35 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             float pr[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) pr[k] = fast_exp2(fmaf(sv[k], sl2, -mu));
-            pop[cb] = make_uint4(S::pack2(pr[0], pr[1]), S::pack2(pr[2], pr[3]),
-                                 S::pack2(pr[4], pr[5]), S::pack2(pr[6], pr[7]));
+            // bf16 weights: a rounded part plus its rounded remainder, both through the
+            // matrix cores, so the value product sees about 16 significand bits of every
+            // weight instead of bf16's 8 (with 8 bits a short row's output can miss the
+            // decode bar by the weights' rounding alone).  fp16 weights keep 11 bits in
+            // one part.
+            if constexpr (kSplitWeights) {
+                const uint2 w01 = split_pack2<S>(pr[0], pr[1]);
+                const uint2 w23 = split_pack2<S>(pr[2], pr[3]);
+                const uint2 w45 = split_pack2<S>(pr[4], pr[5]);
+                const uint2 w67 = split_pack2<S>(pr[6], pr[7]);
+                pop[cb] = make_uint4(w01.x, w23.x, w45.x, w67.x);
+                pol[cb] = make_uint4(w01.y, w23.y, w45.y, w67.y);
+            } else {
+                pop[cb] = make_uint4(S::pack2(pr[0], pr[1]), S::pack2(pr[2], pr[3]),
+                                     S::pack2(pr[4], pr[5]), S::pack2(pr[6], pr[7]));
+            }
             // the column sums of the weights, on the matrix cores: an all-ones A operand
-            // puts sum_k P[k][n] in every row of column n (the same rounded weights the
-            // value product uses)
+            // puts sum_k P[k][n] in every row of column n (the same parts the value
+            // product uses)
             lacc[cb] = S::mfma_k32(ones, pop[cb], lacc[cb]);
+            if constexpr (kSplitWeights) lacc[cb] = S::mfma_k32(ones, pol[cb], lacc[cb]);
         }
 #pragma unroll
         for (int e = 0; e < DB; ++e)
 #pragma unroll
-            for (int cb = 0; cb < NC; ++cb) acc[cb][e] = S::mfma_k32(vop[e], pop[cb], acc[cb][e]);
+            for (int cb = 0; cb < NC; ++cb) {
+                acc[cb][e] = S::mfma_k32(vop[e], pop[cb], acc[cb][e]);
+                if constexpr (kSplitWeights) acc[cb][e] = S::mfma_k32(vop[e], pol[cb], acc[cb][e]);
+            }
     };
     // one stage: its 32-key runs in turn, up to this wave's last position
     auto compute = [&](int j, int buf) {

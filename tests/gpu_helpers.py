@@ -39,6 +39,18 @@ def oracle_for_seqs(dc: DeviceCase, seqs):
     return np.stack(out)
 
 
+SIG = {"bf16": 8, "f16": 11}      # significand bits of each io type
+
+
+def flat_bar(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Per element: the max-abs bar TOL, except where rounding the exact value to the io
+    type by itself costs more (half an ulp of |ref|: bf16 at |o| >= 4, fp16 at |o| >= 8),
+    there that half ulp plus an eighth of the bar."""
+    _, e = np.frexp(np.abs(ref))
+    half_ulp = np.ldexp(1.0, e - 1 - SIG[dtype])
+    return np.where(half_ulp < TOL[dtype], TOL[dtype], half_ulp + TOL[dtype] / 8)
+
+
 def max_abs_err(gpu_bits: np.ndarray, ref: np.ndarray, dtype: str) -> float:
     got = oracle.to_f64(gpu_bits, dtype)
     assert np.all(np.isfinite(got)), "non-finite output"

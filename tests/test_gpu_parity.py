@@ -20,7 +20,7 @@ from workloads import config_by_name, make_case, nan_bits, round_to_bits  # noqa
 from workloads.configs import DecodeConfig  # noqa: E402
 
 from .gpu_helpers import (  # noqa: E402
-    TOL, DeviceCase, max_abs_err, oracle_after_write, oracle_for_seqs, to_dev, to_host_bits,
+    TOL, DeviceCase, flat_bar, max_abs_err, oracle_after_write, oracle_for_seqs, to_dev, to_host_bits,
 )
 
 
@@ -242,6 +242,19 @@ def test_block_permutation_bit_identical_and_deterministic():
     t2 = np.where(tables >= 0, pi[np.maximum(tables, 0)], -1).astype(np.int32)
     out2 = _run_custom(cfg, lens, t2, kp2, vp2, q)
     assert np.array_equal(out, out2)
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(32, 8, 128, "bf16"), (14, 2, 64, "f16"), (8, 8, 128, "bf16")])
+def test_short_contexts_meet_the_flat_bar(hq, hkv, d, dtype):
+    """Contexts of 2 to 33 tokens average few values, so rounding the softmax weights for
+    the value product would show there first: every element within the flat bar."""
+    lens = list(range(2, 34)) * 2
+    cfg, lens, tables, kp, vp, q = _custom_case(lens, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=40 + d)
+    out = _run_custom(cfg, lens, tables, kp, vp, q)
+    ref = oracle.paged_decode(q, kp, vp, tables, lens, cfg.scale, 16, dtype)
+    err = np.abs(oracle.to_f64(out, dtype) - ref)
+    _say(f"short contexts {dtype} G={hq // hkv}: max abs err {err.max():.3e}")
+    assert np.all(err <= flat_bar(ref, dtype))
 
 
 def test_table_padding_is_never_read():
