@@ -377,18 +377,24 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
         const uint2 ptl = make_uint2(p01.y, p23.y);
         // V^T operand of element e: (tok 4c, 4c+1 | 4c+2, 4c+3) at element EPL*n + e;
         // rows past the valid tokens were loaded as zeros
+        // all rounded-part products first, then the remainders: the two products into one
+        // accumulator are never back to back
+        uint2 vev[EPL / 2], vod[EPL / 2];
 #pragma unroll
         for (int q = 0; q < EPL / 2; ++q) {
             const uint32_t w0 = v_word(buf, 0, q);
             const uint32_t w1 = v_word(buf, 1, q);
             const uint32_t w2 = v_word(buf, 2, q);
             const uint32_t w3 = v_word(buf, 3, q);
-            const uint2 even = make_uint2(lo_halves(w0, w1), lo_halves(w2, w3));
-            const uint2 odd = make_uint2(hi_halves(w0, w1), hi_halves(w2, w3));
-            acc[2 * q] = S::mfma_k16(even, pt, acc[2 * q]);
-            acc[2 * q + 1] = S::mfma_k16(odd, pt, acc[2 * q + 1]);
-            acc[2 * q] = S::mfma_k16(even, ptl, acc[2 * q]);
-            acc[2 * q + 1] = S::mfma_k16(odd, ptl, acc[2 * q + 1]);
+            vev[q] = make_uint2(lo_halves(w0, w1), lo_halves(w2, w3));
+            vod[q] = make_uint2(hi_halves(w0, w1), hi_halves(w2, w3));
+            acc[2 * q] = S::mfma_k16(vev[q], pt, acc[2 * q]);
+            acc[2 * q + 1] = S::mfma_k16(vod[q], pt, acc[2 * q + 1]);
+        }
+#pragma unroll
+        for (int q = 0; q < EPL / 2; ++q) {
+            acc[2 * q] = S::mfma_k16(vev[q], ptl, acc[2 * q]);
+            acc[2 * q + 1] = S::mfma_k16(vod[q], ptl, acc[2 * q + 1]);
         }
         if constexpr (MODE == kItem) {     // last block of a partition: emit it
             const int j = walk.jb + k;

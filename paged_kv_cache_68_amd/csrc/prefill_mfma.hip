@@ -359,15 +359,21 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             // puts sum_k P[k][n] in every row of column n (the same parts the value
             // product uses)
             lacc[cb] = S::mfma_k32(ones, pop[cb], lacc[cb]);
-            if constexpr (kSplitWeights) lacc[cb] = S::mfma_k32(ones, pol[cb], lacc[cb]);
         }
+        // all rounded-part products first, then the remainders: the two products into one
+        // accumulator are never back to back
 #pragma unroll
         for (int e = 0; e < DB; ++e)
 #pragma unroll
-            for (int cb = 0; cb < NC; ++cb) {
-                acc[cb][e] = S::mfma_k32(vop[e], pop[cb], acc[cb][e]);
-                if constexpr (kSplitWeights) acc[cb][e] = S::mfma_k32(vop[e], pol[cb], acc[cb][e]);
-            }
+            for (int cb = 0; cb < NC; ++cb) acc[cb][e] = S::mfma_k32(vop[e], pop[cb], acc[cb][e]);
+        if constexpr (kSplitWeights) {
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) lacc[cb] = S::mfma_k32(ones, pol[cb], lacc[cb]);
+#pragma unroll
+            for (int e = 0; e < DB; ++e)
+#pragma unroll
+                for (int cb = 0; cb < NC; ++cb) acc[cb][e] = S::mfma_k32(vop[e], pol[cb], acc[cb][e]);
+        }
     };
     // one stage: its 32-key runs in turn, up to this wave's last position
     auto compute = [&](int j, int buf) {
