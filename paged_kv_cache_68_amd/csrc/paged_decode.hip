@@ -114,6 +114,9 @@ __global__ __launch_bounds__(256) void pa_partition_valu(DecodeArgs a, int n_ite
     // through this wave's LDS staging area so that every lane writes whole lines.
     extern __shared__ float smem[];
     float* stage = smem + wave * G * (D + 4);     // [G][D], then (m, l) per head, 16-B aligned
+    // per_item >= the partition count: this wave walks whole sequences and writes their
+    // final output once, with no partial results
+    const bool whole = !SPLIT && per_item >= a.num_parts;
     auto flush = [&](int p) {
         merge_rows();
         if (r == 0) {
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(256) void pa_partition_valu(DecodeArgs a, int n_ite
                     *reinterpret_cast<float2*>(stage + G * D + 2 * g) = make_float2(m[g], l[g]);
         }
         // the LDS operations of one wave complete in order: the reads below see the writes
-        store_partition<S, D>(a, it, G, p, stage, stage + G * D, lane);
+        store_partition<S, D>(a, it, G, p, stage, stage + G * D, lane, whole);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             m[g] = -INFINITY;
@@ -202,9 +205,10 @@ __global__ __launch_bounds__(256) void pa_partition_valu(DecodeArgs a, int n_ite
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw[i][g], vf[e], acc[g][e]);
         }
-        if constexpr (!SPLIT) {     // last block of a partition: emit it
+        if constexpr (!SPLIT) {     // last block of a partition (or of the sequence): emit it
             const int j = walk.jb + k;
-            if ((j + 1) % a.part_blocks == 0 || k + 1 == walk.nk) flush(j / a.part_blocks);
+            if (whole ? k + 1 == walk.nk : ((j + 1) % a.part_blocks == 0 || k + 1 == walk.nk))
+                flush(j / a.part_blocks);
         }
     };
 
@@ -304,24 +308,51 @@ __global__ __launch_bounds__(256) void pa_reduce(DecodeArgs a) {
     for (int e = 0; e < PER; ++e) o[e] = S::narrow(lsum > 0.f ? A[e] / lsum : 0.f);
 }
 
+// Partitions per wave of the VALU kernel's item plan (0: the split plan is used).
+template <class S, int D, int G>
+int valu_parts_per_wave(const DecodeArgs& a) {
+    const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.num_parts;
+    if (split_items(items)) return 0;
+    static const int64_t slots = resident_waves(reinterpret_cast<const void*>(&pa_partition_valu<S, D, G, false>));
+    return partitions_per_wave(items, slots, a.num_parts, a.part_blocks);
+}
+
 template <class S, int D, int G>
 hipError_t launch_part_t(const DecodeArgs& a, hipStream_t stream) {
     const int64_t items = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.num_parts;
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidValue;
     const size_t lds = static_cast<size_t>(kWavesPerGroup) * G * (D + 4) * sizeof(float);
-    if (split_items(items)) {
+    const int per = valu_parts_per_wave<S, D, G>(a);
+    if (per == 0) {
         hipLaunchKernelGGL((pa_partition_valu<S, D, G, true>), dim3(static_cast<unsigned>(items)),
                            dim3(64 * kWavesPerGroup), lds, stream, a, static_cast<int>(items), 1);
     } else {
-        static const int64_t slots = resident_waves(reinterpret_cast<const void*>(&pa_partition_valu<S, D, G, false>));
-        const int per = partitions_per_wave(items, slots, a.num_parts, a.part_blocks);
         const int64_t waves = static_cast<int64_t>(a.batch) * a.num_kv_heads * ceil_div(a.num_parts, per);
         const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
         hipLaunchKernelGGL((pa_partition_valu<S, D, G, false>), dim3(static_cast<unsigned>(groups)),
                            dim3(64 * kWavesPerGroup), lds, stream, a, static_cast<int>(waves), per);
     }
     return hipGetLastError();
+}
+
+// Partitions the VALU kernel combines by itself: all of them when each wave walks whole
+// sequences, else none (1).
+template <class S, int D>
+int valu_chunk(int group, const DecodeArgs& a) {
+    int per = 0;
+    switch (group) {
+        case 1: per = valu_parts_per_wave<S, D, 1>(a); break;
+        case 2: per = valu_parts_per_wave<S, D, 2>(a); break;
+        case 3: per = valu_parts_per_wave<S, D, 3>(a); break;
+        case 4: per = valu_parts_per_wave<S, D, 4>(a); break;
+        case 5: per = valu_parts_per_wave<S, D, 5>(a); break;
+        case 6: per = valu_parts_per_wave<S, D, 6>(a); break;
+        case 7: per = valu_parts_per_wave<S, D, 7>(a); break;
+        case 8: per = valu_parts_per_wave<S, D, 8>(a); break;
+        default: break;
+    }
+    return per >= a.num_parts ? a.num_parts : 1;
 }
 
 template <class S, int D>
@@ -368,9 +399,11 @@ static int kernel_choice(int kv_dtype, int io_dtype, int head_dim, int group, co
 }
 
 int partition_chunk(int kv_dtype, int io_dtype, int head_dim, int group, const DecodeArgs& a) {
-    return kernel_choice(kv_dtype, io_dtype, head_dim, group, a) == 1
-               ? partition_chunk_mfma(kv_dtype, io_dtype, group, head_dim, a)
-               : 1;
+    if (kernel_choice(kv_dtype, io_dtype, head_dim, group, a) == 1)
+        return partition_chunk_mfma(kv_dtype, io_dtype, group, head_dim, a);
+    if (kv_dtype == KV_DTYPE_F16)
+        return head_dim == 64 ? valu_chunk<F16, 64>(group, a) : valu_chunk<F16, 128>(group, a);
+    return head_dim == 64 ? valu_chunk<BF16, 64>(group, a) : valu_chunk<BF16, 128>(group, a);
 }
 
 hipError_t launch_partitions(int kv_dtype, int io_dtype, int head_dim, int group,

@@ -188,9 +188,10 @@ __device__ __forceinline__ size_t part_row(const DecodeArgs& a, int b, int kvh, 
 // with 16-byte accesses, so the global writes are whole contiguous lines.
 template <class S, int D>
 __device__ __forceinline__ void store_partition(const DecodeArgs& a, const Item& it, int G, int p,
-                                                const float* st_acc, const float* st_ml, int lane) {
+                                                const float* st_acc, const float* st_ml, int lane,
+                                                bool whole = false) {
     const int n = G * D;
-    if (it.nparts == 1) {
+    if (it.nparts == 1 || whole) {     // whole: the state covers every partition
         uint16_t* o = a.out + (static_cast<size_t>(it.b) * a.num_q_heads + it.kvh * G) * D;
         for (int i = lane * 8; i < n; i += 512) {
             const float lg = st_ml[2 * (i / D) + 1];

@@ -257,6 +257,22 @@ def test_short_contexts_meet_the_flat_bar(hq, hkv, d, dtype):
     assert np.all(err <= flat_bar(ref, dtype))
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 4)])
+def test_valu_kernel_with_whole_sequences_per_wave(monkeypatch, hq, hkv):
+    """The VALU kernel's item plan with every partition of a sequence on one wave (no
+    partial results, no reduce): the oracle's answer, sequences of 0 to 3,000 tokens."""
+    monkeypatch.setenv("PAGEDKV_KERNEL", "valu")
+    monkeypatch.setenv("PAGEDKV_SPLIT", "0")
+    monkeypatch.setenv("PAGEDKV_PARTS_PER_WAVE", "16")
+    lens = [3000, 777, 16, 1, 0, 513, 2048, 1500]
+    cfg, lens, tables, kp, vp, q = _custom_case(lens, hq=hq, hkv=hkv, d=128, dtype="f16", seed=70 + hq)
+    out = _run_custom(cfg, lens, tables, kp, vp, q)
+    ref = oracle.paged_decode(q, kp, vp, tables, lens, cfg.scale, 16, "f16")
+    err = np.abs(oracle.to_f64(out, "f16") - ref)
+    _say(f"VALU whole-sequence waves G={hq // hkv}: max abs err {err.max():.3e}")
+    assert np.all(err <= flat_bar(ref, "f16"))
+
+
 def test_table_padding_is_never_read():
     cfg, lens, tables, kp, vp, q = _custom_case([20, 100, 3], seed=8)
     base = _run_custom(cfg, lens, tables, kp, vp, q)
