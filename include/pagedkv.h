@@ -154,14 +154,19 @@ kv_status_t kv_host_pool_create(const kv_pool_desc_t* desc, void* host_base, siz
  * NULL. */
 int32_t kv_pool_is_host(const kv_pool_t* pool);
 
-/* Destroy a handle; frees the pool memory only if the library allocated it.
- * NULL is accepted and ignored.  The caller must ensure no enqueued work still uses it. */
+/* Destroy a handle; frees the pool memory only if the library allocated it (the pool is
+ * cut into blocks once and lives as long as the engine: "Why AI servers waste memory, and
+ * how paging fixes it", "The idea: a block table").  NULL is accepted and ignored.  The
+ * caller must ensure no enqueued work still uses it. */
 kv_status_t kv_pool_destroy(kv_pool_t* pool);
 
-/* Copy the pool's descriptor into *desc. */
+/* Copy the pool's descriptor into *desc (the geometry of "PagedAttention and Virtual
+ * Memory Management", section 3: block size, heads, head size, element bytes). */
 kv_status_t kv_pool_get_desc(const kv_pool_t* pool, kv_pool_desc_t* desc);
 
-/* Device addresses of layer `layer`'s K and V caches (either output may be NULL). */
+/* Device addresses of layer `layer`'s K and V caches (either output may be NULL): the
+ * per-layer pool bases PoolPtr_K and PoolPtr_V of "PagedAttention and Virtual Memory
+ * Management", section 4 (Addr_K / Addr_V), laid out as kv_pool_bytes states. */
 kv_status_t kv_pool_layer_ptrs(const kv_pool_t* pool, int32_t layer, void** k_cache,
                                void** v_cache);
 
@@ -182,10 +187,13 @@ kv_status_t kv_pool_layer_ptrs(const kv_pool_t* pool, int32_t layer, void** k_ca
 kv_status_t reshape_and_cache(kv_pool_t* pool, int32_t layer, const void* key, const void* value,
                               const int64_t* slot_mapping, int32_t num_tokens, hipStream_t stream);
 
-/* Workspace bytes paged_attention_decode needs for this batch shape: fp32 partial
- * results (running max, running sum and unnormalised accumulator) of every
- * (sequence, query head, partition).  0 when no sequence can have more than one
- * partition (then workspace may be NULL).  partition_size 0 means 512.
+/* Workspace bytes paged_attention_decode needs for this batch shape: the intermediate
+ * (m, l, O) that each thread block of a split sequence leaves for the cross-block
+ * reduction ("PagedAttention and Virtual Memory Management", section 4), in fp32 --
+ * running max, running sum and unnormalised accumulator -- of every (sequence, query
+ * head, partition).  0 when no sequence can have more than one partition (then workspace
+ * may be NULL).  partition_size 0 means 512.  block_size (the pool's) fixes how many
+ * partitions max_blocks_per_seq blocks can hold.
  * Returns SIZE_MAX for invalid arguments. */
 size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                        int32_t max_blocks_per_seq, int32_t block_size,
