@@ -71,29 +71,33 @@ def algorithmic_bytes(lens, hq, hkv, d, kv_elem, io_elem=2, block_size=16, table
 # the sources that decide the decode partition kernel's code and launch shape
 DECODE_SOURCES = ("api.cpp", "device_common.h", "internal.h", "paged_decode.hip",
                   "paged_decode_mfma.hip", "partition_common.h")
+# ... and those of the shared-prefix step (its prefix pass is the multi-token kernel)
+CASCADE_SOURCES = DECODE_SOURCES + ("prefill_mfma.hip",)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(names=DECODE_SOURCES) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_68_amd", "csrc")
-    for name in DECODE_SOURCES:
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch of the partition kernel from a committed rocprofv3 counter
-    run (profiles/<kernel>_<workload>_traffic.json: TCC_EA0_RDREQ_DRAM_32B and
+def load_traffic(workload: str, kernel: str = PARTITION_KERNEL):
+    """HBM bytes per launch of the partition kernel (or per shared-prefix step, kernel
+    "pa_cascade") from a committed rocprofv3 counter run
+    (profiles/<kernel>_<workload>_traffic.json: TCC_EA0_RDREQ_DRAM_32B and
     TCC_EA0_WRREQ_WRITE_DRAM_32B, requests to DRAM counted in 32-byte units, so bytes =
     32 x count with no calibration), if taken on the current source."""
-    path = os.path.join(PROFILE_DIR, f"{PARTITION_KERNEL}_{workload}_traffic.json")
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    names = CASCADE_SOURCES if kernel == "pa_cascade" else DECODE_SOURCES
+    if rec.get("kernel_source_hash") != kernel_source_hash(names):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -633,6 +637,9 @@ def main(argv=None):
     ap.add_argument("--separate-write", action="store_true",
                     help="launch reshape_and_cache on its own instead of folding the cache "
                          "write into the partition kernel")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="for a batch of forks of one prefix, time the plain decode instead of "
+                         "paged_attention_decode_shared_prefix")
     ap.add_argument("--cold", action="store_true",
                     help="also time each step after evicting the last-level cache (done by "
                          "default when the step's working set fits in it)")
@@ -667,7 +674,7 @@ def main(argv=None):
 def _main_gpu(args, workers):
     import torch
     import paged_kv_cache_68_amd as pk
-    from workloads import config_by_name, make_case
+    from workloads import config_by_name, is_fork, make_case
     from tests.device_case import DeviceCase
 
     if not torch.cuda.is_available():
@@ -726,12 +733,18 @@ def _main_gpu(args, workers):
         nbytes["partition_kernel"] += nbytes["write"]
         nbytes["partition_kernel_unique"] += nbytes["write"]
 
+    # forks of one prefix: the shared-prefix entry point (the shared blocks read once for
+    # the batch), unless --no-shared-prefix
+    prefix_blocks = len(case.shared_blocks) if is_fork(cfg) and not args.no_shared_prefix else 0
+    cascade = prefix_blocks > 0
+
     # the step as a serving loop runs it: buffers checked once, one library call per step
     # (partitions, then the reduce when some sequence needs one)
     dstep = pk.DecodeStep(dc.pool, 0, dc.out, dc.query, dc.tables, dc.lens,
                           new_key=dc.new_key if fused else None,
                           new_value=dc.new_value if fused else None, scale=cfg.scale,
-                          partition_size=cfg.partition_size, workspace=dc.workspace)
+                          partition_size=cfg.partition_size,
+                          workspace=None if cascade else dc.workspace, prefix_blocks=prefix_blocks)
 
     def step(on=None, ev_a=None, ev_b=None):
         st = stream if on is None else on
@@ -741,6 +754,10 @@ def _main_gpu(args, workers):
             dstep(st)
             return
         ev_a.record(st)
+        if cascade:              # one call: the prefix pass, the suffixes and the merge
+            dstep(st)
+            ev_b.record(st)
+            return
         dstep.partitions(st)
         ev_b.record(st)
         dstep.reduce(st)
@@ -768,14 +785,17 @@ def _main_gpu(args, workers):
     torch.cuda.synchronize()
     part_times = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
     part_ms = float(np.median(part_times))
-    # the kernel's HBM bytes: each distinct token row once (forks of a prefix share rows)
-    achieved = nbytes["partition_kernel_unique"] / (part_ms * 1e-3) / 1e9
-    effective = nbytes["partition_kernel"] / (part_ms * 1e-3) / 1e9
+    # the kernel's HBM bytes: each distinct token row once (forks of a prefix share rows);
+    # the shared-prefix step's three kernels together also write the output once
+    kernel_bytes = nbytes["partition_kernel_unique"] + (nbytes["o"] if cascade else 0)
+    logical_bytes = nbytes["partition_kernel"] + (nbytes["o"] if cascade else 0)
+    achieved = kernel_bytes / (part_ms * 1e-3) / 1e9
+    effective = logical_bytes / (part_ms * 1e-3) / 1e9
     seqs_per_s = cfg.batch / (ms_step * 1e-3)
     print(f"[bench] {ms_step * 1e3:.1f} us/step, partition kernel {part_ms * 1e3:.1f} us "
           f"= {achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
-    traffic = load_traffic(cfg.name)
+    traffic = load_traffic(cfg.name, "pa_cascade" if cascade else PARTITION_KERNEL)
     result = {
         "metric": METRIC,
         "value": seqs_per_s,
@@ -796,20 +816,23 @@ def _main_gpu(args, workers):
             "q_heads": cfg.num_q_heads, "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
             "block_size": cfg.block_size, "pool_blocks": cfg.num_blocks,
             "partition_size": cfg.partition_size, "accumulate": "f32",
-            "step": ("paged_attention_partitions_append (cache write folded in) + reduce" if fused
+            "step": ("paged_attention_decode_shared_prefix (cache write folded in; "
+                     f"{prefix_blocks} shared blocks)" if cascade else
+                     "paged_attention_partitions_append (cache write folded in) + reduce" if fused
                      else "reshape_and_cache + paged_attention (partitions + reduce)"),
         },
         "step_hbm_gbps": nbytes["step"] / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": nbytes["step"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "roofline": {
             "bound": "hbm",
-            "kernel": PARTITION_KERNEL,
+            "kernel": ("pa_prefill_mfma (dense prefix pass) + pa_partition_mfma (suffixes) + "
+                       "pa_cascade_reduce, timed together" if cascade else PARTITION_KERNEL),
             "achieved": achieved,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": nbytes["partition_kernel_unique"],
+            "algorithmic_bytes_per_launch": kernel_bytes,
             "avg_launch_us": part_ms * 1e3,
             "launch_us_stat": f"median of {args.steps} HIP-event durations (mean "
                               f"{np.mean(part_times) * 1e3:.1f} us), events on the kernel's stream "
@@ -821,7 +844,7 @@ def _main_gpu(args, workers):
         # rate (every sequence's rows, as if each were read from HBM) is reported beside it
         result["roofline"]["effective"] = {
             "achieved": effective, "unit": "GB/s",
-            "logical_bytes_per_launch": nbytes["partition_kernel"],
+            "logical_bytes_per_launch": logical_bytes,
             "note": "every sequence's K/V rows counted, shared rows once per sequence",
         }
     # --graph: also time the same step captured once in a HIP graph and replayed back to

@@ -224,7 +224,8 @@ size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
  *                 when one work-group holds all of a sequence's partitions, otherwise
  *                 by a second kernel over partial results in the workspace.
  *  workspace    : >= paged_attention_workspace_bytes(...) bytes of device memory,
- *                 16-byte aligned; contents on entry do not matter.
+ *                 256-byte aligned (else KV_ERR_INVALID_ARG); contents on entry do not
+ *                 matter.
  * Table entries outside [0, num_blocks) for blocks a sequence uses are skipped (the
  * output is then meaningless but no memory outside the pool is read).
  * Errors: KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED (group size), KV_ERR_WORKSPACE,
@@ -289,6 +290,52 @@ kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* o
                                    int32_t batch, int32_t num_q_heads, float scale,
                                    int32_t partition_size, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
+
+/* Decode attention for a batch whose sequences begin with the same blocks: sequences
+ * forked from one prompt, or requests that found one cached prefix ("Why AI servers
+ * waste memory, and how paging fixes it", "Sharing a prefix with copy-on-write": forked
+ * sequences point at the prompt's blocks until they write; "PagedAttention: Treating KV
+ * Memory Like Virtual Memory", "A separate mechanism: automatic prefix caching").  The
+ * result is that of paged_attention_decode (or _append, with new_key / new_value) on the
+ * same arguments, up to rounding: the same attention over each sequence's whole
+ * context, summed in another order.
+ *  prefix_blocks : the first prefix_blocks entries of every table row are row 0's (the
+ *                  caller, who forked the sequences, knows this count; it is not looked
+ *                  for).  0 runs paged_attention_decode(_append) itself.
+ * The shared keys are read once for the whole batch instead of once per sequence: the
+ * batch's query rows of each KV head form one dense tile against the prefix's keys
+ * (matrix cores; the prefix is split over work-groups), each sequence's remaining blocks
+ * go through the decode kernels, and a last kernel combines the two sets of partial
+ * results (m, l, O) per (sequence, query head) with the cross-block rule ("PagedAttention
+ * and Virtual Memory Management", section 4), deterministically.
+ * Preconditions (checked in checked mode, PAGEDKV_CHECK=1; otherwise the output is
+ * undefined if they fail, and nothing outside the pool is read): a row's entries among
+ * the first prefix_blocks that its length uses equal row 0's; with new tokens, every
+ * sequence of length L > 0 has L > prefix_blocks * B (the token goes into a block of
+ * its own, never into a shared one) and prefix_blocks < max_blocks_per_seq.  A sequence
+ * shorter than the prefix attends over its own length of it.
+ *  workspace : >= paged_attention_shared_prefix_workspace_bytes(...) bytes, 256-byte
+ *              aligned; contents on entry do not matter.
+ * Other arguments, errors and the cache write as paged_attention_decode_append
+ * (new_key and new_value both NULL: no write, as paged_attention_decode). */
+kv_status_t paged_attention_decode_shared_prefix(const kv_pool_t* pool, int32_t layer, void* out,
+                                                 const void* query, const void* new_key,
+                                                 const void* new_value, const int32_t* block_tables,
+                                                 int32_t max_blocks_per_seq,
+                                                 const int32_t* context_lens, int32_t batch,
+                                                 int32_t num_q_heads, float scale,
+                                                 int32_t prefix_blocks, int32_t partition_size,
+                                                 void* workspace, size_t workspace_bytes,
+                                                 hipStream_t stream);
+/* Workspace bytes of paged_attention_decode_shared_prefix for this shape on the current
+ * device (the prefix's split follows the device's size): the prefix's partial results
+ * (fp32 m, l and O of every (sequence, query head, split)), then the suffixes' partial
+ * results (as paged_attention_workspace_bytes, for the entries after the prefix, with one
+ * partition counted too).  With prefix_blocks == 0, paged_attention_workspace_bytes.
+ * SIZE_MAX for invalid arguments (null or host pool, sizes out of range). */
+size_t paged_attention_shared_prefix_workspace_bytes(const kv_pool_t* pool, int32_t batch,
+                                                     int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                                     int32_t prefix_blocks, int32_t partition_size);
 
 /* Bytes of the scratch array the library keeps on each GPU for
  * paged_attention_decode_noalloc (64 MiB). */

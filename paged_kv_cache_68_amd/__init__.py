@@ -25,7 +25,8 @@ __all__ = [
     "BlockManager", "OutOfBlocks", "copy_blocks", "paged_attention_prefill", "PrefixCache",
     "hash_block", "swap_blocks", "paged_attention_decode_append", "paged_attention_partitions_append",
     "paged_attention_prefill_split", "prefill_workspace_bytes", "alloc_prefill_workspace",
-    "DecodeStep", "paged_attention_decode_noalloc",
+    "DecodeStep", "paged_attention_decode_noalloc", "paged_attention_decode_shared_prefix",
+    "shared_prefix_workspace_bytes", "alloc_shared_prefix_workspace",
 ]
 
 BLOCK_SIZE = 16
@@ -431,6 +432,68 @@ def paged_attention_decode_noalloc(pool: KVPool, layer: int, out, query, block_t
     return out
 
 
+def shared_prefix_workspace_bytes(pool: KVPool, batch, num_q_heads, max_blocks_per_seq,
+                                  prefix_blocks, partition_size=0) -> int:
+    """Workspace bytes of paged_attention_decode_shared_prefix for this shape on the
+    current device."""
+    n = int(lib().paged_attention_shared_prefix_workspace_bytes(
+        pool.handle, int(batch), int(num_q_heads), int(max_blocks_per_seq), int(prefix_blocks),
+        int(partition_size)))
+    if n == (1 << 64) - 1:
+        raise ValueError("shared_prefix_workspace_bytes: invalid arguments")
+    return n
+
+
+def alloc_shared_prefix_workspace(pool: KVPool, batch, num_q_heads, max_blocks_per_seq,
+                                  prefix_blocks, partition_size=0):
+    torch = _torch()
+    n = shared_prefix_workspace_bytes(pool, batch, num_q_heads, max_blocks_per_seq, prefix_blocks,
+                                      partition_size)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=pool.device)
+
+
+def _shared_prefix_args(pool, layer, out, query, block_tables, context_lens, prefix_blocks,
+                        new_key, new_value, scale, partition_size, workspace):
+    """The checked argument list of paged_attention_decode_shared_prefix (no stream)."""
+    if (new_key is None) != (new_value is None):
+        raise ValueError("paged_attention_decode_shared_prefix: give both new_key and new_value, or neither")
+    batch, hq, max_blocks = _check_decode_args(pool, out, query, block_tables, context_lens,
+                                               new_key, new_value, workspace)
+    prefix_blocks = int(prefix_blocks)
+    if not 0 <= prefix_blocks <= max_blocks:
+        raise ValueError(f"prefix_blocks: {prefix_blocks} is outside [0, {max_blocks}]")
+    if workspace is None:
+        workspace = alloc_shared_prefix_workspace(pool, batch, hq, max_blocks, prefix_blocks,
+                                                  partition_size)
+    if scale is None:
+        scale = 1.0 / math.sqrt(pool.head_dim)
+    vp = ctypes.c_void_p
+    args = [pool.handle, ctypes.c_int32(int(layer)), vp(_ptr(out)), vp(_ptr(query)),
+            vp(_ptr(new_key)), vp(_ptr(new_value)), vp(_ptr(block_tables)),
+            ctypes.c_int32(max_blocks), vp(_ptr(context_lens)), ctypes.c_int32(batch),
+            ctypes.c_int32(hq), ctypes.c_float(float(scale)), ctypes.c_int32(prefix_blocks),
+            ctypes.c_int32(int(partition_size)), vp(_ptr(workspace)),
+            ctypes.c_size_t(_nbytes(workspace))]
+    return args, workspace
+
+
+def paged_attention_decode_shared_prefix(pool: KVPool, layer: int, out, query, block_tables,
+                                         context_lens, prefix_blocks, new_key=None, new_value=None,
+                                         scale=None, partition_size=0, workspace=None, stream=None):
+    """paged_attention_decode(_append) for a batch whose table rows all begin with the
+    same ``prefix_blocks`` entries (row 0's): the shared keys are read once for the batch.
+    With ``new_key`` / ``new_value`` the new tokens are written first, as in
+    paged_attention_decode_append; they must fall after the prefix."""
+    args, _ = _shared_prefix_args(pool, layer, out, query, block_tables, context_lens,
+                                  prefix_blocks, new_key, new_value, scale, partition_size,
+                                  workspace)
+    check(lib().paged_attention_decode_shared_prefix(*args, _stream(stream)),
+          "paged_attention_decode_shared_prefix")
+    return out
+
+
 class DecodeStep:
     """One decode step prepared once for buffers a serving loop reuses: the tensors are
     checked when the step is built, and each call is then a single call into the library
@@ -444,13 +507,28 @@ class DecodeStep:
     storage (update their contents in place between calls).  Lengths and tables are read
     on the device at each call, so they may change, within the shapes given here.
     ``stream`` (a torch stream or a raw handle) fixes the stream; without it each call
-    uses torch's current stream."""
+    uses torch's current stream.
+
+    ``prefix_blocks`` > 0: the rows of ``block_tables`` share their first prefix_blocks
+    entries, and each call is paged_attention_decode_shared_prefix (a single phase:
+    ``partitions()`` / ``reduce()`` are not available)."""
 
     def __init__(self, pool: KVPool, layer: int, out, query, block_tables, context_lens,
                  new_key=None, new_value=None, scale=None, partition_size=0, workspace=None,
-                 stream=None):
+                 stream=None, prefix_blocks=0):
         if (new_key is None) != (new_value is None):
             raise ValueError("DecodeStep: give both new_key and new_value, or neither")
+        self._stream = None if stream is None else ctypes.c_void_p(_stream(stream))
+        self.out = out
+        if int(prefix_blocks) > 0:
+            args, workspace = _shared_prefix_args(pool, layer, out, query, block_tables,
+                                                  context_lens, prefix_blocks, new_key, new_value,
+                                                  scale, partition_size, workspace)
+            self._keep = (pool, out, query, block_tables, context_lens, new_key, new_value, workspace)
+            self._whole = ("paged_attention_decode_shared_prefix",
+                           lib().paged_attention_decode_shared_prefix, args)
+            self._first = self._second = None
+            return
         batch, hq, max_blocks = _check_decode_args(pool, out, query, block_tables, context_lens,
                                                    new_key, new_value, workspace)
         if workspace is None:
@@ -475,10 +553,10 @@ class DecodeStep:
             self._whole = ("paged_attention_decode", L.paged_attention_decode, head + tail)
             self._first = ("paged_attention_partitions", L.paged_attention_partitions, head + tail)
         self._second = ("paged_attention_reduce", L.paged_attention_reduce, head + tail)
-        self._stream = None if stream is None else vp(_stream(stream))
-        self.out = out
 
     def _run(self, call, stream):
+        if call is None:
+            raise ValueError("DecodeStep: a shared-prefix step runs as one call")
         name, fn, args = call
         st = fn(*args, self._stream if stream is None and self._stream is not None else _stream(stream))
         if st:

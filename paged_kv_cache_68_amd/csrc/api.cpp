@@ -71,7 +71,7 @@ kv_status_t check_decode(const kv_pool_t* pool, int32_t layer, void* out, const 
                          const int32_t* block_tables, int32_t max_blocks,
                          const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                          float scale, int32_t partition_size, void* workspace,
-                         size_t workspace_bytes, DecodeShape* shape) {
+                         size_t workspace_bytes, DecodeShape* shape, bool check_workspace = true) {
     if (!pool || pool->host) return KV_ERR_INVALID_ARG;
     const kv_pool_desc_t& d = pool->desc;
     if (layer < 0 || layer >= d.num_layers) return KV_ERR_INVALID_ARG;
@@ -102,7 +102,7 @@ kv_status_t check_decode(const kv_pool_t* pool, int32_t layer, void* out, const 
     if (static_cast<int64_t>(batch) * d.num_kv_heads * num_parts > INT32_MAX)
         return KV_ERR_INVALID_ARG;
     const size_t need = workspace_for(batch, num_q_heads, d.head_dim, num_parts);
-    if (need > 0) {
+    if (need > 0 && check_workspace) {
         if (!workspace || workspace_bytes < need) return KV_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return KV_ERR_INVALID_ARG;
     }
@@ -138,6 +138,9 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = d.num_kv_heads;
     a.max_blocks = max_blocks;
+    a.table_stride = max_blocks;
+    a.len_offset = 0;
+    a.keep_partials = 0;
     a.num_blocks = d.num_blocks;
     a.block_size = d.block_size;
     a.tile_tokens = d.block_size < pkv::kTile ? d.block_size : pkv::kTile;
@@ -399,7 +402,187 @@ kv_status_t prefill_impl(const kv_pool_t* pool, int32_t layer, void* out, const 
     pa.num_tokens = num_tokens;
     pa.ws_acc = pl.splits > 1 ? static_cast<float*>(workspace) : nullptr;
     pa.ws_ml = pl.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_offset) : nullptr;
+    pa.dense_len = 0;
     return pkv::launch_prefill(d.dtype, io_dtype(d), d.head_dim, pa, stream) == hipSuccess
+               ? KV_OK
+               : KV_ERR_HIP;
+}
+
+// ---- decode over a shared prefix (see paged_attention_decode_shared_prefix)
+
+constexpr int kMaxCascadeSplits = 64;
+
+// The launch shape of a shared-prefix decode (host values only).
+struct CascadePlan {
+    int32_t group = 0;
+    int waves = 4;              // prefix pass: waves per work-group
+    int64_t row_tiles = 0;      // prefix pass: row tiles per KV head (batch * group rows)
+    int splits = 1;             // prefix pass: work-groups sharing each row tile's keys
+    int32_t suffix_blocks = 0;  // table entries after the prefix
+    DecodeShape suffix;         // the suffix's partition shape (num_parts 0 if no entries)
+    size_t pre_ml_offset = 0;   // prefix partials: acc at 0, (m, l) here
+    size_t suffix_offset = 0;   // suffix partials (acc, then (m, l)) from here
+    size_t total = 0;           // workspace bytes
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+kv_status_t plan_cascade(const kv_pool_t* pool, int32_t batch, int32_t num_q_heads,
+                         int32_t max_blocks, int32_t prefix_blocks, int32_t partition_size,
+                         CascadePlan* cp) {
+    const kv_pool_desc_t& d = pool->desc;
+    if (batch < 1 || num_q_heads < 1 || max_blocks < 1 || prefix_blocks < 1 || prefix_blocks > max_blocks)
+        return KV_ERR_INVALID_ARG;
+    if (num_q_heads % d.num_kv_heads != 0) return KV_ERR_UNSUPPORTED;
+    cp->group = num_q_heads / d.num_kv_heads;
+    if (cp->group > pkv::kMaxGroup) return KV_ERR_UNSUPPORTED;
+    if (partition_size == 0) partition_size = pkv::kDefaultPartition;
+    if (partition_size < d.block_size || partition_size % d.block_size != 0) return KV_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(max_blocks) * d.block_size > INT32_MAX) return KV_ERR_INVALID_ARG;
+    // prefix pass: the batch's query rows of a KV head are one row range; 8-wave
+    // work-groups (256 rows) stage each key once for all of them when there are that many
+    // (PAGEDKV_PREFILL_WAVES=4|8 forces the choice)
+    const int64_t rows = static_cast<int64_t>(batch) * cp->group;
+    const char* ew = getenv("PAGEDKV_PREFILL_WAVES");
+    const int forced = ew ? atoi(ew) : 0;
+    cp->waves = (forced == 4 || forced == 8) ? forced : (rows >= 256 ? 8 : 4);
+    cp->row_tiles = ceil_div(rows, 32 * cp->waves);
+    const int64_t wgs = static_cast<int64_t>(d.num_kv_heads) * cp->row_tiles;
+    int64_t resident = pkv::prefill_resident_groups(d.dtype, io_dtype(d), d.head_dim, cp->waves);
+    if (resident <= 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+        resident = 2 * static_cast<int64_t>(cus);     // no occupancy known: two per CU
+    }
+    // enough work-groups to fill the resident slots, each with at least two 64-key stages
+    const int64_t stages = ceil_div(static_cast<int64_t>(prefix_blocks) * d.block_size, 64);
+    int64_t splits = wgs < resident ? ceil_div(resident, wgs) : 1;
+    splits = std::min<int64_t>({splits, kMaxCascadeSplits, std::max<int64_t>(1, stages / 2)});
+    const char* e = getenv("PAGEDKV_CASCADE_SPLITS");
+    if (e && atoi(e) >= 1) splits = std::min(atoi(e), kMaxCascadeSplits);
+    cp->splits = static_cast<int>(splits);
+    if (wgs * cp->splits > INT32_MAX) return KV_ERR_INVALID_ARG;
+    const size_t pre = prefill_partial_bytes(batch, num_q_heads, d.head_dim, cp->splits, &cp->pre_ml_offset);
+    // suffix pass: the decode's shape over the entries after the prefix; its partial
+    // results are kept even for a single partition
+    cp->suffix_blocks = max_blocks - prefix_blocks;
+    cp->suffix = DecodeShape();
+    cp->suffix.group = cp->group;
+    cp->suffix_offset = align256(pre);
+    cp->total = cp->suffix_offset;
+    if (cp->suffix_blocks > 0) {
+        const int32_t tile = d.block_size < pkv::kTile ? d.block_size : pkv::kTile;
+        if (partition_size > pkv::kMaxPartition || partition_size > pkv::kMaxTilesPerWave * tile)
+            return KV_ERR_UNSUPPORTED;
+        cp->suffix.part_blocks = partition_size / tile;
+        cp->suffix.num_parts = static_cast<int32_t>(
+            ceil_div(static_cast<int64_t>(cp->suffix_blocks) * d.block_size, partition_size));
+        if (static_cast<int64_t>(batch) * d.num_kv_heads * cp->suffix.num_parts > INT32_MAX)
+            return KV_ERR_INVALID_ARG;
+        const size_t n = static_cast<size_t>(batch) * num_q_heads * cp->suffix.num_parts;
+        cp->suffix.ws_needed = align256(n * d.head_dim * sizeof(float)) + n * 2 * sizeof(float);
+        cp->total += cp->suffix.ws_needed;
+    }
+    return KV_OK;
+}
+
+kv_status_t shared_prefix_impl(const kv_pool_t* pool, int32_t layer, void* out, const void* query,
+                               const void* new_key, const void* new_value,
+                               const int32_t* block_tables, int32_t max_blocks,
+                               const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                               float scale, int32_t prefix_blocks, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if ((new_key == nullptr) != (new_value == nullptr)) return KV_ERR_INVALID_ARG;
+    if (new_key && (!aligned(new_key) || !aligned(new_value))) return KV_ERR_INVALID_ARG;
+    if (prefix_blocks == 0)
+        return decode_impl(kBoth, pool, layer, out, query, block_tables, max_blocks, context_lens,
+                           batch, num_q_heads, scale, partition_size, workspace, workspace_bytes,
+                           stream, new_key, new_value);
+    DecodeShape s;
+    kv_status_t st = check_decode(pool, layer, out, query, block_tables, max_blocks, context_lens,
+                                  batch, num_q_heads, scale, partition_size, nullptr, 0, &s, false);
+    if (st != KV_OK) return st;
+    if (prefix_blocks < 0 || (batch > 0 && prefix_blocks > max_blocks)) return KV_ERR_INVALID_ARG;
+    if (batch == 0) return KV_OK;
+    // a new token at position L - 1 needs a table entry after the prefix
+    if (new_key && prefix_blocks == max_blocks) return KV_ERR_INVALID_ARG;
+    CascadePlan cp;
+    st = plan_cascade(pool, batch, num_q_heads, max_blocks, prefix_blocks, partition_size, &cp);
+    if (st != KV_OK) return st;
+    if (!workspace || workspace_bytes < cp.total) return KV_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return KV_ERR_INVALID_ARG;
+    const kv_pool_desc_t& d = pool->desc;
+    if (checked_mode()) {
+        st = check_tables_on_device(pool, block_tables, max_blocks, context_lens, batch, stream);
+        if (st == KV_OK)
+            st = run_check(0, stream, [&](uint32_t* status, uint32_t*) {
+                return pkv::launch_check_shared_prefix(block_tables, max_blocks, context_lens, batch,
+                                                       prefix_blocks, d.block_size, new_key ? 1 : 0,
+                                                       status, stream);
+            });
+        if (st == KV_OK && new_key) {
+            const int64_t slots = static_cast<int64_t>(d.num_blocks) * d.block_size;
+            st = run_check(slots, stream, [&](uint32_t* status, uint32_t* seen) {
+                return pkv::launch_check_append_slots(block_tables, max_blocks, context_lens, batch,
+                                                      d.num_blocks, d.block_size, seen, status, stream);
+            });
+        }
+        if (st != KV_OK) return st;
+    }
+    char* ws = static_cast<char*>(workspace);
+    const int32_t prefix_len = prefix_blocks * d.block_size;
+
+    // 1. the prefix: every query row against keys [0, prefix_len) of table row 0
+    DecodeShape one;
+    one.group = cp.group;
+    one.part_blocks = 1;
+    one.num_parts = 1;
+    pkv::PrefillArgs pa;
+    pa.a = make_args(pool, layer, out, query, block_tables, max_blocks, context_lens, batch,
+                     num_q_heads, scale, nullptr, one);
+    pa.a.stream_loads = 0;
+    pa.a.streamed = 0;
+    pa.qstart = nullptr;
+    pa.group = cp.group;
+    pa.row_tiles = static_cast<int32_t>(cp.row_tiles);
+    pa.waves = cp.waves;
+    pa.buffer_bytes = pool->cache_bytes < (size_t(1) << 31) ? static_cast<int32_t>(pool->cache_bytes) : 0;
+    pa.splits = cp.splits;
+    pa.num_tokens = batch;
+    pa.ws_acc = reinterpret_cast<float*>(ws);
+    pa.ws_ml = reinterpret_cast<float*>(ws + cp.pre_ml_offset);
+    pa.dense_len = prefix_len;
+    if (pkv::launch_prefill_dense(d.dtype, io_dtype(d), d.head_dim, pa, stream) != hipSuccess)
+        return KV_ERR_HIP;
+
+    // 2. the suffixes: the decode over the entries after the prefix, partial results kept
+    pkv::DecodeArgs a = make_args(pool, layer, out, query, block_tables + prefix_blocks,
+                                  cp.suffix_blocks, context_lens, batch, num_q_heads, scale,
+                                  ws + cp.suffix_offset, cp.suffix);
+    a.table_stride = max_blocks;
+    a.len_offset = prefix_len;
+    a.keep_partials = 1;
+    pkv::DecodeArgs r = a;
+    if (cp.suffix_blocks > 0) {
+        a.new_k = static_cast<const uint16_t*>(new_key);
+        a.new_v = static_cast<const uint16_t*>(new_value);
+        if (pkv::launch_partitions(d.dtype, io_dtype(d), d.head_dim, cp.group, a, stream) != hipSuccess)
+            return KV_ERR_HIP;
+        const int chunk = pkv::partition_chunk(d.dtype, io_dtype(d), d.head_dim, cp.group, a);
+        r.part_blocks = a.part_blocks * chunk;
+        r.num_parts = static_cast<int32_t>(ceil_div(a.num_parts, chunk));
+    } else {
+        r.part_blocks = 1;      // no entries: every suffix is empty
+        r.num_parts = 1;
+    }
+
+    // 3. prefix and suffix partial results combined per (sequence, query head)
+    return pkv::launch_cascade_reduce(io_dtype(d), d.head_dim, r, pa.ws_acc, pa.ws_ml, cp.splits,
+                                      stream) == hipSuccess
                ? KV_OK
                : KV_ERR_HIP;
 }
@@ -769,6 +952,37 @@ kv_status_t kv_pool_gather(const kv_pool_t* pool, int32_t layer, const int32_t* 
         d.num_blocks, d.block_size, d.num_kv_heads * d.head_dim * static_cast<int32_t>(elem_bytes(d)),
         k_out, v_out, stream);
     return e == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+size_t paged_attention_shared_prefix_workspace_bytes(const kv_pool_t* pool, int32_t batch,
+                                                     int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                                     int32_t prefix_blocks, int32_t partition_size) {
+    if (!pool || pool->host || batch < 0 || num_q_heads < 1 || max_blocks_per_seq < 1 ||
+        prefix_blocks < 0 || prefix_blocks > max_blocks_per_seq)
+        return SIZE_MAX;
+    if (prefix_blocks == 0 || batch == 0)
+        return batch == 0 ? 0
+                          : paged_attention_workspace_bytes(batch, num_q_heads, pool->desc.head_dim,
+                                                            max_blocks_per_seq, pool->desc.block_size,
+                                                            partition_size);
+    CascadePlan cp;
+    if (plan_cascade(pool, batch, num_q_heads, max_blocks_per_seq, prefix_blocks, partition_size, &cp) != KV_OK)
+        return SIZE_MAX;
+    return cp.total;
+}
+
+kv_status_t paged_attention_decode_shared_prefix(const kv_pool_t* pool, int32_t layer, void* out,
+                                                 const void* query, const void* new_key,
+                                                 const void* new_value, const int32_t* block_tables,
+                                                 int32_t max_blocks_per_seq,
+                                                 const int32_t* context_lens, int32_t batch,
+                                                 int32_t num_q_heads, float scale,
+                                                 int32_t prefix_blocks, int32_t partition_size,
+                                                 void* workspace, size_t workspace_bytes,
+                                                 hipStream_t stream) {
+    return shared_prefix_impl(pool, layer, out, query, new_key, new_value, block_tables,
+                              max_blocks_per_seq, context_lens, batch, num_q_heads, scale,
+                              prefix_blocks, partition_size, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

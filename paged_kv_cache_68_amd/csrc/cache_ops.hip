@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void append_kv(DecodeArgs a) {
     const int L = clamped_length(a, b);
     if (L == 0) return;
     const int last = L - 1;
-    const int blk = a.tables[static_cast<size_t>(b) * a.max_blocks + last / a.block_size];
+    const int blk = a.tables[static_cast<size_t>(b) * a.table_stride + last / a.block_size];
     if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) return;
     const size_t slot = static_cast<size_t>(blk) * a.block_size + last % a.block_size;
     const int words = a.row_bytes / (KV8 ? 2 : 4);          // 32-bit words of the input row

@@ -7,7 +7,9 @@
 //    the pool, and every length is in [0, max_blocks * B] (the fast path clamps);
 //  * slot mappings: every slot is below num_blocks * B (negative = no write, allowed) and
 //    no slot appears twice (the fast path's result is then unspecified);
-//  * query offsets (prefill): non-decreasing, chunk sizes within max_query_len.
+//  * query offsets (prefill): non-decreasing, chunk sizes within max_query_len;
+//  * a shared prefix (decode over a forked prompt): every sequence's used entries among
+//    the first prefix_blocks are row 0's, and a new token is never written into them.
 
 #include <hip/hip_runtime.h>
 
@@ -19,7 +21,25 @@ namespace pkv {
 namespace {
 
 constexpr uint32_t kBadBlock = 1u, kBadLength = 2u, kBadSlot = 4u, kDuplicateSlot = 8u,
-                   kBadQueryStart = 16u;
+                   kBadQueryStart = 16u, kBadPrefix = 32u;
+
+__global__ __launch_bounds__(256) void check_shared_prefix(const int32_t* __restrict__ tables,
+                                                           int32_t max_blocks,
+                                                           const int32_t* __restrict__ lens,
+                                                           int32_t batch, int32_t prefix_blocks,
+                                                           int32_t block_size, int32_t appending,
+                                                           uint32_t* status) {
+    const int b = blockIdx.x;
+    if (b >= batch) return;
+    const int L = lens[b];
+    uint32_t bad = 0;
+    const int64_t prefix_len = static_cast<int64_t>(prefix_blocks) * block_size;
+    if (appending && L > 0 && L <= prefix_len) bad |= kBadPrefix;
+    const int used = L <= 0 ? 0 : min(prefix_blocks, (L + block_size - 1) / block_size);
+    for (int j = threadIdx.x; j < used; j += blockDim.x)
+        if (tables[static_cast<size_t>(b) * max_blocks + j] != tables[j]) bad |= kBadPrefix;
+    if (bad) atomicOr(status, bad);
+}
 
 __global__ __launch_bounds__(256) void check_tables(const int32_t* __restrict__ tables, int32_t max_blocks,
                                                     const int32_t* __restrict__ lens, int32_t batch,
@@ -106,6 +126,15 @@ hipError_t launch_check_slots(const int64_t* slots, int32_t n, int64_t num_slots
                        dim3(256), 0, stream, seen, words);
     hipLaunchKernelGGL(check_slots, dim3((n + 255) / 256), dim3(256), 0, stream, slots, n, num_slots,
                        seen, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_check_shared_prefix(const int32_t* tables, int32_t max_blocks, const int32_t* lens,
+                                      int32_t batch, int32_t prefix_blocks, int32_t block_size,
+                                      int32_t appending, uint32_t* status, hipStream_t stream) {
+    if (batch <= 0) return hipSuccess;
+    hipLaunchKernelGGL(check_shared_prefix, dim3(batch), dim3(256), 0, stream, tables, max_blocks,
+                       lens, batch, prefix_blocks, block_size, appending, status);
     return hipGetLastError();
 }
 

@@ -36,8 +36,8 @@ struct DecodeArgs {
     const uint8_t* k;        // [nb][block_size][Hkv][D], elements of the storage type
     const uint8_t* v;
     int32_t row_bytes;       // bytes of one token row of K (Hkv * D * element bytes)
-    const int32_t* tables;   // [B][max_blocks]
-    const int32_t* lens;     // [B]
+    const int32_t* tables;   // [B][table_stride], max_blocks entries of each row used
+    const int32_t* lens;     // [B]: context lengths; the kernels see lens[b] - len_offset
     uint16_t* out;           // [B][Hq][D]
     const uint16_t* new_k;   // [B][Hkv][D] io type, or null: the token at position L - 1 of
     const uint16_t* new_v;   // each sequence, written into its slot (found through the
@@ -47,7 +47,13 @@ struct DecodeArgs {
     int32_t batch;
     int32_t num_q_heads;
     int32_t num_kv_heads;
-    int32_t max_blocks;      // table row length
+    int32_t max_blocks;      // table entries per sequence (from `tables` on)
+    int32_t table_stride;    // entries between two sequences' rows (>= max_blocks)
+    int32_t len_offset;      // tokens before the table's first entry (a shared prefix
+                             // handled elsewhere): a sequence holds lens[b] - len_offset
+    int32_t keep_partials;   // 1: every sequence's partitions go to the workspace as
+                             // partial results, even a single one (no final output is
+                             // written; a sequence without tokens writes nothing)
     int32_t num_blocks;      // blocks in the pool
     int32_t block_size;      // tokens per block: 8, 16, 32 or 64
     int32_t tile_tokens;     // tokens per tile the kernels walk: min(block_size, 16)
@@ -77,6 +83,9 @@ struct PrefillArgs {
     int32_t num_tokens;      // (splits > 1) rows of the query: bounds the partial results
     float* ws_acc;           // (splits > 1) [num_tokens * num_q_heads][splits][D]
     float* ws_ml;            // (splits > 1) [num_tokens * num_q_heads][splits][2]: (m, l)
+    int32_t dense_len;       // (dense launch) keys [0, dense_len) of table row 0, shared by
+                             // the num_tokens queries of a decode batch ([B][Hq][D]):
+                             // query t sees the first min(lens[t], dense_len) of them
 };
 
 // A call that can touch more K/V bytes than this streams them past the last-level cache
@@ -105,6 +114,17 @@ hipError_t launch_reduce(int io_dtype, int head_dim, const DecodeArgs& a, hipStr
 int prefill_waves_for(int64_t seq_heads, int64_t rows);
 hipError_t launch_prefill(int kv_dtype, int io_dtype, int head_dim, const PrefillArgs& pa,
                           hipStream_t stream);
+// The shared prefix of a decode batch (PrefillArgs::dense_len): grid num_kv_heads x
+// row_tiles x splits, partial results always written (splits >= 1).
+hipError_t launch_prefill_dense(int kv_dtype, int io_dtype, int head_dim, const PrefillArgs& pa,
+                                hipStream_t stream);
+// The cascade reduce: each (sequence, query head) combines `pre_parts` partial results of
+// its shared prefix ([B * Hq][pre_parts] rows of pre_acc / pre_ml) with the partial
+// results the partition kernel left for its suffix (`a` as for launch_reduce, with
+// keep_partials set and len_offset the prefix length), in that order.
+hipError_t launch_cascade_reduce(int io_dtype, int head_dim, const DecodeArgs& a,
+                                 const float* pre_acc, const float* pre_ml, int pre_parts,
+                                 hipStream_t stream);
 // work-groups of a prefill launch with `waves` waves each that the GPU holds at once
 int64_t prefill_resident_groups(int kv_dtype, int io_dtype, int head_dim, int waves);
 constexpr int kMaxPrefillSplits = 8;
@@ -126,6 +146,11 @@ hipError_t launch_check_slots(const int64_t* slots, int32_t n, int64_t num_slots
 hipError_t launch_check_append_slots(const int32_t* tables, int32_t max_blocks, const int32_t* lens,
                                      int32_t batch, int32_t num_blocks, int32_t block_size,
                                      uint32_t* seen, uint32_t* status, hipStream_t stream);
+// (decode over a shared prefix) used prefix entries equal row 0's; with `appending`, no
+// sequence's last position lies in the prefix
+hipError_t launch_check_shared_prefix(const int32_t* tables, int32_t max_blocks, const int32_t* lens,
+                                      int32_t batch, int32_t prefix_blocks, int32_t block_size,
+                                      int32_t appending, uint32_t* status, hipStream_t stream);
 hipError_t launch_check_query_start(const int32_t* qs, int32_t batch, int32_t max_query_len,
                                     uint32_t* status, hipStream_t stream);
 hipError_t launch_clear_word(uint32_t* w, hipStream_t stream);

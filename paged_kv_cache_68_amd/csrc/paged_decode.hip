@@ -308,6 +308,103 @@ __global__ __launch_bounds__(256) void pa_reduce(DecodeArgs a) {
     for (int e = 0; e < PER; ++e) o[e] = S::narrow(lsum > 0.f ? A[e] / lsum : 0.f);
 }
 
+// The cascade reduce, one wave per (sequence, query head): entries 0 .. pre_parts - 1 are
+// the partial results of the batch's shared prefix (pre_ml / pre_acc rows
+// pair * pre_parts + s), the next ones the partitions of the sequence's suffix (rows
+// G apart, as in pa_reduce; as many as its length gives, possibly none).  All are
+// combined with the cross-block rule: O = sum_k w_k acc_k / sum_k w_k l_k,
+// w_k = 2^(m_k - max m), an entry that saw no key (m = -inf) weighing 0.  The wave's four
+// 16-lane groups take entries k = 4j + group (D / 16 elements per lane), with up to eight
+// entries' loads in flight per lane, and the groups' sums are added at the end in a fixed
+// order: the result does not depend on timing.
+template <class S, int D>
+__global__ __launch_bounds__(256) void pa_cascade_reduce(DecodeArgs a, const float* pre_acc,
+                                                         const float* pre_ml, int pre_parts) {
+    constexpr int PER = D / 16;    // elements per lane
+    constexpr int U = 8;           // entries per lane and round
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4;
+    const int l16 = lane & 15;
+    const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (pair >= a.batch * a.num_q_heads) return;
+    const int b = pair / a.num_q_heads;
+    const int h = pair % a.num_q_heads;
+    const int L = clamped_length(a, b);
+    const int ntiles = (L + a.tile_tokens - 1) / a.tile_tokens;
+    const int nsuf = (ntiles + a.part_blocks - 1) / a.part_blocks;
+    const int n = pre_parts + nsuf;
+
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const size_t srow0 = part_row(a, b, h / G, 0, G) + h % G;
+    const size_t prow0 = static_cast<size_t>(pair) * pre_parts;
+    auto row_of = [&](int k) -> size_t {      // the entry's row of (m, l) and accumulators
+        return k < pre_parts ? prow0 + k : srow0 + static_cast<size_t>(k - pre_parts) * G;
+    };
+    auto ml_of = [&](int k) -> float2 {
+        return reinterpret_cast<const float2*>(k < pre_parts ? pre_ml : a.ws_ml)[row_of(k)];
+    };
+
+    float M = -INFINITY;
+    for (int k = lane; k < n; k += 64) M = fmaxf(M, ml_of(k).x);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+    float A[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) A[e] = 0.f;
+    float lsum = 0.f;
+    for (int k0 = grp; k0 < n; k0 += 4 * U) {
+        float2 v[U];
+        float4 x[U][PER / 4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + 4 * u;
+            v[u] = make_float2(-INFINITY, 0.f);
+            if (k < n) {
+                v[u] = ml_of(k);
+                const float4* src = reinterpret_cast<const float4*>(
+                    (k < pre_parts ? pre_acc : a.ws_acc) + row_of(k) * D + PER * l16);
+#pragma unroll
+                for (int q = 0; q < PER / 4; ++q) x[u][q] = src[q];
+            } else {
+#pragma unroll
+                for (int q = 0; q < PER / 4; ++q) x[u][q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = (M == -INFINITY || v[u].x == -INFINITY) ? 0.f : fast_exp2(v[u].x - M);
+            lsum += w * v[u].y;
+#pragma unroll
+            for (int q = 0; q < PER / 4; ++q) {
+                A[4 * q] = fmaf(w, x[u][q].x, A[4 * q]);
+                A[4 * q + 1] = fmaf(w, x[u][q].y, A[4 * q + 1]);
+                A[4 * q + 2] = fmaf(w, x[u][q].z, A[4 * q + 2]);
+                A[4 * q + 3] = fmaf(w, x[u][q].w, A[4 * q + 3]);
+            }
+        }
+    }
+    // groups (0 + 1) + (2 + 3), the same in every lane of a column
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        A[e] += __shfl_xor(A[e], 16);
+        A[e] += __shfl_xor(A[e], 32);
+    }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (grp != 0) return;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    uint32_t packed[PER / 2];
+#pragma unroll
+    for (int e = 0; e < PER; e += 2) packed[e / 2] = S::pack2(A[e] * inv, A[e + 1] * inv);
+    uint16_t* o = a.out + (static_cast<size_t>(b) * a.num_q_heads + h) * D + PER * l16;
+    if constexpr (PER == 8) {
+        *reinterpret_cast<uint4*>(o) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    } else {
+        *reinterpret_cast<uint2*>(o) = make_uint2(packed[0], packed[1]);
+    }
+}
+
 // Partitions per wave of the VALU kernel's item plan (0: the split plan is used).
 template <class S, int D, int G>
 int valu_parts_per_wave(const DecodeArgs& a) {
@@ -371,6 +468,18 @@ hipError_t launch_part_g(int group, const DecodeArgs& a, hipStream_t stream) {
 }
 
 template <class S, int D>
+hipError_t launch_cascade_t(const DecodeArgs& a, const float* pre_acc, const float* pre_ml,
+                            int pre_parts, hipStream_t stream) {
+    const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
+    if (pairs <= 0) return hipSuccess;
+    const int64_t groups = (pairs + 3) / 4;
+    if (groups > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((pa_cascade_reduce<S, D>), dim3(static_cast<unsigned>(groups)), dim3(256), 0,
+                       stream, a, pre_acc, pre_ml, pre_parts);
+    return hipGetLastError();
+}
+
+template <class S, int D>
 hipError_t launch_reduce_t(const DecodeArgs& a, hipStream_t stream) {
     const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
     if (pairs <= 0 || a.num_parts <= 1) return hipSuccess;
@@ -431,6 +540,19 @@ hipError_t launch_reduce(int io_dtype, int head_dim, const DecodeArgs& a, hipStr
     } else if (io_dtype == KV_DTYPE_BF16) {
         if (head_dim == 64) return launch_reduce_t<BF16, 64>(a, stream);
         if (head_dim == 128) return launch_reduce_t<BF16, 128>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_cascade_reduce(int io_dtype, int head_dim, const DecodeArgs& a,
+                                 const float* pre_acc, const float* pre_ml, int pre_parts,
+                                 hipStream_t stream) {
+    if (io_dtype == KV_DTYPE_F16) {
+        if (head_dim == 64) return launch_cascade_t<F16, 64>(a, pre_acc, pre_ml, pre_parts, stream);
+        if (head_dim == 128) return launch_cascade_t<F16, 128>(a, pre_acc, pre_ml, pre_parts, stream);
+    } else if (io_dtype == KV_DTYPE_BF16) {
+        if (head_dim == 64) return launch_cascade_t<BF16, 64>(a, pre_acc, pre_ml, pre_parts, stream);
+        if (head_dim == 128) return launch_cascade_t<BF16, 128>(a, pre_acc, pre_ml, pre_parts, stream);
     }
     return hipErrorInvalidValue;
 }

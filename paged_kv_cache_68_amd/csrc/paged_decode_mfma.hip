@@ -106,7 +106,7 @@ struct PairWalk {
         jb = j_begin;
         j_end = j_stop;
         nk = j_stop > j_begin ? (j_stop - j_begin + 1) / 2 : 0;
-        const int32_t* trow = a.tables + static_cast<size_t>(it.b) * a.max_blocks;
+        const int32_t* trow = a.tables + static_cast<size_t>(it.b) * a.table_stride;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int k = 64 * t + lane;
@@ -176,7 +176,7 @@ __device__ __forceinline__ void walk_pairs3(const DecodeArgs& a, const Item& it,
 template <class S, int D, bool KV8>
 __device__ __forceinline__ void append_token(const DecodeArgs& a, int b, int kvh, int L, int lane) {
     const int last = L - 1;
-    const int blk = a.tables[static_cast<size_t>(b) * a.max_blocks + last / a.block_size];
+    const int blk = a.tables[static_cast<size_t>(b) * a.table_stride + last / a.block_size];
     if (static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks) && lane < D / 2) {
         const size_t slot = static_cast<size_t>(blk) * a.block_size + last % a.block_size;
         const size_t src = (static_cast<size_t>(b) * a.num_kv_heads + kvh) * (D / 2) + lane;

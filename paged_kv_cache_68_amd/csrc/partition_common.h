@@ -30,9 +30,10 @@ struct Item {
     int j0, j1;
 };
 
-// Length of sequence b, clamped to [0, table width * B].
+// Tokens of sequence b that the table holds (its length less len_offset), clamped to
+// [0, table width * B].
 __device__ __forceinline__ int clamped_length(const DecodeArgs& a, int b) {
-    const int L = a.lens[b];
+    const int L = a.lens[b] - a.len_offset;
     const int cap = a.max_blocks * a.block_size;
     return L < 0 ? 0 : (L > cap ? cap : L);
 }
@@ -66,7 +67,7 @@ struct BlockWalk {
         jb = it.j0 + first;
         js = step;
         nk = it.j1 > jb ? (it.j1 - jb + js - 1) / js : 0;
-        const int32_t* trow = a.tables + static_cast<size_t>(it.b) * a.max_blocks;
+        const int32_t* trow = a.tables + static_cast<size_t>(it.b) * a.table_stride;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int k = 64 * t + lane;
@@ -80,7 +81,7 @@ struct BlockWalk {
         jb = j_begin;
         js = 1;
         nk = j_end > jb ? j_end - jb : 0;
-        const int32_t* trow = a.tables + static_cast<size_t>(it.b) * a.max_blocks;
+        const int32_t* trow = a.tables + static_cast<size_t>(it.b) * a.table_stride;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int k = 64 * t + lane;
@@ -185,13 +186,15 @@ __device__ __forceinline__ size_t part_row(const DecodeArgs& a, int b, int kvh, 
 // One wave writes the result of partition p of its item from a staging area in LDS
 // (st_acc[G][D] accumulators, st_ml[G][2] running max / sum): the final output if the
 // sequence has a single partition, else the fp32 partials.  All 64 lanes take part, each
-// with 16-byte accesses, so the global writes are whole contiguous lines.
+// with 16-byte accesses, so the global writes are whole contiguous lines.  `whole`: the
+// state covers every partition of the sequence; kept as a partial result (keep_partials)
+// it is the only one, at slot 0 of rows [B][Hkv][1][G].
 template <class S, int D>
 __device__ __forceinline__ void store_partition(const DecodeArgs& a, const Item& it, int G, int p,
                                                 const float* st_acc, const float* st_ml, int lane,
                                                 bool whole = false) {
     const int n = G * D;
-    if (it.nparts == 1 || whole) {     // whole: the state covers every partition
+    if (!a.keep_partials && (it.nparts == 1 || whole)) {
         uint16_t* o = a.out + (static_cast<size_t>(it.b) * a.num_q_heads + it.kvh * G) * D;
         for (int i = lane * 8; i < n; i += 512) {
             const float lg = st_ml[2 * (i / D) + 1];
@@ -206,7 +209,8 @@ __device__ __forceinline__ void store_partition(const DecodeArgs& a, const Item&
             *reinterpret_cast<uint4*>(o + i) = make_uint4(w[0], w[1], w[2], w[3]);
         }
     } else {
-        const size_t row0 = part_row(a, it.b, it.kvh, p, G);
+        const size_t row0 = whole ? (static_cast<size_t>(it.b) * a.num_kv_heads + it.kvh) * G
+                                  : part_row(a, it.b, it.kvh, p, G);
         float* dst = a.ws_acc + row0 * D;
         for (int i = lane * 4; i < n; i += 256)
             *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(st_acc + i);
@@ -237,7 +241,7 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
             lsum += f * sm_ml[(w * G + g) * 2 + 1];
             A += f * sm_acc[(w * G + g) * D + dd];
         }
-        if (it.nparts == 1) {
+        if (it.nparts == 1 && !a.keep_partials) {
             a.out[out_row0 + idx] = S::narrow(lsum > 0.f ? A / lsum : 0.f);
         } else {
             const size_t row = part_row(a, it.b, it.kvh, it.p, G) + g;
@@ -279,7 +283,7 @@ __device__ __forceinline__ void merge_slots_and_store(const DecodeArgs& a, int b
             lsum += f * st[per_head + 2 * g + 1];
             A += f * st[rem];
         }
-        if (whole) {
+        if (whole && !a.keep_partials) {
             a.out[out0 + idx] = S::narrow(lsum > 0.f ? A / lsum : 0.f);
         } else {
             const size_t row =
@@ -293,10 +297,11 @@ __device__ __forceinline__ void merge_slots_and_store(const DecodeArgs& a, int b
     }
 }
 
-// Zero output for a sequence with no tokens (written once, by partition 0's item).
+// Zero output for a sequence with no tokens (written once, by partition 0's item).  With
+// keep_partials nothing: such a sequence has no partial results.
 template <int D>
 __device__ __forceinline__ void store_empty(const DecodeArgs& a, const Item& it, int G, int t0, int nt) {
-    if (it.p != 0) return;
+    if (it.p != 0 || a.keep_partials) return;
     const size_t out_row0 = (static_cast<size_t>(it.b) * a.num_q_heads + it.kvh * G) * D;
     for (int i = t0; i < G * D; i += nt) a.out[out_row0 + i] = 0;
 }

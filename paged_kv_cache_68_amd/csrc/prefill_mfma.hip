@@ -73,8 +73,15 @@ constexpr int kPfRuns = 2;          // 32-key runs per LDS stage (one barrier pe
 // SPLIT: pa.splits work-groups share each row tile's key stages, each taking an equal
 // run of them and writing its rows' unnormalised partial results (acc, m, l) for
 // pa_prefill_merge to combine.
-template <class S, int D, int W, bool KV8, bool SPLIT>
+// DENSE (with SPLIT): the shared prefix of a decode batch.  The batch's queries are the
+// rows of one "sequence" (token t = sequence t, all num_tokens of them), the keys are
+// positions [0, dense_len) of table row 0, and row t's causal limit is its own length:
+// it sees keys [0, min(lens[t], dense_len)).  The partial results cover the prefix only;
+// the suffix of each sequence is walked by the decode kernels and the two are combined
+// by the cascade reduce.
+template <class S, int D, int W, bool KV8, bool SPLIT, bool DENSE = false>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void pa_prefill_mfma(PrefillArgs pa) {
+    static_assert(!DENSE || SPLIT, "the dense form writes partial results");
     const DecodeArgs& a = pa.a;
     constexpr int NC = 2;
     constexpr int KT = 32 * kPfRuns;             // keys per LDS stage
@@ -114,10 +121,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int rt = pa.row_tiles - 1 - tile_id % pa.row_tiles;
     const int rest = tile_id / pa.row_tiles;
     const int kvh = rest % a.num_kv_heads;
-    const int b = rest / a.num_kv_heads;
-    const int q0 = pa.qstart[b];
-    const int nq = pa.qstart[b + 1] - q0;
-    const int L = clamped_length(a, b);
+    const int b = DENSE ? 0 : rest / a.num_kv_heads;
+    const int q0 = DENSE ? 0 : pa.qstart[b];
+    const int nq = DENSE ? pa.num_tokens : pa.qstart[b + 1] - q0;
+    const int L = DENSE ? pa.dense_len : clamped_length(a, b);
     const int rows = nq * G;
     const int group_row0 = rt * kPfRowsPerWave * W;
     if (group_row0 >= rows) return;              // the whole work-group is past the chunk
@@ -139,8 +146,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int t = r / G;
         const int g = r - t * G;
         tok[cb] = t;
-        qpos[cb] = (r < rows) ? L - nq + t : -1;     // -1: no such row / before position 0
-        if (qpos[cb] < 0) qpos[cb] = -1;
+        if constexpr (DENSE) {
+            qpos[cb] = (r < rows) ? min(max(a.lens[t], 0), L) - 1 : -1;
+        } else {
+            qpos[cb] = (r < rows) ? L - nq + t : -1;     // -1: no such row / before position 0
+            if (qpos[cb] < 0) qpos[cb] = -1;
+        }
         const size_t qrow = (static_cast<size_t>(q0 + t) * a.num_q_heads + kvh * G + g) * D;
 #pragma unroll
         for (int i = 0; i < NQK; ++i) {
@@ -149,7 +160,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     }
     // first and last position of each column block (wave-uniform): rows are in token
-    // order, so the block's first row has its smallest position
+    // order, so the block's first row has its smallest position (dense: any order, so
+    // the smallest is searched for)
     int last[NC];
     int first[NC];
     int wave_last = -1;
@@ -161,11 +173,18 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         last[cb] = uniform(x);
         wave_last = max(wave_last, last[cb]);
         const int r0 = row_base + cb * 16;
-        first[cb] = r0 < rows ? L - nq + r0 / G : -1;
+        if constexpr (DENSE) {
+            int y = qpos[cb];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) y = min(y, __shfl_xor(y, off));
+            first[cb] = uniform(y);
+        } else {
+            first[cb] = r0 < rows ? L - nq + r0 / G : -1;
+        }
     }
-    // the work-group's last position: its last row's
+    // the work-group's last position: its last row's (dense: the prefix's last key)
     const int group_rows_end = min(rows, group_row0 + kPfRowsPerWave * W);
-    const int group_last = L - nq + (group_rows_end - 1) / G;
+    const int group_last = DENSE ? L - 1 : L - nq + (group_rows_end - 1) / G;
     const int nstages = group_last >= 0 ? group_last / KT + 1 : 0;
     const int wave_stages = wave_last >= 0 ? wave_last / KT + 1 : 0;
 
@@ -184,7 +203,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 
     // ---- staging: global (through the table) -> registers -> LDS.  Thread chunk u is
     // key (tid + u THREADS) / CPR of the stage, 8 values at part (tid + u THREADS) % CPR.
-    const int* table = a.tables + static_cast<size_t>(b) * a.max_blocks;
+    const int* table = a.tables + static_cast<size_t>(b) * a.table_stride;
     const int bshift = __builtin_ctz(a.block_size);
     const uint32_t block_bytes = static_cast<uint32_t>(a.block_size * a.row_bytes);
     Raw rk[PER_T], rv[PER_T];
@@ -523,12 +542,21 @@ __global__ __launch_bounds__(256) void pa_prefill_merge(PrefillArgs pa) {
     }
 }
 
-template <class S, int D, bool KV8, bool SPLIT>
+template <class S, int D, bool KV8, bool SPLIT, bool DENSE = false>
 void launch_main(const PrefillArgs& pa, unsigned grid, hipStream_t stream) {
     if (pa.waves == 8)
-        hipLaunchKernelGGL((pa_prefill_mfma<S, D, 8, KV8, SPLIT>), dim3(grid), dim3(64 * 8), 0, stream, pa);
+        hipLaunchKernelGGL((pa_prefill_mfma<S, D, 8, KV8, SPLIT, DENSE>), dim3(grid), dim3(64 * 8), 0, stream, pa);
     else
-        hipLaunchKernelGGL((pa_prefill_mfma<S, D, 4, KV8, SPLIT>), dim3(grid), dim3(64 * 4), 0, stream, pa);
+        hipLaunchKernelGGL((pa_prefill_mfma<S, D, 4, KV8, SPLIT, DENSE>), dim3(grid), dim3(64 * 4), 0, stream, pa);
+}
+
+template <class S, int D, bool KV8>
+hipError_t launch_dense_t(const PrefillArgs& pa, hipStream_t stream) {
+    const int64_t wgs = static_cast<int64_t>(pa.a.num_kv_heads) * pa.row_tiles * pa.splits;
+    if (wgs <= 0) return hipSuccess;
+    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+    launch_main<S, D, KV8, true, true>(pa, static_cast<unsigned>(wgs), stream);
+    return hipGetLastError();
 }
 
 template <class S, int D, bool KV8>
@@ -584,6 +612,19 @@ int64_t prefill_resident_groups(int kv_dtype, int io_dtype, int head_dim, int wa
         if (head_dim == 128) return kv8 ? resident_groups_t<BF16, 128, true>(waves) : resident_groups_t<BF16, 128, false>(waves);
     }
     return 0;
+}
+
+hipError_t launch_prefill_dense(int kv_dtype, int io_dtype, int head_dim, const PrefillArgs& pa,
+                                hipStream_t stream) {
+    const bool kv8 = kv_dtype == KV_DTYPE_FP8_E4M3;
+    if (io_dtype == KV_DTYPE_F16) {
+        if (head_dim == 64) return kv8 ? launch_dense_t<F16, 64, true>(pa, stream) : launch_dense_t<F16, 64, false>(pa, stream);
+        if (head_dim == 128) return kv8 ? launch_dense_t<F16, 128, true>(pa, stream) : launch_dense_t<F16, 128, false>(pa, stream);
+    } else if (io_dtype == KV_DTYPE_BF16) {
+        if (head_dim == 64) return kv8 ? launch_dense_t<BF16, 64, true>(pa, stream) : launch_dense_t<BF16, 64, false>(pa, stream);
+        if (head_dim == 128) return kv8 ? launch_dense_t<BF16, 128, true>(pa, stream) : launch_dense_t<BF16, 128, false>(pa, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill(int kv_dtype, int io_dtype, int head_dim, const PrefillArgs& pa,

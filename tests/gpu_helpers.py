@@ -55,3 +55,21 @@ def max_abs_err(gpu_bits: np.ndarray, ref: np.ndarray, dtype: str) -> float:
     got = oracle.to_f64(gpu_bits, dtype)
     assert np.all(np.isfinite(got)), "non-finite output"
     return float(np.max(np.abs(got - ref)))
+
+
+def relabelled(dc: DeviceCase, seed: int):
+    """A copy of the pool with block p moved to pi(p), and the matching tables."""
+    import torch
+
+    import paged_kv_cache_68_amd as pk
+    cfg = dc.cfg
+    nb = cfg.num_blocks
+    pi = torch.randperm(nb, generator=torch.Generator().manual_seed(seed)).cuda()
+    inv = torch.argsort(pi)
+    pool2 = pk.KVPool(1, nb, cfg.num_kv_heads, cfg.head_dim, cfg.kv, block_size=cfg.block_size,
+                      io_dtype=cfg.dtype)
+    for which in ("k_cache", "v_cache"):
+        torch.index_select(getattr(dc.pool, which)(0), 0, inv, out=getattr(pool2, which)(0))
+    t = dc.tables
+    tables2 = torch.where(t >= 0, pi[t.clamp(min=0).long()].to(torch.int32), t).contiguous()
+    return pool2, tables2, pi

@@ -32,7 +32,9 @@ import oracle  # noqa: E402
 import paged_kv_cache_68_amd as pk  # noqa: E402
 from workloads import config_by_name, make_case  # noqa: E402
 
-from .gpu_helpers import TOL, DeviceCase, max_abs_err, oracle_for_seqs, to_host_bits  # noqa: E402
+from .gpu_helpers import (  # noqa: E402
+    TOL, DeviceCase, max_abs_err, oracle_for_seqs, relabelled as _relabelled, to_host_bits,
+)
 
 
 def _say(msg):
@@ -54,21 +56,6 @@ def bench_variant(idx, block_size=None, kv=None):
 def _device_case(cfg):
     where = "device" if cfg.index in (3, 5) else "host"
     return DeviceCase(make_case(cfg, where=where, poison=where == "host"))
-
-
-def _relabelled(dc, seed):
-    """A copy of the pool with block p moved to pi(p), and the matching tables."""
-    cfg = dc.cfg
-    nb = cfg.num_blocks
-    pi = torch.randperm(nb, generator=torch.Generator().manual_seed(seed)).cuda()
-    inv = torch.argsort(pi)
-    pool2 = pk.KVPool(1, nb, cfg.num_kv_heads, cfg.head_dim, cfg.kv, block_size=cfg.block_size,
-                      io_dtype=cfg.dtype)
-    for which in ("k_cache", "v_cache"):
-        torch.index_select(getattr(dc.pool, which)(0), 0, inv, out=getattr(pool2, which)(0))
-    t = dc.tables
-    tables2 = torch.where(t >= 0, pi[t.clamp(min=0).long()].to(torch.int32), t).contiguous()
-    return pool2, tables2, pi
 
 
 def _step(pool, dc, tables, out):

@@ -87,3 +87,22 @@ def test_large_configs_metadata(idx):
         assert np.all(lens == 8192)
     else:
         assert lens.min() >= 1 and lens.max() <= 4096
+
+
+def test_fork_batches():
+    """fork_<P>_<S>: cfg.batch forks of a P-token prefix, U[1, S] private tokens each; the
+    full blocks of the prefix are shared, the partial one copied on write."""
+    import dataclasses
+
+    from workloads import fork_shape
+    assert fork_shape(config_by_name(4)) == (SHARED_PREFIX_TOKENS, 64, 512)
+    cfg = dataclasses.replace(config_by_name(4), index=77, batch=8, num_blocks=200,
+                              lengths="fork_100_40")
+    c = make_case(cfg)
+    assert fork_shape(cfg) == (100, 8, 40)
+    t = c.block_tables
+    assert np.all(t[:, :6] == t[0, :6]) and list(c.shared_blocks) == list(t[0, :6])
+    assert len(c.cow_copies) == 7 and len(set(t[:, 6].tolist())) == 8
+    assert np.all(c.lengths > 100) and np.all(c.lengths <= 140)
+    private = t[:, 6:][t[:, 6:] >= 0]
+    assert len(private) == len(set(private.tolist()))

@@ -13,4 +13,6 @@ from .gen import (  # noqa: F401
     nan_bits,
     round_to_bits,
     bits_dtype_name,
+    fork_shape,
+    is_fork,
 )

@@ -158,8 +158,23 @@ def _make_scattered_host(cfg, rng, lens, poison):
     return tables, used, pools
 
 
+def fork_shape(cfg: DecodeConfig):
+    """(prefix tokens, forks, largest private suffix) of a forked-batch config:
+    "shared_prefix" is 64 forks of 4,103 tokens with U[1, 512] more each;
+    "fork_<P>_<S>" is cfg.batch forks of P tokens with U[1, S] more each."""
+    if cfg.lengths == "shared_prefix":
+        return SHARED_PREFIX_TOKENS, SHARED_FORKS, 512
+    _, p, s = cfg.lengths.split("_")
+    return int(p), cfg.batch, int(s)
+
+
+def is_fork(cfg: DecodeConfig) -> bool:
+    return cfg.lengths == "shared_prefix" or cfg.lengths.startswith("fork_")
+
+
 def _make_shared_prefix_host(cfg, rng, poison):
-    """Fork 64 ways from a 4,103-token prefix, copy-on-write the shared partial block.
+    """Fork 64 ways from a 4,103-token prefix (or as fork_shape says), copy-on-write the
+    shared partial block.
 
     Follows the append rule of "Why AI servers waste memory, and how paging fixes
     it" ("Sharing a prefix with copy-on-write"): a fork copies the table and raises
@@ -174,22 +189,23 @@ def _make_shared_prefix_host(cfg, rng, poison):
     free = deque(int(x) for x in rng.permutation(nb))
     ref = np.zeros(nb, dtype=np.int64)
 
-    n_prefix_blocks = _blocks_for(SHARED_PREFIX_TOKENS, bs)
+    n_tokens, forks, suffix_max = fork_shape(cfg)
+    n_prefix_blocks = _blocks_for(n_tokens, bs)
     prefix = [free.popleft() for _ in range(n_prefix_blocks)]
     ref[prefix] = 1
     # prefix tokens (the parent's prompt)
     for j, blk in enumerate(prefix):
-        n_valid = min(bs, SHARED_PREFIX_TOKENS - j * bs)
+        n_valid = min(bs, n_tokens - j * bs)
         kp[blk, :n_valid] = _host_values((n_valid, H, d), rng, cfg.kv)
         vp[blk, :n_valid] = _host_values((n_valid, H, d), rng, cfg.kv)
     # fork: every child copies the parent's table; counts rise by forks-1
-    tables = [list(prefix) for _ in range(SHARED_FORKS)]
-    ref[prefix] += SHARED_FORKS - 1
-    suffix = rng.integers(1, 512, size=SHARED_FORKS, endpoint=True)
-    lens = SHARED_PREFIX_TOKENS + suffix
+    tables = [list(prefix) for _ in range(forks)]
+    ref[prefix] += forks - 1
+    suffix = rng.integers(1, suffix_max, size=forks, endpoint=True)
+    lens = n_tokens + suffix
     copies = []
-    for b in range(SHARED_FORKS):
-        n = SHARED_PREFIX_TOKENS
+    for b in range(forks):
+        n = n_tokens
         last = tables[b][-1]
         if n % bs != 0 and ref[last] > 1:        # shared block with room -> private copy
             new = free.popleft()
@@ -212,11 +228,11 @@ def _make_shared_prefix_host(cfg, rng, poison):
                 kp[blk, o] = _host_values((H, d), rng, cfg.kv)
                 vp[blk, o] = _host_values((H, d), rng, cfg.kv)
     width = max(len(t) for t in tables)
-    tab = np.full((SHARED_FORKS, width), -1, dtype=np.int32)
+    tab = np.full((forks, width), -1, dtype=np.int32)
     for b, t in enumerate(tables):
         tab[b, :len(t)] = t
     used = np.array(sorted({x for t in tables for x in t}), dtype=np.int64)
-    return (lens.astype(np.int32), tab, used, [kp, vp], np.array(prefix[:SHARED_PREFIX_TOKENS // bs]),
+    return (lens.astype(np.int32), tab, used, [kp, vp], np.array(prefix[:n_tokens // bs], dtype=np.int64),
             ref, copies)
 
 
@@ -233,7 +249,7 @@ def make_case(cfg: DecodeConfig, where: str = "host", poison: bool = True,
     bs, H, d, Hq = cfg.block_size, cfg.num_kv_heads, cfg.head_dim, cfg.num_q_heads
     shared = ref = None
     copies = []
-    if cfg.lengths == "shared_prefix":
+    if is_fork(cfg):
         if where != "host":
             raise ValueError("the shared-prefix case is built on the host")
         lens, tables, used, pools, shared, ref, copies = _make_shared_prefix_host(cfg, rng, poison)
