@@ -129,12 +129,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int group_row0 = rt * kPfRowsPerWave * W;
     if (group_row0 >= rows) return;              // the whole work-group is past the chunk
     const int row_base = group_row0 + wave * kPfRowsPerWave;
-    // a negative scale is applied as a positive one to negated keys (exact, done while
-    // staging), so that the running maximum of the raw scores is that of the scaled ones
-    // (a zero scale runs as 1e-30: every weight is then exactly 1, as it should be, and
-    // masked scores stay -inf instead of becoming 0 * inf)
+    // a negative scale is applied as a positive one to the negated query (exact), so that
+    // the running maximum of the raw scores is that of the scaled ones (a zero scale runs
+    // as 1e-30: every weight is then exactly 1, as it should be, and masked scores stay
+    // -inf instead of becoming 0 * inf)
     const float sl2 = fmaxf(fabsf(a.scale_log2), 1e-30f);
-    const bool negate_keys = a.scale_log2 < 0.f;
+    const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
     // this lane's column in each block: row -> (token, head), position, Q^T operand
     int qpos[NC];
@@ -157,6 +157,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int i = 0; i < NQK; ++i) {
             qv[cb][i] = qpos[cb] >= 0 ? *reinterpret_cast<const uint4*>(a.q + qrow + 32 * i + 8 * c)
                                       : make_uint4(0, 0, 0, 0);
+            qv[cb][i].x ^= qsign;
+            qv[cb][i].y ^= qsign;
+            qv[cb][i].z ^= qsign;
+            qv[cb][i].w ^= qsign;
         }
     }
     // first and last position of each column block (wave-uniform): rows are in token
@@ -263,14 +267,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int u = 0; u < PER_T; ++u) {
             const int q = tid + u * THREADS;
             if (q < CHUNKS) {
-                uint4 kx = widen(rk[u]);
-                if (negate_keys) {
-                    kx.x ^= 0x80008000u;
-                    kx.y ^= 0x80008000u;
-                    kx.z ^= 0x80008000u;
-                    kx.w ^= 0x80008000u;
-                }
-                *reinterpret_cast<uint4*>(&lds_k[buf][(q / CPR) * ROWB_K + (q % CPR) * 16]) = kx;
+                *reinterpret_cast<uint4*>(&lds_k[buf][(q / CPR) * ROWB_K + (q % CPR) * 16]) = widen(rk[u]);
                 *reinterpret_cast<uint4*>(&lds_v[buf][(q / CPR) * ROWB_V + (q % CPR) * 16]) = widen(rv[u]);
             }
         }

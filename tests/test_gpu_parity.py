@@ -179,7 +179,7 @@ def _custom_case(lens, hq=8, hkv=2, d=128, dtype="bf16", nb=None, seed=0):
     return cfg, lens, tables, kp, vp, q
 
 
-def _run_custom(cfg, lens, tables, kp, vp, q, part=512):
+def _run_custom(cfg, lens, tables, kp, vp, q, part=512, scale=None):
     pool = pk.KVPool(1, cfg.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.dtype)
     pool.k_cache(0).copy_(to_dev(kp, cfg.dtype))
     pool.v_cache(0).copy_(to_dev(vp, cfg.dtype))
@@ -187,8 +187,24 @@ def _run_custom(cfg, lens, tables, kp, vp, q, part=512):
     out = torch.empty_like(qd)
     td = torch.from_numpy(tables).cuda()
     ld = torch.from_numpy(lens).cuda()
-    pk.paged_attention_decode(pool, 0, out, qd, td, ld, scale=cfg.scale, partition_size=part)
+    pk.paged_attention_decode(pool, 0, out, qd, td, ld, scale=cfg.scale if scale is None else scale,
+                              partition_size=part)
     return to_host_bits(out)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+@pytest.mark.parametrize("hq,env", [(8, {}), (8, {"PAGEDKV_SPLIT": "0", "PAGEDKV_GROUP": "0"}),
+                                    (2, {"PAGEDKV_KERNEL": "valu"}), (2, {"PAGEDKV_KERNEL": "mfma"})])
+def test_negative_and_zero_scale(monkeypatch, scale, hq, env):
+    """The scale multiplies q.k whatever its sign: a negative one favours the lowest
+    scores, zero gives every position the same weight (the mean of the values)."""
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    lens = [1, 17, 600, 1500]
+    cfg, lens, tables, kp, vp, q = _custom_case(lens, hq=hq, seed=31)
+    out = _run_custom(cfg, lens, tables, kp, vp, q, scale=scale)
+    ref = oracle.paged_decode(q, kp, vp, tables, lens, scale, 16, cfg.dtype)
+    assert np.all(np.abs(oracle.to_f64(out, cfg.dtype) - ref) <= flat_bar(ref, cfg.dtype))
 
 
 @pytest.mark.parametrize("part", [16, 64, 512, 4096])

@@ -97,7 +97,7 @@ def _case(chunks, B, hq, hkv, d, io, kv, seed):
     return lens, qs, tables, kp, vp, q, nb
 
 
-def _run(B, lens, qs, tables, kp, vp, q, nb, hkv, d, io, kv):
+def _run(B, lens, qs, tables, kp, vp, q, nb, hkv, d, io, kv, scale=None):
     pool = pk.KVPool(1, nb, hkv, d, kv, block_size=B, io_dtype=io)
     pool.k_cache(0).copy_(to_dev(kp, kv))
     pool.v_cache(0).copy_(to_dev(vp, kv))
@@ -106,9 +106,22 @@ def _run(B, lens, qs, tables, kp, vp, q, nb, hkv, d, io, kv):
     maxq = int(np.max(np.diff(qs))) if len(qs) > 1 else 0
     pk.paged_attention_prefill(pool, 0, out, qd, torch.from_numpy(qs).cuda(), maxq,
                                torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
-                               scale=1.0 / math.sqrt(d))
+                               scale=1.0 / math.sqrt(d) if scale is None else scale)
     torch.cuda.synchronize()
     return to_host_bits(out)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+@pytest.mark.parametrize("io,kv", [("bf16", "bf16"), ("f16", "fp8")])
+def test_prefill_negative_and_zero_scale(scale, io, kv):
+    """A negative scale runs as a positive one on the negated query; zero weighs every
+    visible position equally."""
+    B, hq, hkv, d = 16, 32, 8, 128
+    _say(f"prefill scale {scale} io={io} kv={kv}")
+    lens, qs, tables, kp, vp, q, nb = _case(CHUNKS, B, hq, hkv, d, io, kv, seed=300)
+    got = _run(B, lens, qs, tables, kp, vp, q, nb, hkv, d, io, kv, scale=scale)
+    ref = oracle.paged_prefill(q, qs, kp, vp, tables, lens, scale, B, kv, q_dtype=io)
+    _check(got, ref, qs, tables, lens, vp, B, kv, io, hkv)
 
 
 CHUNKS = [(1, 1), (1, 100), (17, 17), (40, 100), (200, 700), (513, 513), (64, 2000), (0, 50),

@@ -48,7 +48,7 @@ def _garbage_workspace(pool, batch, hq, max_blocks, prefix_blocks, part):
 
 
 def _run(dc, prefix_blocks, append=True, workspace=None, tables=None, lens=None, pool=None,
-         out=None):
+         out=None, scale=None):
     cfg = dc.cfg
     pool = pool or dc.pool
     tables = dc.tables if tables is None else tables
@@ -60,7 +60,8 @@ def _run(dc, prefix_blocks, append=True, workspace=None, tables=None, lens=None,
     pk.paged_attention_decode_shared_prefix(
         pool, 0, out, dc.query, tables, lens, prefix_blocks,
         new_key=dc.new_key if append else None, new_value=dc.new_value if append else None,
-        scale=cfg.scale, partition_size=cfg.partition_size, workspace=workspace)
+        scale=cfg.scale if scale is None else scale, partition_size=cfg.partition_size,
+        workspace=workspace)
     return to_host_bits(out)
 
 
@@ -174,6 +175,19 @@ def test_sequences_shorter_than_the_prefix_and_an_all_prefix_table():
     ref2 = oracle.paged_decode(case.query, kp, vp, case.block_tables[:, :P],
                                lens2, cfg.scale, cfg.block_size, cfg.kv, q_dtype=cfg.dtype)
     _check_bar(out2, ref2, cfg.dtype, "all-prefix tables")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+def test_negative_and_zero_scale(scale):
+    cfg = _fork_cfg(785, 32, 8, 128, "bf16", 16, 700, 300, 6)
+    case = make_case(cfg)
+    P = _prefix_blocks(case)
+    dc = DeviceCase(case)
+    out = _run(dc, P, scale=scale)
+    _, kp, vp = oracle_after_write(case)
+    ref = oracle.paged_decode(case.query, kp, vp, case.block_tables, case.lengths, scale,
+                              cfg.block_size, cfg.kv, q_dtype=cfg.dtype)
+    _check_bar(out, ref, cfg.dtype, f"scale {scale}")
 
 
 def test_zero_prefix_blocks_is_plain_decode():
