@@ -734,8 +734,11 @@ def _main_gpu(args, workers):
         nbytes["partition_kernel_unique"] += nbytes["write"]
 
     # forks of one prefix: the shared-prefix entry point (the shared blocks read once for
-    # the batch), unless --no-shared-prefix
-    prefix_blocks = len(case.shared_blocks) if is_fork(cfg) and not args.no_shared_prefix else 0
+    # the batch, as many as the tables share), unless --no-shared-prefix
+    prefix_blocks = 0
+    if is_fork(cfg) and not args.no_shared_prefix:
+        prefix_blocks = pk.shared_prefix_blocks(case.block_tables, case.lengths, cfg.block_size,
+                                                appending=fused)
     cascade = prefix_blocks > 0
 
     # the step as a serving loop runs it: buffers checked once, one library call per step

@@ -327,6 +327,21 @@ kv_status_t paged_attention_decode_shared_prefix(const kv_pool_t* pool, int32_t 
                                                  int32_t prefix_blocks, int32_t partition_size,
                                                  void* workspace, size_t workspace_bytes,
                                                  hipStream_t stream);
+/* The largest prefix_blocks that paged_attention_decode_shared_prefix accepts for these
+ * tables (host arrays, as kv_bm_export and kv_pc_export fill them): the number of leading
+ * entries of row 0 that are blocks (>= 0) and that every other sequence has too, where a
+ * sequence is held only to the entries its length uses (ceil(L / B); a shorter sequence
+ * sees its own part of the prefix).  With appending != 0, also at most (L - 1) / B for
+ * every sequence of length L > 0: its new token must fall after the prefix, in a block
+ * of its own (copy-on-write keeps the written block private; "Why AI servers waste
+ * memory, and how paging fixes it", "Sharing a prefix with copy-on-write").
+ *  tables  : [batch][max_blocks] int32; lengths: [batch] int32 (clamped to the table).
+ * Returns the count, 0 when nothing is shared, or -1 for invalid arguments (null
+ * pointers, batch < 1, max_blocks < 1, block_size not 8, 16, 32 or 64).  Reads only the
+ * arrays; nothing is enqueued. */
+int32_t kv_shared_prefix_blocks(const int32_t* tables, const int32_t* lengths, int32_t batch,
+                                int32_t max_blocks, int32_t block_size, int32_t appending);
+
 /* Workspace bytes of paged_attention_decode_shared_prefix for this shape on the current
  * device (the prefix's split follows the device's size): the prefix's partial results
  * (fp32 m, l and O of every (sequence, query head, split)), then the suffixes' partial

@@ -26,7 +26,7 @@ __all__ = [
     "hash_block", "swap_blocks", "paged_attention_decode_append", "paged_attention_partitions_append",
     "paged_attention_prefill_split", "prefill_workspace_bytes", "alloc_prefill_workspace",
     "DecodeStep", "paged_attention_decode_noalloc", "paged_attention_decode_shared_prefix",
-    "shared_prefix_workspace_bytes", "alloc_shared_prefix_workspace",
+    "shared_prefix_workspace_bytes", "alloc_shared_prefix_workspace", "shared_prefix_blocks",
 ]
 
 BLOCK_SIZE = 16
@@ -430,6 +430,24 @@ def paged_attention_decode_noalloc(pool: KVPool, layer: int, out, query, block_t
                                                _stream(stream)),
           "paged_attention_decode_noalloc")
     return out
+
+
+def shared_prefix_blocks(tables, lengths, block_size=BLOCK_SIZE, appending=False) -> int:
+    """The largest prefix_blocks paged_attention_decode_shared_prefix accepts for these
+    host tables ([B, max_blocks] int32) and lengths ([B] int32): numpy arrays or CPU
+    tensors, as BlockManager.export / PrefixCache.export return them.  ``appending``: the
+    step also writes each sequence's token at position L - 1, which must fall after the
+    prefix."""
+    import numpy as np
+    t = np.ascontiguousarray(np.asarray(tables), dtype=np.int32)
+    n = np.ascontiguousarray(np.asarray(lengths), dtype=np.int32)
+    if t.ndim != 2 or n.ndim != 1 or n.shape[0] != t.shape[0]:
+        raise ValueError(f"shared_prefix_blocks: tables {t.shape} and lengths {n.shape} do not match")
+    r = int(lib().kv_shared_prefix_blocks(t.ctypes.data, n.ctypes.data, int(t.shape[0]),
+                                          int(t.shape[1]), int(block_size), int(bool(appending))))
+    if r < 0:
+        raise ValueError("shared_prefix_blocks: invalid arguments")
+    return r
 
 
 def shared_prefix_workspace_bytes(pool: KVPool, batch, num_q_heads, max_blocks_per_seq,

@@ -25,6 +25,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -325,6 +326,37 @@ kv_status_t kv_bm_free_list(const kv_block_manager_t* m, int32_t* blocks, int32_
     }
     *num = m->num_free;
     return KV_OK;
+}
+
+// The largest prefix the shared-prefix decode accepts for these host tables (see
+// include/pagedkv.h): row 0's leading blocks, cut at the first entry a sequence uses
+// that differs from row 0's, and with new tokens before each sequence's last position.
+int32_t kv_shared_prefix_blocks(const int32_t* tables, const int32_t* lengths, int32_t batch,
+                                int32_t max_blocks, int32_t block_size, int32_t appending) {
+    if (!tables || !lengths || batch < 1 || max_blocks < 1 ||
+        (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64))
+        return -1;
+    auto used = [&](int32_t b) -> int32_t {      // entries sequence b's length reaches
+        const int64_t L = std::min<int64_t>(std::max<int32_t>(lengths[b], 0),
+                                            static_cast<int64_t>(max_blocks) * block_size);
+        return static_cast<int32_t>((L + block_size - 1) / block_size);
+    };
+    int32_t p = 0;                               // row 0's leading blocks
+    while (p < max_blocks && tables[p] >= 0) ++p;
+    for (int32_t b = 1; b < batch && p > 0; ++b) {
+        const int32_t* row = tables + static_cast<size_t>(b) * max_blocks;
+        const int32_t n = std::min(p, used(b));
+        int32_t j = 0;
+        while (j < n && row[j] == tables[j]) ++j;
+        if (j < n) p = j;                        // a used entry differs from row 0's
+    }
+    if (appending) {
+        for (int32_t b = 0; b < batch && p > 0; ++b) {
+            const int32_t L = std::min<int64_t>(lengths[b], static_cast<int64_t>(max_blocks) * block_size);
+            if (L > 0) p = std::min(p, (L - 1) / block_size);
+        }
+    }
+    return p;
 }
 
 }  // extern "C"

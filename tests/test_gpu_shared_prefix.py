@@ -82,6 +82,7 @@ def test_64_forks_of_4103_tokens_match_the_oracle():
     case = make_case(cfg)
     P = _prefix_blocks(case)
     assert P == 256
+    assert pk.shared_prefix_blocks(case.block_tables, case.lengths, cfg.block_size, appending=True) == P
     _say(f"shared prefix {cfg.name}: {P} blocks")
     dc = DeviceCase(case)
     out = _run(dc, P)
