@@ -344,7 +344,8 @@ int32_t kv_shared_prefix_blocks(const int32_t* tables, const int32_t* lengths, i
 
 /* Workspace bytes of paged_attention_decode_shared_prefix for this shape on the current
  * device (the prefix's split follows the device's size): the prefix's partial results
- * (fp32 m, l and O of every (sequence, query head, split)), then the suffixes' partial
+ * (m, l and a scale in fp32, O as 16-bit integers times that scale, for every (sequence,
+ * query head, split)), then the suffixes' partial
  * results (as paged_attention_workspace_bytes, for the entries after the prefix, with one
  * partition counted too).  With prefix_blocks == 0, paged_attention_workspace_bytes.
  * SIZE_MAX for invalid arguments (null or host pool, sizes out of range). */

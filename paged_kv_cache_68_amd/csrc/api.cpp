@@ -420,12 +420,21 @@ struct CascadePlan {
     int splits = 1;             // prefix pass: work-groups sharing each row tile's keys
     int32_t suffix_blocks = 0;  // table entries after the prefix
     DecodeShape suffix;         // the suffix's partition shape (num_parts 0 if no entries)
-    size_t pre_ml_offset = 0;   // prefix partials: acc at 0, (m, l) here
+    size_t pre_ml_offset = 0;   // prefix partials: int16 acc at 0, (m, l, scale, 0) here
     size_t suffix_offset = 0;   // suffix partials (acc, then (m, l)) from here
     size_t total = 0;           // workspace bytes
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// bytes of the prefix pass's partial results: int16 accumulators, then (m, l, scale, 0)
+size_t dense_partial_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim, int splits,
+                           size_t* ml_offset) {
+    const size_t parts = static_cast<size_t>(batch) * num_q_heads * splits;
+    const size_t acc = align256(parts * head_dim * sizeof(int16_t));
+    if (ml_offset) *ml_offset = acc;
+    return acc + parts * 4 * sizeof(float);
+}
 
 kv_status_t plan_cascade(const kv_pool_t* pool, int32_t batch, int32_t num_q_heads,
                          int32_t max_blocks, int32_t prefix_blocks, int32_t partition_size,
@@ -466,7 +475,7 @@ kv_status_t plan_cascade(const kv_pool_t* pool, int32_t batch, int32_t num_q_hea
     if (e && atoi(e) >= 1) splits = std::min(atoi(e), kMaxCascadeSplits);
     cp->splits = static_cast<int>(splits);
     if (wgs * cp->splits > INT32_MAX) return KV_ERR_INVALID_ARG;
-    const size_t pre = prefill_partial_bytes(batch, num_q_heads, d.head_dim, cp->splits, &cp->pre_ml_offset);
+    const size_t pre = dense_partial_bytes(batch, num_q_heads, d.head_dim, cp->splits, &cp->pre_ml_offset);
     // suffix pass: the decode's shape over the entries after the prefix; its partial
     // results are kept even for a single partition
     cp->suffix_blocks = max_blocks - prefix_blocks;
@@ -581,8 +590,9 @@ kv_status_t shared_prefix_impl(const kv_pool_t* pool, int32_t layer, void* out, 
     }
 
     // 3. prefix and suffix partial results combined per (sequence, query head)
-    return pkv::launch_cascade_reduce(io_dtype(d), d.head_dim, r, pa.ws_acc, pa.ws_ml, cp.splits,
-                                      stream) == hipSuccess
+    return pkv::launch_cascade_reduce(io_dtype(d), d.head_dim, r,
+                                      reinterpret_cast<const int16_t*>(pa.ws_acc), pa.ws_ml,
+                                      cp.splits, stream) == hipSuccess
                ? KV_OK
                : KV_ERR_HIP;
 }

@@ -82,10 +82,14 @@ struct PrefillArgs {
     int32_t splits;          // work-groups sharing each row tile's key range (1: none)
     int32_t num_tokens;      // (splits > 1) rows of the query: bounds the partial results
     float* ws_acc;           // (splits > 1) [num_tokens * num_q_heads][splits][D]
+                             // (dense launch: int16 [..][splits][D], see dense_len)
     float* ws_ml;            // (splits > 1) [num_tokens * num_q_heads][splits][2]: (m, l)
+                             // (dense launch: [..][splits][4]: (m, l, scale, 0))
     int32_t dense_len;       // (dense launch) keys [0, dense_len) of table row 0, shared by
                              // the num_tokens queries of a decode batch ([B][Hq][D]):
-                             // query t sees the first min(lens[t], dense_len) of them
+                             // query t sees the first min(lens[t], dense_len) of them;
+                             // each (row, split) leaves acc / scale as int16 and
+                             // (m, l, scale)
 };
 
 // A call that can touch more K/V bytes than this streams them past the last-level cache
@@ -119,11 +123,12 @@ hipError_t launch_prefill(int kv_dtype, int io_dtype, int head_dim, const Prefil
 hipError_t launch_prefill_dense(int kv_dtype, int io_dtype, int head_dim, const PrefillArgs& pa,
                                 hipStream_t stream);
 // The cascade reduce: each (sequence, query head) combines `pre_parts` partial results of
-// its shared prefix ([B * Hq][pre_parts] rows of pre_acc / pre_ml) with the partial
+// its shared prefix ([B * Hq][pre_parts] rows of pre_acc (int16) / pre_ml (m, l, scale, 0),
+// as the dense launch leaves them) with the partial
 // results the partition kernel left for its suffix (`a` as for launch_reduce, with
 // keep_partials set and len_offset the prefix length), in that order.
 hipError_t launch_cascade_reduce(int io_dtype, int head_dim, const DecodeArgs& a,
-                                 const float* pre_acc, const float* pre_ml, int pre_parts,
+                                 const int16_t* pre_acc, const float* pre_ml, int pre_parts,
                                  hipStream_t stream);
 // work-groups of a prefill launch with `waves` waves each that the GPU holds at once
 int64_t prefill_resident_groups(int kv_dtype, int io_dtype, int head_dim, int waves);

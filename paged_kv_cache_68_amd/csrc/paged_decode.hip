@@ -26,6 +26,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "partition_common.h"
 
 namespace pkv {
@@ -308,20 +310,21 @@ __global__ __launch_bounds__(256) void pa_reduce(DecodeArgs a) {
     for (int e = 0; e < PER; ++e) o[e] = S::narrow(lsum > 0.f ? A[e] / lsum : 0.f);
 }
 
-// The cascade reduce, one wave per (sequence, query head): entries 0 .. pre_parts - 1 are
-// the partial results of the batch's shared prefix (pre_ml / pre_acc rows
-// pair * pre_parts + s), the next ones the partitions of the sequence's suffix (rows
-// G apart, as in pa_reduce; as many as its length gives, possibly none).  All are
-// combined with the cross-block rule: O = sum_k w_k acc_k / sum_k w_k l_k,
+// The cascade reduce, one wave per (sequence, query head): the partial results of the
+// batch's shared prefix (pre_parts of them, rows pair * pre_parts + s: 16-bit integers
+// q with acc = q * scale, and (m, l, scale, 0)), then those of the sequence's suffix
+// partitions (fp32, rows G apart as in pa_reduce; as many as its length gives, possibly
+// none).  All are combined with the cross-block rule: O = sum_k w_k acc_k / sum_k w_k l_k,
 // w_k = 2^(m_k - max m), an entry that saw no key (m = -inf) weighing 0.  The wave's four
-// 16-lane groups take entries k = 4j + group (D / 16 elements per lane), with up to eight
-// entries' loads in flight per lane, and the groups' sums are added at the end in a fixed
-// order: the result does not depend on timing.
+// 16-lane groups take entries 4j + group (D / 16 elements per lane), up to eight entries'
+// loads in flight per lane, and the groups' sums are added at the end in a fixed order:
+// the result does not depend on timing.
 template <class S, int D>
-__global__ __launch_bounds__(256) void pa_cascade_reduce(DecodeArgs a, const float* pre_acc,
+__global__ __launch_bounds__(256) void pa_cascade_reduce(DecodeArgs a, const int16_t* pre_acc,
                                                          const float* pre_ml, int pre_parts) {
     constexpr int PER = D / 16;    // elements per lane
     constexpr int U = 8;           // entries per lane and round
+    using Raw = typename std::conditional<PER == 8, uint4, uint2>::type;   // PER int16
     const int lane = threadIdx.x & 63;
     const int grp = lane >> 4;
     const int l16 = lane & 15;
@@ -332,48 +335,74 @@ __global__ __launch_bounds__(256) void pa_cascade_reduce(DecodeArgs a, const flo
     const int L = clamped_length(a, b);
     const int ntiles = (L + a.tile_tokens - 1) / a.tile_tokens;
     const int nsuf = (ntiles + a.part_blocks - 1) / a.part_blocks;
-    const int n = pre_parts + nsuf;
 
     const int G = a.num_q_heads / a.num_kv_heads;
     const size_t srow0 = part_row(a, b, h / G, 0, G) + h % G;
     const size_t prow0 = static_cast<size_t>(pair) * pre_parts;
-    auto row_of = [&](int k) -> size_t {      // the entry's row of (m, l) and accumulators
-        return k < pre_parts ? prow0 + k : srow0 + static_cast<size_t>(k - pre_parts) * G;
-    };
-    auto ml_of = [&](int k) -> float2 {
-        return reinterpret_cast<const float2*>(k < pre_parts ? pre_ml : a.ws_ml)[row_of(k)];
-    };
+    const float4* pml = reinterpret_cast<const float4*>(pre_ml) + prow0;
+    const float2* sml = reinterpret_cast<const float2*>(a.ws_ml) + srow0;
 
     float M = -INFINITY;
-    for (int k = lane; k < n; k += 64) M = fmaxf(M, ml_of(k).x);
+    for (int k = lane; k < pre_parts; k += 64) M = fmaxf(M, pml[k].x);
+    for (int k = lane; k < nsuf; k += 64) M = fmaxf(M, sml[static_cast<size_t>(k) * G].x);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    auto weight = [&](float m) { return (M == -INFINITY || m == -INFINITY) ? 0.f : fast_exp2(m - M); };
 
     float A[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) A[e] = 0.f;
     float lsum = 0.f;
-    for (int k0 = grp; k0 < n; k0 += 4 * U) {
+    // the prefix's entries
+    for (int k0 = grp; k0 < pre_parts; k0 += 4 * U) {
+        float4 v[U];
+        Raw x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + 4 * u;
+            v[u] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+            x[u] = Raw{};
+            if (k < pre_parts) {
+                v[u] = pml[k];
+                x[u] = *reinterpret_cast<const Raw*>(pre_acc + (prow0 + k) * D + PER * l16);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = weight(v[u].x);
+            lsum += w * v[u].y;
+            const float ws = w * v[u].z;
+            const uint32_t* q = reinterpret_cast<const uint32_t*>(&x[u]);
+#pragma unroll
+            for (int e = 0; e < PER; e += 2) {
+                const int32_t lo = static_cast<int32_t>(q[e / 2] << 16) >> 16;
+                const int32_t hi = static_cast<int32_t>(q[e / 2]) >> 16;
+                A[e] = fmaf(ws, static_cast<float>(lo), A[e]);
+                A[e + 1] = fmaf(ws, static_cast<float>(hi), A[e + 1]);
+            }
+        }
+    }
+    // the suffix's partitions
+    for (int k0 = grp; k0 < nsuf; k0 += 4 * U) {
         float2 v[U];
         float4 x[U][PER / 4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = k0 + 4 * u;
             v[u] = make_float2(-INFINITY, 0.f);
-            if (k < n) {
-                v[u] = ml_of(k);
+#pragma unroll
+            for (int q = 0; q < PER / 4; ++q) x[u][q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (k < nsuf) {
+                v[u] = sml[static_cast<size_t>(k) * G];
                 const float4* src = reinterpret_cast<const float4*>(
-                    (k < pre_parts ? pre_acc : a.ws_acc) + row_of(k) * D + PER * l16);
+                    a.ws_acc + (srow0 + static_cast<size_t>(k) * G) * D + PER * l16);
 #pragma unroll
                 for (int q = 0; q < PER / 4; ++q) x[u][q] = src[q];
-            } else {
-#pragma unroll
-                for (int q = 0; q < PER / 4; ++q) x[u][q] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float w = (M == -INFINITY || v[u].x == -INFINITY) ? 0.f : fast_exp2(v[u].x - M);
+            const float w = weight(v[u].x);
             lsum += w * v[u].y;
 #pragma unroll
             for (int q = 0; q < PER / 4; ++q) {
@@ -468,7 +497,7 @@ hipError_t launch_part_g(int group, const DecodeArgs& a, hipStream_t stream) {
 }
 
 template <class S, int D>
-hipError_t launch_cascade_t(const DecodeArgs& a, const float* pre_acc, const float* pre_ml,
+hipError_t launch_cascade_t(const DecodeArgs& a, const int16_t* pre_acc, const float* pre_ml,
                             int pre_parts, hipStream_t stream) {
     const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
     if (pairs <= 0) return hipSuccess;
@@ -545,7 +574,7 @@ hipError_t launch_reduce(int io_dtype, int head_dim, const DecodeArgs& a, hipStr
 }
 
 hipError_t launch_cascade_reduce(int io_dtype, int head_dim, const DecodeArgs& a,
-                                 const float* pre_acc, const float* pre_ml, int pre_parts,
+                                 const int16_t* pre_acc, const float* pre_ml, int pre_parts,
                                  hipStream_t stream) {
     if (io_dtype == KV_DTYPE_F16) {
         if (head_dim == 64) return launch_cascade_t<F16, 64>(a, pre_acc, pre_ml, pre_parts, stream);

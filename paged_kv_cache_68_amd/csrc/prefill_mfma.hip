@@ -425,7 +425,43 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         if (j + 1 < j_hi) stage_store((j + 1) & 1);      // its last readers passed the barrier
     }
 
-    if constexpr (SPLIT) {
+    if constexpr (DENSE) {
+        // partial results of the prefix, in half the bytes: each row's accumulator as 16-bit
+        // integers q = round(acc * 2^(14 - x)), where 2^x bounds the row's largest magnitude
+        // (|q| < 2^14, every element within 2^-15 of that bound), and (m, l, 2^(x - 14)).
+        // Lane (n, c) holds elements 16 e + 4 c + rr of row n.
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
+            float mx = 0.f;
+#pragma unroll
+            for (int e = 0; e < DB; ++e)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, fabsf(acc[cb][e][rr]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));      // the row's four lanes
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            int x = 0;
+            (void)frexpf(mx, &x);                    // mx < 2^x (x = 0 for an all-zero row)
+            const float to_q = ldexpf(1.f, 14 - x);
+            const int r = row_base + cb * 16 + n;
+            if (r >= rows) continue;
+            const int t = tok[cb];
+            const int g = r - t * G;
+            const int64_t part = (static_cast<int64_t>(t) * a.num_q_heads + kvh * G + g) * pa.splits + split;
+            int16_t* dst = reinterpret_cast<int16_t*>(pa.ws_acc) + part * D + 4 * c;
+#pragma unroll
+            for (int e = 0; e < DB; ++e) {
+                const uint32_t lo = (static_cast<uint32_t>(__float2int_rn(acc[cb][e][0] * to_q)) & 0xffffu) |
+                                    (static_cast<uint32_t>(__float2int_rn(acc[cb][e][1] * to_q)) << 16);
+                const uint32_t hi = (static_cast<uint32_t>(__float2int_rn(acc[cb][e][2] * to_q)) & 0xffffu) |
+                                    (static_cast<uint32_t>(__float2int_rn(acc[cb][e][3] * to_q)) << 16);
+                *reinterpret_cast<uint2*>(dst + 16 * e) = make_uint2(lo, hi);
+            }
+            if (c == 0)
+                *reinterpret_cast<float4*>(pa.ws_ml + 4 * part) =
+                    make_float4(m[cb], lacc[cb][0], ldexpf(1.f, x - 14), 0.f);
+        }
+        return;
+    } else if constexpr (SPLIT) {
         // partial results: lane (n, c) holds elements 16 e + 4 c + rr of row n; (m, l) as
         // the running maximum (base-2 units, -inf if no key was seen) and weight sum
 #pragma unroll
