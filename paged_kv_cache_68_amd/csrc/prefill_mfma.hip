@@ -136,6 +136,89 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const float sl2 = fmaxf(fabsf(a.scale_log2), 1e-30f);
     const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
+    // ---- staging: global (through the table) -> registers -> LDS.  Thread chunk u is
+    // key (tid + u THREADS) / CPR of the stage, 8 values at part (tid + u THREADS) % CPR.
+    const int* table = a.tables + static_cast<size_t>(b) * a.table_stride;
+    const int bshift = __builtin_ctz(a.block_size);
+    const uint32_t block_bytes = static_cast<uint32_t>(a.block_size * a.row_bytes);
+    Raw rk[PER_T], rv[PER_T];
+    int tb[PER_T];                               // table entries of the stage being fetched
+    const __amdgpu_buffer_rsrc_t rsrc_k = make_rsrc(a.k, pa.buffer_bytes);
+    const __amdgpu_buffer_rsrc_t rsrc_v = make_rsrc(a.v, pa.buffer_bytes);
+
+    auto fetch_table = [&](int j) {
+#pragma unroll
+        for (int u = 0; u < PER_T; ++u) {
+            const int q = tid + u * THREADS;
+            const int pos = j * KT + q / CPR;
+            tb[u] = (q < CHUNKS && pos < L) ? table[pos >> bshift] : -1;
+        }
+    };
+    auto fetch = [&](int j) {
+#pragma unroll
+        for (int u = 0; u < PER_T; ++u) {
+            const int q = tid + u * THREADS;
+            const int pos = j * KT + q / CPR;
+            const int blk = tb[u];
+            const bool ok = q < CHUNKS && static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
+            const uint32_t inner = static_cast<uint32_t>((pos & (a.block_size - 1)) * a.row_bytes +
+                                                         (kvh * D + (q % CPR) * 8) * EB);
+            if (pa.buffer_bytes > 0) {
+                // an entry outside the pool (or past the length) reads past the buffer's
+                // end, which returns zeros
+                const uint32_t off = ok ? static_cast<uint32_t>(blk) * block_bytes + inner : 0x80000000u;
+                if constexpr (KV8) {
+                    rk[u] = load8(rsrc_k, static_cast<int>(off));
+                    rv[u] = load8(rsrc_v, static_cast<int>(off));
+                } else {
+                    rk[u] = load16(rsrc_k, static_cast<int>(off));
+                    rv[u] = load16(rsrc_v, static_cast<int>(off));
+                }
+            } else {
+                // an entry outside the pool (or past the length) reads block 0 and stages zeros
+                const size_t off = static_cast<size_t>(ok ? static_cast<uint32_t>(blk) : 0u) * block_bytes + inner;
+                const Raw xk = *reinterpret_cast<const Raw*>(a.k + off);
+                const Raw xv = *reinterpret_cast<const Raw*>(a.v + off);
+                rk[u] = ok ? xk : Raw{};
+                rv[u] = ok ? xv : Raw{};
+            }
+        }
+    };
+    auto widen = [&](const Raw& x) -> uint4 {
+        if constexpr (KV8) {
+            const uint2 lo = fp8x4_to<S>(x.x);
+            const uint2 hi = fp8x4_to<S>(x.y);
+            return make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+            return x;
+        }
+    };
+    auto stage_store = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < PER_T; ++u) {
+            const int q = tid + u * THREADS;
+            if (q < CHUNKS) {
+                *reinterpret_cast<uint4*>(&lds_k[buf][(q / CPR) * ROWB_K + (q % CPR) * 16]) = widen(rk[u]);
+                *reinterpret_cast<uint4*>(&lds_v[buf][(q / CPR) * ROWB_V + (q % CPR) * 16]) = widen(rv[u]);
+            }
+        }
+    };
+
+    // dense: the key range is known from the arguments alone, so the first stage's table
+    // entries and rows are requested before anything else (ahead of the queries and the
+    // lengths, which only the masks need)
+    int j_lo = 0, j_hi = 0;
+    if constexpr (DENSE) {
+        const int ns = (L + KT - 1) / KT;
+        const int per = (ns + pa.splits - 1) / pa.splits;
+        j_lo = min(ns, split * per);
+        j_hi = min(ns, j_lo + per);
+        if (j_lo < j_hi) {
+            fetch_table(j_lo);
+            fetch(j_lo);
+        }
+    }
+
     // this lane's column in each block: row -> (token, head), position, Q^T operand
     int qpos[NC];
     int tok[NC];
@@ -204,74 +287,6 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
         for (int e = 0; e < DB; ++e) acc[cb][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-
-    // ---- staging: global (through the table) -> registers -> LDS.  Thread chunk u is
-    // key (tid + u THREADS) / CPR of the stage, 8 values at part (tid + u THREADS) % CPR.
-    const int* table = a.tables + static_cast<size_t>(b) * a.table_stride;
-    const int bshift = __builtin_ctz(a.block_size);
-    const uint32_t block_bytes = static_cast<uint32_t>(a.block_size * a.row_bytes);
-    Raw rk[PER_T], rv[PER_T];
-    int tb[PER_T];                               // table entries of the stage being fetched
-    const __amdgpu_buffer_rsrc_t rsrc_k = make_rsrc(a.k, pa.buffer_bytes);
-    const __amdgpu_buffer_rsrc_t rsrc_v = make_rsrc(a.v, pa.buffer_bytes);
-
-    auto fetch_table = [&](int j) {
-#pragma unroll
-        for (int u = 0; u < PER_T; ++u) {
-            const int q = tid + u * THREADS;
-            const int pos = j * KT + q / CPR;
-            tb[u] = (q < CHUNKS && pos < L) ? table[pos >> bshift] : -1;
-        }
-    };
-    auto fetch = [&](int j) {
-#pragma unroll
-        for (int u = 0; u < PER_T; ++u) {
-            const int q = tid + u * THREADS;
-            const int pos = j * KT + q / CPR;
-            const int blk = tb[u];
-            const bool ok = q < CHUNKS && static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
-            const uint32_t inner = static_cast<uint32_t>((pos & (a.block_size - 1)) * a.row_bytes +
-                                                         (kvh * D + (q % CPR) * 8) * EB);
-            if (pa.buffer_bytes > 0) {
-                // an entry outside the pool (or past the length) reads past the buffer's
-                // end, which returns zeros
-                const uint32_t off = ok ? static_cast<uint32_t>(blk) * block_bytes + inner : 0x80000000u;
-                if constexpr (KV8) {
-                    rk[u] = load8(rsrc_k, static_cast<int>(off));
-                    rv[u] = load8(rsrc_v, static_cast<int>(off));
-                } else {
-                    rk[u] = load16(rsrc_k, static_cast<int>(off));
-                    rv[u] = load16(rsrc_v, static_cast<int>(off));
-                }
-            } else {
-                // an entry outside the pool (or past the length) reads block 0 and stages zeros
-                const size_t off = static_cast<size_t>(ok ? static_cast<uint32_t>(blk) : 0u) * block_bytes + inner;
-                const Raw xk = *reinterpret_cast<const Raw*>(a.k + off);
-                const Raw xv = *reinterpret_cast<const Raw*>(a.v + off);
-                rk[u] = ok ? xk : Raw{};
-                rv[u] = ok ? xv : Raw{};
-            }
-        }
-    };
-    auto widen = [&](const Raw& x) -> uint4 {
-        if constexpr (KV8) {
-            const uint2 lo = fp8x4_to<S>(x.x);
-            const uint2 hi = fp8x4_to<S>(x.y);
-            return make_uint4(lo.x, lo.y, hi.x, hi.y);
-        } else {
-            return x;
-        }
-    };
-    auto stage_store = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < PER_T; ++u) {
-            const int q = tid + u * THREADS;
-            if (q < CHUNKS) {
-                *reinterpret_cast<uint4*>(&lds_k[buf][(q / CPR) * ROWB_K + (q % CPR) * 16]) = widen(rk[u]);
-                *reinterpret_cast<uint4*>(&lds_v[buf][(q / CPR) * ROWB_V + (q % CPR) * 16]) = widen(rv[u]);
-            }
-        }
-    };
 
     // ---- one run of 32 keys for this wave.  Both column blocks always run: a block
     // whose rows all precede the run gets only masked scores, zero weights and no
@@ -402,16 +417,20 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     };
 
     // ---- this work-group's stages [j_lo, j_hi): all of them, or its split's equal run
-    int j_lo = 0, j_hi = nstages;
-    if constexpr (SPLIT) {
-        const int per = (nstages + pa.splits - 1) / pa.splits;
-        j_lo = min(nstages, split * per);
-        j_hi = min(nstages, j_lo + per);
+    if constexpr (!DENSE) {
+        j_hi = nstages;
+        if constexpr (SPLIT) {
+            const int per = (nstages + pa.splits - 1) / pa.splits;
+            j_lo = min(nstages, split * per);
+            j_hi = min(nstages, j_lo + per);
+        }
     }
     // ---- pipeline: fetch stage j + 1 while computing stage j
     if (j_lo < j_hi) {
-        fetch_table(j_lo);
-        fetch(j_lo);
+        if constexpr (!DENSE) {
+            fetch_table(j_lo);
+            fetch(j_lo);
+        }
         stage_store(j_lo & 1);
         if (j_lo + 1 < j_hi) fetch_table(j_lo + 1);
     }
