@@ -128,6 +128,8 @@ SMALL = [
     (16, 2, 128, "bf16", 16, 1000, 2000, 4, "", "64"),         # more splits than stages
     (28, 4, 64, "bf16", 16, 2407, 9, 16, "", None),            # a 2,407-token prompt, 16 requests
     (6, 2, 128, "f16", 16, 16 * 3, 1, 33, "fp8", None),        # a full-block prefix, 1-token suffixes
+    (16, 4, 64, "bf16", 32, 200, 100, 5, "fp8", None),         # FP8 with head size 64, 32-token blocks
+    (8, 1, 64, "f16", 8, 77, 600, 7, "", "2"),                  # one KV head, G = 8, 8-token blocks
 ]
 
 
