@@ -337,27 +337,48 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                 sc[cb][st] = x;
             }
         uint4 pop[NC], pol[NC];                  // weights: rounded parts, remainders
+        float sv[NC][8];
 #pragma unroll
-        for (int cb = 0; cb < NC; ++cb) {
-            float sv[8];
+        for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sv[4 * st + r] = sc[cb][st][r];
-            if (first[cb] < tpos + 31) {                     // wave-uniform: some key after a row
+                for (int r = 0; r < 4; ++r) sv[cb][4 * st + r] = sc[cb][st][r];
+        // The mask and the rare rescale are one branch each for both column blocks, so that
+        // the weights and value products of both blocks form one stretch of code for the
+        // scheduler (8% faster on the chunked-prefill step than a branch per block).
+        // Causal mask, for every block when some block has a key after one of its rows
+        // (a block whose rows all follow the run's last key is left unchanged by it).
+        bool need_mask = false;
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) need_mask = need_mask || first[cb] < tpos + 31;
+        if (need_mask) {                                     // wave-uniform
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const int key = (k < 4) ? 4 * c + k : 16 + 4 * c + (k - 4);
-                    if (tpos + key > qpos[cb]) sv[k] = -INFINITY;
+                    if (tpos + key > qpos[cb]) sv[cb][k] = -INFINITY;
                 }
-            }
-            // this lane's maximum; the column's (over the four c-lanes) is needed only when
-            // some score passes the running maximum by more than 2^8
-            float mb = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(sv[0], sv[1]), sv[2]),
-                                       __builtin_fmaxf(__builtin_fmaxf(sv[3], sv[4]), sv[5]));
-            mb = __builtin_fmaxf(mb, __builtin_fmaxf(sv[6], sv[7]));
-            if (__any(mb * sl2 > m[cb] + 8.f)) {
-                const float mbs = max_across_c(mb) * sl2;    // -inf stays -inf
+        }
+        // this lane's maxima; a column's (over the four c-lanes) is needed only when some
+        // score passes the running maximum by more than 2^8
+        float mb[NC];
+        bool grow[NC];
+        bool any_grow = false;
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
+            float x = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(sv[cb][0], sv[cb][1]), sv[cb][2]),
+                                      __builtin_fmaxf(__builtin_fmaxf(sv[cb][3], sv[cb][4]), sv[cb][5]));
+            mb[cb] = __builtin_fmaxf(x, __builtin_fmaxf(sv[cb][6], sv[cb][7]));
+            grow[cb] = __any(mb[cb] * sl2 > m[cb] + 8.f);
+            any_grow = any_grow || grow[cb];
+        }
+        if (any_grow) {                                      // wave-uniform, rare
+#pragma unroll
+            for (int cb = 0; cb < NC; ++cb) {
+                if (!grow[cb]) continue;
+                const float mbs = max_across_c(mb[cb]) * sl2;    // -inf stays -inf
                 const float mn = __builtin_fmaxf(m[cb], mbs);
                 const float mu = (mn == -INFINITY) ? 0.f : mn;
                 const float alpha = fast_exp2(m[cb] - mu);   // 0 while nothing was seen
@@ -366,10 +387,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                 lacc[cb] *= alpha;
                 m[cb] = mn;
             }
+        }
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
             const float mu = (m[cb] == -INFINITY) ? 0.f : m[cb];
             float pr[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) pr[k] = fast_exp2(fmaf(sv[k], sl2, -mu));
+            for (int k = 0; k < 8; ++k) pr[k] = fast_exp2(fmaf(sv[cb][k], sl2, -mu));
             // bf16 weights: a rounded part plus its rounded remainder, both through the
             // matrix cores, so the value product sees about 16 significand bits of every
             // weight instead of bf16's 8 (with 8 bits a short row's output can miss the
