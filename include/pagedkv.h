@@ -305,9 +305,13 @@ kv_status_t paged_attention_reduce(const kv_pool_t* pool, int32_t layer, void* o
  * The shared keys are read once for the whole batch instead of once per sequence: the
  * batch's query rows of each KV head form one dense tile against the prefix's keys
  * (matrix cores; the prefix is split over work-groups), each sequence's remaining blocks
- * go through the decode kernels, and a last kernel combines the two sets of partial
- * results (m, l, O) per (sequence, query head) with the cross-block rule ("PagedAttention
- * and Virtual Memory Management", section 4), deterministically.
+ * go through the decode kernels, and the two sets of partial results (m, l, O) are
+ * combined per (sequence, query head) with the cross-block rule ("PagedAttention and
+ * Virtual Memory Management", section 4), deterministically.  When the table entries
+ * after the prefix hold at most max(partition_size, 1,024) tokens, each sequence's
+ * remaining blocks are one partition and the decode kernel combines and writes the
+ * output itself (two launches); otherwise a third kernel combines the partial results
+ * (and so always with PAGEDKV_CASCADE_FUSE=0).
  * Preconditions (checked in checked mode, PAGEDKV_CHECK=1; otherwise the output is
  * undefined if they fail, and nothing outside the pool is read): a row's entries among
  * the first prefix_blocks that its length uses equal row 0's; with new tokens, every
@@ -345,9 +349,10 @@ int32_t kv_shared_prefix_blocks(const int32_t* tables, const int32_t* lengths, i
 /* Workspace bytes of paged_attention_decode_shared_prefix for this shape on the current
  * device (the prefix's split follows the device's size): the prefix's partial results
  * (m, l and a scale in fp32, O as 16-bit integers times that scale, for every (sequence,
- * query head, split)), then the suffixes' partial
- * results (as paged_attention_workspace_bytes, for the entries after the prefix, with one
- * partition counted too).  With prefix_blocks == 0, paged_attention_workspace_bytes.
+ * query head, split)), then, when the combine takes a kernel of its own, the suffixes'
+ * partial results (as paged_attention_workspace_bytes, for the entries after the prefix,
+ * with one partition counted too).  With prefix_blocks == 0,
+ * paged_attention_workspace_bytes.
  * SIZE_MAX for invalid arguments (null or host pool, sizes out of range). */
 size_t paged_attention_shared_prefix_workspace_bytes(const kv_pool_t* pool, int32_t batch,
                                                      int32_t num_q_heads, int32_t max_blocks_per_seq,

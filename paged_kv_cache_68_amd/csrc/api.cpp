@@ -141,6 +141,9 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     a.table_stride = max_blocks;
     a.len_offset = 0;
     a.keep_partials = 0;
+    a.pre_acc = nullptr;
+    a.pre_ml = nullptr;
+    a.pre_parts = 0;
     a.num_blocks = d.num_blocks;
     a.block_size = d.block_size;
     a.tile_tokens = d.block_size < pkv::kTile ? d.block_size : pkv::kTile;
@@ -423,7 +426,13 @@ struct CascadePlan {
     size_t pre_ml_offset = 0;   // prefix partials: int16 acc at 0, (m, l, scale, 0) here
     size_t suffix_offset = 0;   // suffix partials (acc, then (m, l)) from here
     size_t total = 0;           // workspace bytes
+    bool fused = false;         // every suffix in one partition: the suffix kernel combines
+                                // the prefix partials and writes the output (no reduce)
 };
+
+// Suffixes up to this many tokens (the table width after the prefix) are walked as one
+// partition, so that the suffix kernel can write the final output itself.
+constexpr int32_t kFusedSuffixTokens = 1024;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -487,6 +496,17 @@ kv_status_t plan_cascade(const kv_pool_t* pool, int32_t batch, int32_t num_q_hea
         const int32_t tile = d.block_size < pkv::kTile ? d.block_size : pkv::kTile;
         if (partition_size > pkv::kMaxPartition || partition_size > pkv::kMaxTilesPerWave * tile)
             return KV_ERR_UNSUPPORTED;
+        // one partition per suffix when the table width after the prefix allows it
+        // (PAGEDKV_CASCADE_FUSE=0: partial results and the cascade reduce instead)
+        const int64_t width = static_cast<int64_t>(cp->suffix_blocks) * d.block_size;
+        const char* ef = getenv("PAGEDKV_CASCADE_FUSE");
+        if (!(ef && ef[0] == '0') && width <= std::max<int64_t>(partition_size, kFusedSuffixTokens)) {
+            cp->fused = true;
+            cp->suffix.part_blocks = static_cast<int32_t>(std::max<int64_t>(width, partition_size) / tile);
+            cp->suffix.num_parts = 1;
+            cp->suffix.ws_needed = 0;
+            return KV_OK;
+        }
         cp->suffix.part_blocks = partition_size / tile;
         cp->suffix.num_parts = static_cast<int32_t>(
             ceil_div(static_cast<int64_t>(cp->suffix_blocks) * d.block_size, partition_size));
@@ -569,11 +589,23 @@ kv_status_t shared_prefix_impl(const kv_pool_t* pool, int32_t layer, void* out, 
         return KV_ERR_HIP;
 
     // 2. the suffixes: the decode over the entries after the prefix, partial results kept
+    //    (fused: one partition per suffix, combined with the prefix's partials and written
+    //    as the output by the suffix kernel itself; a sequence without a suffix too)
     pkv::DecodeArgs a = make_args(pool, layer, out, query, block_tables + prefix_blocks,
                                   cp.suffix_blocks, context_lens, batch, num_q_heads, scale,
                                   ws + cp.suffix_offset, cp.suffix);
     a.table_stride = max_blocks;
     a.len_offset = prefix_len;
+    if (cp.fused) {
+        a.pre_acc = reinterpret_cast<const int16_t*>(pa.ws_acc);
+        a.pre_ml = pa.ws_ml;
+        a.pre_parts = cp.splits;
+        a.new_k = static_cast<const uint16_t*>(new_key);
+        a.new_v = static_cast<const uint16_t*>(new_value);
+        return pkv::launch_partitions(d.dtype, io_dtype(d), d.head_dim, cp.group, a, stream) == hipSuccess
+                   ? KV_OK
+                   : KV_ERR_HIP;
+    }
     a.keep_partials = 1;
     pkv::DecodeArgs r = a;
     if (cp.suffix_blocks > 0) {

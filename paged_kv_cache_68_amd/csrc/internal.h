@@ -54,6 +54,10 @@ struct DecodeArgs {
     int32_t keep_partials;   // 1: every sequence's partitions go to the workspace as
                              // partial results, even a single one (no final output is
                              // written; a sequence without tokens writes nothing)
+    const int16_t* pre_acc;  // pre_parts > 0: a shared prefix's partial results, combined
+    const float* pre_ml;     // with each sequence's (single-partition) result before it is
+    int32_t pre_parts;       // written: [B][Hq][pre_parts][D] int16 accumulators and
+                             // [B][Hq][pre_parts] (m, l, scale, 0)
     int32_t num_blocks;      // blocks in the pool
     int32_t block_size;      // tokens per block: 8, 16, 32 or 64
     int32_t tile_tokens;     // tokens per tile the kernels walk: min(block_size, 16)

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void pa_partition_valu(DecodeArgs a, int n_ite
     if (!SPLIT && item >= n_items) return;
     const Item it = decode_item(a, item, SPLIT ? 1 : per_item);
     if (it.L == 0) {
-        store_empty<D>(a, it, G, SPLIT ? threadIdx.x : lane, SPLIT ? blockDim.x : 64);
+        store_empty<S, D>(a, it, G, SPLIT ? threadIdx.x : lane, SPLIT ? blockDim.x : 64);
         return;
     }
     if (it.p >= it.nparts) return;

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
                         per_item, wave / heads, ppw);
         // both exits below are the same for the whole work-group (same sequence, chunk)
         if (it.L == 0) {
-            if (it.p == 0) store_empty<D>(a, it, G, lane, 64);
+            if (it.p == 0) store_empty<S, D>(a, it, G, lane, 64);
             return;
         }
         if (chunk_id * per_item >= it.nparts) return;
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
         if (MODE == kItem && item >= n_items) return;
         it = decode_item(a, item, SPLIT ? 1 : per_item);
         if (it.L == 0) {
-            store_empty<D>(a, it, G, SPLIT ? threadIdx.x : lane, SPLIT ? blockDim.x : 64);
+            store_empty<S, D>(a, it, G, SPLIT ? threadIdx.x : lane, SPLIT ? blockDim.x : 64);
             return;
         }
         if (it.p >= it.nparts) return;

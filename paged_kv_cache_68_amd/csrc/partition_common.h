@@ -183,6 +183,90 @@ __device__ __forceinline__ size_t part_row(const DecodeArgs& a, int b, int kvh, 
     return ((static_cast<size_t>(b) * a.num_kv_heads + kvh) * a.num_parts + p) * G;
 }
 
+// A shared prefix handled elsewhere (pre_parts > 0) leaves, per query row (b * Hq + h),
+// pre_parts partial results: int16 accumulators with a per-result scale, and (m, l).
+// These fold results [s0, s1) of row `row`, elements [dd0, dd0 + 8), into the running
+// state (Mt, L, acc) with the cross-block rule of "PagedAttention and Virtual Memory
+// Management" section 4, in ascending order, eight at a time (their loads all in flight).
+template <int D>
+__device__ __forceinline__ void fold_prefix8(const DecodeArgs& a, size_t row, int dd0, int s0, int s1,
+                                             float& Mt, float& L, float (&acc)[8]) {
+    constexpr int U = 8;
+    const int np = a.pre_parts;
+    const float4* ml = reinterpret_cast<const float4*>(a.pre_ml) + row * np;
+    const int16_t* q = a.pre_acc + row * np * D + dd0;
+    for (int sb = s0; sb < s1; sb += U) {
+        float4 e[U];
+        uint4 qq[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = sb + u < s1;
+            e[u] = ok ? ml[sb + u] : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+            qq[u] = ok ? *reinterpret_cast<const uint4*>(q + static_cast<size_t>(sb + u) * D)
+                       : make_uint4(0, 0, 0, 0);
+        }
+        float cm = e[0].x;
+#pragma unroll
+        for (int u = 1; u < U; ++u) cm = fmaxf(cm, e[u].x);
+        if (cm > Mt) {                           // (Mt = -inf: nothing kept yet, so nothing scaled)
+            const float f = (Mt == -INFINITY) ? 0.f : fast_exp2(Mt - cm);
+            L *= f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] *= f;
+            Mt = cm;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = (e[u].x == -INFINITY) ? 0.f : fast_exp2(e[u].x - Mt);
+            L += w * e[u].y;
+            const float ws = w * e[u].z;
+            const uint32_t qw[4] = {qq[u].x, qq[u].y, qq[u].z, qq[u].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                acc[2 * k] += ws * static_cast<float>(static_cast<int16_t>(qw[k] & 0xffffu));
+                acc[2 * k + 1] += ws * static_cast<float>(static_cast<int16_t>(qw[k] >> 16));
+            }
+        }
+    }
+}
+
+// Two running states combined with the same rule: (Mt, L, acc) absorbs (Mq, Lq, accq).
+__device__ __forceinline__ void fold_state8(float& Mt, float& L, float (&acc)[8], float Mq, float Lq,
+                                            const float* accq) {
+    const float Mn = fmaxf(Mt, Mq);
+    const float f1 = (Mt == -INFINITY) ? 0.f : fast_exp2(Mt - Mn);
+    const float f2 = (Mq == -INFINITY) ? 0.f : fast_exp2(Mq - Mn);
+    L = f1 * L + f2 * Lq;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = f1 * acc[k] + f2 * accq[k];
+    Mt = Mn;
+}
+
+// Elements [dd0, dd0 + 8) of output row `row` from a running state.
+template <class S, int D>
+__device__ __forceinline__ void write_state8(const DecodeArgs& a, size_t row, int dd0, float L,
+                                             const float (&acc)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        w[k] = static_cast<uint32_t>(S::narrow(L > 0.f ? acc[2 * k] / L : 0.f)) |
+               (static_cast<uint32_t>(S::narrow(L > 0.f ? acc[2 * k + 1] / L : 0.f)) << 16);
+    *reinterpret_cast<uint4*>(a.out + row * D + dd0) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// The final output of elements [dd0, dd0 + 8) of row `row`: this sequence's own result
+// (M, lsum, A) first, then every prefix result in ascending order.
+template <class S, int D>
+__device__ __forceinline__ void cascade_store8(const DecodeArgs& a, size_t row, int dd0, float M,
+                                               float lsum, const float (&A)[8]) {
+    float Mt = M, L = lsum;
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = A[k];
+    fold_prefix8<D>(a, row, dd0, 0, a.pre_parts, Mt, L, acc);
+    write_state8<S, D>(a, row, dd0, L, acc);
+}
+
 // One wave writes the result of partition p of its item from a staging area in LDS
 // (st_acc[G][D] accumulators, st_ml[G][2] running max / sum): the final output if the
 // sequence has a single partition, else the fp32 partials.  All 64 lanes take part, each
@@ -194,7 +278,16 @@ __device__ __forceinline__ void store_partition(const DecodeArgs& a, const Item&
                                                 const float* st_acc, const float* st_ml, int lane,
                                                 bool whole = false) {
     const int n = G * D;
-    if (!a.keep_partials && (it.nparts == 1 || whole)) {
+    if (a.pre_parts > 0) {           // (a single partition: the whole suffix)
+        const size_t row0 = static_cast<size_t>(it.b) * a.num_q_heads + it.kvh * G;
+        for (int i = lane * 8; i < n; i += 512) {
+            const int g = i / D;
+            const float4 x0 = *reinterpret_cast<const float4*>(st_acc + i);
+            const float4 x1 = *reinterpret_cast<const float4*>(st_acc + i + 4);
+            const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            cascade_store8<S, D>(a, row0 + g, i - g * D, st_ml[2 * g], st_ml[2 * g + 1], v);
+        }
+    } else if (!a.keep_partials && (it.nparts == 1 || whole)) {
         uint16_t* o = a.out + (static_cast<size_t>(it.b) * a.num_q_heads + it.kvh * G) * D;
         for (int i = lane * 8; i < n; i += 512) {
             const float lg = st_ml[2 * (i / D) + 1];
@@ -224,9 +317,67 @@ __device__ __forceinline__ void store_partition(const DecodeArgs& a, const Item&
 // partition, else the fp32 partials (m, l, acc) for the reduce kernel.
 template <class S, int D>
 __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const Item& it, int G,
-                                                      const float* sm_ml, const float* sm_acc) {
+                                                      float* sm_ml, float* sm_acc) {
     constexpr int W = kWavesPerGroup;
     const int h0 = it.kvh * G;
+    if (a.pre_parts > 0) {
+        // (a single partition: the whole suffix) E groups of 8 output elements; Q threads
+        // per group each fold an equal, consecutive share of the prefix results (one batch
+        // of loads each for up to 32 of them); the first thread of each group then takes
+        // the suffix's own result, its share and the others' shares in ascending order
+        // (exchanged through the accumulators' LDS area once every wave's has been read).
+        // Every thread of the work-group takes part: the two barriers are uniform.
+        const int E = G * D / 8;
+        const int Q = min(4, max(1, static_cast<int>(blockDim.x) / E));
+        const int t = threadIdx.x;
+        const int e = t % E;
+        const int qi = t / E;
+        const bool active = qi < Q;
+        const int g = (e * 8) / D;
+        const int dd0 = e * 8 - g * D;
+        const size_t row = static_cast<size_t>(it.b) * a.num_q_heads + h0 + g;
+        const int per = (a.pre_parts + Q - 1) / Q;
+        float Mq = -INFINITY, Lq = 0.f;
+        float accq[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) accq[k] = 0.f;
+        if (active) fold_prefix8<D>(a, row, dd0, min(a.pre_parts, qi * per), min(a.pre_parts, (qi + 1) * per), Mq, Lq, accq);
+        float M = -INFINITY, lsum = 0.f;
+        float A[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) A[k] = 0.f;
+        if (active && qi == 0) {
+            M = sm_ml[g * 2];
+#pragma unroll
+            for (int w = 1; w < W; ++w) M = fmaxf(M, sm_ml[(w * G + g) * 2]);
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const float f = (M == -INFINITY) ? 0.f : fast_exp2(sm_ml[(w * G + g) * 2] - M);
+                lsum += f * sm_ml[(w * G + g) * 2 + 1];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) A[k] += f * sm_acc[(w * G + g) * D + dd0 + k];
+            }
+        }
+        __syncthreads();                         // every wave's accumulators have been read
+        float* xs = sm_acc;                      // shares 1 .. Q-1: [Q-1][E][10] floats
+        if (active && qi > 0) {
+            float* x = xs + ((qi - 1) * E + e) * 10;
+            x[0] = Mq;
+            x[1] = Lq;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[2 + k] = accq[k];
+        }
+        __syncthreads();
+        if (active && qi == 0) {
+            fold_state8(M, lsum, A, Mq, Lq, accq);
+            for (int j = 1; j < Q; ++j) {
+                const float* x = xs + ((j - 1) * E + e) * 10;
+                fold_state8(M, lsum, A, x[0], x[1], x + 2);
+            }
+            write_state8<S, D>(a, row, dd0, lsum, A);
+        }
+        return;
+    }
     const size_t out_row0 = (static_cast<size_t>(it.b) * a.num_q_heads + h0) * D;
     for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
         const int g = idx / D;
@@ -298,10 +449,19 @@ __device__ __forceinline__ void merge_slots_and_store(const DecodeArgs& a, int b
 }
 
 // Zero output for a sequence with no tokens (written once, by partition 0's item).  With
-// keep_partials nothing: such a sequence has no partial results.
-template <int D>
+// keep_partials nothing: such a sequence has no partial results.  With a shared prefix
+// handled elsewhere (pre_parts > 0), the prefix's partial results alone.
+template <class S, int D>
 __device__ __forceinline__ void store_empty(const DecodeArgs& a, const Item& it, int G, int t0, int nt) {
-    if (it.p != 0 || a.keep_partials) return;
+    if (it.p != 0) return;
+    if (a.pre_parts > 0) {
+        const size_t row0 = static_cast<size_t>(it.b) * a.num_q_heads + it.kvh * G;
+        const float none[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int i = t0 * 8; i < G * D; i += nt * 8)
+            cascade_store8<S, D>(a, row0 + i / D, i % D, -INFINITY, 0.f, none);
+        return;
+    }
+    if (a.keep_partials) return;
     const size_t out_row0 = (static_cast<size_t>(it.b) * a.num_q_heads + it.kvh * G) * D;
     for (int i = t0; i < G * D; i += nt) a.out[out_row0 + i] = 0;
 }

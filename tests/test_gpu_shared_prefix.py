@@ -9,6 +9,11 @@ blocks (forks of one prompt: "Why AI servers waste memory, and how paging fixes 
 max-abs bar per element.  The batches come from the fork generator of workloads/
 (copy-on-write of the shared partial block, private suffixes).
 
+Both forms of the step are covered: the fused one (every suffix in one partition: the
+suffix kernel combines the prefix's partial results and writes the output) and the three
+launches with the cascade reduce (PAGEDKV_CASCADE_FUSE=0, and suffixes wider than the
+fused form takes).
+
 Covered: the 64-fork Llama-3-8B batch (bench.py's shared-prefix workload) and small
 forks over fp16 / bf16 / FP8 pools, block sizes 8-64, GQA groups 1-16, head sizes 64 and
 128, prefix splits forced to 1, 3 and 64 (more splits than stages: empty splits), suffixes
@@ -65,6 +70,10 @@ def _run(dc, prefix_blocks, append=True, workspace=None, tables=None, lens=None,
     return to_host_bits(out)
 
 
+# the fused step, and the prefix and suffix partial results combined by the cascade reduce
+FUSE = pytest.mark.parametrize("fuse", ["1", "0"], ids=["fused", "reduce"])
+
+
 def _check_bar(out_bits, ref, dtype, what):
     got = oracle.to_f64(out_bits, dtype)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
@@ -75,15 +84,17 @@ def _check_bar(out_bits, ref, dtype, what):
 
 # ------------------------------------------------------------------ the 64-fork batch
 
-def test_64_forks_of_4103_tokens_match_the_oracle():
+@FUSE
+def test_64_forks_of_4103_tokens_match_the_oracle(monkeypatch, fuse):
     """bench.py's shared-prefix workload (256 full shared blocks, a copy-on-write tail
     block, U[1, 512] private tokens), with the new tokens written by the call."""
+    monkeypatch.setenv("PAGEDKV_CASCADE_FUSE", fuse)
     cfg = config_by_name(4)
     case = make_case(cfg)
     P = _prefix_blocks(case)
     assert P == 256
     assert pk.shared_prefix_blocks(case.block_tables, case.lengths, cfg.block_size, appending=True) == P
-    _say(f"shared prefix {cfg.name}: {P} blocks")
+    _say(f"shared prefix {cfg.name}: {P} blocks, fuse {fuse}")
     dc = DeviceCase(case)
     out = _run(dc, P)
     ref, kp, vp = oracle_after_write(case)
@@ -93,11 +104,13 @@ def test_64_forks_of_4103_tokens_match_the_oracle():
     assert np.array_equal(to_host_bits(dc.pool.v_cache(0)), vp)
 
 
-def test_64_forks_relabelled_and_repeated_give_identical_bits():
+@FUSE
+def test_64_forks_relabelled_and_repeated_give_identical_bits(monkeypatch, fuse):
+    monkeypatch.setenv("PAGEDKV_CASCADE_FUSE", fuse)
     cfg = config_by_name(4)
     case = make_case(cfg)
     P = _prefix_blocks(case)
-    _say(f"shared prefix relabel {cfg.name}")
+    _say(f"shared prefix relabel {cfg.name}, fuse {fuse}")
     dc = DeviceCase(case)
     pool2, tables2, _ = relabelled(dc, seed=4004)
     first = _run(dc, P)                       # writes the new tokens into dc.pool
@@ -133,9 +146,11 @@ SMALL = [
 ]
 
 
+@FUSE
 @pytest.mark.parametrize("spec", SMALL, ids=[f"{s[0]}x{s[1]}x{s[2]}_{s[8] or s[3]}_b{s[4]}_p{s[5]}" for s in SMALL])
-def test_small_forks_match_the_oracle(monkeypatch, spec):
+def test_small_forks_match_the_oracle(monkeypatch, spec, fuse):
     hq, hkv, d, io, bs, prefix, smax, batch, kv, splits = spec
+    monkeypatch.setenv("PAGEDKV_CASCADE_FUSE", fuse)
     if splits:
         monkeypatch.setenv("PAGEDKV_CASCADE_SPLITS", splits)
     cfg = _fork_cfg(700 + hq + d + bs, hq, hkv, d, io, bs, prefix, smax, batch, kv)
@@ -143,7 +158,7 @@ def test_small_forks_match_the_oracle(monkeypatch, spec):
     assert fork_shape(cfg) == (prefix, batch, smax)
     P = _prefix_blocks(case)
     assert P == prefix // bs
-    _say(f"shared prefix {cfg.name}: {P} blocks, splits {splits or 'planned'}")
+    _say(f"shared prefix {cfg.name}: {P} blocks, splits {splits or 'planned'}, fuse {fuse}")
     dc = DeviceCase(case)
     out = _run(dc, P)
     ref, kp, vp = oracle_after_write(case)
@@ -152,10 +167,13 @@ def test_small_forks_match_the_oracle(monkeypatch, spec):
     assert np.array_equal(to_host_bits(dc.pool.v_cache(0)), vp)
 
 
-def test_sequences_shorter_than_the_prefix_and_an_all_prefix_table():
+@FUSE
+def test_sequences_shorter_than_the_prefix_and_an_all_prefix_table(monkeypatch, fuse):
     """No new tokens (they are written beforehand): some lengths are cut inside the prefix
-    (0, 1, one short of a block, the prefix exactly); then the tables are cut to the
-    prefix's entries, so no sequence has a suffix at all."""
+    (0, 1, one short of a block, the prefix exactly: in the fused form their output is the
+    prefix's partial results alone); then the tables are cut to the prefix's entries, so
+    no sequence has a suffix at all."""
+    monkeypatch.setenv("PAGEDKV_CASCADE_FUSE", fuse)
     cfg = _fork_cfg(781, 16, 4, 128, "bf16", 16, 16 * 20 + 5, 300, 9)
     case = make_case(cfg)
     P = _prefix_blocks(case)
@@ -180,8 +198,10 @@ def test_sequences_shorter_than_the_prefix_and_an_all_prefix_table():
     _check_bar(out2, ref2, cfg.dtype, "all-prefix tables")
 
 
+@FUSE
 @pytest.mark.parametrize("scale", [-0.3, 0.0])
-def test_negative_and_zero_scale(scale):
+def test_negative_and_zero_scale(monkeypatch, scale, fuse):
+    monkeypatch.setenv("PAGEDKV_CASCADE_FUSE", fuse)
     cfg = _fork_cfg(785, 32, 8, 128, "bf16", 16, 700, 300, 6)
     case = make_case(cfg)
     P = _prefix_blocks(case)
