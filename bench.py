@@ -740,6 +740,12 @@ def _main_gpu(args, workers):
         prefix_blocks = pk.shared_prefix_blocks(case.block_tables, case.lengths, cfg.block_size,
                                                 appending=fused)
     cascade = prefix_blocks > 0
+    # the library combines in the suffix kernel when the table entries after the prefix
+    # hold at most max(partition size, 1,024) tokens (else, or with PAGEDKV_CASCADE_FUSE=0,
+    # a third kernel does)
+    suffix_width = (case.block_tables.shape[1] - prefix_blocks) * cfg.block_size
+    combined_in_suffix = (cascade and 0 < suffix_width <= max(cfg.partition_size, 1024)
+                          and os.environ.get("PAGEDKV_CASCADE_FUSE", "1") != "0")
 
     # the step as a serving loop runs it: buffers checked once, one library call per step
     # (partitions, then the reduce when some sequence needs one)
@@ -757,7 +763,7 @@ def _main_gpu(args, workers):
             dstep(st)
             return
         ev_a.record(st)
-        if cascade:              # one call: the prefix pass, the suffixes and the merge
+        if cascade:              # one call: the prefix pass and the suffixes (and the merge)
             dstep(st)
             ev_b.record(st)
             return
@@ -789,7 +795,7 @@ def _main_gpu(args, workers):
     part_times = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
     part_ms = float(np.median(part_times))
     # the kernel's HBM bytes: each distinct token row once (forks of a prefix share rows);
-    # the shared-prefix step's three kernels together also write the output once
+    # the shared-prefix step's kernels together also write the output once
     kernel_bytes = nbytes["partition_kernel_unique"] + (nbytes["o"] if cascade else 0)
     logical_bytes = nbytes["partition_kernel"] + (nbytes["o"] if cascade else 0)
     achieved = kernel_bytes / (part_ms * 1e-3) / 1e9
@@ -828,8 +834,11 @@ def _main_gpu(args, workers):
         "step_frac_of_peak": nbytes["step"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("pa_prefill_mfma (dense prefix pass) + pa_partition_mfma (suffixes) + "
-                       "pa_cascade_reduce, timed together" if cascade else PARTITION_KERNEL),
+            "kernel": (("pa_prefill_mfma (dense prefix pass) + pa_partition_mfma (suffixes, "
+                        "combined with the prefix and written), timed together")
+                       if combined_in_suffix else
+                       ("pa_prefill_mfma (dense prefix pass) + pa_partition_mfma (suffixes) + "
+                        "pa_cascade_reduce, timed together") if cascade else PARTITION_KERNEL),
             "achieved": achieved,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

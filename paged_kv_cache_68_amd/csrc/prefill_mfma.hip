@@ -77,8 +77,8 @@ constexpr int kPfRuns = 2;          // 32-key runs per LDS stage (one barrier pe
 // rows of one "sequence" (token t = sequence t, all num_tokens of them), the keys are
 // positions [0, dense_len) of table row 0, and row t's causal limit is its own length:
 // it sees keys [0, min(lens[t], dense_len)).  The partial results cover the prefix only;
-// the suffix of each sequence is walked by the decode kernels and the two are combined
-// by the cascade reduce.
+// the suffix of each sequence is walked by the decode kernels, which combine the two
+// (or leave theirs for the cascade reduce).
 template <class S, int D, int W, bool KV8, bool SPLIT, bool DENSE = false>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void pa_prefill_mfma(PrefillArgs pa) {
     static_assert(!DENSE || SPLIT, "the dense form writes partial results");

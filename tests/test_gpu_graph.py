@@ -1,6 +1,6 @@
 """The decode step captured in a HIP graph (torch.cuda.graph): the launches the benchmark
 times -- the partition kernel with the new tokens written in, then the reduce, or the
-shared-prefix step's three kernels -- enqueue no memset and no host synchronisation, so
+shared-prefix step's kernels -- enqueue no memset and no host synchronisation, so
 they capture; every replay, with the program's own eager work and synchronisations
 between replays, gives the eager bits."""
 
@@ -50,10 +50,13 @@ def test_decode_step_in_a_graph(cfg_idx):
     _say(f"  {cfg.name}: 4 replays equal the eager step")
 
 
-def test_shared_prefix_step_in_a_graph():
-    """The 64-fork step through paged_attention_decode_shared_prefix (prefix pass, suffix
-    partitions with the cache write, cascade reduce): three launches, no memset, no host
+@pytest.mark.parametrize("fuse", ["1", "0"], ids=["fused", "reduce"])
+def test_shared_prefix_step_in_a_graph(monkeypatch, fuse):
+    """The 64-fork step through paged_attention_decode_shared_prefix (prefix pass, then the
+    suffix partitions with the cache write, which combine and write the output themselves,
+    or whose partial results the cascade reduce combines): no memset, no host
     synchronisation; every replay gives the eager bits."""
+    monkeypatch.setenv("PAGEDKV_CASCADE_FUSE", fuse)
     cfg = config_by_name(4)
     _say(f"graph capture, shared prefix: {cfg.name}")
     case = make_case(cfg, poison=False)
