@@ -910,7 +910,7 @@ def _main_gpu(args, workers):
         torch.cuda.synchronize()
         step_us = float(np.median([e[0].elapsed_time(e[2]) for e in ev])) * 1e3
         result["cold_cache"] = {
-            "how": "512 MiB write between steps; median of HIP-event step times (write + partitions + reduce)",
+            "how": "512 MiB write between steps; median of HIP-event times of the step alone",
             "unique_kv_bytes": footprint,
             "us_per_step": step_us,
             "seqs_per_s": cfg.batch / (step_us * 1e-6),
