@@ -167,6 +167,31 @@ def test_small_forks_match_the_oracle(monkeypatch, spec, fuse):
     assert np.array_equal(to_host_bits(dc.pool.v_cache(0)), vp)
 
 
+@pytest.mark.parametrize("spec", [SMALL[0], SMALL[1], SMALL[7]],
+                         ids=["g7_f16", "g1_bf16_valu", "g4_fp8_d64"])
+def test_fused_form_in_the_one_wave_per_item_plans(monkeypatch, spec):
+    """The fused form where each wave owns a whole suffix (PAGEDKV_SPLIT=0: the item plans
+    of the matrix-core and VALU kernels, whose waves combine and write their rows alone),
+    with some lengths cut inside the prefix (their output: the prefix's results alone)."""
+    hq, hkv, d, io, bs, prefix, smax, batch, kv, _ = spec
+    monkeypatch.setenv("PAGEDKV_CASCADE_FUSE", "1")
+    monkeypatch.setenv("PAGEDKV_SPLIT", "0")
+    cfg = _fork_cfg(760 + hq + d + bs, hq, hkv, d, io, bs, prefix, smax, batch, kv)
+    case = make_case(cfg)
+    P = _prefix_blocks(case)
+    _say(f"fused, one wave per item: {cfg.name}")
+    _, kp, vp = oracle_after_write(case)
+    lens = case.lengths.copy()
+    lens[[0, 1]] = [0, 3]
+    dc = DeviceCase(case)
+    dc.write()
+    out = _run(dc, P, append=False, lens=torch.from_numpy(lens).cuda())
+    ref = oracle.paged_decode(case.query, kp, vp, case.block_tables, lens, cfg.scale,
+                              cfg.block_size, cfg.kv, q_dtype=cfg.dtype)
+    _check_bar(out, ref, cfg.dtype, f"{cfg.name} item plans")
+    assert not oracle.to_f64(out[0], cfg.dtype).any(), "an empty sequence gets zeros"
+
+
 @FUSE
 def test_sequences_shorter_than_the_prefix_and_an_all_prefix_table(monkeypatch, fuse):
     """No new tokens (they are written beforehand): some lengths are cut inside the prefix
