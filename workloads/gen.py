@@ -96,6 +96,9 @@ def draw_lengths(cfg: DecodeConfig, rng: np.random.Generator) -> np.ndarray:
         lens = np.full(cfg.batch, 8192, dtype=np.int64)
     elif cfg.lengths == "uniform_4096":
         lens = rng.integers(1, 4096, size=cfg.batch, endpoint=True).astype(np.int64)
+    elif cfg.lengths.startswith("uniform_"):          # "uniform_<N>": U[1, N]
+        lens = rng.integers(1, int(cfg.lengths.split("_")[1]), size=cfg.batch,
+                            endpoint=True).astype(np.int64)
     else:
         raise ValueError(cfg.lengths)
     assert lens.shape == (cfg.batch,)
