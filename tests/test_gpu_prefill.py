@@ -303,3 +303,48 @@ def test_split_prompt_of_2407_tokens(monkeypatch):
                                          workspace=short)
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+# ------------------------------------------------------------------ random shapes
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_prefill_shapes(seed, monkeypatch):
+    """Seeded random shapes: 1-4 sequences with chunks of 0-300 new tokens at the end of
+    contexts of up to 1,200 positions (sometimes more queries than positions), KV heads
+    and group, head size, io type and storage, block size; the key range split over 1-8
+    work-groups by paged_attention_prefill_split (its plan) or forced."""
+    rng = np.random.default_rng(77_000 + seed)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([g for g in (1, 2, 3, 4, 7, 8, 16) if g * hkv <= 64]))
+    d = int(rng.choice([64, 128]))
+    io = str(rng.choice(["f16", "bf16"]))
+    kv = "fp8" if rng.random() < 0.3 else io
+    B = int(rng.choice([8, 16, 32, 64]))
+    chunks = []
+    for _ in range(int(rng.integers(1, 5))):
+        L = int(rng.integers(0, 1201))
+        n = int(rng.integers(0, 301))
+        chunks.append((n, L))
+    if sum(n for n, _ in chunks) == 0:
+        chunks[0] = (1, chunks[0][1])
+    splits = str(rng.choice(["plan", "1", "2", "3", "8"]))
+    if splits != "plan":
+        monkeypatch.setenv("PAGEDKV_PREFILL_SPLITS", splits)
+    _say(f"random prefill {seed}: {g * hkv}/{hkv} x {d} {io}/{kv} B{B} chunks {chunks} splits {splits}")
+    lens, qs, tables, kp, vp, q, nb = _case(chunks, B, g * hkv, hkv, d, io, kv, seed=300 + seed)
+    pool = pk.KVPool(1, nb, hkv, d, kv, block_size=B, io_dtype=io)
+    pool.k_cache(0).copy_(to_dev(kp, kv))
+    pool.v_cache(0).copy_(to_dev(vp, kv))
+    qd = to_dev(q, io)
+    out = torch.full_like(qd, 7.0)
+    maxq = int(np.max(np.diff(qs)))
+    nt = int(qs[-1])
+    ws = pk.alloc_prefill_workspace(pool, len(lens), g * hkv, nt, maxq, tables.shape[1])
+    if ws is not None:
+        ws.fill_(0xFF)
+    pk.paged_attention_prefill_split(pool, 0, out, qd, torch.from_numpy(qs).cuda(), maxq,
+                                     torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                                     scale=1.0 / math.sqrt(d), workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.paged_prefill(q, qs, kp, vp, tables, lens, 1.0 / math.sqrt(d), B, kv, q_dtype=io)
+    _check(to_host_bits(out), ref, qs, tables, lens, vp, B, kv, io, hkv)
