@@ -28,18 +28,23 @@ def to_host_bits(t) -> np.ndarray:
 
 
 class DeviceCase:
-    """A decode case resident on the GPU: pool, inputs and output buffer."""
+    """A decode case resident on the GPU: pool, inputs and output buffer.  With
+    ``num_layers`` > 1 (host cases) the case's K/V go to layer ``layer`` of the pool and
+    every other layer holds NaN bits, so a read of the wrong layer shows."""
 
-    def __init__(self, case: DecodeCase, device="cuda"):
+    def __init__(self, case: DecodeCase, device="cuda", num_layers: int = 1, layer: int = 0):
         cfg = case.cfg
         self.case = case
         self.cfg = cfg
+        self.layer = layer
         if case.where == "host":
-            self.pool = pk.KVPool(1, cfg.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.kv,
+            self.pool = pk.KVPool(num_layers, cfg.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.kv,
                                   block_size=cfg.block_size, io_dtype=cfg.dtype,
                                   device=device)
-            self.pool.k_cache(0).copy_(to_dev(case.k_pool, cfg.kv, device))
-            self.pool.v_cache(0).copy_(to_dev(case.v_pool, cfg.kv, device))
+            if num_layers > 1:
+                self.pool.memory.fill_(0xFF)     # NaN bits in fp16, bf16 and E4M3 alike
+            self.pool.k_cache(layer).copy_(to_dev(case.k_pool, cfg.kv, device))
+            self.pool.v_cache(layer).copy_(to_dev(case.v_pool, cfg.kv, device))
         else:
             # device-generated pools: adopt their memory as a one-layer pool
             k, v = case.k_pool, case.v_pool
@@ -60,7 +65,7 @@ class DeviceCase:
                                             self.tables.shape[1], cfg.partition_size)
 
     def write(self):
-        pk.reshape_and_cache(self.pool, 0, self.new_key, self.new_value, self.slots)
+        pk.reshape_and_cache(self.pool, self.layer, self.new_key, self.new_value, self.slots)
 
     def decode(self, partition_size=None):
         part = self.cfg.partition_size if partition_size is None else partition_size
@@ -68,7 +73,7 @@ class DeviceCase:
         if partition_size is not None:
             ws = pk.alloc_workspace(self.pool, self.query.shape[0], self.query.shape[1],
                                     self.tables.shape[1], part)
-        pk.paged_attention_decode(self.pool, 0, self.out, self.query, self.tables, self.lens,
+        pk.paged_attention_decode(self.pool, self.layer, self.out, self.query, self.tables, self.lens,
                                   scale=self.cfg.scale, partition_size=part, workspace=ws)
         return self.out
 
@@ -79,11 +84,11 @@ class DeviceCase:
     def step_append(self):
         """The step with the cache write folded into the partition kernel (each sequence's
         new token goes to position L - 1), then the reduce: the launches bench.py times."""
-        pk.paged_attention_partitions_append(self.pool, 0, self.out, self.query, self.new_key,
+        pk.paged_attention_partitions_append(self.pool, self.layer, self.out, self.query, self.new_key,
                                              self.new_value, self.tables, self.lens,
                                              self.cfg.scale, self.cfg.partition_size,
                                              self.workspace)
-        pk.paged_attention_reduce(self.pool, 0, self.out, self.query, self.tables, self.lens,
+        pk.paged_attention_reduce(self.pool, self.layer, self.out, self.query, self.tables, self.lens,
                                   self.cfg.scale, self.cfg.partition_size, self.workspace)
         return self.out
 
@@ -92,6 +97,6 @@ class DeviceCase:
         L = int(self.case.lengths[b])
         nblk = max(1, -(-L // self.cfg.block_size))
         ids = torch.from_numpy(self.case.block_tables[b, :nblk].astype(np.int64)).to(self.out.device)
-        kb = to_host_bits(self.pool.k_cache(0).index_select(0, ids))
-        vb = to_host_bits(self.pool.v_cache(0).index_select(0, ids))
+        kb = to_host_bits(self.pool.k_cache(self.layer).index_select(0, ids))
+        vb = to_host_bits(self.pool.v_cache(self.layer).index_select(0, ids))
         return kb, vb, np.arange(nblk)

@@ -328,13 +328,17 @@ def test_random_prefill_shapes(seed, monkeypatch):
     if sum(n for n, _ in chunks) == 0:
         chunks[0] = (1, chunks[0][1])
     splits = str(rng.choice(["plan", "1", "2", "3", "8"]))
+    layers = int(rng.integers(1, 4))
+    layer = int(rng.integers(0, layers))
     if splits != "plan":
         monkeypatch.setenv("PAGEDKV_PREFILL_SPLITS", splits)
-    _say(f"random prefill {seed}: {g * hkv}/{hkv} x {d} {io}/{kv} B{B} chunks {chunks} splits {splits}")
+    _say(f"random prefill {seed}: {g * hkv}/{hkv} x {d} {io}/{kv} B{B} chunks {chunks} splits {splits}"
+         f" layer {layer} of {layers}")
     lens, qs, tables, kp, vp, q, nb = _case(chunks, B, g * hkv, hkv, d, io, kv, seed=300 + seed)
-    pool = pk.KVPool(1, nb, hkv, d, kv, block_size=B, io_dtype=io)
-    pool.k_cache(0).copy_(to_dev(kp, kv))
-    pool.v_cache(0).copy_(to_dev(vp, kv))
+    pool = pk.KVPool(layers, nb, hkv, d, kv, block_size=B, io_dtype=io)
+    pool.memory.fill_(0xFF)                          # the other layers: NaN bits
+    pool.k_cache(layer).copy_(to_dev(kp, kv))
+    pool.v_cache(layer).copy_(to_dev(vp, kv))
     qd = to_dev(q, io)
     out = torch.full_like(qd, 7.0)
     maxq = int(np.max(np.diff(qs)))
@@ -342,7 +346,7 @@ def test_random_prefill_shapes(seed, monkeypatch):
     ws = pk.alloc_prefill_workspace(pool, len(lens), g * hkv, nt, maxq, tables.shape[1])
     if ws is not None:
         ws.fill_(0xFF)
-    pk.paged_attention_prefill_split(pool, 0, out, qd, torch.from_numpy(qs).cuda(), maxq,
+    pk.paged_attention_prefill_split(pool, layer, out, qd, torch.from_numpy(qs).cuda(), maxq,
                                      torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
                                      scale=1.0 / math.sqrt(d), workspace=ws)
     torch.cuda.synchronize()
