@@ -269,10 +269,11 @@ __device__ __forceinline__ void cascade_store8(const DecodeArgs& a, size_t row, 
 
 // One wave writes the result of partition p of its item from a staging area in LDS
 // (st_acc[G][D] accumulators, st_ml[G][2] running max / sum): the final output if the
-// sequence has a single partition, else the fp32 partials.  All 64 lanes take part, each
-// with 16-byte accesses, so the global writes are whole contiguous lines.  `whole`: the
-// state covers every partition of the sequence; kept as a partial result (keep_partials)
-// it is the only one, at slot 0 of rows [B][Hkv][1][G].
+// sequence has a single partition (combined first with a shared prefix's partial results
+// when pre_parts > 0), else the fp32 partials.  All 64 lanes take part, each with 16-byte
+// accesses, so the global writes are whole contiguous lines.  `whole`: the state covers
+// every partition of the sequence; kept as a partial result (keep_partials) it is the
+// only one, at slot 0 of rows [B][Hkv][1][G].
 template <class S, int D>
 __device__ __forceinline__ void store_partition(const DecodeArgs& a, const Item& it, int G, int p,
                                                 const float* st_acc, const float* st_ml, int lane,
@@ -314,7 +315,8 @@ __device__ __forceinline__ void store_partition(const DecodeArgs& a, const Item&
 // Four waves that shared one item have left their (m, l) in sm_ml[W][G][2] and their
 // accumulators in sm_acc[W][G][D] (dimension order); merge them with the cross-block
 // rule and write the partition's result: the final output if the sequence has a single
-// partition, else the fp32 partials (m, l, acc) for the reduce kernel.
+// partition (combined first with a shared prefix's partial results when pre_parts > 0),
+// else the fp32 partials (m, l, acc) for the reduce kernel.
 template <class S, int D>
 __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const Item& it, int G,
                                                       float* sm_ml, float* sm_acc) {
@@ -341,7 +343,9 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeArgs& a, const
         float accq[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) accq[k] = 0.f;
-        if (active) fold_prefix8<D>(a, row, dd0, min(a.pre_parts, qi * per), min(a.pre_parts, (qi + 1) * per), Mq, Lq, accq);
+        if (active)
+            fold_prefix8<D>(a, row, dd0, min(a.pre_parts, qi * per), min(a.pre_parts, (qi + 1) * per),
+                            Mq, Lq, accq);
         float M = -INFINITY, lsum = 0.f;
         float A[8];
 #pragma unroll
