@@ -617,7 +617,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 100 untimed steps: the step time settles after a few dozen (the host-side launch path
+    # warms up; the kernel itself is steady from the first steps)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="c3", help="workload: c1..c5 or a config name")
     ap.add_argument("--block-size", type=int, default=None,
                     help="rebuild the workload with this block size (8, 16, 32, 64); the pool "
