@@ -70,6 +70,14 @@ constexpr int kPfRowsPerWave = 32;  // two 16-row column blocks
 
 constexpr int kPfRuns = 2;          // 32-key runs per LDS stage (one barrier per stage)
 
+// A split launch gives each row tile its own number of key-range splits: at most the
+// planned count, and no more than leave every split at least this many 64-key stages.
+// A tile with one split writes its rows' output itself and needs no merge.
+constexpr int kMinSplitStages = 4;
+__device__ __forceinline__ int tile_splits(int planned, int nstages) {
+    return min(planned, max(1, nstages / kMinSplitStages));
+}
+
 // SPLIT: pa.splits work-groups share each row tile's key stages, each taking an equal
 // run of them and writing its rows' unnormalised partial results (acc, m, l) for
 // pa_prefill_merge to combine.
@@ -448,10 +456,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     };
 
     // ---- this work-group's stages [j_lo, j_hi): all of them, or its split's equal run
+    int nsplit = 1;                              // this row tile's splits
     if constexpr (!DENSE) {
         j_hi = nstages;
         if constexpr (SPLIT) {
-            const int per = (nstages + pa.splits - 1) / pa.splits;
+            nsplit = tile_splits(pa.splits, nstages);
+            if (split >= nsplit) return;         // the whole work-group: before any barrier
+            const int per = (nstages + nsplit - 1) / nsplit;
             j_lo = min(nstages, split * per);
             j_hi = min(nstages, j_lo + per);
         }
@@ -511,9 +522,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                     make_float4(m[cb], lacc[cb][0], ldexpf(1.f, x - 14), 0.f);
         }
         return;
-    } else if constexpr (SPLIT) {
+    } else if (SPLIT && nsplit > 1) {
         // partial results: lane (n, c) holds elements 16 e + 4 c + rr of row n; (m, l) as
-        // the running maximum (base-2 units, -inf if no key was seen) and weight sum
+        // the running maximum (base-2 units, -inf if no key was seen) and weight sum (a
+        // tile with one split falls through to the output below)
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb) {
             const int r = row_base + cb * 16 + n;
@@ -570,6 +582,12 @@ __global__ __launch_bounds__(256) void pa_prefill_merge(PrefillArgs pa) {
     const int q0 = pa.qstart[b];
     const int rows = (pa.qstart[b + 1] - q0) * G;
     const int tile_rows = 32 * pa.waves;
+    // the tile's split count, as the main kernel takes it; a tile of one split wrote its
+    // output itself
+    const int nq = pa.qstart[b + 1] - q0;
+    const int tile_last = clamped_length(a, b) - nq + (min(rows, (rt + 1) * tile_rows) - 1) / G;
+    const int nsplit = tile_splits(pa.splits, tile_last >= 0 ? tile_last / (32 * kPfRuns) + 1 : 0);
+    if (nsplit <= 1) return;
     const int r = rt * tile_rows + sub * 16 + static_cast<int>(threadIdx.x >> 4);
     if (r >= min(rows, (rt + 1) * tile_rows)) return;
     const int t = r / G;
@@ -577,9 +595,9 @@ __global__ __launch_bounds__(256) void pa_prefill_merge(PrefillArgs pa) {
     const int g = r - t * G;
     const int64_t row = static_cast<int64_t>(q0 + t) * a.num_q_heads + kvh * G + g;
     const int l16 = threadIdx.x & 15;
-    const int S_ = pa.splits;
-    const float2* ml = reinterpret_cast<const float2*>(pa.ws_ml) + row * S_;
-    const float* acc = pa.ws_acc + row * S_ * D + PER * l16;
+    const int S_ = nsplit;                       // of pa.splits slots per row
+    const float2* ml = reinterpret_cast<const float2*>(pa.ws_ml) + row * pa.splits;
+    const float* acc = pa.ws_acc + row * pa.splits * D + PER * l16;
     float2 v[kMaxPrefillSplits];
     float x[kMaxPrefillSplits][PER];
 #pragma unroll
