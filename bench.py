@@ -639,6 +639,8 @@ def main(argv=None):
     ap.add_argument("--separate-write", action="store_true",
                     help="launch reshape_and_cache on its own instead of folding the cache "
                          "write into the partition kernel")
+    ap.add_argument("--longest-first", action="store_true",
+                    help="build the decode batch longest sequence first (kv_decode_order)")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="for a batch of forks of one prefix, time the plain decode instead of "
                          "paged_attention_decode_shared_prefix")
@@ -717,6 +719,14 @@ def _main_gpu(args, workers):
         cfg = dataclasses.replace(cfg, kv_dtype=args.kv_dtype, name=f"{cfg.name}_{args.kv_dtype}kv")
     print(f"[bench] building {cfg.name} on the device", file=sys.stderr, flush=True)
     case = make_case(cfg, where="device" if cfg.index in (3, 5) else "host", poison=False)
+    if args.longest_first:
+        # the batch built in kv_decode_order's order (a scheduler's choice; the pools and
+        # every sequence's data are unchanged)
+        import dataclasses
+        order = pk.decode_order(case.lengths)
+        case = dataclasses.replace(case, lengths=case.lengths[order], block_tables=case.block_tables[order],
+                                   slot_mapping=case.slot_mapping[order], query=case.query[order],
+                                   new_key=case.new_key[order], new_value=case.new_value[order])
     dc = DeviceCase(case)
     nbytes = algorithmic_bytes(case.lengths, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
                                cfg.elem_bytes, 2, cfg.block_size, tables=case.block_tables)
@@ -831,6 +841,7 @@ def _main_gpu(args, workers):
                      f"{prefix_blocks} shared blocks)" if cascade else
                      "paged_attention_partitions_append (cache write folded in) + reduce" if fused
                      else "reshape_and_cache + paged_attention (partitions + reduce)"),
+            "batch_order": "longest first (kv_decode_order)" if args.longest_first else "as generated",
         },
         "step_hbm_gbps": nbytes["step"] / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": nbytes["step"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,

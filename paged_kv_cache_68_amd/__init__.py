@@ -450,6 +450,20 @@ def shared_prefix_blocks(tables, lengths, block_size=BLOCK_SIZE, appending=False
     return r
 
 
+def decode_order(lengths):
+    """A batch order for a decode step (kv_decode_order): the indices of the host
+    ``lengths`` ([B] int32, numpy or CPU tensor) by length, longest first, ties in batch
+    order.  Build the step's batch in this order (queries, tables, lengths, outputs alike)."""
+    import numpy as np
+    n = np.ascontiguousarray(np.asarray(lengths), dtype=np.int32)
+    if n.ndim != 1:
+        raise ValueError(f"decode_order: lengths must be one-dimensional, not {n.shape}")
+    order = np.empty(n.shape[0], dtype=np.int32)
+    if int(lib().kv_decode_order(n.ctypes.data, int(n.shape[0]), order.ctypes.data)) != 0:
+        raise ValueError("decode_order: invalid arguments")
+    return order
+
+
 def shared_prefix_workspace_bytes(pool: KVPool, batch, num_q_heads, max_blocks_per_seq,
                                   prefix_blocks, partition_size=0) -> int:
     """Workspace bytes of paged_attention_decode_shared_prefix for this shape on the

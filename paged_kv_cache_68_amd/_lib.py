@@ -86,6 +86,7 @@ SIGNATURES = {
                                                     _i32, _i32, _f32, _i32, _i32, _vp, _sz, _vp]),
     "paged_attention_shared_prefix_workspace_bytes": (_sz, [_pool, _i32, _i32, _i32, _i32, _i32]),
     "kv_shared_prefix_blocks": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32]),
+    "kv_decode_order": (_i32, [_vp, _i32, _vp]),
     "kv_pool_gather": (_i32, [_pool, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
     "kv_copy_blocks": (_i32, [_pool, _vp, _i32, _vp]),
     "kv_host_pool_create": (_i32, [ctypes.POINTER(KVPoolDesc), _vp, _sz, ctypes.POINTER(_pool)]),

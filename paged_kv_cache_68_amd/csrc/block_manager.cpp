@@ -359,4 +359,13 @@ int32_t kv_shared_prefix_blocks(const int32_t* tables, const int32_t* lengths, i
     return p;
 }
 
+// A batch order for a decode step: the sequences by length, longest first, ties in batch
+// order (see include/pagedkv.h).
+int32_t kv_decode_order(const int32_t* lengths, int32_t batch, int32_t* order) {
+    if (!lengths || !order || batch < 0) return -1;
+    for (int32_t i = 0; i < batch; ++i) order[i] = i;
+    std::stable_sort(order, order + batch, [&](int32_t x, int32_t y) { return lengths[x] > lengths[y]; });
+    return 0;
+}
+
 }  // extern "C"
