@@ -4,6 +4,7 @@ oracle: packed chunks of several sequences, causal rows over paged K/V, every bl
 and chunks with more queries than positions."""
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -307,7 +308,8 @@ def test_split_prompt_of_2407_tokens(monkeypatch):
 
 # ------------------------------------------------------------------ random shapes
 
-@pytest.mark.parametrize("seed", range(12))
+# PAGEDKV_TEST_RANDOM_CASES=n widens the sweep (default 12 cases)
+@pytest.mark.parametrize("seed", range(int(os.environ.get("PAGEDKV_TEST_RANDOM_CASES", "0")) or 12))
 def test_random_prefill_shapes(seed, monkeypatch):
     """Seeded random shapes: 1-4 sequences with chunks of 0-300 new tokens at the end of
     contexts of up to 1,200 positions (sometimes more queries than positions), KV heads

@@ -11,6 +11,8 @@ split, item and group plans, the matrix-core and VALU kernels) fall where they m
 fork cases draw a prefix of 1-1,500 tokens and private suffixes of U[1, 1-1,200] tokens
 (fused or with the reduce, as the table width decides)."""
 
+import os
+
 import numpy as np
 import pytest
 
@@ -24,6 +26,10 @@ from workloads import make_case  # noqa: E402
 from workloads.configs import DecodeConfig  # noqa: E402
 
 from .gpu_helpers import DeviceCase, flat_bar, oracle_after_write, to_host_bits  # noqa: E402
+
+
+# PAGEDKV_TEST_RANDOM_CASES=n widens both sweeps (default 24 decode and 12 fork cases)
+_N = int(os.environ.get("PAGEDKV_TEST_RANDOM_CASES", "0"))
 
 
 def _say(msg):
@@ -71,7 +77,7 @@ def _desc(cfg, layers, layer):
             f" layer {layer} of {layers}")
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(_N or 24))
 def test_random_decode_shapes(seed):
     layers, layer, cfg = _draw(seed, fork=False)
     _say(_desc(cfg, layers, layer))
@@ -84,14 +90,15 @@ def test_random_decode_shapes(seed):
     assert np.array_equal(to_host_bits(dc.pool.v_cache(layer)), vp)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(_N or 12))
 def test_random_fork_shapes(seed):
     layers, layer, cfg = _draw(seed, fork=True)
     _say(_desc(cfg, layers, layer))
     case = make_case(cfg)
     P = len(case.shared_blocks)
-    # (a single sequence shares any number of its own blocks: the generator's prefix is one)
-    assert 0 < P <= pk.shared_prefix_blocks(case.block_tables, case.lengths, cfg.block_size,
+    # (a single sequence shares any number of its own blocks: the generator's prefix is one;
+    # a prefix shorter than one block shares none, and the call is then the plain step)
+    assert 0 <= P <= pk.shared_prefix_blocks(case.block_tables, case.lengths, cfg.block_size,
                                             appending=True)
     dc = DeviceCase(case, num_layers=layers, layer=layer)
     n = pk.shared_prefix_workspace_bytes(dc.pool, cfg.batch, cfg.num_q_heads,
