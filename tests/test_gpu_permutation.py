@@ -130,7 +130,10 @@ def test_reported_variants_full_size_against_the_oracle(idx, bs, kv):
     dc = _device_case(cfg)
     lens = dc.case.lengths
     order = np.argsort(lens, kind="stable")
-    seqs = sorted({int(order[0]), int(order[-1]), *[int(x) for x in order[:: max(1, cfg.batch // 6)]]})
+    if cfg.batch <= 64:                         # the 64 x 8,192 batch: every sequence
+        seqs = list(range(cfg.batch))
+    else:                                       # shortest, longest and every 8th by length
+        seqs = sorted({int(order[0]), int(order[-1]), *[int(x) for x in order[::8]]})
     _say(f"full size {cfg.name}: oracle on sequences {seqs}")
     out = _step(dc.pool, dc, dc.tables, torch.empty_like(dc.query))
     ref = oracle_for_seqs(dc, seqs)
