@@ -144,6 +144,7 @@ pkv::DecodeArgs make_args(const kv_pool_t* pool, int32_t layer, void* out, const
     a.pre_acc = nullptr;
     a.pre_ml = nullptr;
     a.pre_parts = 0;
+    a.order = nullptr;
     a.num_blocks = d.num_blocks;
     a.block_size = d.block_size;
     a.tile_tokens = d.block_size < pkv::kTile ? d.block_size : pkv::kTile;

@@ -71,6 +71,8 @@ struct DecodeArgs {
                              // cache holds (the plan's input; the hint can be overridden)
     int32_t layer_bytes;     // bytes of this layer's K (and V) cache if at most 0x7FF00000,
                              // else 0: lets a wave address any block with 32-bit offsets
+    const int32_t* order;    // [B] or null: the group plan's work-groups take sequences in
+                             // this order (longest first) instead of batch order
 };
 
 // Multi-token (prefill) attention: the decode arguments (queries and outputs are

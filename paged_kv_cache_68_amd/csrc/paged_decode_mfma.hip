@@ -198,6 +198,44 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, int b, int kvh
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// The batch's sequences longest first, for the group plan's work-groups: a counting sort
+// of the lengths in tiles, scaled into kOrderBuckets keys, in one work-group.  Sequences
+// with equal keys land in an unspecified order among themselves; which work-group takes a
+// sequence changes no result.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderBuckets = 2 * kOrderThreads;
+__global__ __launch_bounds__(kOrderThreads) void pa_length_order(DecodeArgs a, int32_t* order) {
+    __shared__ int start[kOrderBuckets];
+    __shared__ int scan[kOrderThreads];
+    const int tid = threadIdx.x;
+    const int64_t max_tiles = static_cast<int64_t>(a.max_blocks) << a.tiles_log2;
+    auto key = [&](int b) {                      // 0 for the longest
+        const int64_t tiles = (clamped_length(a, b) + a.tile_tokens - 1) / a.tile_tokens;
+        const int64_t k = tiles * (kOrderBuckets - 1) / (max_tiles > 0 ? max_tiles : 1);
+        return kOrderBuckets - 1 - static_cast<int>(k < kOrderBuckets - 1 ? k : kOrderBuckets - 1);
+    };
+    for (int i = tid; i < kOrderBuckets; i += kOrderThreads) start[i] = 0;
+    __syncthreads();
+    for (int b = tid; b < a.batch; b += kOrderThreads) atomicAdd(&start[key(b)], 1);
+    __syncthreads();
+    // exclusive prefix sum over the buckets, two per thread
+    const int h0 = start[2 * tid];
+    const int own = h0 + start[2 * tid + 1];
+    scan[tid] = own;
+    __syncthreads();
+    for (int off = 1; off < kOrderThreads; off <<= 1) {
+        const int v = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    const int before = scan[tid] - own;
+    start[2 * tid] = before;
+    start[2 * tid + 1] = before + h0;
+    __syncthreads();
+    for (int b = tid; b < a.batch; b += kOrderThreads) order[atomicAdd(&start[key(b)], 1)] = b;
+}
+
 template <class S, int D, int MODE, bool NT, bool KV8, bool PAIR = false>
 __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, int n_items,
                                                          int per_item, int ppw, int heads) {
@@ -221,8 +259,9 @@ __global__ __launch_bounds__(512) void pa_partition_mfma(DecodeArgs a, int G, in
         const int ngrp = a.num_kv_heads / heads;
         const int rest = group_id / ngrp;
         chunk_id = rest / a.batch;
-        it = group_item(a, rest % a.batch, (group_id % ngrp) * heads + wave % heads, chunk_id,
-                        per_item, wave / heads, ppw);
+        const int b = a.order ? a.order[rest % a.batch] : rest % a.batch;
+        it = group_item(a, b, (group_id % ngrp) * heads + wave % heads, chunk_id, per_item,
+                        wave / heads, ppw);
         // both exits below are the same for the whole work-group (same sequence, chunk)
         if (it.L == 0) {
             if (it.p == 0) store_empty<S, D>(a, it, G, lane, 64);
@@ -507,6 +546,21 @@ hipError_t launch_t(int group, const DecodeArgs& a, hipStream_t stream) {
         DecodeArgs g = a;
         g.xcd_chunk = 0;
         const int64_t wgs = static_cast<int64_t>(a.batch) * (a.num_kv_heads / pl.heads) * pl.chunks;
+        // Whole sequences per work-group (one chunk, so no partial results in the
+        // workspace) in many rounds of work-groups: the sequences go longest first, so
+        // that the longest do not start last and run alone at the end.  The order sits at
+        // the start of the workspace (at least B * Hq * 2 * (D + 2) floats whenever the
+        // plan has more than one partition).  PAGEDKV_ORDER=0 keeps batch order, =1 orders
+        // whenever the plan allows it.
+        const char* eo = getenv("PAGEDKV_ORDER");
+        const int64_t resident = group_target_waves<S, D, KV8>() / pl.group_waves;
+        const bool may_order = pl.chunks == 1 && a.ws_acc != nullptr && a.batch > 1 &&
+                               !a.keep_partials && a.pre_parts == 0;
+        if (may_order && (eo ? eo[0] == '1' : wgs > 2 * resident)) {
+            int32_t* order = reinterpret_cast<int32_t*>(a.ws_acc);
+            hipLaunchKernelGGL(pa_length_order, dim3(1), dim3(kOrderThreads), 0, stream, a, order);
+            g.order = order;
+        }
         // 8-token blocks go two to a tile when one resource can reach the whole layer
         const bool pair = a.block_size == 8 && a.layer_bytes > 0 && !getenv_is0("PAGEDKV_PAIR");
         auto kernel = pair ? (a.stream_loads ? pa_partition_mfma<S, D, kGroup, true, KV8, true>

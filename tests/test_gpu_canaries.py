@@ -56,7 +56,9 @@ def _pool(nb, hkv, d, dtype, B=16, layers=1, host=False, seed=0):
 
 PLANS = [{}, {"PAGEDKV_SPLIT": "1"}, {"PAGEDKV_SPLIT": "0", "PAGEDKV_GROUP": "0"},
          {"PAGEDKV_SPLIT": "0", "PAGEDKV_GROUP_HEADS": "2", "PAGEDKV_GROUP_SLOTS": "2", "PAGEDKV_GROUP_PPW": "1"},
-         {"PAGEDKV_KERNEL": "valu"}]
+         {"PAGEDKV_KERNEL": "valu"},
+         {"PAGEDKV_SPLIT": "0", "PAGEDKV_GROUP_HEADS": "1", "PAGEDKV_GROUP_SLOTS": "8", "PAGEDKV_GROUP_PPW": "2",
+          "PAGEDKV_ORDER": "1"}]
 
 
 @pytest.mark.parametrize("plan", range(len(PLANS)))

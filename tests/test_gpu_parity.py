@@ -381,6 +381,53 @@ def test_streaming_loads_give_identical_bits(group, monkeypatch):
     assert max_abs_err(outs[1], ref, "bf16") <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("hq,hkv,d,dtype,heads,slots,ppw", [
+    (32, 8, 128, "bf16", 1, 4, 3), (32, 8, 128, "bf16", 2, 2, 5), (8, 8, 128, "f16", 2, 2, 5)])
+def test_longest_first_order_gives_identical_bits(hq, hkv, d, dtype, heads, slots, ppw, monkeypatch):
+    """Group plans with one chunk per sequence may take the sequences longest first (a
+    one-work-group kernel writes the order into the workspace, PAGEDKV_ORDER=1 forces
+    it): the same bits as in batch order, and the oracle's values."""
+    monkeypatch.setenv("PAGEDKV_SPLIT", "0")
+    monkeypatch.setenv("PAGEDKV_GROUP_HEADS", str(heads))
+    monkeypatch.setenv("PAGEDKV_GROUP_SLOTS", str(slots))
+    monkeypatch.setenv("PAGEDKV_GROUP_PPW", str(ppw))
+    lens = [1, 15, 16, 17, 511, 512, 513, 1024, 1025, 2000, 0, 4500, 33, 4500, 7]
+    cfg, lens, tables, kp, vp, q = _custom_case(lens, hq=hq, hkv=hkv, d=d, dtype=dtype, seed=15)
+    outs = {}
+    for order in ("0", "1"):
+        monkeypatch.setenv("PAGEDKV_ORDER", order)
+        outs[order] = _run_custom(cfg, lens, tables, kp, vp, q, 512)
+    assert np.array_equal(outs["0"], outs["1"])
+    ref = oracle.paged_decode(q, kp, vp, tables, lens, cfg.scale, 16, dtype)
+    assert max_abs_err(outs["1"], ref, dtype) <= TOL[dtype]
+    assert not outs["1"][10].any()
+
+
+@pytest.mark.parametrize("kv", ["", "fp8"])
+def test_longest_first_order_on_a_ragged_batch(kv, monkeypatch):
+    """300 sequences of U[1, 1,500] tokens, MHA heads (the group plan with whole
+    sequences per work-group), the cache write folded in: longest first (forced) and
+    batch order give the same bits, the pool the oracle's bytes, the output the oracle's
+    values to the flat bar."""
+    cfg = DecodeConfig(index=7100, name="ragged_mha_b300", num_q_heads=8, num_kv_heads=8,
+                       head_dim=128, dtype="f16", block_size=16, num_blocks=300 * 94 + 16,
+                       batch=300, lengths="uniform_1500", partition_size=512,
+                       description="ragged MHA batch", kv_dtype=kv)
+    case = make_case(cfg)
+    outs = {}
+    for order in ("0", "1"):
+        monkeypatch.setenv("PAGEDKV_ORDER", order)
+        dc = DeviceCase(case)
+        outs[order] = to_host_bits(dc.step_append())
+    assert np.array_equal(outs["0"], outs["1"])
+    ref, kp, vp = oracle_after_write(case)
+    got = oracle.to_f64(outs["1"], cfg.dtype)
+    _say(f"ragged batch{' fp8' if kv else ''}: max abs err {np.abs(got - ref).max():.3e}")
+    assert np.all(np.abs(got - ref) <= flat_bar(ref, cfg.dtype))
+    assert np.array_equal(to_host_bits(dc.pool.k_cache(0)), kp)
+    assert np.array_equal(to_host_bits(dc.pool.v_cache(0)), vp)
+
+
 # ------------------------------------------------------------------ long contexts
 
 @pytest.mark.parametrize("plan", [{}, {"PAGEDKV_GROUP": "0"}, {"PAGEDKV_SPLIT": "1"}])

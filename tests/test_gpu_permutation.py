@@ -81,6 +81,7 @@ CASES = [
     ("c3_b8_paired", 3, 8, None, {}),
     ("c3_fp8", 3, None, "fp8", {}),
     ("c5_g1", 5, None, None, {}),
+    ("c5_g1_batch_order", 5, None, None, {"PAGEDKV_ORDER": "0"}),
     ("c5_fp8", 5, None, "fp8", {}),
     ("c2_split", 2, None, None, {}),
     ("c4_shared_prefix", 4, None, None, {}),
