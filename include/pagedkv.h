@@ -222,7 +222,12 @@ size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
  *                 rule ("PagedAttention and Virtual Memory Management", section 4,
  *                 cross-block reduction): inside the partition kernel, through LDS,
  *                 when one work-group holds all of a sequence's partitions, otherwise
- *                 by a second kernel over partial results in the workspace.
+ *                 by a second kernel over partial results in the workspace.  When
+ *                 work-groups hold whole sequences and the batch needs several rounds of
+ *                 them, a one-work-group kernel first writes the sequences' order by
+ *                 length, longest first, to the start of the workspace, and the
+ *                 work-groups take the sequences in that order (so the longest do not
+ *                 start last); the results do not depend on the order.
  *  workspace    : >= paged_attention_workspace_bytes(...) bytes of device memory,
  *                 256-byte aligned (else KV_ERR_INVALID_ARG); contents on entry do not
  *                 matter.
@@ -354,19 +359,22 @@ int32_t kv_shared_prefix_blocks(const int32_t* tables, const int32_t* lengths, i
  * with one partition counted too).  With prefix_blocks == 0,
  * paged_attention_workspace_bytes.
  * SIZE_MAX for invalid arguments (null or host pool, sizes out of range). */
-/* A batch order for a decode step whose sequences differ in length: the indices of
- * `lengths` (host array, [batch] int32) sorted by length, longest first, equal lengths in
- * batch order, written to `order` (host, [batch] int32).  The decode kernels take their
- * work in batch order, so a batch built in this order (queries, tables, lengths and
- * outputs permuted alike) leaves the shortest work for the end of the launch, when the
- * GPU is draining.  A scheduling aid for callers that build the batch, not an operation
- * the pages define; the attention's result per sequence does not depend on the order.
- * Returns 0, or -1 for null pointers or batch < 0.  Reads and writes host memory only. */
-int32_t kv_decode_order(const int32_t* lengths, int32_t batch, int32_t* order);
 
 size_t paged_attention_shared_prefix_workspace_bytes(const kv_pool_t* pool, int32_t batch,
                                                      int32_t num_q_heads, int32_t max_blocks_per_seq,
                                                      int32_t prefix_blocks, int32_t partition_size);
+
+/* A batch order for a decode step whose sequences differ in length: the indices of
+ * `lengths` (host array, [batch] int32) sorted by length, longest first, equal lengths in
+ * batch order, written to `order` (host, [batch] int32).  Most launch plans take their
+ * work in batch order (large batches of whole sequences per work-group order themselves,
+ * see paged_attention_decode), so a batch built in this order (queries, tables, lengths
+ * and outputs permuted alike) leaves the shortest work for the end of the launch, when
+ * the GPU is draining.  A scheduling aid for callers that build the batch, not an
+ * operation the pages define; the attention's result per sequence does not depend on the
+ * order.  Returns 0, or -1 for null pointers or batch < 0.  Reads and writes host memory
+ * only. */
+int32_t kv_decode_order(const int32_t* lengths, int32_t batch, int32_t* order);
 
 /* Bytes of the scratch array the library keeps on each GPU for
  * paged_attention_decode_noalloc (64 MiB). */
