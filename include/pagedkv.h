@@ -359,7 +359,6 @@ int32_t kv_shared_prefix_blocks(const int32_t* tables, const int32_t* lengths, i
  * with one partition counted too).  With prefix_blocks == 0,
  * paged_attention_workspace_bytes.
  * SIZE_MAX for invalid arguments (null or host pool, sizes out of range). */
-
 size_t paged_attention_shared_prefix_workspace_bytes(const kv_pool_t* pool, int32_t batch,
                                                      int32_t num_q_heads, int32_t max_blocks_per_seq,
                                                      int32_t prefix_blocks, int32_t partition_size);
